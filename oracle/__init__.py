@@ -1,0 +1,118 @@
+"""CPU oracle for the SparCML hot path (error-feedback Top-k, 4-bit stochastic
+quantization, sparse reduction with the dense switch).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by ``__graft_entry__.smoke()``
+and by the bench's ``cpu_baseline`` leg, never by the product package. It
+shares no code with the HIP path. The arithmetic lives in ``oracle.cpp``; this
+module only marshals numpy arrays through ctypes.
+
+Parity status per function (what pins it is in each C function's header):
+  topk_ef   pinned (brute force, characterisation, special cases, EF identity)
+  philox    pinned (rocRAND's Philox-4x32-10 engine, compared in a test)
+  q4 / dq4  pinned by invariants and unbiasedness; the exact code stream is
+            fixed by the reading documented in oracle.cpp
+  reduce    pinned (np.bincount / np.unique, overlap extremes, switch at T)
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build(force=True)
+        L = ctypes.CDLL(path)
+        u32, u64, f64, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
+        L.oracle_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp]
+        L.oracle_topk_ef.restype = None
+        L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_q4.argtypes = [u32, u64, u32, u64, u32, vp, vp, vp]
+        L.oracle_q4.restype = None
+        L.oracle_dq4.argtypes = [u32, u64, u32, vp, vp, vp]
+        L.oracle_dq4.restype = None
+        L.oracle_reduce.argtypes = [u32, u64, f64, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_reduce.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def topk_ef(grad, residual, k):
+    """grad, residual: [P, N] float32. Returns (idx [P,k] u32, val [P,k] f32,
+    r_new [P,N] f32). The inputs are not modified."""
+    g = _c(grad, np.float32)
+    r = _c(residual, np.float32).copy()
+    assert g.ndim == 2 and g.shape == r.shape
+    P, N = g.shape
+    k = int(k)
+    assert 0 <= k <= N
+    idx = np.zeros((P, k), np.uint32)
+    val = np.zeros((P, k), np.float32)
+    lib().oracle_topk_ef(P, N, k, _ptr(g), _ptr(r), _ptr(idx), _ptr(val))
+    return idx, val, r
+
+
+def philox4x32_10(counter, key):
+    c = np.ascontiguousarray(counter, np.uint32)
+    kk = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oracle_philox4x32_10(_ptr(c), _ptr(kk), _ptr(out))
+    return out
+
+
+def q4(val, bucket, seed, step):
+    """val: [P, n] float32 -> (codes [P, ceil(n/2)] u8, scales [P, ceil(n/bucket)] f32)."""
+    v = _c(val, np.float32)
+    P, n = v.shape
+    codes = np.zeros((P, (n + 1) // 2), np.uint8)
+    scales = np.zeros((P, (n + bucket - 1) // bucket), np.float32)
+    lib().oracle_q4(P, n, int(bucket), int(seed), int(step), _ptr(v), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dq4(codes, scales, n, bucket):
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.float32)
+    P = c.shape[0]
+    out = np.zeros((P, n), np.float32)
+    lib().oracle_dq4(P, n, int(bucket), _ptr(c), _ptr(s), _ptr(out))
+    return out
+
+
+def reduce(offsets, idx, val, N, delta):
+    """offsets: [P+1] u64 (node p owns [offsets[p], offsets[p+1])), idx u32, val f32.
+    Returns (K, is_dense, out_idx, out_val): dense -> out_idx empty, out_val [N];
+    sparse -> out_idx [K] ascending, out_val [K]."""
+    off = _c(offsets, np.uint64)
+    ii = _c(idx, np.uint32)
+    vv = _c(val, np.float32)
+    P = off.shape[0] - 1
+    out_idx = np.zeros(max(N, 1), np.uint32)
+    out_val = np.zeros(max(N, 1), np.float32)
+    K = np.zeros(1, np.uint64)
+    dense = np.zeros(1, np.uint32)
+    rc = lib().oracle_reduce(P, N, float(delta), _ptr(off), _ptr(ii), _ptr(vv), _ptr(K),
+                             _ptr(dense), _ptr(out_idx), _ptr(out_val))
+    if rc != 0:
+        raise ValueError("oracle_reduce: an index is >= N")
+    K = int(K[0])
+    if dense[0]:
+        return K, True, np.zeros(0, np.uint32), out_val[:N].copy()
+    return K, False, out_idx[:K].copy(), out_val[:K].copy()

@@ -1,0 +1,163 @@
+"""Seeded synthetic workloads for the hot path.
+
+This module holds only input generation: no step of the method's arithmetic.
+Both the HIP path and the CPU oracle consume what it produces (the oracle gets
+host copies). Every seed is a documented pure function of
+(workload, node, step); see ``seed_of``.
+
+The five workloads stand in for the gradient sizes and value distributions
+that the SparCML experiments imply (ResNet20 on CIFAR-10, an LSTM/ASR model,
+URL-style sparse features, a wide ResNet on ImageNet); no dataset or trained
+weights are involved.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    N: int                   # gradient length per node (feature dimension for sparse input)
+    P: int                   # nodes whose contributions sit in this GPU's HBM
+    delta: float             # dense switch: result dense iff K >= ceil(delta * N)
+    steps: int               # error-feedback steps
+    kind: str                # "gauss" | "segments" | "laplace" | "zipf"
+    k: int = 0               # Top-k per node (0 for already-sparse input)
+    scale: float = 1.0       # std (gauss, segments base) or Laplace b
+    nnz: int = 0             # per-node nonzeros of already-sparse input
+    zipf_s: float = 0.0
+    segments: int = 0        # number of layer segments (kind == "segments")
+    q4_bucket: int = 0       # 0: no quantization
+    wid: int = 0             # workload id used in seeds
+
+    @property
+    def has_topk(self) -> bool:
+        return self.kind != "zipf"
+
+    def threshold(self) -> float:
+        return math.ceil(self.delta * float(self.N))
+
+
+def frac_k(N: int, num: int, den: int) -> int:
+    """k = floor(N * num / den) in exact integer arithmetic (1% -> 1/100)."""
+    return (N * num) // den
+
+
+def _w0(N=65536, P=4):
+    return Workload("gauss65536_p4_k1pct", N, P, 0.25, 1, "gauss", k=frac_k(N, 1, 100), wid=0)
+
+
+def _w1(N=272474, P=16, steps=5):
+    return Workload("resnet20_272474_p16_k5pct_ef5", N, P, 0.25, steps, "segments",
+                    k=frac_k(N, 5, 100), segments=20, wid=1)
+
+
+def _w2(N=1 << 26, P=8, steps=10):
+    return Workload("laplace_2p26_p8_k1pct_ef10", N, P, 0.3, steps, "laplace",
+                    k=frac_k(N, 1, 100), scale=1e-3, wid=2)
+
+
+def _w3(N=1 << 22, P=32, nnz=65536):
+    return Workload("zipf_2p22_p32_nnz65536", N, P, 0.25, 1, "zipf", nnz=nnz, zipf_s=1.1, wid=3)
+
+
+def _w4(N=1 << 27, P=64, steps=2):
+    return Workload("wideresnet_2p27_p64_k0p5pct_q4b512_ef2", N, P, 0.3, steps, "gauss",
+                    k=frac_k(N, 5, 1000), scale=1e-3, q4_bucket=512, wid=4)
+
+
+_FACTORIES = [_w0, _w1, _w2, _w3, _w4]
+
+
+def workload(i: int, **overrides) -> Workload:
+    """Workload i at its full size, or with N / P / steps / nnz overridden
+    (k is re-derived from the same fraction for a smaller N)."""
+    return _FACTORIES[i](**overrides)
+
+
+# Config-1 segment scale seed: chosen so that the five error-feedback steps
+# cross the dense threshold (checked by tests/test_workloads.py).
+SEGMENT_SIGMA_SEED = 7
+
+
+def seed_of(w: Workload, node: int, step: int, salt: int = 0) -> int:
+    return (w.wid * 1_000_003 + step * 10_007 + node * 101 + salt * 7_919 + 12_345) & ((1 << 62) - 1)
+
+
+def segment_bounds(N: int, segments: int):
+    """floor(N / S) per segment, the last one taking the remainder."""
+    base = N // segments
+    starts = [s * base for s in range(segments)]
+    ends = starts[1:] + [N]
+    return list(zip(starts, ends))
+
+
+def segment_sigmas(w: Workload) -> np.ndarray:
+    rng = np.random.default_rng(SEGMENT_SIGMA_SEED + 1000 * w.wid)
+    return (10.0 ** rng.uniform(-4.0, -1.0, size=w.segments)).astype(np.float64)
+
+
+def gradient(w: Workload, node: int, step: int, device="cpu", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense fp32 gradient of one node at one step, generated on `device`."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed_of(w, node, step))
+    N = w.N
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=device)
+    if w.kind == "gauss":
+        torch.randn(N, generator=gen, device=device, out=out)
+        if w.scale != 1.0:
+            out.mul_(w.scale)
+    elif w.kind == "segments":
+        torch.randn(N, generator=gen, device=device, out=out)
+        for (a, b), sig in zip(segment_bounds(N, w.segments), segment_sigmas(w)):
+            out[a:b].mul_(float(sig))
+    elif w.kind == "laplace":
+        # inverse CDF from uniforms kept inside the open interval (0, 1)
+        torch.rand(N, generator=gen, device=device, out=out)
+        eps = 2.0 ** -25
+        out.mul_(1.0 - 2 * eps).add_(eps)
+        out.sub_(0.5)
+        sgn = torch.sign(out)
+        out.abs_().mul_(-2.0).add_(1.0).log_().mul_(-w.scale).mul_(sgn)
+    else:
+        raise ValueError(f"workload {w.name} has no dense gradient")
+    return out
+
+
+def gradients(w: Workload, step: int, device="cpu", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((w.P, w.N), dtype=torch.float32, device=device)
+    for p in range(w.P):
+        gradient(w, p, step, device=device, out=out[p])
+    return out
+
+
+def zipf_sparse(w: Workload):
+    """Already-sparse contributions: per node `nnz` distinct indices whose
+    ranks follow Zipf(s) truncated to [1, N], mapped through one shared seeded
+    permutation (heavy overlap between nodes), sorted ascending; values N(0,1).
+    Returns (offsets [P+1] u64, idx u32, val f32) as numpy arrays."""
+    perm = np.random.default_rng(seed_of(w, 0, 0, salt=1)).permutation(w.N).astype(np.uint32)
+    idx_parts, val_parts = [], []
+    for p in range(w.P):
+        rng = np.random.default_rng(seed_of(w, p, 0))
+        chosen = np.zeros(0, np.int64)
+        while chosen.size < w.nnz:
+            draw = rng.zipf(w.zipf_s, size=4 * w.nnz)
+            draw = draw[draw <= w.N]
+            merged = np.concatenate([chosen, draw])
+            _, first = np.unique(merged, return_index=True)
+            chosen = merged[np.sort(first)][: w.nnz]
+        ids = np.sort(perm[chosen - 1])
+        idx_parts.append(ids.astype(np.uint32))
+        val_parts.append(rng.standard_normal(w.nnz).astype(np.float32))
+    offsets = np.zeros(w.P + 1, np.uint64)
+    offsets[1:] = np.cumsum([len(a) for a in idx_parts])
+    return offsets, np.concatenate(idx_parts), np.concatenate(val_parts)
