@@ -1,0 +1,194 @@
+/*
+ * sparcml.h - C ABI of the MI355X (gfx950) SparCML hot path.
+ *
+ * Three operations of SparCML's data-parallel gradient reduction, run on one
+ * GPU whose HBM holds the contributions of P nodes:
+ *   - error-feedback Top-k sparsification      (sparcml_topk_ef)
+ *   - 4-bit stochastic quantization and back   (sparcml_q4, sparcml_dq4)
+ *   - sum of P sparse contributions with a switch to a dense result
+ *                                               (sparcml_sparse_reduce)
+ *
+ * Sources, cited by page title and section: "SparCML: High-Performance Sparse
+ * Communication for Machine Learning" (paperlayer.ai digest of arXiv
+ * 1802.08021v3) and the arXiv abstract on the mlsanity summary page of the
+ * same paper.
+ *
+ * Conventions shared by every call:
+ *   - Pointers marked "device" are HIP device allocations on the current
+ *     device; pointers marked "host" are ordinary host memory.
+ *   - The caller owns every buffer. The library allocates nothing and keeps
+ *     no state between calls, apart from the optional profiling events below.
+ *   - Calls are asynchronous on `stream` and stream-ordered, in the spirit of
+ *     the non-blocking collectives of the paper (section 7, "Non-Blocking
+ *     Operations"): results are valid once the stream has reached them.
+ *   - The return value reports argument errors (nothing is launched) and
+ *     launch errors. The library never aborts, throws or prints. Errors in
+ *     the contents of device buffers are reported in device-written flags.
+ *   - Arrays are node-major: node p's part of a [P][n] array starts at p*n.
+ */
+#ifndef SPARCML_H
+#define SPARCML_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sparcml_status {
+  SPARCML_OK = 0,
+  SPARCML_ERR_INVALID_ARG = 1, /* a null pointer, size, alignment or value out of range */
+  SPARCML_ERR_WORKSPACE = 2,   /* workspace null or smaller than the *_workspace size */
+  SPARCML_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} sparcml_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sparcml_status_string(sparcml_status status);
+
+/* ------------------------------------------------------------------------
+ * Error-feedback Top-k
+ *
+ * Paper section 2.2 ("Communication-Reduction Techniques"): every node sends
+ * the k components of largest magnitude and accumulates the omitted ones for
+ * the next iteration. Section 4 ("Sparse Quantized Reduction"): the unapplied
+ * part is carried forward as residual error.
+ *
+ * For each node p and each i < N:
+ *   a_i   = grad_i + residual_i          (one fp32 add, round to nearest even)
+ *   S     = the k positions that come first when ordered by |a_i| descending
+ *           (compared as the IEEE bit pattern with the sign cleared, so -0
+ *           ties +0) and then by index ascending: ties go to the lower index
+ *   out_idx[p][0..k) = S in ascending order, out_val[p][j] = a[out_idx[p][j]]
+ *   residual_i = a_i, except +0.0 at the positions in S      (in place)
+ * Hence residual_new + scatter(out_val) == grad + residual_old exactly.
+ *
+ *   P, N      nodes and elements per node; N < 2^32, P*N < 2^40
+ *   k         0 <= k <= N (k == 0 only folds grad into residual)
+ *   grad      device, [P][N] fp32, read only, 16-byte aligned
+ *   residual  device, [P][N] fp32, read and overwritten, 16-byte aligned
+ *   out_idx   device, [P][k] uint32 (may be NULL when k == 0)
+ *   out_val   device, [P][k] fp32   (may be NULL when k == 0)
+ *   ws        device workspace of at least sparcml_topk_ef_workspace(P,N,k)
+ *             bytes; its content on entry does not matter. After the call the
+ *             first 4*P bytes hold, per node, which path produced the result
+ *             (0: predicted-threshold candidates, 1: exact rescan), and the
+ *             next 4*P bytes hold a nonzero value for a node whose internal
+ *             consistency check failed (never expected).
+ * grad and residual must not overlap; neither may overlap the outputs.
+ * Inputs are expected finite (NaN and Inf are ordered by their bit pattern).
+ * ---------------------------------------------------------------------- */
+size_t sparcml_topk_ef_workspace(uint32_t P, uint64_t N, uint64_t k);
+
+sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k,
+                               const float* grad, float* residual,
+                               uint32_t* out_idx, float* out_val,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * 4-bit stochastic quantization (paper section 6, "Supporting Low-Precision
+ * Communication": buckets quantized independently and stochastically, each
+ * with one full-precision scale; section 2.2: zero-mean quantization noise).
+ *
+ * Per node p the n values form buckets of `bucket` consecutive positions (the
+ * last one may be partial). For bucket j: scale = max |v| (exact) and
+ * st = scale / 7. Position e with value v gets
+ *   level = 0                                     if scale == 0
+ *   level = floor(x) + (u < x - floor(x))         otherwise,
+ *           x = (|v| / scale) * 7  (two fp32 roundings, no fused multiply-add)
+ *           u = (w >> 8) * 2^-24, w = word (e & 3) of the Philox-4x32-10 block
+ *               for counter {e >> 2, p, step, 0} and key {seed lo32, seed hi32}
+ *   code = (v < 0 ? 8 : 0) | level
+ * Codes are packed two per byte, even positions in the low nibble; each node's
+ * row is ceil(n/2) bytes and an unused high nibble is zero.
+ * dq4 returns (code & 8 ? -1 : +1) * (level * st), rounded in fp32.
+ *
+ *   bucket    multiple of 8, 8 <= bucket <= 2^20
+ *   val       device, [P][n] fp32
+ *   codes     device, [P][ceil(n/2)] uint8
+ *   scales    device, [P][ceil(n/bucket)] fp32
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                          const float* val, uint8_t* codes, float* scales, hipStream_t stream);
+
+sparcml_status sparcml_dq4(uint32_t P, uint64_t n, uint32_t bucket,
+                           const uint8_t* codes, const float* scales, float* val,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse reduction with the dense switch.
+ *
+ * Paper section 5.1 ("Data Representation: Sparse Streams"): index-value
+ * pairs that switch to a dense representation once fill-in passes the
+ * threshold delta. Section 5.2: the reduction is a coordinate-wise sum with
+ * neutral element 0. Section 5.3: the result is dense when its size K reaches
+ * delta; a rough estimate of K chooses the algorithm. Appendix B: K counts
+ * the indices in the union of the contributed sets (uniform-sampling estimate
+ * in B.1).
+ *
+ *   K = |union of the index sets|   (an index counts even if its sum is 0)
+ *   T = ceil(delta * N), computed in double
+ *   K >= T  -> dense:  out_val[i] = sum of the values at index i, 0 elsewhere,
+ *                      for every i < N; out_idx is not written
+ *   K <  T  -> sparse: out_idx[0..K) = the union ascending, out_val[0..K) = sums
+ * Sums are accumulated in fp64 and rounded to fp32 once.
+ *
+ *   P          1 <= P <= 1024 nodes
+ *   N          index space, 1 <= N < 2^32
+ *   delta      finite; delta <= 0 is always dense, T > N never dense
+ *   h_offsets  host, [P+1] uint64, nondecreasing, h_offsets[0] == 0: node p
+ *              owns pairs [h_offsets[p], h_offsets[p+1])
+ *   idx, val   device, [h_offsets[P]] uint32 / fp32; each node's indices
+ *              strictly ascending and < N
+ *   expected_nnz_hint  0: estimate K from the nonzero counts (uniform model
+ *              of Appendix B.1); else the caller's estimate. It only chooses
+ *              between the dense-first and the count-first algorithm; the
+ *              result does not depend on it.
+ *   out_idx    device, uint32, capacity min(N, T-1) (T > 0), else unused
+ *   out_val    device, fp32, capacity N (entries past K in the sparse case
+ *              are unspecified)
+ *   d_result   device, one sparcml_reduce_result, written by the GPU
+ *   ws         device workspace of sparcml_sparse_reduce_workspace(P, N, nnz)
+ *
+ * Indices >= N or not strictly ascending within a node set bits in
+ * d_result->flags; the outputs are then unspecified but no write leaves the
+ * stated capacities.
+ * ---------------------------------------------------------------------- */
+typedef struct sparcml_reduce_result {
+  uint64_t nnz;      /* K */
+  uint32_t is_dense; /* 1: out_val holds N dense values; 0: K sparse pairs */
+  uint32_t flags;    /* SPARCML_FLAG_* bits, 0 for valid input */
+} sparcml_reduce_result;
+
+#define SPARCML_FLAG_INDEX_RANGE 1u    /* an index >= N */
+#define SPARCML_FLAG_NOT_ASCENDING 2u  /* a node's indices not strictly ascending */
+
+size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nnz);
+
+sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
+                                     const uint64_t* h_offsets,
+                                     const uint32_t* idx, const float* val,
+                                     uint64_t expected_nnz_hint,
+                                     uint32_t* out_idx, float* out_val,
+                                     sparcml_reduce_result* d_result,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Uniform-model estimate of K used when no hint is given (Appendix B.1):
+ * N * (1 - prod_p (1 - nnz_p / N)), capped by sum_p nnz_p. Host only. */
+double sparcml_estimate_nnz(uint32_t P, uint64_t N, const uint64_t* h_offsets);
+
+/* ------------------------------------------------------------------------
+ * Profiling hook (measurement only). Records `start` on the stream right
+ * before, and `stop` right after, the streaming error-feedback kernel of the
+ * next sparcml_topk_ef call made by the calling thread; the events are then
+ * forgotten. Pass NULL, NULL to cancel. The events belong to the caller.
+ * ---------------------------------------------------------------------- */
+void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARCML_H */

@@ -1,0 +1,220 @@
+"""MI355X (gfx950) SparCML hot path: error-feedback Top-k, 4-bit stochastic
+quantization and sparse reduction with the dense switch.
+
+Thin ctypes binding over the C ABI in include/sparcml.h: it checks tensor
+dtype/device/contiguity, allocates outputs and workspaces with torch, and
+passes raw pointers and the current HIP stream. Every step of the path runs
+in the HIP kernels of libsparcml.so; there is no CPU fallback. If the library
+is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparcml.so")
+
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3
+FLAG_INDEX_RANGE, FLAG_NOT_ASCENDING = 1, 2
+
+_lib = None
+
+
+class SparcmlError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        msg = _load().sparcml_status_string(status).decode()
+        super().__init__(f"{what}: {msg}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m sparse_gradient_reduction_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    u32, u64, sz, vp, f64 = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_double
+    st = ctypes.c_int
+    L.sparcml_status_string.argtypes = [st]
+    L.sparcml_status_string.restype = ctypes.c_char_p
+    L.sparcml_topk_ef_workspace.argtypes = [u32, u64, u64]
+    L.sparcml_topk_ef_workspace.restype = sz
+    L.sparcml_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, vp]
+    L.sparcml_topk_ef.restype = st
+    L.sparcml_q4.argtypes = [u32, u64, u32, u64, u32, vp, vp, vp, vp]
+    L.sparcml_q4.restype = st
+    L.sparcml_dq4.argtypes = [u32, u64, u32, vp, vp, vp, vp]
+    L.sparcml_dq4.restype = st
+    L.sparcml_sparse_reduce_workspace.argtypes = [u32, u64, u64]
+    L.sparcml_sparse_reduce_workspace.restype = sz
+    L.sparcml_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
+    L.sparcml_sparse_reduce.restype = st
+    L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
+    L.sparcml_estimate_nnz.restype = f64
+    L.sparcml_profile_next_topk.argtypes = [vp, vp]
+    L.sparcml_profile_next_topk.restype = None
+    _lib = L
+    return L
+
+
+def lib():
+    """The loaded ctypes handle of libsparcml.so."""
+    return _load()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor on a GPU")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _raise(status: int, what: str):
+    if status != OK:
+        raise SparcmlError(status, what)
+
+
+# ---------------------------------------------------------------------------
+def topk_ef_workspace_bytes(P: int, N: int, k: int) -> int:
+    return int(_load().sparcml_topk_ef_workspace(P, N, k))
+
+
+def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optional[torch.Tensor] = None,
+            out_val: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Error-feedback Top-k on [P, N] fp32 `grad`; `residual` is updated in place.
+    Returns (idx [P, k] int32 holding uint32 indices, val [P, k] float32)."""
+    _check_dev(grad, torch.float32, "grad")
+    _check_dev(residual, torch.float32, "residual")
+    if grad.dim() != 2 or grad.shape != residual.shape:
+        raise ValueError("grad and residual must both be [P, N]")
+    P, N = grad.shape
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty((P, k), dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty((P, k), dtype=torch.float32, device=dev)
+    need = topk_ef_workspace_bytes(P, N, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    L = _load()
+    st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
+                           _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_topk_ef")
+    return out_idx, out_val
+
+
+def topk_ef_paths(workspace: torch.Tensor, P: int) -> torch.Tensor:
+    """Per node, which path the last sparcml_topk_ef in `workspace` took
+    (0 candidates, 1 exact rescan), and its consistency flag: [2, P] int32."""
+    return workspace[: 8 * P].view(torch.int32).view(2, P)
+
+
+# ---------------------------------------------------------------------------
+def q4(val: torch.Tensor, bucket: int, seed: int, step: int, codes: Optional[torch.Tensor] = None,
+       scales: Optional[torch.Tensor] = None):
+    """[P, n] fp32 -> (codes [P, ceil(n/2)] uint8, scales [P, ceil(n/bucket)] fp32)."""
+    _check_dev(val, torch.float32, "val")
+    P, n = val.shape
+    dev = val.device
+    if codes is None:
+        codes = torch.empty((P, (n + 1) // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((P, (n + bucket - 1) // bucket), dtype=torch.float32, device=dev)
+    st = _load().sparcml_q4(P, n, bucket, seed & ((1 << 64) - 1), step, _ptr(val), _ptr(codes), _ptr(scales),
+                            ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_q4")
+    return codes, scales
+
+
+def dq4(codes: torch.Tensor, scales: torch.Tensor, n: int, bucket: int, out: Optional[torch.Tensor] = None):
+    _check_dev(codes, torch.uint8, "codes")
+    _check_dev(scales, torch.float32, "scales")
+    P = codes.shape[0]
+    if out is None:
+        out = torch.empty((P, n), dtype=torch.float32, device=codes.device)
+    st = _load().sparcml_dq4(P, n, bucket, _ptr(codes), _ptr(scales), _ptr(out),
+                             ctypes.c_void_p(_stream(codes.device)))
+    _raise(st, "sparcml_dq4")
+    return out
+
+
+# ---------------------------------------------------------------------------
+def dense_threshold(delta: float, N: int) -> int:
+    t = math.ceil(delta * float(N))
+    return max(0, min(t, N + 1))
+
+
+def sparse_reduce_workspace_bytes(P: int, N: int, total_nnz: int) -> int:
+    return int(_load().sparcml_sparse_reduce_workspace(P, N, total_nnz))
+
+
+def estimate_nnz(offsets: Sequence[int], N: int) -> float:
+    off = (ctypes.c_uint64 * len(offsets))(*[int(x) for x in offsets])
+    return float(_load().sparcml_estimate_nnz(len(offsets) - 1, N, off))
+
+
+class ReduceOutput:
+    """Device-resident result of sparse_reduce. `result` is a 16-byte tensor
+    holding sparcml_reduce_result; `read()` copies it to the host."""
+
+    def __init__(self, result, out_idx, out_val, N):
+        self.result, self.out_idx, self.out_val, self.N = result, out_idx, out_val, N
+
+    def read(self):
+        r = self.result.cpu()
+        nnz = int(r[:8].view(torch.int64).item())
+        is_dense = bool(r[8:12].view(torch.int32).item())
+        flags = int(r[12:16].view(torch.int32).item())
+        return nnz, is_dense, flags
+
+    def host(self):
+        """(K, is_dense, flags, idx, val) as host tensors: dense -> idx empty, val [N];
+        sparse -> idx [K] int64, val [K]."""
+        K, dense, flags = self.read()
+        if dense:
+            return K, True, flags, torch.zeros(0, dtype=torch.int64), self.out_val[: self.N].cpu()
+        idx = self.out_idx[:K].cpu().to(torch.int64) & 0xFFFFFFFF
+        return K, False, flags, idx, self.out_val[:K].cpu()
+
+
+def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
+                  expected_nnz_hint: int = 0, out_idx: Optional[torch.Tensor] = None,
+                  out_val: Optional[torch.Tensor] = None, result: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> ReduceOutput:
+    """Sum of P sparse contributions (node p owns pairs [offsets[p], offsets[p+1])).
+    idx: int32 tensor holding uint32 indices, val: float32 tensor."""
+    _check_dev(idx, torch.int32, "idx")
+    _check_dev(val, torch.float32, "val")
+    P = len(offsets) - 1
+    off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
+    dev = idx.device
+    T = dense_threshold(delta, N)
+    cap = 0 if T == 0 else min(N, T - 1)
+    if out_idx is None:
+        out_idx = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty(N, dtype=torch.float32, device=dev)
+    if result is None:
+        result = torch.zeros(16, dtype=torch.uint8, device=dev)
+    need = sparse_reduce_workspace_bytes(P, N, int(offsets[-1]))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = _load().sparcml_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val), int(expected_nnz_hint),
+                                       _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
+                                       workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_sparse_reduce")
+    return ReduceOutput(result, out_idx, out_val, N)

@@ -1,0 +1,135 @@
+// C ABI of the SparCML hot path: argument checks, workspace sizing, launch.
+// The declarations and their contracts are in include/sparcml.h.
+#include "sparcml.h"
+
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sparcml_status from_hip(hipError_t e) { return e == hipSuccess ? SPARCML_OK : SPARCML_ERR_HIP; }
+
+constexpr uint64_t kMaxN = 0xFFFFFFFFull;  // indices are uint32
+
+// T = ceil(delta * N) in double, clamped to [0, N + 1]
+uint64_t dense_threshold(double delta, uint64_t N) {
+  const double t = std::ceil(delta * (double)N);
+  if (!(t > 0.0)) return 0;
+  if (t > (double)N) return N + 1;
+  return (uint64_t)t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparcml_status_string(sparcml_status status) {
+  switch (status) {
+    case SPARCML_OK: return "SPARCML_OK";
+    case SPARCML_ERR_INVALID_ARG: return "SPARCML_ERR_INVALID_ARG: invalid argument";
+    case SPARCML_ERR_WORKSPACE: return "SPARCML_ERR_WORKSPACE: workspace missing or too small";
+    case SPARCML_ERR_HIP: return "SPARCML_ERR_HIP: HIP runtime or launch error";
+  }
+  return "SPARCML: unknown status";
+}
+
+void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop) {
+  g_prof_start = start;
+  g_prof_stop = stop;
+}
+
+// --------------------------------------------------------------------------
+size_t sparcml_topk_ef_workspace(uint32_t P, uint64_t N, uint64_t k) {
+  if (P == 0 || N > kMaxN || k > N || P > 65535u) return 0;
+  return sparcml::topk_workspace_bytes(P, N, k);
+}
+
+sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                               uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
+  g_prof_start = g_prof_stop = nullptr;
+  if (P == 0 || P > 65535u || N > kMaxN || k > N) return SPARCML_ERR_INVALID_ARG;
+  if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
+  if (N == 0) return SPARCML_OK;
+  if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
+  if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
+  return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));
+}
+
+// --------------------------------------------------------------------------
+static bool q4_args_ok(uint32_t P, uint64_t n, uint32_t bucket) {
+  if (P == 0 || P > 65535u) return false;
+  if (bucket < 8 || bucket > (1u << 20) || (bucket % 8) != 0) return false;
+  if (n >= (1ull << 34)) return false;
+  const uint64_t nb = (n + bucket - 1) / bucket;
+  if ((nb + 3) / 4 > 0x7FFFFFFFull || (n + 2047) / 2048 > 0x7FFFFFFFull) return false;
+  return true;
+}
+
+sparcml_status sparcml_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                          const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
+  if (!q4_args_ok(P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+  if (n == 0) return SPARCML_OK;
+  if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
+  return from_hip(sparcml::q4_launch(P, n, bucket, seed, step, val, codes, scales, stream));
+}
+
+sparcml_status sparcml_dq4(uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes, const float* scales,
+                           float* val, hipStream_t stream) {
+  if (!q4_args_ok(P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+  if (n == 0) return SPARCML_OK;
+  if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
+  return from_hip(sparcml::dq4_launch(P, n, bucket, codes, scales, val, stream));
+}
+
+// --------------------------------------------------------------------------
+double sparcml_estimate_nnz(uint32_t P, uint64_t N, const uint64_t* h_offsets) {
+  if (!h_offsets || N == 0) return 0.0;
+  double miss = 1.0, sum = 0.0;
+  for (uint32_t p = 0; p < P; ++p) {
+    const double c = (double)(h_offsets[p + 1] - h_offsets[p]);
+    sum += c;
+    const double q = c / (double)N;
+    miss *= (q >= 1.0 ? 0.0 : 1.0 - q);
+  }
+  const double e = (double)N * (1.0 - miss);
+  return e < sum ? e : sum;
+}
+
+size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nnz) {
+  if (P == 0 || P > 1024u || N == 0 || N > kMaxN || total_nnz > kMaxN) return 0;
+  return sparcml::reduce_workspace_bytes(P, N, total_nnz);
+}
+
+sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                     const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
+                                     uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !std::isfinite(delta)) return SPARCML_ERR_INVALID_ARG;
+  if (!h_offsets || !d_result || !out_val || !aligned16(out_val)) return SPARCML_ERR_INVALID_ARG;
+  if (h_offsets[0] != 0) return SPARCML_ERR_INVALID_ARG;
+  for (uint32_t p = 0; p < P; ++p)
+    if (h_offsets[p + 1] < h_offsets[p]) return SPARCML_ERR_INVALID_ARG;
+  const uint64_t total = h_offsets[P];
+  if (total > kMaxN) return SPARCML_ERR_INVALID_ARG;
+  if (total > 0 && (!idx || !val)) return SPARCML_ERR_INVALID_ARG;
+  const uint64_t T = dense_threshold(delta, N);
+  const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);
+  if (cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
+  const double est = expected_nnz_hint ? (double)expected_nnz_hint : sparcml_estimate_nnz(P, N, h_offsets);
+  const bool dense_first = est >= (double)T;
+  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, dense_first, out_idx, cap, out_val,
+                                                reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws,
+                                                stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels: wave64 ballots and prefix
+// counts, block-wide scans through LDS, and the magnitude key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sparcml {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming (non-temporal) 16-byte load and store: the data is touched once.
+__device__ __forceinline__ f32x4 load_nt(const f32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_nt(f32x4 v, f32x4* p) { __builtin_nontemporal_store(v, p); }
+
+// |a| ordering key: the IEEE bit pattern with the sign cleared. For finite
+// values it is monotone in |a|, and -0 and +0 share key 0.
+__device__ __forceinline__ uint32_t mag_key(float a) {
+  return __float_as_uint(a) & 0x7FFFFFFFu;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool pred) { return __ballot(pred); }
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t t = __shfl_up(v, d, kWave);
+    if (lane >= (uint32_t)d) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+// Exclusive prefix sum over the threads of a block (thread order), with the
+// block total. `scratch` holds NT/64 + 1 words of LDS. Contains barriers: all
+// threads of the block must call it.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
+  constexpr int NW = NT / kWave;
+  const uint32_t lane = lane_id();
+  const uint32_t wid = threadIdx.x / kWave;
+  uint32_t inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int w = 0; w < NW; ++w) {
+      uint32_t t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[NW] = run;
+  }
+  __syncthreads();
+  uint32_t excl = scratch[wid] + inc - v;
+  total = scratch[NW];
+  __syncthreads();
+  return excl;
+}
+
+// Radix-select step over a histogram `hist` of `nbins` bins (LDS or global):
+// finds the highest bin b such that the count of items in bins >= b reaches
+// `rank` (1-based, rank >= 1), and the count in bins strictly above b. If the
+// histogram holds fewer than `rank` items, returns bin 0 with `above` = total
+// of bins > 0. `scratch` holds NT/64 + 3 words of LDS. All threads call it;
+// all receive the result.
+template <int NT>
+__device__ __forceinline__ void block_find_suffix(const uint32_t* hist, int nbins, uint32_t rank,
+                                                  uint32_t* scratch, uint32_t& bin, uint32_t& above) {
+  const int per = nbins / NT;  // bins per thread, nbins is a multiple of NT
+  // thread t owns bins [nbins-1-t*per-(per-1), nbins-1-t*per], walked top down
+  const int top = nbins - 1 - (int)threadIdx.x * per;
+  uint32_t s = 0;
+  for (int i = 0; i < per; ++i) s += hist[top - i];
+  uint32_t total;
+  uint32_t before = block_exclusive_scan<NT>(s, scratch, total);
+  constexpr int NW = NT / kWave;
+  if (threadIdx.x == 0) {
+    scratch[NW + 1] = 0u;
+    scratch[NW + 2] = total - hist[0];
+  }
+  __syncthreads();
+  if (before < rank && before + s >= rank) {
+    uint32_t run = before;
+    for (int i = 0; i < per; ++i) {
+      uint32_t c = hist[top - i];
+      if (run + c >= rank) {
+        scratch[NW + 1] = (uint32_t)(top - i);
+        scratch[NW + 2] = run;
+        break;
+      }
+      run += c;
+    }
+  }
+  __syncthreads();
+  bin = scratch[NW + 1];
+  above = scratch[NW + 2];
+  __syncthreads();
+}
+
+}  // namespace sparcml

@@ -1,0 +1,119 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every
+function include/sparcml.h declares, and rejects bad arguments before
+launching anything."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import sparse_gradient_reduction_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparcml.h")
+
+if not os.path.exists(sg.LIB_PATH):
+    pytest.skip("libsparcml.so not built", allow_module_level=True)
+
+FAKE = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
+FAKE_ODD = ctypes.c_void_p(4100)   # not 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparcml_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ["sparcml_topk_ef", "sparcml_sparse_reduce", "sparcml_q4", "sparcml_dq4",
+                 "sparcml_topk_ef_workspace", "sparcml_sparse_reduce_workspace", "sparcml_status_string"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = sg.lib()
+    for st in range(4):
+        s = L.sparcml_status_string(st).decode()
+        assert s.startswith("SPARCML")
+    assert L.sparcml_status_string(99).decode()
+
+
+def test_topk_argument_checks():
+    L = sg.lib()
+    ws = sg.topk_ef_workspace_bytes(4, 1000, 10)
+    assert ws > 0
+    call = lambda P, N, k, g=FAKE, r=FAKE, oi=FAKE, ov=FAKE, w=FAKE, wb=ws: L.sparcml_topk_ef(
+        P, N, k, g, r, oi, ov, w, wb, None)
+    assert call(0, 1000, 10) == sg.ERR_INVALID_ARG
+    assert call(4, 1000, 1001) == sg.ERR_INVALID_ARG
+    assert call(4, 1 << 32, 10) == sg.ERR_INVALID_ARG
+    assert call(4, 1000, 10, g=None) == sg.ERR_INVALID_ARG
+    assert call(4, 1000, 10, r=FAKE_ODD) == sg.ERR_INVALID_ARG
+    assert call(4, 1000, 10, oi=None) == sg.ERR_INVALID_ARG
+    assert call(4, 1000, 10, w=None) == sg.ERR_WORKSPACE
+    assert call(4, 1000, 10, wb=ws - 1) == sg.ERR_WORKSPACE
+    assert sg.topk_ef_workspace_bytes(0, 10, 1) == 0
+    assert sg.topk_ef_workspace_bytes(2, 10, 11) == 0
+
+
+def test_q4_argument_checks():
+    L = sg.lib()
+    assert L.sparcml_q4(2, 100, 12, 1, 0, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG  # bucket % 8
+    assert L.sparcml_q4(2, 100, 0, 1, 0, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_q4(0, 100, 512, 1, 0, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_q4(2, 100, 512, 1, 0, None, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_q4(2, 100, 512, 1, 0, FAKE_ODD, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_dq4(2, 100, 512, FAKE, None, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_q4(2, 0, 512, 1, 0, None, None, None, None) == sg.OK  # nothing to do
+
+
+def test_reduce_argument_checks():
+    L = sg.lib()
+    off = (ctypes.c_uint64 * 3)(0, 5, 9)
+    ws = sg.sparse_reduce_workspace_bytes(2, 100, 9)
+    assert ws > 0
+    f64 = ctypes.c_double
+
+    def call(P=2, N=100, delta=0.25, o=off, oi=FAKE, ov=FAKE, res=FAKE, w=FAKE, wb=ws):
+        return L.sparcml_sparse_reduce(P, N, f64(delta), o, FAKE, FAKE, 0, oi, ov, res, w, wb, None)
+
+    assert call(delta=float("nan")) == sg.ERR_INVALID_ARG
+    assert call(delta=float("inf")) == sg.ERR_INVALID_ARG
+    assert call(P=0) == sg.ERR_INVALID_ARG
+    assert call(P=1025) == sg.ERR_INVALID_ARG
+    assert call(N=0) == sg.ERR_INVALID_ARG
+    assert call(o=None) == sg.ERR_INVALID_ARG
+    assert call(o=(ctypes.c_uint64 * 3)(0, 5, 4)) == sg.ERR_INVALID_ARG  # decreasing
+    assert call(o=(ctypes.c_uint64 * 3)(1, 5, 9)) == sg.ERR_INVALID_ARG  # not starting at 0
+    assert call(ov=FAKE_ODD) == sg.ERR_INVALID_ARG
+    assert call(oi=None) == sg.ERR_INVALID_ARG
+    assert call(res=None) == sg.ERR_INVALID_ARG
+    assert call(w=None) == sg.ERR_WORKSPACE
+    assert call(wb=ws - 1) == sg.ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("P,N,k", [(1, 1000, 10), (8, 1 << 20, 10485), (64, 4096, 0), (3, 17, 17)])
+def test_estimate_matches_uniform_closed_form(P, N, k):
+    """Appendix B.1 (uniform sampling): E[K] = N(1 - (1 - k/N)^P), never above P*k."""
+    offsets = [p * k for p in range(P + 1)]
+    got = sg.estimate_nnz(offsets, N)
+    want = min(N * (1 - (1 - k / N) ** P), P * k)
+    assert math.isclose(got, want, rel_tol=1e-12, abs_tol=1e-9)
+    assert got <= P * k + 1e-9
+
+
+def test_dense_threshold_reading():
+    assert sg.dense_threshold(0.25, 65536) == 16384
+    assert sg.dense_threshold(0.3, 1 << 27) == 40265319
+    assert sg.dense_threshold(0.0, 10) == 0
+    assert sg.dense_threshold(-1.0, 10) == 0
+    assert sg.dense_threshold(1.5, 10) == 11

@@ -1,0 +1,159 @@
+"""GPU parity: sparcml_sparse_reduce against the oracle. Union size K, the
+dense decision and the index list must match exactly; sums within
+1e-6 * P * max|v| (the oracle sums in fp64 and rounds once; so does the GPU,
+in another order)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_gradient_reduction_amd as sg
+from sparse_gradient_reduction_amd import workloads as W
+from tests.gpu_util import reduce_tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_reduce(off, idx, val, N, delta, dev, hint=0):
+    it = torch.from_numpy(np.ascontiguousarray(idx, np.uint32).view(np.int32)).to(dev)
+    vt = torch.from_numpy(np.ascontiguousarray(val, np.float32)).to(dev)
+    out = sg.sparse_reduce([int(x) for x in off], it, vt, N, delta, expected_nnz_hint=hint)
+    torch.cuda.synchronize()
+    return out.host()
+
+
+def _check(off, idx, val, N, delta, dev, hint=0, P=None):
+    P = P if P is not None else len(off) - 1
+    K, dense, oi, ov = oracle.reduce(off, idx, val, N, delta)
+    gK, gdense, flags, gi, gv = _gpu_reduce(off, idx, val, N, delta, dev, hint)
+    assert flags == 0
+    assert gK == K and gdense == dense, (gK, K, gdense, dense)
+    gv = gv.numpy()
+    if not dense:
+        np.testing.assert_array_equal(gi.numpy().astype(np.uint32), oi)
+    tol = reduce_tolerance(P, val)
+    err = np.max(np.abs(gv.astype(np.float64) - ov)) if ov.size else 0.0
+    assert err <= tol, (err, tol)
+    return K, dense
+
+
+def _random_sparse(rng, P, N, nnz_max):
+    parts, vals = [], []
+    for _ in range(P):
+        n = int(rng.integers(0, nnz_max + 1))
+        ids = np.sort(rng.choice(N, size=min(n, N), replace=False)).astype(np.uint32)
+        parts.append(ids)
+        vals.append(rng.standard_normal(ids.size).astype(np.float32))
+    off = np.zeros(P + 1, np.uint64)
+    off[1:] = np.cumsum([a.size for a in parts])
+    return off, np.concatenate(parts), np.concatenate(vals)
+
+
+@pytest.mark.parametrize("P,N,nnz,delta", [
+    (1, 1, 1, 0.25), (1, 100, 30, 0.5), (3, 8191, 500, 0.25), (4, 8192, 3000, 0.25),
+    (5, 8193, 2000, 0.3), (8, 30000, 4000, 0.25), (8, 30000, 9000, 0.25), (16, 100003, 2000, 0.05),
+    (2, 1 << 20, 5000, 0.3), (64, 65536, 800, 0.25),
+])
+@pytest.mark.parametrize("hint", ["estimate", "count_first", "dense_first"])
+def test_reduce_random(dev, P, N, nnz, delta, hint):
+    rng = np.random.default_rng(P * 31 + N + nnz)
+    off, idx, val = _random_sparse(rng, P, N, nnz)
+    h = {"estimate": 0, "count_first": 1, "dense_first": N}[hint]
+    print(f"reduce P={P} N={N} nnz<={nnz} delta={delta} hint={hint}", flush=True)
+    _check(off, idx, val, N, delta, dev, hint=h)
+
+
+@pytest.mark.parametrize("N,delta", [(100000, 0.25), (99999, 0.3), (65536, 0.3), (10007, 0.5)])
+@pytest.mark.parametrize("hint", ["count_first", "dense_first"])
+def test_switch_exactly_at_threshold(dev, N, delta, hint):
+    T = math.ceil(delta * N)
+    rng = np.random.default_rng(N)
+    for K_target, want_dense in [(T - 1, False), (T, True), (T + 1, True)]:
+        ids = np.sort(rng.choice(N, K_target, replace=False)).astype(np.uint32)
+        a, b, c = ids[: 2 * K_target // 3], ids[K_target // 3:], ids[::5]
+        idx = np.concatenate([a, b, c]).astype(np.uint32)
+        val = rng.standard_normal(idx.size).astype(np.float32)
+        off = np.array([0, a.size, a.size + b.size, idx.size], np.uint64)
+        K, dense = _check(off, idx, val, N, delta, dev, hint={"count_first": 1, "dense_first": N}[hint])
+        assert K == K_target and dense == want_dense
+
+
+def test_full_overlap_and_disjoint(dev):
+    rng = np.random.default_rng(8)
+    P, N, k = 16, 200000, 3000
+    ids = np.sort(rng.choice(N, k, replace=False)).astype(np.uint32)
+    idx = np.tile(ids, P)
+    val = rng.standard_normal(P * k).astype(np.float32)
+    off = np.arange(P + 1, dtype=np.uint64) * k
+    K, dense = _check(off, idx, val, N, 0.25, dev)
+    assert K == k
+    perm = rng.permutation(N)[: P * k]
+    idx = np.concatenate([np.sort(perm[p * k:(p + 1) * k]) for p in range(P)]).astype(np.uint32)
+    K, dense = _check(off, idx, val, N, 0.5, dev)
+    assert K == P * k
+
+
+def test_empty_and_edge_delta(dev):
+    off = np.zeros(5, np.uint64)
+    e_i, e_v = np.zeros(0, np.uint32), np.zeros(0, np.float32)
+    assert _check(off, e_i, e_v, 50000, 0.25, dev) == (0, False)
+    assert _check(off, e_i, e_v, 50000, 0.0, dev) == (0, True)
+    rng = np.random.default_rng(1)
+    off, idx, val = _random_sparse(rng, 3, 20000, 5000)
+    _check(off, idx, val, 20000, -2.0, dev)   # always dense
+    _check(off, idx, val, 20000, 7.0, dev)    # never dense
+
+
+def test_segment_boundary_indices(dev):
+    N = 3 * 8192 + 5
+    idx = np.array([0, 8191, 8192, 16383, 16384, 24575, 24576, N - 1], np.uint32)
+    val = np.arange(1, 9, dtype=np.float32)
+    off = np.array([0, 4, 8, 8], np.uint64)
+    idx2 = np.concatenate([idx[:4], idx[::2]])
+    val2 = np.concatenate([val[:4], val[::2]])
+    off2 = np.array([0, 4, 8], np.uint64)
+    _check(off, idx, val, N, 0.5, dev)
+    _check(off2, idx2, val2, N, 0.5, dev)
+    _check(off2, idx2, val2, N, 0.0001, dev)
+
+
+def test_max_nodes(dev):
+    rng = np.random.default_rng(2)
+    off, idx, val = _random_sparse(rng, 1024, 50000, 40)
+    _check(off, idx, val, 50000, 0.25, dev)
+    _check(off, idx, val, 50000, 0.25, dev, hint=50000)
+
+
+def test_invalid_input_sets_flags(dev):
+    N = 10000
+    # node 0 not ascending, node 1 has an index >= N
+    idx = np.array([5, 3, 9, 1, 2, N + 7], np.uint32)
+    val = np.ones(6, np.float32)
+    off = [0, 3, 6]
+    for hint in (1, N):
+        _, _, flags, _, _ = _gpu_reduce(off, idx, val, N, 0.25, dev, hint)
+        assert flags & sg.FLAG_NOT_ASCENDING
+        assert flags & sg.FLAG_INDEX_RANGE
+    # a valid call afterwards with the same workspace size is clean
+    _, _, flags, _, _ = _gpu_reduce([0, 2], np.array([1, 4], np.uint32), np.ones(2, np.float32), N, 0.25, dev)
+    assert flags == 0
+
+
+def test_zipf_workload_full_size(dev):
+    """Already-sparse URL-style input: N = 2^22, P = 32, 65536 Zipf(1.1) indices per node."""
+    w = W.workload(3)
+    off, idx, val = W.zipf_sparse(w)
+    K, dense = _check(off, idx, val, w.N, w.delta, dev)
+    assert not dense and 0.1 * w.N < K < 0.3 * w.N
+
+
+def test_reduce_deterministic(dev):
+    rng = np.random.default_rng(21)
+    off, idx, val = _random_sparse(rng, 32, 1 << 18, 20000)
+    a = _gpu_reduce(off, idx, val, 1 << 18, 0.25, dev)
+    b = _gpu_reduce(off, idx, val, 1 << 18, 0.25, dev)
+    assert a[0] == b[0]
+    assert torch.equal(a[3], b[3])
+    assert torch.equal(a[4].view(torch.int32), b[4].view(torch.int32))
