@@ -41,8 +41,14 @@ def lib():
         L.oracle_dq4.restype = None
         L.oracle_reduce.argtypes = [u32, u64, f64, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_reduce.restype = ctypes.c_int
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = ctypes.c_int
         _LIB = L
     return _LIB
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
 
 
 def _ptr(a):

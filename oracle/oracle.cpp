@@ -25,7 +25,12 @@
 #include <cstring>
 #include <vector>
 
+#include <omp.h>
+
 extern "C" {
+
+// Threads an OpenMP region of the oracle may use (reported with CPU timings).
+int oracle_max_threads(void) { return omp_get_max_threads(); }
 
 // ---------------------------------------------------------------------------
 // Error-feedback Top-k  ([SparCML] §2.2 "Communication-Reduction Techniques":

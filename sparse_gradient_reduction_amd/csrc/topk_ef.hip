@@ -80,8 +80,8 @@ Layout make_layout(uint32_t P, uint64_t N, uint64_t k) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.info = take(4ull * P);
-  L.err = take(4ull * P);
+  L.info = take(8ull * P);  // [P] path per node, then [P] consistency flags
+  L.err = L.info + 4ull * P;
   L.state = take(sizeof(NodeState) * P);
   L.h0 = take(4ull * P * kH0);
   L.h1 = take(4ull * P * kH1);
