@@ -15,7 +15,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 sparcml_status from_hip(hipError_t e) { return e == hipSuccess ? SPARCML_OK : SPARCML_ERR_HIP; }
 
-constexpr uint64_t kMaxN = 0xFFFFFFFFull;  // indices are uint32
+constexpr uint64_t kMaxN = 0xFFFFFFFFull;       // indices are uint32
+constexpr uint64_t kMaxTopkN = 0xFFFE0000ull;   // candidate slots stay below 2^32
 
 // T = ceil(delta * N) in double, clamped to [0, N + 1]
 uint64_t dense_threshold(double delta, uint64_t N) {
@@ -46,7 +47,7 @@ void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop) {
 
 // --------------------------------------------------------------------------
 size_t sparcml_topk_ef_workspace(uint32_t P, uint64_t N, uint64_t k) {
-  if (P == 0 || N > kMaxN || k > N || P > 65535u) return 0;
+  if (P == 0 || N > kMaxTopkN || k > N || P > 65535u) return 0;
   return sparcml::topk_workspace_bytes(P, N, k);
 }
 
@@ -55,7 +56,7 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
                                hipStream_t stream) {
   hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
   g_prof_start = g_prof_stop = nullptr;
-  if (P == 0 || P > 65535u || N > kMaxN || k > N) return SPARCML_ERR_INVALID_ARG;
+  if (P == 0 || P > 65535u || N > kMaxTopkN || k > N) return SPARCML_ERR_INVALID_ARG;
   if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
   if (N == 0) return SPARCML_OK;
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;

@@ -56,6 +56,42 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// hist[bin] += 1 for every active lane with `valid`, issuing one LDS atomic
+// per distinct bin in the wave instead of one per lane: keys near a selection
+// threshold crowd into a few bins, where per-lane atomics would serialise.
+__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool valid) {
+  uint64_t todo = ballot(valid);
+  while (todo) {
+    const int leader = __ffsll((long long)todo) - 1;
+    const uint32_t b = (uint32_t)__shfl((int)bin, leader, kWave);
+    const uint64_t same = ballot(valid && bin == b) & todo;
+    if (lane_id() == (uint32_t)leader) atomicAdd(&hist[b], popc64(same));
+    todo &= ~same;
+  }
+}
+
+// Sum of (a, b) over the block. `scratch` holds 2 * NT/64 words of LDS.
+// Contains barriers: all threads of the block must call it.
+template <int NT>
+__device__ __forceinline__ void block_sum2(uint32_t a, uint32_t b, uint32_t* scratch, uint32_t& sa, uint32_t& sb) {
+  constexpr int NW = NT / kWave;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const uint32_t wid = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    scratch[wid] = a;
+    scratch[NW + wid] = b;
+  }
+  __syncthreads();
+  sa = 0;
+  sb = 0;
+  for (int w = 0; w < NW; ++w) {
+    sa += scratch[w];
+    sb += scratch[NW + w];
+  }
+  __syncthreads();
+}
+
 // Exclusive prefix sum over the threads of a block (thread order), with the
 // block total. `scratch` holds NT/64 + 1 words of LDS. Contains barriers: all
 // threads of the block must call it.

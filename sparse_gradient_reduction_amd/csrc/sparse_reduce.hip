@@ -37,7 +37,8 @@ namespace {
 
 constexpr int kSegBits = 13;
 constexpr uint32_t kSeg = 1u << kSegBits;  // 8192 indices per segment
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;              // bounds / count kernels
+constexpr int kWriteThreads = 1024;        // write kernel: 16 waves hide the load latency
 constexpr int kWords = kSeg / 32;          // bitmap words per segment (== kThreads)
 constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
@@ -104,36 +105,50 @@ __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in
 
 // Node-major pass: bounds[p][s] = number of node p's pairs with index < s*8192
 // (s = S stands for N), written by the pair where the run crosses into s.
+// Each thread takes 4 consecutive pairs, so every index is loaded once by the
+// thread that owns it and once more as the left neighbour of the next group.
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R) {
+  constexpr int kPer = 4;
   const uint32_t p = blockIdx.y;
   const uint64_t o0 = R.offs[p];
   const uint64_t nnz = R.offs[p + 1] - o0;
   const uint64_t S = R.S;
   uint32_t* b = R.bounds + (uint64_t)p * (S + 1);
   uint32_t bad = 0u;
-  for (uint64_t j = (uint64_t)blockIdx.x * kThreads + threadIdx.x; j < nnz; j += (uint64_t)gridDim.x * kThreads) {
-    const uint32_t i = idx[o0 + j];
-    const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
-    if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
-    int64_t s_prev = -1;
-    if (j > 0) {
-      const uint32_t ip = idx[o0 + j - 1];
-      if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
-      s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kPer;
+  for (uint64_t j0 = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer; j0 < nnz; j0 += stride) {
+    uint32_t v[kPer + 1];
+    v[0] = j0 > 0 ? idx[o0 + j0 - 1] : 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) v[u + 1] = j0 + u < nnz ? idx[o0 + j0 + u] : 0u;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint64_t j = j0 + u;
+      if (j >= nnz) break;
+      const uint32_t i = v[u + 1];
+      const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
+      if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
+      int64_t s_prev = -1;
+      if (j > 0) {
+        const uint32_t ip = v[u];
+        if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
+        s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
+      }
+      for (int64_t s = s_prev + 1; s <= (int64_t)s_cur; ++s) b[s] = (uint32_t)j;
+      if (j + 1 == nnz)
+        for (uint64_t s = s_cur + 1; s <= S; ++s) b[s] = (uint32_t)nnz;
     }
-    for (int64_t s = s_prev + 1; s <= (int64_t)s_cur; ++s) b[s] = (uint32_t)j;
-    if (j + 1 == nnz)
-      for (uint64_t s = s_cur + 1; s <= S; ++s) b[s] = (uint32_t)nnz;
   }
   if (bad) atomicOr(&R.state->flags, bad);
 }
 
 // Node sub-runs of segment s: pre[p] = exclusive prefix of their lengths,
 // start[p] = absolute index of the first pair. Returns the segment's pair count.
+template <int NT>
 __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
                                               uint32_t* scr) {
   uint32_t carry = 0;
-  for (uint32_t p0 = 0; p0 < R.P; p0 += kThreads) {
+  for (uint32_t p0 = 0; p0 < R.P; p0 += NT) {
     const uint32_t p = p0 + threadIdx.x;
     uint32_t len = 0;
     if (p < R.P) {
@@ -146,7 +161,7 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
       start[p] = (uint32_t)(o0 + b0);
     }
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<kThreads>(len, scr, tot);
+    const uint32_t ex = block_exclusive_scan<NT>(len, scr, tot);
     if (p < R.P) pre[p] = carry + ex;
     carry += tot;
   }
@@ -175,12 +190,24 @@ __global__ __launch_bounds__(kThreads) void k_count(const uint32_t* __restrict__
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs(R, s, pre, start, scr);
-  for (uint32_t f = threadIdx.x; f < total; f += kThreads) {
-    const uint32_t p = find_node(pre, R.P, f);
-    const uint32_t i = idx[start[p] + (f - pre[p])];
-    const uint32_t local = i - seg_lo;
-    if (local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
+  const uint32_t total = load_runs<kThreads>(R, s, pre, start, scr);
+  constexpr int kBatch = 16;
+  for (uint32_t f0 = 0; f0 < total; f0 += kThreads * kBatch) {
+    uint32_t ii[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const uint32_t f = f0 + b * kThreads + threadIdx.x;
+      ii[b] = 0xFFFFFFFFu;
+      if (f < total) {
+        const uint32_t p = find_node(pre, R.P, f);
+        ii[b] = idx[start[p] + (f - pre[p])];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const uint32_t local = ii[b] - seg_lo;
+      if (ii[b] != 0xFFFFFFFFu && local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
+    }
   }
   __syncthreads();
   uint32_t tot;
@@ -214,14 +241,15 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
 enum WriteMode { kDecided = 0, kDenseFirst = 1, kSparseOnly = 2 };
 
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_write(const uint32_t* __restrict__ idx, const float* __restrict__ val,
-                                                    uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                                                    RDev R) {
+__global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restrict__ idx,
+                                                         const float* __restrict__ val,
+                                                         uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
+                                                         RDev R) {
   __shared__ double acc[kSeg];
   __shared__ uint32_t bits[kWords];
   __shared__ uint32_t pre[kMaxP + 1];
   __shared__ uint32_t start[kMaxP];
-  __shared__ uint32_t scr[kThreads / kWave + 3];
+  __shared__ uint32_t scr[kWriteThreads / kWave + 3];
   const uint64_t s = blockIdx.x;
   bool dense;
   if (MODE == kDenseFirst) {
@@ -233,17 +261,17 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint32_t* __restrict__
   }
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
-  for (uint32_t i = threadIdx.x; i < kSeg; i += kThreads) acc[i] = 0.0;
-  bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs(R, s, pre, start, scr);
+  for (uint32_t i = threadIdx.x; i < kSeg; i += kWriteThreads) acc[i] = 0.0;
+  if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
+  const uint32_t total = load_runs<kWriteThreads>(R, s, pre, start, scr);
 
-  constexpr int kBatch = 4;
-  for (uint32_t f0 = 0; f0 < total; f0 += kThreads * kBatch) {
+  constexpr int kBatch = 8;
+  for (uint32_t f0 = 0; f0 < total; f0 += kWriteThreads * kBatch) {
     uint32_t ii[kBatch];
     float vv[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const uint32_t f = f0 + b * kThreads + threadIdx.x;
+      const uint32_t f = f0 + b * kWriteThreads + threadIdx.x;
       ii[b] = 0xFFFFFFFFu;
       vv[b] = 0.0f;
       if (f < total) {
@@ -264,21 +292,22 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint32_t* __restrict__
   }
   __syncthreads();
 
-  const uint32_t word = bits[threadIdx.x];
+  // one bitmap word (32 indices) per thread for the first kWords threads
+  const uint32_t word = threadIdx.x < kWords ? bits[threadIdx.x] : 0u;
   uint32_t seg_total;
-  const uint32_t ex = block_exclusive_scan<kThreads>((uint32_t)__popc(word), scr, seg_total);
+  const uint32_t ex = block_exclusive_scan<kWriteThreads>((uint32_t)__popc(word), scr, seg_total);
   if (MODE == kDenseFirst && threadIdx.x == 0) R.cnt[s] = seg_total;
 
   if (dense) {
     float* out = out_val + seg_lo;
     if (seg_len == kSeg) {
-      for (uint32_t q = threadIdx.x; q < kSeg / 4; q += kThreads) {
+      for (uint32_t q = threadIdx.x; q < kSeg / 4; q += kWriteThreads) {
         const float4 o = make_float4((float)acc[4 * q], (float)acc[4 * q + 1], (float)acc[4 * q + 2],
                                      (float)acc[4 * q + 3]);
         reinterpret_cast<float4*>(out)[q] = o;
       }
     } else {
-      for (uint32_t i = threadIdx.x; i < seg_len; i += kThreads) out[i] = (float)acc[i];
+      for (uint32_t i = threadIdx.x; i < seg_len; i += kWriteThreads) out[i] = (float)acc[i];
     }
   } else {
     uint64_t pos = (uint64_t)R.off[s] + ex;
@@ -328,17 +357,17 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
     for (uint32_t i = 0; i < count; ++i) in.v[i] = h_offsets[first + i];
     hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, stream, R, first, count, in, first == 0 ? 1 : 0);
   }
-  const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 2047) / 2048, 4096));
+  const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
   hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R);
   const dim3 segs((uint32_t)L.S);
   if (dense_first) {
-    hipLaunchKernelGGL(k_write<kDenseFirst>, segs, dim3(kThreads), 0, stream, idx, val, out_idx, out_val, R);
+    hipLaunchKernelGGL(k_write<kDenseFirst>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    hipLaunchKernelGGL(k_write<kSparseOnly>, segs, dim3(kThreads), 0, stream, idx, val, out_idx, out_val, R);
+    hipLaunchKernelGGL(k_write<kSparseOnly>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
   } else {
     hipLaunchKernelGGL(k_count, segs, dim3(kThreads), 0, stream, idx, R);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    hipLaunchKernelGGL(k_write<kDecided>, segs, dim3(kThreads), 0, stream, idx, val, out_idx, out_val, R);
+    hipLaunchKernelGGL(k_write<kDecided>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
   }
   return hipGetLastError();
 }

@@ -39,10 +39,10 @@ def test_topk_random_shapes(dev, P, N, k):
 
 
 def test_topk_ties_take_lowest_indices_rescan_path(dev):
-    P, N, k = 3, 100000, 777
+    P, N, k = 3, 300000, 777
     g = np.full((P, N), 0.5, np.float32)
     g[1, ::3] = -0.5
-    g[2, 80000:] = 0.25  # 80000 ties: still more than the list holds
+    g[2, 240000:] = 0.25  # 240000 ties: still more than the list holds
     r = np.zeros_like(g)
     _check(g, r, k, dev, expect_path=1)  # far more candidates than the list holds
 
@@ -61,8 +61,8 @@ def test_topk_sample_underestimate_takes_rescan_path(dev):
     P, N, k = 2, 1 << 20, 60000
     rng = np.random.default_rng(9)
     g = (rng.standard_normal((P, N)) * 1e-3).astype(np.float32)
-    for c in range(512):
-        s = c * (N - 64) // 511
+    for c in range(1024):  # the 1024 sampled chunks of 64 elements
+        s = c * (N - 64) // 1023
         g[:, s:s + 64] = (10.0 + rng.random((P, 64))).astype(np.float32)
     r = np.zeros_like(g)
     _check(g, r, k, dev, expect_path=1)
