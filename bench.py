@@ -29,7 +29,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-nodes", type=int, default=8, help="nodes in the oracle's timed sample")
     ap.add_argument("--seed", type=int, default=987654321)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy 1 GiB device-to-device once before warmup (reference for PMC byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_stream_wideresnet_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "sparse_gradient_reduction_amd", "csrc", f)
+                  for f in ("topk_ef.hip", "device_common.hpp")]
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per k_stream launch from the committed PMC summary, if it was
+    taken on this workload with the kernel source as it is now; else None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    with open(TRAFFIC_SUMMARY) as fh:
+        for line in fh:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("source_sha256") != kernel_source_sha256() or fields.get("workload") != workload_name:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class HipEvents:
@@ -94,6 +129,12 @@ def main():
     ws_red = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ev = HipEvents()
     step_events = [[ev.create() for _ in range(4)] for _ in range(steps)]
@@ -177,7 +218,7 @@ def main():
         "topk_rescan_nodes": int(paths[0].sum()),
         "roofline": {"kernel": "k_stream (error-feedback accumulate + candidate compaction)",
                      "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "avg_launch_ms": round(t_k1, 4), "algorithmic_bytes": k1_bytes},
         "cpu_baseline": None,
     }
