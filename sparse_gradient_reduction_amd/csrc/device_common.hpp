@@ -15,6 +15,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 load_nt(const f32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_nt(f32x4 v, f32x4* p) { __builtin_nontemporal_store(v, p); }
 
+// MI355X spreads consecutive workgroups of a launch round-robin over its 8
+// XCDs, each with its own L2. For kernels whose neighbouring work items share
+// cache lines at their edges, this maps the launch-order block id b (of B) to
+// a work item so that each XCD walks one contiguous range of work items.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t B) {
+  const uint32_t xcd = b % kXcds, i = b / kXcds;
+  const uint32_t per = B / kXcds, rem = B % kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + i;
+}
+
 // |a| ordering key: the IEEE bit pattern with the sign cleared. For finite
 // values it is monotone in |a|, and -0 and +0 share key 0.
 __device__ __forceinline__ uint32_t mag_key(float a) {

@@ -8,7 +8,7 @@
 // one index range; Appendix B, K is the size of the union of the index sets.
 //
 // One GPU holds all P contributions. The index space is cut into segments of
-// 8192 indices, the one-GPU analogue of the split phase's index-range owners;
+// 4096 indices, the one-GPU analogue of the split phase's index-range owners;
 // a workgroup owns one segment, takes each node's sub-run of pairs falling in
 // it, and merges them by scatter-adding into an LDS-resident fp64 tile of the
 // segment with an occupancy bitmap beside it (ds_add_f64 makes the sums
@@ -35,15 +35,14 @@
 namespace sparcml {
 namespace {
 
-constexpr int kSegBits = 13;
-constexpr uint32_t kSeg = 1u << kSegBits;  // 8192 indices per segment
-constexpr int kThreads = 256;              // bounds / count kernels
-constexpr int kWriteThreads = 1024;        // write kernel: 16 waves hide the load latency
-constexpr int kWords = kSeg / 32;          // bitmap words per segment (== kThreads)
+constexpr int kSegBits = 12;
+constexpr uint32_t kSeg = 1u << kSegBits;  // 4096 indices per segment
+constexpr int kThreads = 256;              // bounds kernel
+constexpr int kWords = kSeg / 32;          // bitmap words per segment
 constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
 
-static_assert(kWords == kThreads, "one bitmap word per thread");
+
 
 struct State {
   uint32_t flags;
@@ -79,6 +78,8 @@ Layout make_layout(uint32_t P, uint64_t N) {
 struct RDev {
   uint32_t P;
   uint32_t N;
+  uint32_t total;  // pairs over all nodes
+  uint32_t pad;
   uint64_t S;
   uint64_t T;
   uint64_t out_idx_cap;
@@ -103,8 +104,10 @@ __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in
   }
 }
 
-// Node-major pass: bounds[p][s] = number of node p's pairs with index < s*8192
-// (s = S stands for N), written by the pair where the run crosses into s.
+// Node-major pass: start[s][p] = absolute index of node p's first pair with
+// index >= s*4096 (s = S stands for N), written by the pair where the run
+// crosses into segment s. The table is segment-major, so a segment's
+// workgroup reads its P run starts from consecutive words.
 // Each thread takes 4 consecutive pairs, so every index is loaded once by the
 // thread that owns it and once more as the left neighbour of the next group.
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R) {
@@ -113,8 +116,14 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
   const uint64_t o0 = R.offs[p];
   const uint64_t nnz = R.offs[p + 1] - o0;
   const uint64_t S = R.S;
-  uint32_t* b = R.bounds + (uint64_t)p * (S + 1);
+  uint32_t* b = R.bounds + p;  // entry s at b[s * P]
+  const uint64_t P = R.P;
   uint32_t bad = 0u;
+  if (nnz == 0) {  // an empty node starts every segment at its offset
+    if (blockIdx.x == 0)
+      for (uint64_t s = threadIdx.x; s <= S; s += kThreads) b[s * P] = (uint32_t)o0;
+    return;
+  }
   const uint64_t stride = (uint64_t)gridDim.x * kThreads * kPer;
   for (uint64_t j0 = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer; j0 < nnz; j0 += stride) {
     uint32_t v[kPer + 1];
@@ -134,31 +143,49 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
         if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
         s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
       }
-      for (int64_t s = s_prev + 1; s <= (int64_t)s_cur; ++s) b[s] = (uint32_t)j;
+      for (int64_t s = s_prev + 1; s <= (int64_t)s_cur; ++s) b[(uint64_t)s * P] = (uint32_t)(o0 + j);
       if (j + 1 == nnz)
-        for (uint64_t s = s_cur + 1; s <= S; ++s) b[s] = (uint32_t)nnz;
+        for (uint64_t s = s_cur + 1; s <= S; ++s) b[s * P] = (uint32_t)(o0 + nnz);
     }
   }
   if (bad) atomicOr(&R.state->flags, bad);
 }
 
-// Node sub-runs of segment s: pre[p] = exclusive prefix of their lengths,
-// start[p] = absolute index of the first pair. Returns the segment's pair count.
+// Node runs of segment s: pre[p] = exclusive prefix of their lengths,
+// start[p] = absolute index of the first pair; returns the segment's pair
+// count. Starts are clamped to [0, total pairs], which keeps every later load
+// in bounds even for input whose order check failed. With at most 64 nodes
+// one wave builds the table (no block scan).
 template <int NT>
 __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
                                               uint32_t* scr) {
+  const uint32_t* b = R.bounds + s * R.P;
+  if (R.P <= (uint32_t)kWave) {
+    if (threadIdx.x < kWave) {
+      const uint32_t p = threadIdx.x;
+      uint32_t len = 0;
+      if (p < R.P) {
+        const uint32_t b0 = std::min<uint32_t>(b[p], R.total);
+        const uint32_t b1 = std::min<uint32_t>(b[R.P + p], R.total);
+        len = b1 > b0 ? b1 - b0 : 0u;
+        start[p] = b0;
+      }
+      const uint32_t inc = wave_inclusive_scan(len);
+      if (p < R.P) pre[p] = inc - len;
+      if (p == R.P - 1) pre[R.P] = inc;
+    }
+    __syncthreads();
+    return pre[R.P];
+  }
   uint32_t carry = 0;
   for (uint32_t p0 = 0; p0 < R.P; p0 += NT) {
     const uint32_t p = p0 + threadIdx.x;
     uint32_t len = 0;
     if (p < R.P) {
-      const uint64_t o0 = R.offs[p];
-      const uint64_t nnz = R.offs[p + 1] - o0;
-      const uint32_t* b = R.bounds + (uint64_t)p * (R.S + 1);
-      const uint64_t b0 = std::min<uint64_t>(b[s], nnz);
-      const uint64_t b1 = std::min<uint64_t>(b[s + 1], nnz);
-      len = b1 > b0 ? (uint32_t)(b1 - b0) : 0u;
-      start[p] = (uint32_t)(o0 + b0);
+      const uint32_t b0 = std::min<uint32_t>(b[p], R.total);
+      const uint32_t b1 = std::min<uint32_t>(b[R.P + p], R.total);
+      len = b1 > b0 ? b1 - b0 : 0u;
+      start[p] = b0;
     }
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan<NT>(len, scr, tot);
@@ -181,23 +208,33 @@ __device__ __forceinline__ uint32_t find_node(const uint32_t* pre, uint32_t P, u
   return lo;
 }
 
-__global__ __launch_bounds__(kThreads) void k_count(const uint32_t* __restrict__ idx, RDev R) {
+// One workgroup per segment: short, independent workgroups kept more
+// segments in flight than long ones walking several segments (measured). The
+// bitmap's 128 words live in the first two waves, so only they stay for the
+// compaction; the others leave once the merge is done.
+constexpr int kCountThreads = 128;
+constexpr int kWriteThreads = 512;
+constexpr int kWordWaves = kWords / kWave;  // 2
+static_assert(kWords % kWave == 0 && kWords <= kCountThreads, "bitmap words cover whole waves");
+
+template <int MAXP>
+__global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R) {
+  constexpr int NT = kCountThreads;
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[kMaxP + 1];
-  __shared__ uint32_t start[kMaxP];
-  __shared__ uint32_t scr[kThreads / kWave + 3];
-  const uint64_t s = blockIdx.x;
+  __shared__ uint32_t pre[MAXP + 1];
+  __shared__ uint32_t start[MAXP];
+  __shared__ uint32_t scr[NT / kWave + 3];
+  const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
-  bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<kThreads>(R, s, pre, start, scr);
-  constexpr int kBatch = 16;
-  for (uint32_t f0 = 0; f0 < total; f0 += kThreads * kBatch) {
+  if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
+  const uint32_t total = load_runs<NT>(R, s, pre, start, scr);
+  constexpr int kBatch = 24;
+  for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const uint32_t f = f0 + b * kThreads + threadIdx.x;
-      ii[b] = 0xFFFFFFFFu;
+      const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
         const uint32_t p = find_node(pre, R.P, f);
         ii[b] = idx[start[p] + (f - pre[p])];
@@ -206,13 +243,20 @@ __global__ __launch_bounds__(kThreads) void k_count(const uint32_t* __restrict__
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t local = ii[b] - seg_lo;
-      if (ii[b] != 0xFFFFFFFFu && local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
+      if (f0 + b * NT + threadIdx.x < total && local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
     }
   }
   __syncthreads();
-  uint32_t tot;
-  block_exclusive_scan<kThreads>((uint32_t)__popc(bits[threadIdx.x]), scr, tot);
-  if (threadIdx.x == 0) R.cnt[s] = tot;
+  const uint32_t wid = threadIdx.x / kWave;
+  if (wid >= (uint32_t)kWordWaves) return;
+  const uint32_t c = wave_sum((uint32_t)__popc(bits[threadIdx.x]));
+  if (lane_id() == 0) scr[wid] = c;
+  __syncthreads();  // only the word waves are left
+  if (threadIdx.x == 0) {
+    uint32_t tot = 0;
+    for (int w = 0; w < kWordWaves; ++w) tot += scr[w];
+    R.cnt[s] = tot;
+  }
 }
 
 __global__ __launch_bounds__(1024) void k_decide(RDev R) {
@@ -240,40 +284,37 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
 
 enum WriteMode { kDecided = 0, kDenseFirst = 1, kSparseOnly = 2 };
 
-template <int MODE>
+template <int MODE, int MAXP>
 __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restrict__ idx,
                                                          const float* __restrict__ val,
                                                          uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
                                                          RDev R) {
+  constexpr int NT = kWriteThreads;
   __shared__ double acc[kSeg];
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[kMaxP + 1];
-  __shared__ uint32_t start[kMaxP];
-  __shared__ uint32_t scr[kWriteThreads / kWave + 3];
-  const uint64_t s = blockIdx.x;
-  bool dense;
-  if (MODE == kDenseFirst) {
-    dense = true;
-  } else {
-    dense = R.state->is_dense != 0u;
-    if (MODE == kSparseOnly && dense) return;
-    if (!dense && R.cnt[s] == 0u) return;
-  }
+  __shared__ uint32_t pre[MAXP + 1];
+  __shared__ uint32_t start[MAXP];
+  __shared__ uint32_t scr[NT / kWave + 3];
+  const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
+  // these loads and the run table's go out together: one round trip
+  const bool dense = MODE == kDenseFirst ? true : R.state->is_dense != 0u;
+  const uint32_t seg_cnt = MODE == kDenseFirst ? 1u : R.cnt[s];
+  const uint32_t seg_off = MODE == kDenseFirst ? 0u : R.off[s];
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
-  for (uint32_t i = threadIdx.x; i < kSeg; i += kWriteThreads) acc[i] = 0.0;
+  for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<kWriteThreads>(R, s, pre, start, scr);
+  const uint32_t total = load_runs<NT>(R, s, pre, start, scr);
+  if (MODE == kSparseOnly && dense) return;
+  if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
   constexpr int kBatch = 8;
-  for (uint32_t f0 = 0; f0 < total; f0 += kWriteThreads * kBatch) {
+  for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch];
     float vv[kBatch];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
-      const uint32_t f = f0 + b * kWriteThreads + threadIdx.x;
-      ii[b] = 0xFFFFFFFFu;
-      vv[b] = 0.0f;
+      const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
         const uint32_t p = find_node(pre, R.P, f);
         const uint32_t j = start[p] + (f - pre[p]);
@@ -284,7 +325,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t local = ii[b] - seg_lo;
-      if (ii[b] != 0xFFFFFFFFu && local < seg_len) {
+      if (f0 + b * NT + threadIdx.x < total && local < seg_len) {
         atomicAdd(&acc[local], (double)vv[b]);
         atomicOr(&bits[local >> 5], 1u << (local & 31));
       }
@@ -292,36 +333,47 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   }
   __syncthreads();
 
-  // one bitmap word (32 indices) per thread for the first kWords threads
-  const uint32_t word = threadIdx.x < kWords ? bits[threadIdx.x] : 0u;
-  uint32_t seg_total;
-  const uint32_t ex = block_exclusive_scan<kWriteThreads>((uint32_t)__popc(word), scr, seg_total);
-  if (MODE == kDenseFirst && threadIdx.x == 0) R.cnt[s] = seg_total;
-
   if (dense) {
     float* out = out_val + seg_lo;
     if (seg_len == kSeg) {
-      for (uint32_t q = threadIdx.x; q < kSeg / 4; q += kWriteThreads) {
+      for (uint32_t q = threadIdx.x; q < kSeg / 4; q += NT) {
         const float4 o = make_float4((float)acc[4 * q], (float)acc[4 * q + 1], (float)acc[4 * q + 2],
                                      (float)acc[4 * q + 3]);
         reinterpret_cast<float4*>(out)[q] = o;
       }
     } else {
-      for (uint32_t i = threadIdx.x; i < seg_len; i += kWriteThreads) out[i] = (float)acc[i];
+      for (uint32_t i = threadIdx.x; i < seg_len; i += NT) out[i] = (float)acc[i];
     }
-  } else {
-    uint64_t pos = (uint64_t)R.off[s] + ex;
-    uint32_t w = word;
-    while (w) {
-      const uint32_t b = __ffs(w) - 1;
-      w &= w - 1;
-      const uint32_t local = threadIdx.x * 32 + b;
-      if (pos < R.out_idx_cap) {
-        out_idx[pos] = seg_lo + local;
-        out_val[pos] = (float)acc[local];
-      }
-      ++pos;
+    if (MODE != kDenseFirst) return;
+  }
+  // union size (dense-first) or ordered compaction (sparse), in the word waves
+  const uint32_t wid = threadIdx.x / kWave;
+  if (wid >= (uint32_t)kWordWaves) return;
+  const uint32_t word = bits[threadIdx.x];
+  const uint32_t c = (uint32_t)__popc(word);
+  const uint32_t inc = wave_inclusive_scan(c);
+  if (lane_id() == kWave - 1) scr[wid] = inc;
+  __syncthreads();  // only the word waves are left
+  uint32_t before = 0, tot = 0;
+  for (int w = 0; w < kWordWaves; ++w) {
+    if (w < (int)wid) before += scr[w];
+    tot += scr[w];
+  }
+  if (MODE == kDenseFirst) {
+    if (threadIdx.x == 0) R.cnt[s] = tot;
+    if (dense) return;
+  }
+  uint64_t pos = (uint64_t)seg_off + before + inc - c;
+  uint32_t w = word;
+  while (w) {
+    const uint32_t b = __ffs(w) - 1;
+    w &= w - 1;
+    const uint32_t local = threadIdx.x * 32 + b;
+    if (pos < R.out_idx_cap) {
+      out_idx[pos] = seg_lo + local;
+      out_val[pos] = (float)acc[local];
     }
+    ++pos;
   }
 }
 
@@ -338,6 +390,8 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   RDev R;
   R.P = P;
   R.N = (uint32_t)N;
+  R.total = (uint32_t)h_offsets[P];
+  R.pad = 0;
   R.S = L.S;
   R.T = T;
   R.out_idx_cap = out_idx_cap;
@@ -360,15 +414,26 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
   hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R);
   const dim3 segs((uint32_t)L.S);
+  // run tables sized for up to 256 nodes keep the write workgroups small
+  const bool small_p = P <= 256;
+#define SPARCML_WRITE(M)                                                                                  \
+  do {                                                                                                  \
+    if (small_p)                                                                                        \
+      hipLaunchKernelGGL((k_write<M, 256>), segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R); \
+    else                                                                                                \
+      hipLaunchKernelGGL((k_write<M, kMaxP>), segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R); \
+  } while (0)
   if (dense_first) {
-    hipLaunchKernelGGL(k_write<kDenseFirst>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
+    SPARCML_WRITE(kDenseFirst);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    hipLaunchKernelGGL(k_write<kSparseOnly>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
+    SPARCML_WRITE(kSparseOnly);
   } else {
-    hipLaunchKernelGGL(k_count, segs, dim3(kThreads), 0, stream, idx, R);
+    if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R);
+    else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    hipLaunchKernelGGL(k_write<kDecided>, segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R);
+    SPARCML_WRITE(kDecided);
   }
+#undef SPARCML_WRITE
   return hipGetLastError();
 }
 

@@ -16,9 +16,11 @@
 //   stream   one pass over 1024-element tiles: a = grad + residual; elements
 //            with key >= lo are compacted in index order inside the tile
 //            (wave ballots and prefix counts) and appended as one run to the
-//            node's candidate buffer, reserved with one atomic on one of 64
+//            node's candidate buffer, reserved with one atomic on one of 256
 //            counters (one counter would serialise the tiles; runs of 16
-//            neighbouring tiles share a counter, so they land close together);
+//            neighbouring tiles share a counter, so they land close together,
+//            and 256 counters exceed the slot groups in flight, so groups do
+//            not interleave inside a region);
 //            residual is written back as a, with stored candidates whose key
 //            is >= mid written as +0 (they are almost surely selected).
 //   tsum     candidate counts summed per group of 1024 tiles.
@@ -53,7 +55,7 @@ namespace {
 constexpr int kStreamThreads = 256;
 constexpr int kTile = 4 * kStreamThreads;                 // 1024 elements per tile, one float4 per thread
 constexpr int kNW = kStreamThreads / kWave;               // waves per stream block
-constexpr int kSub = 64;                                  // interleaved reservation counters per node
+constexpr int kSub = 256;                                 // reservation counters per node
 constexpr int kTilesPerSlot = 16;                         // consecutive tiles sharing a counter
 constexpr int kSampleChunks = 1024;
 constexpr int kSampleChunk = 64;
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
   for (uint32_t i = tid; i < kH0; i += kPredictThreads) D.h0[(size_t)p * kH0 + i] = 0u;
   for (uint32_t i = tid; i < kH1; i += kPredictThreads) D.h1[(size_t)p * kH1 + i] = 0u;
   for (uint32_t i = tid; i < kH2; i += kPredictThreads) D.h2[(size_t)p * kH2 + i] = 0u;
-  if (tid < kSub) D.sub[((size_t)p * kSub + tid) * 32] = 0u;
+  for (uint32_t i = tid; i < kSub; i += kPredictThreads) D.sub[((size_t)p * kSub + i) * 32] = 0u;
   for (uint32_t i = tid; i < 4096; i += kPredictThreads) h1[i] = 0u;
   for (uint32_t i = tid; i < 2048; i += kPredictThreads) h2lo[i] = h2mid[i] = 0u;
 
@@ -246,8 +248,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
   __shared__ uint32_t s_cnt[kNW];
   __shared__ uint32_t s_base;
   __shared__ uint32_t s_stored;
-  const uint32_t p = blockIdx.y;
-  const uint32_t t = blockIdx.x;
+  // each XCD streams one contiguous stretch of tiles (steadier than the
+  // default round-robin of consecutive tiles over the 8 XCDs)
+  const uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
+  const uint32_t p = w / (uint32_t)D.MT;
+  const uint32_t t = w % (uint32_t)D.MT;
   if (t >= node_tiles(D, p)) return;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id();
@@ -774,7 +779,7 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
   hipLaunchKernelGGL(k_predict, dim3(P), dim3(kPredictThreads), 0, stream, grad, residual, D);
   hipError_t e = hipSuccess;
   if (ev_start) e = hipEventRecord(ev_start, stream);
-  hipLaunchKernelGGL(k_stream, dim3((uint32_t)L.MT, P), dim3(kStreamThreads), 0, stream, grad, residual, D);
+  hipLaunchKernelGGL(k_stream, dim3((uint32_t)(L.MT * P)), dim3(kStreamThreads), 0, stream, grad, residual, D);
   if (ev_stop && e == hipSuccess) e = hipEventRecord(ev_stop, stream);
   if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess || k == 0) return e;
