@@ -67,6 +67,11 @@ def measured_traffic(workload_name: str):
         return None
 
 
+def med(xs):
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
 class HipEvents:
     """Raw HIP events (the C ABI's profiling hook takes hipEvent_t)."""
 
@@ -179,6 +184,43 @@ def main():
     t_red = sum(ev.elapsed_ms(m[2], m[3]) for m in step_events) / steps
     t_gpu_step = sum(ev.elapsed_ms(m[0], m[3]) for m in step_events) / steps
     t_k1 = sum(ev.elapsed_ms(a, b) for a, b in k1_events) / steps
+    k1_list = sorted(ev.elapsed_ms(a, b) for a, b in k1_events)
+    step_list = sorted(ev.elapsed_ms(m[0], m[3]) for m in step_events)
+
+    # ---- reduce alone, cold (LLC flushed by a 1 GiB write) and warm --------
+    def time_reduce(cold, reps=10):
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in e:
+            if cold:
+                flush.fill_(1.0)
+            a.record()
+            sg.sparse_reduce(offsets, idx.view(-1), red_in_last.view(-1), N, w.delta, out_idx=red_idx,
+                             out_val=red_val, result=red_res, workspace=ws_red)
+            b.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in e)
+
+    red_in_last = dval if B else val
+    red_cold = time_reduce(True)
+    red_warm = time_reduce(False)
+
+    # ---- attainable-bandwidth ceiling: plain torch streaming kernels on [P][N]
+    scratch = torch.empty_like(residual)
+    def time_torch(fn, reps=5):
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in e:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return min(a.elapsed_time(b) for a, b in e)
+
+    t_copy = time_torch(lambda: scratch.copy_(residual))
+    t_add = time_torch(lambda: torch.add(pool[0], residual, out=scratch))
+    del scratch
+
     K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()
     paths = sg.topk_ef_paths(ws_topk, P).cpu()
     assert flags == 0 and int(paths[1].abs().sum()) == 0
@@ -210,16 +252,26 @@ def main():
                    "ef_steps": "carried across all timed steps", "parallelism": "none (1 GPU)"},
         "breakdown_ms": {"topk_ef": round(t_topk, 4), "q4_dq4": round(t_q, 4), "sparse_reduce": round(t_red, 4),
                          "gpu_step": round(t_gpu_step, 4)},
+        "step_gpu_ms_median_min": [round(med(step_list), 4), round(step_list[0], 4)],
         "topk_gelem_per_s": round(P * N / (t_topk * 1e-3) / 1e9, 2),
         "reduce_input_gb_per_s": round(b_red_in / (t_red * 1e-3) / 1e9, 2),
         "reduce_frac_hbm_peak": round((b_red_in + b_red_out) / (t_red * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_frac_hbm_peak": round(b_step / (t_gpu_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "reduce_alone_ms": {"cold_median": round(med(red_cold), 4), "cold_min": round(red_cold[0], 4),
+                            "warm_median": round(med(red_warm), 4), "warm_min": round(red_warm[0], 4),
+                            "cold_input_gb_per_s": round(b_red_in / (med(red_cold) * 1e-3) / 1e9, 2)},
         "reduce_result": {"nnz": K, "dense": is_dense},
         "topk_rescan_nodes": int(paths[0].sum()),
         "roofline": {"kernel": "k_stream (error-feedback accumulate + candidate compaction)",
                      "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
-                     "avg_launch_ms": round(t_k1, 4), "algorithmic_bytes": k1_bytes},
+                     "avg_launch_ms": round(t_k1, 4), "median_min_launch_ms": [round(med(k1_list), 4),
+                                                                              round(k1_list[0], 4)],
+                     "algorithmic_bytes": k1_bytes},
+        "streaming_ceiling": {"what": "torch kernels on the same [P][N] fp32 arrays, best of 5",
+                              "copy_gb_per_s": round(8 * P * N / (t_copy * 1e-3) / 1e9, 1),
+                              "add_gb_per_s": round(12 * P * N / (t_add * 1e-3) / 1e9, 1),
+                              "k_stream_over_add": round(t_add / t_k1, 4)},
         "cpu_baseline": None,
     }
 

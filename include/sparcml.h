@@ -41,7 +41,7 @@ extern "C" {
 typedef enum sparcml_status {
   SPARCML_OK = 0,
   SPARCML_ERR_INVALID_ARG = 1, /* a null pointer, size, alignment or value out of range */
-  SPARCML_ERR_WORKSPACE = 2,   /* workspace null or smaller than the *_workspace size */
+  SPARCML_ERR_WORKSPACE = 2,   /* workspace null, not 256-byte aligned, or smaller than the *_workspace size */
   SPARCML_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
 } sparcml_status;
 
@@ -73,7 +73,8 @@ const char* sparcml_status_string(sparcml_status status);
  *   out_idx   device, [P][k] uint32 (may be NULL when k == 0)
  *   out_val   device, [P][k] fp32   (may be NULL when k == 0)
  *   ws        device workspace of at least sparcml_topk_ef_workspace(P,N,k)
- *             bytes; its content on entry does not matter. After the call the
+ *             bytes, 256-byte aligned (as hipMalloc returns); its content on
+ *             entry does not matter. After the call the
  *             first 4*P bytes hold, per node, which path produced the result
  *             (0: predicted-threshold candidates, 1: exact rescan), and the
  *             next 4*P bytes hold a nonzero value for a node whose internal
@@ -152,6 +153,7 @@ sparcml_status sparcml_dq4(uint32_t P, uint64_t n, uint32_t bucket,
  *              are unspecified)
  *   d_result   device, one sparcml_reduce_result, written by the GPU
  *   ws         device workspace of sparcml_sparse_reduce_workspace(P, N, nnz)
+ *              bytes, 256-byte aligned; content on entry does not matter
  *
  * Indices >= N or not strictly ascending within a node set bits in
  * d_result->flags; the outputs are then unspecified but no write leaves the

@@ -12,6 +12,7 @@ thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 sparcml_status from_hip(hipError_t e) { return e == hipSuccess ? SPARCML_OK : SPARCML_ERR_HIP; }
 
@@ -62,7 +63,7 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   if (N == 0) return SPARCML_OK;
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
+  if (!ws || !aligned256(ws) || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
   return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));
 }
 
@@ -126,7 +127,7 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const
   const uint64_t T = dense_threshold(delta, N);
   const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);
   if (cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
+  if (!ws || !aligned256(ws) || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
   const double est = expected_nnz_hint ? (double)expected_nnz_hint : sparcml_estimate_nnz(P, N, h_offsets);
   const bool dense_first = est >= (double)T;
   return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, dense_first, out_idx, cap, out_val,

@@ -23,7 +23,8 @@
 //   count    (count-first) per segment: union size from the LDS bitmap
 //   decide   exclusive scan of segment counts, K, dense iff K >= T
 //   write    per segment: fp64 LDS accumulate, then dense tile or compacted
-//            sparse pairs at the segment's offset
+//            sparse pairs (staged in LDS, stored coalesced) at the segment's
+//            offset
 // Dense-first (estimate >= T): write<dense> also counts; decide; a sparse
 // rewrite runs only if the exact K turned out below T.
 #include "device_common.hpp"
@@ -108,8 +109,8 @@ __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in
 // index >= s*4096 (s = S stands for N), written by the pair where the run
 // crosses into segment s. The table is segment-major, so a segment's
 // workgroup reads its P run starts from consecutive words.
-// Each thread takes 4 consecutive pairs, so every index is loaded once by the
-// thread that owns it and once more as the left neighbour of the next group.
+// Lanes load consecutive pairs (coalesced); a pair's left neighbour comes from
+// the lane below through a cross-lane shift, and only lane 0 loads its own.
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R) {
   constexpr int kPer = 4;
   const uint32_t p = blockIdx.y;
@@ -124,22 +125,27 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
       for (uint64_t s = threadIdx.x; s <= S; s += kThreads) b[s * P] = (uint32_t)o0;
     return;
   }
+  const bool lane0 = lane_id() == 0;
   const uint64_t stride = (uint64_t)gridDim.x * kThreads * kPer;
-  for (uint64_t j0 = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * kPer; j0 < nnz; j0 += stride) {
-    uint32_t v[kPer + 1];
-    v[0] = j0 > 0 ? idx[o0 + j0 - 1] : 0u;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) v[u + 1] = j0 + u < nnz ? idx[o0 + j0 + u] : 0u;
+  for (uint64_t j0 = (uint64_t)blockIdx.x * kThreads * kPer; j0 < nnz; j0 += stride) {
+    uint32_t v[kPer], w[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const uint64_t j = j0 + u;
-      if (j >= nnz) break;
-      const uint32_t i = v[u + 1];
+      const uint64_t j = j0 + (uint64_t)u * kThreads + threadIdx.x;
+      v[u] = j < nnz ? idx[o0 + j] : 0u;
+      w[u] = (lane0 && j > 0 && j < nnz) ? idx[o0 + j - 1] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t up = __shfl_up(v[u], 1);
+      const uint64_t j = j0 + (uint64_t)u * kThreads + threadIdx.x;
+      if (j >= nnz) continue;
+      const uint32_t i = v[u];
       const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
       if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
       int64_t s_prev = -1;
       if (j > 0) {
-        const uint32_t ip = v[u];
+        const uint32_t ip = lane0 ? w[u] : up;
         if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
         s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
       }
@@ -209,9 +215,10 @@ __device__ __forceinline__ uint32_t find_node(const uint32_t* pre, uint32_t P, u
 }
 
 // One workgroup per segment: short, independent workgroups kept more
-// segments in flight than long ones walking several segments (measured). The
-// bitmap's 128 words live in the first two waves, so only they stay for the
-// compaction; the others leave once the merge is done.
+// segments in flight than long ones walking several segments (measured).
+// Counting needs only the bitmap's 128 words, held by the first two waves;
+// the others leave once the merge is done. The sparse compaction stages the
+// segment's pairs in LDS so that its global stores are coalesced.
 constexpr int kCountThreads = 128;
 constexpr int kWriteThreads = 512;
 constexpr int kWordWaves = kWords / kWave;  // 2
@@ -259,15 +266,52 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   }
 }
 
+// Exclusive scan of the segment counts by one workgroup: each thread loads
+// 32 consecutive counts at once (one round trip per 32768 segments, 16-byte
+// loads where the run is whole), scans them in registers, and the
+// per-thread totals are scanned across the block.
 __global__ __launch_bounds__(1024) void k_decide(RDev R) {
+  constexpr int kPer = 32;
   __shared__ uint32_t scr[1024 / kWave + 3];
   uint64_t carry = 0;
-  for (uint64_t s0 = 0; s0 < R.S; s0 += 1024) {
-    const uint64_t s = s0 + threadIdx.x;
-    const uint32_t c = s < R.S ? R.cnt[s] : 0u;
+  for (uint64_t s0 = 0; s0 < R.S; s0 += 1024 * kPer) {
+    const uint64_t first = s0 + (uint64_t)threadIdx.x * kPer;
+    const bool whole = first + kPer <= R.S;  // cnt and off are 256-byte aligned, first % 32 == 0
+    uint32_t c[kPer];
+    if (whole) {
+      const uint4* src = reinterpret_cast<const uint4*>(R.cnt + first);
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) {
+        const uint4 x = src[q];
+        c[4 * q] = x.x;
+        c[4 * q + 1] = x.y;
+        c[4 * q + 2] = x.z;
+        c[4 * q + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) c[u] = first + u < R.S ? R.cnt[first + u] : 0u;
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) sum += c[u];
     uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<1024>(c, scr, tot);
-    if (s < R.S) R.off[s] = (uint32_t)(carry + ex);
+    uint32_t run = (uint32_t)carry + block_exclusive_scan<1024>(sum, scr, tot);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t x = c[u];
+      c[u] = run;
+      run += x;
+    }
+    if (whole) {
+      uint4* dst = reinterpret_cast<uint4*>(R.off + first);
+#pragma unroll
+      for (int q = 0; q < kPer / 4; ++q) dst[q] = make_uint4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (first + u < R.S) R.off[first + u] = c[u];
+    }
     carry += tot;
   }
   if (threadIdx.x == 0) {
@@ -346,34 +390,46 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
     }
     if (MODE != kDenseFirst) return;
   }
-  // union size (dense-first) or ordered compaction (sparse), in the word waves
-  const uint32_t wid = threadIdx.x / kWave;
-  if (wid >= (uint32_t)kWordWaves) return;
-  const uint32_t word = bits[threadIdx.x];
-  const uint32_t c = (uint32_t)__popc(word);
-  const uint32_t inc = wave_inclusive_scan(c);
-  if (lane_id() == kWave - 1) scr[wid] = inc;
-  __syncthreads();  // only the word waves are left
-  uint32_t before = 0, tot = 0;
-  for (int w = 0; w < kWordWaves; ++w) {
-    if (w < (int)wid) before += scr[w];
-    tot += scr[w];
-  }
-  if (MODE == kDenseFirst) {
-    if (threadIdx.x == 0) R.cnt[s] = tot;
-    if (dense) return;
-  }
-  uint64_t pos = (uint64_t)seg_off + before + inc - c;
-  uint32_t w = word;
-  while (w) {
-    const uint32_t b = __ffs(w) - 1;
-    w &= w - 1;
-    const uint32_t local = threadIdx.x * 32 + b;
-    if (pos < R.out_idx_cap) {
-      out_idx[pos] = seg_lo + local;
-      out_val[pos] = (float)acc[local];
+  if (MODE == kDenseFirst) {  // union size, in the word waves
+    const uint32_t wid = threadIdx.x / kWave;
+    if (wid >= (uint32_t)kWordWaves) return;
+    const uint32_t c = wave_sum((uint32_t)__popc(bits[threadIdx.x]));
+    if (lane_id() == 0) scr[wid] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t tot = 0;
+      for (int w = 0; w < kWordWaves; ++w) tot += scr[w];
+      R.cnt[s] = tot;
     }
-    ++pos;
+    return;
+  }
+  // ordered compaction: each thread owns 8 consecutive indices, stages its
+  // selected pairs in LDS at their rank, then the block stores them coalesced
+  constexpr int kPerT = kSeg / NT;
+  static_assert(kPerT == 8, "one bitmap byte per thread");
+  double v[kPerT];
+#pragma unroll
+  for (int r = 0; r < kPerT; ++r) v[r] = acc[kPerT * threadIdx.x + r];
+  const uint32_t byte = (bits[threadIdx.x / 4] >> (8 * (threadIdx.x & 3))) & 0xFFu;
+  uint32_t tot;
+  uint32_t q = block_exclusive_scan<NT>((uint32_t)__popc(byte), scr, tot);
+  float* sval = reinterpret_cast<float*>(acc);
+  uint32_t* sidx = reinterpret_cast<uint32_t*>(acc) + kSeg;
+#pragma unroll
+  for (int r = 0; r < kPerT; ++r) {
+    if ((byte >> r) & 1u) {
+      sval[q] = (float)v[r];
+      sidx[q] = seg_lo + kPerT * threadIdx.x + r;
+      ++q;
+    }
+  }
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < tot; i += NT) {
+    const uint64_t pos = (uint64_t)seg_off + i;
+    if (pos < R.out_idx_cap) {
+      out_idx[pos] = sidx[i];
+      out_val[pos] = sval[i];
+    }
   }
 }
 

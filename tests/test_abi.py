@@ -18,6 +18,7 @@ if not os.path.exists(sg.LIB_PATH):
 
 FAKE = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
 FAKE_ODD = ctypes.c_void_p(4100)   # not 16-byte aligned
+FAKE_WS_ODD = ctypes.c_void_p(4096 + 128)  # 16- but not 256-byte aligned
 
 
 def declared_functions():
@@ -60,6 +61,7 @@ def test_topk_argument_checks():
     assert call(4, 1000, 10, r=FAKE_ODD) == sg.ERR_INVALID_ARG
     assert call(4, 1000, 10, oi=None) == sg.ERR_INVALID_ARG
     assert call(4, 1000, 10, w=None) == sg.ERR_WORKSPACE
+    assert call(4, 1000, 10, w=FAKE_WS_ODD) == sg.ERR_WORKSPACE
     assert call(4, 1000, 10, wb=ws - 1) == sg.ERR_WORKSPACE
     assert sg.topk_ef_workspace_bytes(0, 10, 1) == 0
     assert sg.topk_ef_workspace_bytes(2, 10, 11) == 0
@@ -98,6 +100,7 @@ def test_reduce_argument_checks():
     assert call(oi=None) == sg.ERR_INVALID_ARG
     assert call(res=None) == sg.ERR_INVALID_ARG
     assert call(w=None) == sg.ERR_WORKSPACE
+    assert call(w=FAKE_WS_ODD) == sg.ERR_WORKSPACE
     assert call(wb=ws - 1) == sg.ERR_WORKSPACE
 
 

@@ -119,6 +119,32 @@ def test_segment_boundary_indices(dev):
     _check(off2, idx2, val2, N, 0.0001, dev)
 
 
+def test_segment_boundary_indices_4096(dev):
+    """Indices on both sides of every 4096-index segment edge, from several
+    nodes, with a ragged last segment."""
+    N = 5 * 4096 + 77
+    edges = [0, 4095, 4096, 8191, 8192, 12287, 12288, 16383, 16384, 20479, 20480, N - 1]
+    idx = np.array(edges, np.uint32)
+    parts = [idx, idx[1::2], idx[::3], np.zeros(0, np.uint32), idx[-2:]]
+    off = np.zeros(len(parts) + 1, np.uint64)
+    off[1:] = np.cumsum([a.size for a in parts])
+    cat = np.concatenate(parts)
+    val = np.arange(1, cat.size + 1, dtype=np.float32)
+    _check(off, cat, val, N, 0.5, dev)
+    _check(off, cat, val, N, 0.0001, dev)
+
+
+def test_many_segments_scan_rounds(dev):
+    """More than 32768 segments (the count scan takes two rounds, the second
+    ragged) in both the sparse and the dense result."""
+    N = 4096 * 40001 + 123
+    rng = np.random.default_rng(21)
+    off, idx, val = _random_sparse(rng, 3, N, 60000)
+    idx[-1] = N - 1 if idx.size and off[-1] - off[-2] > 0 and idx[-1] < N - 1 else idx[-1]
+    _check(off, idx, val, N, 0.25, dev)
+    _check(off, idx, val, N, 0.0, dev)
+
+
 def test_max_nodes(dev):
     rng = np.random.default_rng(2)
     off, idx, val = _random_sparse(rng, 1024, 50000, 40)
