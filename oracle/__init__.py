@@ -9,8 +9,10 @@ module only marshals numpy arrays through ctypes.
 Parity status per function (what pins it is in each C function's header):
   topk_ef   pinned (brute force, characterisation, special cases, EF identity)
   philox    pinned (rocRAND's Philox-4x32-10 engine, compared in a test)
-  q4 / dq4  pinned by invariants and unbiasedness; the exact code stream is
-            fixed by the reading documented in oracle.cpp
+  q4 / dq4, qsgd / dqsgd (2, 4, 8 bits)
+            pinned by invariants, unbiasedness and a recomputation from
+            rocRAND's Philox stream; the exact code stream is fixed by the
+            reading documented in oracle.cpp
   reduce    pinned (np.bincount / np.unique, overlap extremes, switch at T)
 """
 import ctypes
@@ -39,6 +41,10 @@ def lib():
         L.oracle_q4.restype = None
         L.oracle_dq4.argtypes = [u32, u64, u32, vp, vp, vp]
         L.oracle_dq4.restype = None
+        L.oracle_qsgd.argtypes = [u32, u32, u64, u32, u64, u32, u32, vp, vp, vp]
+        L.oracle_qsgd.restype = None
+        L.oracle_dqsgd.argtypes = [u32, u32, u64, u32, vp, vp, vp]
+        L.oracle_dqsgd.restype = None
         L.oracle_reduce.argtypes = [u32, u64, f64, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_reduce.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
@@ -99,6 +105,29 @@ def dq4(codes, scales, n, bucket):
     P = c.shape[0]
     out = np.zeros((P, n), np.float32)
     lib().oracle_dq4(P, n, int(bucket), _ptr(c), _ptr(s), _ptr(out))
+    return out
+
+
+def qsgd(val, bits, bucket, seed, step, node0=0):
+    """val: [P, n] float32, bits in {2, 4, 8}; row r is node node0 + r ->
+    (codes [P, ceil(n*bits/8)] u8, scales [P, ceil(n/bucket)] f32)."""
+    assert bits in (2, 4, 8)
+    v = _c(val, np.float32)
+    P, n = v.shape
+    codes = np.zeros((P, (n * bits + 7) // 8), np.uint8)
+    scales = np.zeros((P, (n + bucket - 1) // bucket), np.float32)
+    lib().oracle_qsgd(bits, P, n, int(bucket), int(seed), int(step), int(node0), _ptr(v), _ptr(codes),
+                      _ptr(scales))
+    return codes, scales
+
+
+def dqsgd(codes, scales, n, bits, bucket):
+    assert bits in (2, 4, 8)
+    c = _c(codes, np.uint8)
+    s = _c(scales, np.float32)
+    P = c.shape[0]
+    out = np.zeros((P, n), np.float32)
+    lib().oracle_dqsgd(bits, P, n, int(bucket), _ptr(c), _ptr(s), _ptr(out))
     return out
 
 

@@ -117,76 +117,102 @@ void oracle_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], ui
 }
 
 // ---------------------------------------------------------------------------
-// 4-bit stochastic quantization ([SparCML] §6 "Supporting Low-Precision
-// Communication": QSGD quantizes buckets independently and stochastically,
-// each with one full-precision scale; 2-, 4- and 8-bit outputs; §2.2: the
-// quantization noise is zero-mean).
+// b-bit stochastic quantization, b in {2, 4, 8} ([SparCML] §6 "Supporting
+// Low-Precision Communication": QSGD quantizes buckets independently and
+// stochastically, each with one full-precision scale, with 2-, 4- and 8-bit
+// outputs; §2.2: the quantization noise is zero-mean; §4: the reduced dense
+// vector may itself be quantized).
 //
-// Reading used here (the digest gives no formula): per node p, the n values
-// in their given order form buckets of `bucket` consecutive positions, the
-// last one partial. For bucket j:
-//   scale = max |v| over the bucket (exact), st = fl32(scale / 7)
+// Reading used here (the digest gives no formula): a code is a sign bit over
+// b-1 magnitude bits, so there are s = 2^(b-1) - 1 nonzero levels (1, 7,
+// 127). Per row r (node node0 + r), the n values in their given order form
+// buckets of `bucket` consecutive positions, the last one partial. For
+// bucket j:
+//   scale = max |v| over the bucket (exact), st = fl32(scale / s)
 // For position e with value v:
 //   scale == 0 -> level 0
-//   else x = fl32(fl32(|v| / scale) * 7), l = floor(x), f = x - l (exact),
-//        w = word (e & 3) of Philox4x32-10(counter {e>>2, p, step, 0},
+//   else x = fl32(fl32(|v| / scale) * s), l = floor(x), f = x - l (exact),
+//        w = word (e & 3) of Philox4x32-10(counter {e>>2, node0 + r, step, 0},
 //                                          key {lo32(seed), hi32(seed)}),
 //        u = (w >> 8) * 2^-24, level = l + (u < f)
-//   code = ((v < 0) << 3) | level, byte e>>1 of node p's row, even e in the
-//   low nibble; rows are ceil(n/2) bytes.
-// Parity: codes pinned by the level/sign invariants, the unbiasedness of
-// dq4 over many seeds and the rocRAND check of the Philox block; otherwise
-// the code-level stream is fixed by this reading, not by the pages.
+//   code = ((v < 0) << (b-1)) | level
+// Codes are packed 8/b to a byte, position e at bit (e mod 8/b) * b of byte
+// e*b/8 (lowest position in the lowest bits); rows are ceil(n*b/8) bytes and
+// unused bits are zero. The 4-bit case is the format used on the sent values.
+// Parity: codes pinned by the level/sign invariants, the unbiasedness of the
+// dequantized values over many seeds and a recomputation from rocRAND's
+// Philox stream; beyond those the code stream is fixed by this reading, not
+// by the pages.
 // ---------------------------------------------------------------------------
-void oracle_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
-               const float* val, uint8_t* codes, float* scales) {
-  const uint64_t row_bytes = (n + 1) / 2;
+static uint32_t qsgd_levels(uint32_t bits) { return (1u << (bits - 1)) - 1u; }
+
+void oracle_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                 uint32_t node0, const float* val, uint8_t* codes, float* scales) {
+  const uint32_t s = qsgd_levels(bits);
+  const float sf = (float)s;
+  const uint64_t per_byte = 8 / bits;
+  const uint64_t row_bytes = (n * bits + 7) / 8;
   const uint64_t nbuckets = (n + bucket - 1) / bucket;
   const uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
 #pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t p = 0; p < (int64_t)P; ++p) {
-    const float* v = val + (uint64_t)p * n;
-    uint8_t* row = codes + (uint64_t)p * row_bytes;
+  for (int64_t r = 0; r < (int64_t)P; ++r) {
+    const uint32_t node = node0 + (uint32_t)r;
+    const float* v = val + (uint64_t)r * n;
+    uint8_t* row = codes + (uint64_t)r * row_bytes;
     std::memset(row, 0, row_bytes);
     for (uint64_t j = 0; j < nbuckets; ++j) {
       uint64_t lo = j * bucket, hi = std::min<uint64_t>(lo + bucket, n);
       float scale = 0.0f;
       for (uint64_t e = lo; e < hi; ++e) scale = std::max(scale, std::fabs(v[e]));
-      scales[(uint64_t)p * nbuckets + j] = scale;
+      scales[(uint64_t)r * nbuckets + j] = scale;
       for (uint64_t e = lo; e < hi; ++e) {
         uint32_t level = 0;
         if (scale != 0.0f) {
           float ratio = std::fabs(v[e]) / scale;
-          float x = ratio * 7.0f;
+          float x = ratio * sf;
           float l = std::floor(x);
           float f = x - l;
-          uint32_t ctr[4] = {(uint32_t)(e >> 2), (uint32_t)p, step, 0u};
+          uint32_t ctr[4] = {(uint32_t)(e >> 2), node, step, 0u};
           uint32_t w[4];
           oracle_philox4x32_10(ctr, key, w);
           float u = (float)(w[e & 3] >> 8) * (1.0f / 16777216.0f);
           level = (uint32_t)l + (u < f ? 1u : 0u);
         }
-        uint32_t code = ((v[e] < 0.0f) ? 8u : 0u) | level;
-        row[e >> 1] |= (uint8_t)((e & 1) ? (code << 4) : code);
+        uint32_t code = ((v[e] < 0.0f) ? (1u << (bits - 1)) : 0u) | level;
+        row[e / per_byte] |= (uint8_t)(code << ((e % per_byte) * bits));
       }
     }
   }
 }
 
-// Inverse of oracle_q4: val = (sign ? -1 : +1) * fl32(level * fl32(scale / 7)).
-void oracle_dq4(uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
-                const float* scales, float* val) {
-  const uint64_t row_bytes = (n + 1) / 2;
+// Inverse of oracle_qsgd: val = (sign ? -1 : +1) * fl32(level * fl32(scale / s)).
+void oracle_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                  const float* scales, float* val) {
+  const uint32_t s = qsgd_levels(bits);
+  const uint64_t per_byte = 8 / bits;
+  const uint64_t row_bytes = (n * bits + 7) / 8;
   const uint64_t nbuckets = (n + bucket - 1) / bucket;
+  const uint32_t mask = (1u << bits) - 1u;
   for (uint64_t p = 0; p < P; ++p) {
     for (uint64_t e = 0; e < n; ++e) {
-      uint8_t byte = codes[p * row_bytes + (e >> 1)];
-      uint32_t code = (e & 1) ? (byte >> 4) : (byte & 0xF);
-      float st = scales[p * nbuckets + e / bucket] / 7.0f;
-      float mag = (float)(code & 7u) * st;
-      val[p * n + e] = (code & 8u) ? -mag : mag;
+      uint8_t byte = codes[p * row_bytes + e / per_byte];
+      uint32_t code = (byte >> ((e % per_byte) * bits)) & mask;
+      float st = scales[p * nbuckets + e / bucket] / (float)s;
+      float mag = (float)(code & s) * st;
+      val[p * n + e] = (code >> (bits - 1)) ? -mag : mag;
     }
   }
+}
+
+// The 4-bit format on node rows 0..P-1.
+void oracle_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+               const float* val, uint8_t* codes, float* scales) {
+  oracle_qsgd(4, P, n, bucket, seed, step, 0u, val, codes, scales);
+}
+
+void oracle_dq4(uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                const float* scales, float* val) {
+  oracle_dqsgd(4, P, n, bucket, codes, scales, val);
 }
 
 // ---------------------------------------------------------------------------

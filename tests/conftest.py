@@ -22,3 +22,21 @@ def dev():
     import sparse_gradient_reduction_amd as sg
     sg.lib()  # raises if the HIP library is missing: no fallback exists
     return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def rocrand_probe():
+    """A small host program that prints rocRAND's Philox-4x32-10 block for
+    each "c0 c1 c2 c3 k0 k1" line of its input (test-only reference)."""
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available to build the rocRAND probe")
+    d = tempfile.mkdtemp(prefix="philox_probe_")
+    exe = os.path.join(d, "probe")
+    subprocess.check_call([hipcc, "-O1", "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                           os.path.join(ROOT, "tests", "rocrand_philox_probe.cpp"), "-o", exe])
+    yield exe
+    shutil.rmtree(d, ignore_errors=True)
