@@ -184,6 +184,7 @@ def main():
     t_red = sum(ev.elapsed_ms(m[2], m[3]) for m in step_events) / steps
     t_gpu_step = sum(ev.elapsed_ms(m[0], m[3]) for m in step_events) / steps
     t_k1 = sum(ev.elapsed_ms(a, b) for a, b in k1_events) / steps
+    K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()  # the timed steps' result
     k1_list = sorted(ev.elapsed_ms(a, b) for a, b in k1_events)
     step_list = sorted(ev.elapsed_ms(m[0], m[3]) for m in step_events)
 
@@ -205,6 +206,54 @@ def main():
     red_cold = time_reduce(True)
     red_warm = time_reduce(False)
 
+    def time_ops(fn, reps=10):
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        fn()
+        for a, b in e:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return med(sorted(a.elapsed_time(b) for a, b in e))
+
+    extra = {}
+    if B:
+        # dequantization fused into the reduce's loader, against dq4 + reduce
+        def unfused():
+            sg.dq4(codes, scales, k, B, out=dval)
+            sg.sparse_reduce(offsets, idx.view(-1), dval.view(-1), N, w.delta, out_idx=red_idx, out_val=red_val,
+                             result=red_res, workspace=ws_red)
+
+        def fused():
+            sg.sparse_reduce_qsgd(offsets, idx.view(-1), codes.view(-1), scales.view(-1), 4, B, N, w.delta,
+                                  out_idx=red_idx, out_val=red_val, result=red_res, workspace=ws_red)
+
+        t_unf, t_fus = time_ops(unfused), time_ops(fused)
+        fused_in = P * k * 4.5 + 4 * P * ((k + B - 1) // B)
+        extra["fused_dq4_reduce"] = {"unfused_ms": round(t_unf, 4), "fused_ms": round(t_fus, 4),
+                                     "fused_input_gb_per_s": round(fused_in / (t_fus * 1e-3) / 1e9, 2)}
+    # the dense phase: a reduce whose result turns dense (delta lowered below K / N), then
+    # 4-bit quantization of the dense sum in buckets of 1024, gated on the device
+    delta_d = 0.25
+    red_idx_d = torch.empty(max(1, min(N, sg.dense_threshold(delta_d, N) - 1)), dtype=torch.int32, device=dev)
+    dcodes = torch.empty(sg.qsgd_row_bytes(4, N), dtype=torch.uint8, device=dev)
+    dscales = torch.empty((N + 1023) // 1024, dtype=torch.float32, device=dev)
+    holder = {}
+
+    def dense_reduce():
+        holder["out"] = sg.sparse_reduce(offsets, idx.view(-1), red_in_last.view(-1), N, delta_d, out_idx=red_idx_d,
+                                         out_val=red_val, result=red_res, workspace=ws_red)
+
+    t_dred = time_ops(dense_reduce)
+    t_dq = time_ops(lambda: sg.qsgd_dense_result(holder["out"], 4, 1024, args.seed, 0, 0, codes=dcodes,
+                                                 scales=dscales))
+    dK, d_is_dense, _ = holder["out"].read()
+    extra["dense_phase"] = {"delta": delta_d, "dense": d_is_dense, "reduce_ms": round(t_dred, 4),
+                            "q4_dense_result_ms": round(t_dq, 4),
+                            "q4_dense_gb_per_s": round((4 * N + N / 2 + 4 * ((N + 1023) // 1024)) / (t_dq * 1e-3) / 1e9,
+                                                       1)}
+    del red_idx_d, dcodes, dscales
+
     # ---- attainable-bandwidth ceiling: plain torch streaming kernels on [P][N]
     scratch = torch.empty_like(residual)
     def time_torch(fn, reps=5):
@@ -221,7 +270,6 @@ def main():
     t_add = time_torch(lambda: torch.add(pool[0], residual, out=scratch))
     del scratch
 
-    K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()
     paths = sg.topk_ef_paths(ws_topk, P).cpu()
     assert flags == 0 and int(paths[1].abs().sum()) == 0
 
@@ -261,6 +309,7 @@ def main():
                             "warm_median": round(med(red_warm), 4), "warm_min": round(red_warm[0], 4),
                             "cold_input_gb_per_s": round(b_red_in / (med(red_cold) * 1e-3) / 1e9, 2)},
         "reduce_result": {"nnz": K, "dense": is_dense},
+        **extra,
         "topk_rescan_nodes": int(paths[0].sum()),
         "roofline": {"kernel": "k_stream (error-feedback accumulate + candidate compaction)",
                      "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

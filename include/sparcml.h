@@ -4,9 +4,12 @@
  * Three operations of SparCML's data-parallel gradient reduction, run on one
  * GPU whose HBM holds the contributions of P nodes:
  *   - error-feedback Top-k sparsification      (sparcml_topk_ef)
- *   - 4-bit stochastic quantization and back   (sparcml_q4, sparcml_dq4)
+ *   - 2-, 4- and 8-bit stochastic quantization and back
+ *                              (sparcml_qsgd, sparcml_dqsgd; sparcml_q4, sparcml_dq4)
  *   - sum of P sparse contributions with a switch to a dense result
- *                                               (sparcml_sparse_reduce)
+ *              (sparcml_sparse_reduce; sparcml_sparse_reduce_qsgd takes
+ *               quantized values; sparcml_qsgd_dense_result quantizes a
+ *               dense result)
  *
  * Sources, cited by page title and section: "SparCML: High-Performance Sparse
  * Communication for Machine Learning" (paperlayer.ai digest of arXiv
@@ -120,6 +123,41 @@ sparcml_status sparcml_dq4(uint32_t P, uint64_t n, uint32_t bucket,
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * b-bit stochastic quantization, b in {2, 4, 8} (paper section 6, "Supporting
+ * Low-Precision Communication": QSGD with 2-, 4- and 8-bit outputs).
+ *
+ * sparcml_q4 / sparcml_dq4 above are the b = 4, node0 = 0 case. In general a
+ * code is a sign bit over b-1 magnitude bits, so a bucket has
+ * s = 2^(b-1) - 1 nonzero levels (1, 7, 127) and st = scale / s. Position e
+ * of row p gets
+ *   level = 0                                     if scale == 0
+ *   level = floor(x) + (u < x - floor(x))         otherwise,
+ *           x = (|v| / scale) * s  (two fp32 roundings, no fused multiply-add)
+ *           u = (w >> 8) * 2^-24, w = word (e & 3) of the Philox-4x32-10 block
+ *               for counter {e >> 2, node0 + p, step, 0} and key
+ *               {seed lo32, seed hi32}
+ *   code = (v < 0 ? 2^(b-1) : 0) | level
+ * Codes are packed 8/b to a byte: position e sits at bit (e mod 8/b) * b of
+ * byte e*b/8, the lowest position in the lowest bits. Each row is
+ * ceil(n*b/8) bytes and unused bits are zero. sparcml_dqsgd returns
+ * (sign ? -1 : +1) * (level * st), rounded in fp32.
+ *
+ *   bits      2, 4 or 8
+ *   bucket    multiple of 8, 8 <= bucket <= 2^20
+ *   node0     node index of row 0 in the Philox counter; node0 + P - 1 < 2^32
+ *   val       device, [P][n] fp32, 16-byte aligned
+ *   codes     device, [P][ceil(n*bits/8)] uint8
+ *   scales    device, [P][ceil(n/bucket)] fp32
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed,
+                            uint32_t step, uint32_t node0, const float* val, uint8_t* codes,
+                            float* scales, hipStream_t stream);
+
+sparcml_status sparcml_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket,
+                             const uint8_t* codes, const float* scales, float* val,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Sparse reduction with the dense switch.
  *
  * Paper section 5.1 ("Data Representation: Sparse Streams"): index-value
@@ -177,6 +215,50 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
                                      uint32_t* out_idx, float* out_val,
                                      sparcml_reduce_result* d_result,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse reduction of quantized contributions (paper section 6: the values
+ * travel as QSGD codes; dequantization is fused into the reduction's load).
+ *
+ * The same operation, arguments, workspace and errors as
+ * sparcml_sparse_reduce, except that node p's values are given as b-bit
+ * codes of its pairs, in pair order, decoded as sparcml_dqsgd decodes them
+ * while they are loaded. The result equals sparcml_sparse_reduce over the
+ * dequantized values.
+ *   bits, bucket  as for sparcml_qsgd
+ *   codes   device: node p's codes start at byte sum_{q<p} ceil(nnz_q*bits/8)
+ *   scales  device: node p's scales start at sum_{q<p} ceil(nnz_q/bucket)
+ * With nnz = n pairs on every node these are exactly the [P][ceil(n*bits/8)]
+ * and [P][ceil(n/bucket)] arrays sparcml_qsgd writes for a [P][n] input.
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N,
+                                          double delta, const uint64_t* h_offsets,
+                                          const uint32_t* idx, const uint8_t* codes,
+                                          const float* scales, uint64_t expected_nnz_hint,
+                                          uint32_t* out_idx, float* out_val,
+                                          sparcml_reduce_result* d_result, void* ws,
+                                          size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Quantization of a dense reduction result, decided on the device (paper
+ * section 4: the sum may be quantized once it has turned dense; section 6:
+ * the dense part of the exchange is the one that travels quantized).
+ *
+ * Reads d_result->is_dense on the device, in stream order after the
+ * reduction that wrote it. If it is 1, codes and scales receive
+ * sparcml_qsgd(bits, 1, N, bucket, seed, step, node, val, ...) of the dense
+ * result val[0..N); otherwise nothing is written. The host never waits.
+ *   d_result  device, written by an earlier sparcml_sparse_reduce(_qsgd) on
+ *             `stream` (or otherwise complete before this call runs)
+ *   val       device, [N] fp32, 16-byte aligned (that reduction's out_val)
+ *   codes     device, [ceil(N*bits/8)] uint8
+ *   scales    device, [ceil(N/bucket)] fp32
+ *   node      the node index in the Philox counter
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_qsgd_dense_result(uint32_t bits, uint64_t N, uint32_t bucket, uint64_t seed,
+                                         uint32_t step, uint32_t node,
+                                         const sparcml_reduce_result* d_result, const float* val,
+                                         uint8_t* codes, float* scales, hipStream_t stream);
 
 /* Uniform-model estimate of K used when no hint is given (Appendix B.1):
  * N * (1 - prod_p (1 - nnz_p / N)), capped by sum_p nnz_p. Host only. */

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) SparCML hot path: error-feedback Top-k, 4-bit stochastic
+"""MI355X (gfx950) SparCML hot path: error-feedback Top-k, 2/4/8-bit stochastic
 quantization and sparse reduction with the dense switch.
 
 Thin ctypes binding over the C ABI in include/sparcml.h: it checks tensor
@@ -53,6 +53,14 @@ def _load():
     L.sparcml_q4.restype = st
     L.sparcml_dq4.argtypes = [u32, u64, u32, vp, vp, vp, vp]
     L.sparcml_dq4.restype = st
+    L.sparcml_qsgd.argtypes = [u32, u32, u64, u32, u64, u32, u32, vp, vp, vp, vp]
+    L.sparcml_qsgd.restype = st
+    L.sparcml_dqsgd.argtypes = [u32, u32, u64, u32, vp, vp, vp, vp]
+    L.sparcml_dqsgd.restype = st
+    L.sparcml_qsgd_dense_result.argtypes = [u32, u64, u32, u64, u32, u32, vp, vp, vp, vp, vp]
+    L.sparcml_qsgd_dense_result.restype = st
+    L.sparcml_sparse_reduce_qsgd.argtypes = [u32, u32, u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
+    L.sparcml_sparse_reduce_qsgd.restype = st
     L.sparcml_sparse_reduce_workspace.argtypes = [u32, u64, u64]
     L.sparcml_sparse_reduce_workspace.restype = sz
     L.sparcml_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
@@ -152,6 +160,40 @@ def dq4(codes: torch.Tensor, scales: torch.Tensor, n: int, bucket: int, out: Opt
     return out
 
 
+def qsgd_row_bytes(bits: int, n: int) -> int:
+    return (n * bits + 7) // 8
+
+
+def qsgd(val: torch.Tensor, bits: int, bucket: int, seed: int, step: int, node0: int = 0,
+         codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """b-bit (2, 4, 8) stochastic quantization of [P, n] fp32; row p is node
+    node0 + p. Returns (codes [P, ceil(n*bits/8)] uint8, scales [P, ceil(n/bucket)] fp32)."""
+    _check_dev(val, torch.float32, "val")
+    P, n = val.shape
+    dev = val.device
+    if codes is None:
+        codes = torch.empty((P, qsgd_row_bytes(bits, n)), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((P, (n + bucket - 1) // bucket), dtype=torch.float32, device=dev)
+    st = _load().sparcml_qsgd(bits, P, n, bucket, seed & ((1 << 64) - 1), step, node0, _ptr(val), _ptr(codes),
+                              _ptr(scales), ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_qsgd")
+    return codes, scales
+
+
+def dqsgd(codes: torch.Tensor, scales: torch.Tensor, n: int, bits: int, bucket: int,
+          out: Optional[torch.Tensor] = None):
+    _check_dev(codes, torch.uint8, "codes")
+    _check_dev(scales, torch.float32, "scales")
+    P = codes.shape[0]
+    if out is None:
+        out = torch.empty((P, n), dtype=torch.float32, device=codes.device)
+    st = _load().sparcml_dqsgd(bits, P, n, bucket, _ptr(codes), _ptr(scales), _ptr(out),
+                               ctypes.c_void_p(_stream(codes.device)))
+    _raise(st, "sparcml_dqsgd")
+    return out
+
+
 # ---------------------------------------------------------------------------
 def dense_threshold(delta: float, N: int) -> int:
     t = math.ceil(delta * float(N))
@@ -191,17 +233,8 @@ class ReduceOutput:
         return K, False, flags, idx, self.out_val[:K].cpu()
 
 
-def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
-                  expected_nnz_hint: int = 0, out_idx: Optional[torch.Tensor] = None,
-                  out_val: Optional[torch.Tensor] = None, result: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> ReduceOutput:
-    """Sum of P sparse contributions (node p owns pairs [offsets[p], offsets[p+1])).
-    idx: int32 tensor holding uint32 indices, val: float32 tensor."""
-    _check_dev(idx, torch.int32, "idx")
-    _check_dev(val, torch.float32, "val")
+def _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result, workspace):
     P = len(offsets) - 1
-    off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
-    dev = idx.device
     T = dense_threshold(delta, N)
     cap = 0 if T == 0 else min(N, T - 1)
     if out_idx is None:
@@ -213,6 +246,67 @@ def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, 
     need = sparse_reduce_workspace_bytes(P, N, int(offsets[-1]))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    return out_idx, out_val, result, workspace
+
+
+def sparse_reduce_qsgd(offsets: Sequence[int], idx: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                       bits: int, bucket: int, N: int, delta: float, expected_nnz_hint: int = 0,
+                       out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+                       result: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None) -> "ReduceOutput":
+    """sparse_reduce with node p's values given as b-bit codes: node p's code
+    row starts at byte sum_{q<p} ceil(nnz_q*bits/8), its scales at
+    sum_{q<p} ceil(nnz_q/bucket) (the layout qsgd writes when every node has
+    the same count)."""
+    _check_dev(idx, torch.int32, "idx")
+    _check_dev(codes, torch.uint8, "codes")
+    _check_dev(scales, torch.float32, "scales")
+    P = len(offsets) - 1
+    off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
+    dev = idx.device
+    out_idx, out_val, result, workspace = _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result,
+                                                          workspace)
+    st = _load().sparcml_sparse_reduce_qsgd(bits, bucket, P, N, float(delta), off, _ptr(idx), _ptr(codes),
+                                            _ptr(scales), int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
+                                            _ptr(result), _ptr(workspace), workspace.numel(),
+                                            ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_sparse_reduce_qsgd")
+    return ReduceOutput(result, out_idx, out_val, N)
+
+
+def qsgd_dense_result(out: "ReduceOutput", bits: int, bucket: int, seed: int, step: int, node: int = 0,
+                      codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None):
+    """Quantize the reduction's dense result on the device if (and only if)
+    it turned out dense; codes/scales are left untouched otherwise. Returns
+    (codes [ceil(N*bits/8)] uint8, scales [ceil(N/bucket)] fp32)."""
+    N = out.N
+    dev = out.out_val.device
+    if codes is None:
+        codes = torch.zeros(qsgd_row_bytes(bits, N), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.zeros((N + bucket - 1) // bucket, dtype=torch.float32, device=dev)
+    _check_dev(codes, torch.uint8, "codes")
+    _check_dev(scales, torch.float32, "scales")
+    st = _load().sparcml_qsgd_dense_result(bits, N, bucket, seed & ((1 << 64) - 1), step, node, _ptr(out.result),
+                                           _ptr(out.out_val), _ptr(codes), _ptr(scales),
+                                           ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_qsgd_dense_result")
+    return codes, scales
+
+
+def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
+                  expected_nnz_hint: int = 0, out_idx: Optional[torch.Tensor] = None,
+                  out_val: Optional[torch.Tensor] = None, result: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None) -> ReduceOutput:
+    """Sum of P sparse contributions (node p owns pairs [offsets[p], offsets[p+1])).
+    idx: int32 tensor holding uint32 indices, val: float32 tensor."""
+    _check_dev(idx, torch.int32, "idx")
+    _check_dev(val, torch.float32, "val")
+    P = len(offsets) - 1
+    off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
+    dev = idx.device
+    out_idx, out_val, result, workspace = _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result,
+                                                          workspace)
     st = _load().sparcml_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val), int(expected_nnz_hint),
                                        _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
                                        workspace.numel(), ctypes.c_void_p(_stream(dev)))

@@ -68,7 +68,8 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
 }
 
 // --------------------------------------------------------------------------
-static bool q4_args_ok(uint32_t P, uint64_t n, uint32_t bucket) {
+static bool qsgd_args_ok(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket) {
+  if (bits != 2 && bits != 4 && bits != 8) return false;
   if (P == 0 || P > 65535u) return false;
   if (bucket < 8 || bucket > (1u << 20) || (bucket % 8) != 0) return false;
   if (n >= (1ull << 34)) return false;
@@ -77,20 +78,41 @@ static bool q4_args_ok(uint32_t P, uint64_t n, uint32_t bucket) {
   return true;
 }
 
-sparcml_status sparcml_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
-                          const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
-  if (!q4_args_ok(P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+sparcml_status sparcml_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                            uint32_t node0, const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
+  if (!qsgd_args_ok(bits, P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+  if ((uint64_t)node0 + P - 1 > 0xFFFFFFFFull) return SPARCML_ERR_INVALID_ARG;
   if (n == 0) return SPARCML_OK;
   if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
-  return from_hip(sparcml::q4_launch(P, n, bucket, seed, step, val, codes, scales, stream));
+  return from_hip(sparcml::qsgd_launch(bits, P, n, bucket, seed, step, node0, nullptr, val, codes, scales, stream));
+}
+
+sparcml_status sparcml_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                             const float* scales, float* val, hipStream_t stream) {
+  if (!qsgd_args_ok(bits, P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+  if (n == 0) return SPARCML_OK;
+  if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
+  return from_hip(sparcml::dqsgd_launch(bits, P, n, bucket, codes, scales, val, stream));
+}
+
+sparcml_status sparcml_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                          const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
+  return sparcml_qsgd(4, P, n, bucket, seed, step, 0u, val, codes, scales, stream);
 }
 
 sparcml_status sparcml_dq4(uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes, const float* scales,
                            float* val, hipStream_t stream) {
-  if (!q4_args_ok(P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
-  if (n == 0) return SPARCML_OK;
+  return sparcml_dqsgd(4, P, n, bucket, codes, scales, val, stream);
+}
+
+sparcml_status sparcml_qsgd_dense_result(uint32_t bits, uint64_t N, uint32_t bucket, uint64_t seed, uint32_t step,
+                                         uint32_t node, const sparcml_reduce_result* d_result, const float* val,
+                                         uint8_t* codes, float* scales, hipStream_t stream) {
+  if (!qsgd_args_ok(bits, 1, N, bucket) || N > kMaxN || !d_result) return SPARCML_ERR_INVALID_ARG;
+  if (N == 0) return SPARCML_OK;
   if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
-  return from_hip(sparcml::dq4_launch(P, n, bucket, codes, scales, val, stream));
+  return from_hip(sparcml::qsgd_launch(bits, 1, N, bucket, seed, step, node, &d_result->is_dense, val, codes,
+                                       scales, stream));
 }
 
 // --------------------------------------------------------------------------
@@ -112,10 +134,11 @@ size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nn
   return sparcml::reduce_workspace_bytes(P, N, total_nnz);
 }
 
-sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
-                                     const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
-                                     uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
-                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                    const uint32_t* idx, const float* val, const sparcml::ReduceQuantized* quant,
+                                    uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                    sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
   if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !std::isfinite(delta)) return SPARCML_ERR_INVALID_ARG;
   if (!h_offsets || !d_result || !out_val || !aligned16(out_val)) return SPARCML_ERR_INVALID_ARG;
   if (h_offsets[0] != 0) return SPARCML_ERR_INVALID_ARG;
@@ -123,16 +146,35 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const
     if (h_offsets[p + 1] < h_offsets[p]) return SPARCML_ERR_INVALID_ARG;
   const uint64_t total = h_offsets[P];
   if (total > kMaxN) return SPARCML_ERR_INVALID_ARG;
-  if (total > 0 && (!idx || !val)) return SPARCML_ERR_INVALID_ARG;
+  if (total > 0 && (!idx || (quant ? (!quant->codes || !quant->scales) : !val))) return SPARCML_ERR_INVALID_ARG;
   const uint64_t T = dense_threshold(delta, N);
   const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);
   if (cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
   const double est = expected_nnz_hint ? (double)expected_nnz_hint : sparcml_estimate_nnz(P, N, h_offsets);
   const bool dense_first = est >= (double)T;
-  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, dense_first, out_idx, cap, out_val,
-                                                reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws,
+  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, dense_first, out_idx, cap,
+                                                out_val, reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws,
                                                 stream));
+}
+
+sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                     const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
+                                     uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
+                                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
+                       ws_bytes, stream);
+}
+
+sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N, double delta,
+                                          const uint64_t* h_offsets, const uint32_t* idx, const uint8_t* codes,
+                                          const float* scales, uint64_t expected_nnz_hint, uint32_t* out_idx,
+                                          float* out_val, sparcml_reduce_result* d_result, void* ws,
+                                          size_t ws_bytes, hipStream_t stream) {
+  if (!qsgd_args_ok(bits, 1, 0, bucket)) return SPARCML_ERR_INVALID_ARG;
+  const sparcml::ReduceQuantized q{bits, bucket, codes, scales};
+  return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, expected_nnz_hint, out_idx, out_val, d_result, ws,
+                       ws_bytes, stream);
 }
 
 }  // extern "C"

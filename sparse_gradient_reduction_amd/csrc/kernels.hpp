@@ -14,11 +14,13 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
                           uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
-// ---- 4-bit stochastic quantization ------------------------------------------
-hipError_t q4_launch(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
-                     const float* val, uint8_t* codes, float* scales, hipStream_t stream);
-hipError_t dq4_launch(uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
-                      const float* scales, float* val, hipStream_t stream);
+// ---- b-bit stochastic quantization (b = 2, 4, 8) ----------------------------
+// gate: null, or a device word that must be nonzero for the quantizer to run
+hipError_t qsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                       uint32_t node0, const uint32_t* gate, const float* val, uint8_t* codes, float* scales,
+                       hipStream_t stream);
+hipError_t dqsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                        const float* scales, float* val, hipStream_t stream);
 
 // ---- sparse reduction --------------------------------------------------------
 struct ReduceResultDev {
@@ -27,9 +29,18 @@ struct ReduceResultDev {
   uint32_t flags;
 };
 size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t total_nnz);
+// quantized input: node p's values are the b-bit codes of its pairs, each
+// node's code row and scale row following the previous node's
+struct ReduceQuantized {
+  uint32_t bits;  // 2, 4 or 8
+  uint32_t bucket;
+  const uint8_t* codes;
+  const float* scales;
+};
+// val is used when quant is null, quant otherwise
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
-                                const uint32_t* idx, const float* val, bool dense_first,
-                                uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
+                                const uint32_t* idx, const float* val, const ReduceQuantized* quant,
+                                bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream);
 
 }  // namespace sparcml

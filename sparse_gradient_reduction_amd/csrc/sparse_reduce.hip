@@ -29,6 +29,7 @@
 // rewrite runs only if the exact K turned out below T.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "qsgd_format.hpp"
 #include "sparcml.h"
 
 #include <algorithm>
@@ -43,8 +44,6 @@ constexpr int kWords = kSeg / 32;          // bitmap words per segment
 constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
 
-
-
 struct State {
   uint32_t flags;
   uint32_t is_dense;
@@ -53,7 +52,7 @@ struct State {
 
 struct Layout {
   uint64_t S;  // segments
-  size_t state, offs, bounds, cnt, off, total;
+  size_t state, offs, qoffs, bounds, cnt, off, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -69,6 +68,7 @@ Layout make_layout(uint32_t P, uint64_t N) {
   };
   L.state = take(sizeof(State));
   L.offs = take(8ull * (P + 1));
+  L.qoffs = take(16ull * (P + 1));  // code-byte and scale offsets per node (quantized input)
   L.bounds = take(4ull * P * (L.S + 1));
   L.cnt = take(4ull * L.S);
   L.off = take(4ull * L.S);
@@ -90,6 +90,14 @@ struct RDev {
   uint32_t* cnt;
   uint32_t* off;
   ReduceResultDev* result;
+  // quantized input only: node p's codes start at byte coffs[p], its
+  // scales at soffs[p]
+  uint32_t bits;
+  uint32_t bucket;
+  const uint8_t* codes;
+  const float* scales;
+  uint64_t* coffs;
+  uint64_t* soffs;
 };
 
 struct InlineOffsets {
@@ -102,6 +110,43 @@ __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in
     R.state->flags = 0u;
     R.state->is_dense = 0u;
     R.state->K = 0ull;
+  }
+}
+
+// Quantized input: code-byte and scale offsets of every node, exclusive
+// prefix sums of ceil(nnz_p * bits / 8) and ceil(nnz_p / bucket) over the
+// nodes (one workgroup; P <= 1024).
+__global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
+  __shared__ uint64_t wc[1024 / kWave], wsc[1024 / kWave];
+  const uint32_t p = threadIdx.x;
+  uint64_t c = 0, q = 0;
+  if (p < R.P) {
+    const uint64_t nnz = R.offs[p + 1] - R.offs[p];
+    c = (nnz * R.bits + 7) / 8;
+    q = (nnz + R.bucket - 1) / R.bucket;
+  }
+  uint64_t ic = c, iq = q;  // inclusive scans within the wave
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t xc = __shfl_up(ic, d), xq = __shfl_up(iq, d);
+    if (lane_id() >= (uint32_t)d) {
+      ic += xc;
+      iq += xq;
+    }
+  }
+  const uint32_t wid = threadIdx.x / kWave;
+  if (lane_id() == kWave - 1) {
+    wc[wid] = ic;
+    wsc[wid] = iq;
+  }
+  __syncthreads();
+  uint64_t bc = 0, bq = 0;
+  for (uint32_t w = 0; w < wid; ++w) {
+    bc += wc[w];
+    bq += wsc[w];
+  }
+  if (p < R.P) {
+    R.coffs[p] = bc + ic - c;
+    R.soffs[p] = bq + iq - q;
   }
 }
 
@@ -157,25 +202,40 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
   if (bad) atomicOr(&R.state->flags, bad);
 }
 
+// Per-node tables of a quantized segment, in LDS: node-relative position of
+// the run's first pair and the node's code-byte and scale offsets.
+template <int MAXP>
+struct QRuns {
+  uint32_t rel[MAXP];
+  uint64_t cb[MAXP];
+  uint64_t sb[MAXP];
+};
+
 // Node runs of segment s: pre[p] = exclusive prefix of their lengths,
 // start[p] = absolute index of the first pair; returns the segment's pair
-// count. Starts are clamped to [0, total pairs], which keeps every later load
-// in bounds even for input whose order check failed. With at most 64 nodes
-// one wave builds the table (no block scan).
-template <int NT>
+// count. Run ends are clamped to the node's own pairs, which keeps every
+// later load inside them even for input whose order check failed. With at
+// most 64 nodes one wave builds the table (no block scan).
+template <int NT, int MAXP>
 __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
-                                              uint32_t* scr) {
+                                              uint32_t* scr, QRuns<MAXP>* q) {
   const uint32_t* b = R.bounds + s * R.P;
+  auto run = [&](uint32_t p) -> uint32_t {
+    const uint32_t lo = (uint32_t)R.offs[p], hi = (uint32_t)R.offs[p + 1];
+    const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[p], lo), hi);
+    const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[R.P + p], lo), hi);
+    start[p] = b0;
+    if (q != nullptr) {
+      q->rel[p] = b0 - lo;
+      q->cb[p] = R.coffs[p];
+      q->sb[p] = R.soffs[p];
+    }
+    return b1 > b0 ? b1 - b0 : 0u;
+  };
   if (R.P <= (uint32_t)kWave) {
     if (threadIdx.x < kWave) {
       const uint32_t p = threadIdx.x;
-      uint32_t len = 0;
-      if (p < R.P) {
-        const uint32_t b0 = std::min<uint32_t>(b[p], R.total);
-        const uint32_t b1 = std::min<uint32_t>(b[R.P + p], R.total);
-        len = b1 > b0 ? b1 - b0 : 0u;
-        start[p] = b0;
-      }
+      const uint32_t len = p < R.P ? run(p) : 0u;
       const uint32_t inc = wave_inclusive_scan(len);
       if (p < R.P) pre[p] = inc - len;
       if (p == R.P - 1) pre[R.P] = inc;
@@ -186,13 +246,7 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
   uint32_t carry = 0;
   for (uint32_t p0 = 0; p0 < R.P; p0 += NT) {
     const uint32_t p = p0 + threadIdx.x;
-    uint32_t len = 0;
-    if (p < R.P) {
-      const uint32_t b0 = std::min<uint32_t>(b[p], R.total);
-      const uint32_t b1 = std::min<uint32_t>(b[R.P + p], R.total);
-      len = b1 > b0 ? b1 - b0 : 0u;
-      start[p] = b0;
-    }
+    const uint32_t len = p < R.P ? run(p) : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan<NT>(len, scr, tot);
     if (p < R.P) pre[p] = carry + ex;
@@ -235,7 +289,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<NT>(R, s, pre, start, scr);
+  const uint32_t total = load_runs<NT, MAXP>(R, s, pre, start, scr, (QRuns<MAXP>*)nullptr);
   constexpr int kBatch = 24;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch];
@@ -328,7 +382,8 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
 
 enum WriteMode { kDecided = 0, kDenseFirst = 1, kSparseOnly = 2 };
 
-template <int MODE, int MAXP>
+// BITS = 0: fp32 values; 2, 4, 8: values decoded from b-bit codes on load
+template <int MODE, int MAXP, int BITS>
 __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restrict__ idx,
                                                          const float* __restrict__ val,
                                                          uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
@@ -339,6 +394,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   __shared__ uint32_t pre[MAXP + 1];
   __shared__ uint32_t start[MAXP];
   __shared__ uint32_t scr[NT / kWave + 3];
+  __shared__ QRuns<BITS ? MAXP : 1> qruns;
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   // these loads and the run table's go out together: one round trip
   const bool dense = MODE == kDenseFirst ? true : R.state->is_dense != 0u;
@@ -348,7 +404,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<NT>(R, s, pre, start, scr);
+  const uint32_t total = load_runs<NT, BITS ? MAXP : 1>(R, s, pre, start, scr, BITS ? &qruns : nullptr);
   if (MODE == kSparseOnly && dense) return;
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
@@ -363,7 +419,14 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
         const uint32_t p = find_node(pre, R.P, f);
         const uint32_t j = start[p] + (f - pre[p]);
         ii[b] = idx[j];
-        vv[b] = val[j];
+        if constexpr (BITS == 0) {
+          vv[b] = val[j];
+        } else {  // dequantize on load: position e of node p
+          using F = Qsgd<BITS>;
+          const uint32_t e = qruns.rel[p] + (f - pre[p]);
+          const uint32_t code = F::code_at(R.codes + qruns.cb[p], e);
+          vv[b] = F::value(code, F::step(R.scales[qruns.sb[p] + e / R.bucket]));
+        }
       }
     }
 #pragma unroll
@@ -437,9 +500,33 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 
 size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t /*total_nnz*/) { return make_layout(P, N).total; }
 
+namespace {
+
+template <int MODE, int MAXP>
+void launch_write(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
+                  uint32_t* out_idx, float* out_val, const RDev& R) {
+  const dim3 block(kWriteThreads);
+  switch (bits) {
+    case 0: hipLaunchKernelGGL((k_write<MODE, MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
+    case 2: hipLaunchKernelGGL((k_write<MODE, MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
+    case 4: hipLaunchKernelGGL((k_write<MODE, MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
+    default: hipLaunchKernelGGL((k_write<MODE, MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
+  }
+}
+
+template <int MODE>
+void launch_write(bool small_p, uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
+                  uint32_t* out_idx, float* out_val, const RDev& R) {
+  // run tables sized for up to 256 nodes keep the write workgroups small
+  if (small_p) launch_write<MODE, 256>(bits, grid, stream, idx, val, out_idx, out_val, R);
+  else launch_write<MODE, kMaxP>(bits, grid, stream, idx, val, out_idx, out_val, R);
+}
+
+}  // namespace
+
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
-                                const uint32_t* idx, const float* val, bool dense_first,
-                                uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
+                                const uint32_t* idx, const float* val, const ReduceQuantized* quant,
+                                bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream) {
   const Layout L = make_layout(P, N);
   char* w = static_cast<char*>(ws);
@@ -457,6 +544,12 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
   R.off = reinterpret_cast<uint32_t*>(w + L.off);
   R.result = d_result;
+  R.bits = quant ? quant->bits : 0u;
+  R.bucket = quant ? quant->bucket : 1u;
+  R.codes = quant ? quant->codes : nullptr;
+  R.scales = quant ? quant->scales : nullptr;
+  R.coffs = reinterpret_cast<uint64_t*>(w + L.qoffs);
+  R.soffs = R.coffs + (P + 1);
 
   uint64_t max_nnz = 0;
   for (uint32_t p = 0; p < P; ++p) max_nnz = std::max<uint64_t>(max_nnz, h_offsets[p + 1] - h_offsets[p]);
@@ -467,29 +560,21 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
     for (uint32_t i = 0; i < count; ++i) in.v[i] = h_offsets[first + i];
     hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, stream, R, first, count, in, first == 0 ? 1 : 0);
   }
+  if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
   hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R);
   const dim3 segs((uint32_t)L.S);
-  // run tables sized for up to 256 nodes keep the write workgroups small
   const bool small_p = P <= 256;
-#define SPARCML_WRITE(M)                                                                                  \
-  do {                                                                                                  \
-    if (small_p)                                                                                        \
-      hipLaunchKernelGGL((k_write<M, 256>), segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R); \
-    else                                                                                                \
-      hipLaunchKernelGGL((k_write<M, kMaxP>), segs, dim3(kWriteThreads), 0, stream, idx, val, out_idx, out_val, R); \
-  } while (0)
   if (dense_first) {
-    SPARCML_WRITE(kDenseFirst);
+    launch_write<kDenseFirst>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    SPARCML_WRITE(kSparseOnly);
+    launch_write<kSparseOnly>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
   } else {
     if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R);
     else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    SPARCML_WRITE(kDecided);
+    launch_write<kDecided>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
   }
-#undef SPARCML_WRITE
   return hipGetLastError();
 }
 

@@ -104,6 +104,33 @@ def test_reduce_argument_checks():
     assert call(wb=ws - 1) == sg.ERR_WORKSPACE
 
 
+def test_qsgd_argument_checks():
+    L = sg.lib()
+    for bits in (0, 1, 3, 16):
+        assert L.sparcml_qsgd(bits, 2, 100, 512, 1, 0, 0, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+        assert L.sparcml_dqsgd(bits, 2, 100, 512, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_qsgd(2, 2, 100, 12, 1, 0, 0, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG  # bucket % 8
+    assert L.sparcml_qsgd(8, 2, 100, 512, 1, 0, 0xFFFFFFFF, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG  # node range
+    assert L.sparcml_qsgd(8, 2, 100, 512, 1, 0, 0, FAKE_ODD, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_qsgd(2, 2, 0, 512, 1, 0, 0, None, None, None, None) == sg.OK  # nothing to do
+    assert L.sparcml_qsgd_dense_result(4, 100, 512, 1, 0, 0, None, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_qsgd_dense_result(5, 100, 512, 1, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_qsgd_dense_result(4, 1 << 33, 512, 1, 0, 0, FAKE, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    off = (ctypes.c_uint64 * 3)(0, 5, 9)
+    ws = sg.sparse_reduce_workspace_bytes(2, 100, 9)
+    f64 = ctypes.c_double
+
+    def red(bits=4, bucket=512, codes=FAKE, scales=FAKE, w=FAKE):
+        return L.sparcml_sparse_reduce_qsgd(bits, bucket, 2, 100, f64(0.25), off, FAKE, codes, scales, 0,
+                                            FAKE, FAKE, FAKE, w, ws, None)
+
+    assert red(bits=3) == sg.ERR_INVALID_ARG
+    assert red(bucket=4) == sg.ERR_INVALID_ARG
+    assert red(codes=None) == sg.ERR_INVALID_ARG
+    assert red(scales=None) == sg.ERR_INVALID_ARG
+    assert red(w=FAKE_WS_ODD) == sg.ERR_WORKSPACE
+
+
 @pytest.mark.parametrize("P,N,k", [(1, 1000, 10), (8, 1 << 20, 10485), (64, 4096, 0), (3, 17, 17)])
 def test_estimate_matches_uniform_closed_form(P, N, k):
     """Appendix B.1 (uniform sampling): E[K] = N(1 - (1 - k/N)^P), never above P*k."""
