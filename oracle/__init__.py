@@ -8,6 +8,9 @@ module only marshals numpy arrays through ctypes.
 
 Parity status per function (what pins it is in each C function's header):
   topk_ef   pinned (brute force, characterisation, special cases, EF identity)
+  topk_ef_bucketed
+            pinned (brute force per bucket, the one-bucket case equals topk_ef,
+            EF identity)
   philox    pinned (rocRAND's Philox-4x32-10 engine, compared in a test)
   q4 / dq4, qsgd / dqsgd (2, 4, 8 bits)
             pinned by invariants, unbiasedness and a recomputation from
@@ -35,6 +38,10 @@ def lib():
         u32, u64, f64, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
         L.oracle_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp]
         L.oracle_topk_ef.restype = None
+        L.oracle_bucketed_count.argtypes = [u64, u32, u32]
+        L.oracle_bucketed_count.restype = u64
+        L.oracle_topk_ef_bucketed.argtypes = [u32, u64, u32, u32, vp, vp, vp, vp]
+        L.oracle_topk_ef_bucketed.restype = None
         L.oracle_philox4x32_10.argtypes = [vp, vp, vp]
         L.oracle_philox4x32_10.restype = None
         L.oracle_q4.argtypes = [u32, u64, u32, u64, u32, vp, vp, vp]
@@ -78,6 +85,25 @@ def topk_ef(grad, residual, k):
     idx = np.zeros((P, k), np.uint32)
     val = np.zeros((P, k), np.float32)
     lib().oracle_topk_ef(P, N, k, _ptr(g), _ptr(r), _ptr(idx), _ptr(val))
+    return idx, val, r
+
+
+def bucketed_count(N, bucket, k_per_bucket):
+    return int(lib().oracle_bucketed_count(int(N), int(bucket), int(k_per_bucket)))
+
+
+def topk_ef_bucketed(grad, residual, bucket, k_per_bucket):
+    """Top-k within every bucket of `bucket` positions. grad, residual: [P, N]
+    float32. Returns (idx [P, K] u32, val [P, K] f32, r_new [P, N] f32) with K
+    = bucketed_count(N, bucket, k_per_bucket); inputs are not modified."""
+    g = _c(grad, np.float32)
+    r = _c(residual, np.float32).copy()
+    assert g.ndim == 2 and g.shape == r.shape
+    P, N = g.shape
+    K = bucketed_count(N, bucket, k_per_bucket)
+    idx = np.zeros((P, K), np.uint32)
+    val = np.zeros((P, K), np.float32)
+    lib().oracle_topk_ef_bucketed(P, N, int(bucket), int(k_per_bucket), _ptr(g), _ptr(r), _ptr(idx), _ptr(val))
     return idx, val, r
 
 

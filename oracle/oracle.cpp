@@ -85,6 +85,67 @@ void oracle_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad,
 }
 
 // ---------------------------------------------------------------------------
+// Bucketed error-feedback Top-k ([SparCML] §8.3: the CIFAR-10 runs keep k
+// entries out of every 512, e.g. 16/512; §2.2 and §4 as above for the
+// selection rule and the residual).
+//
+// Reading used here: per node, the N positions form buckets of `bucket`
+// consecutive positions (the last one partial, restarting per node, as the
+// quantizer's buckets do). Bucket j with len_j positions keeps
+// k_j = min(k_per_bucket, len_j) of them, chosen exactly as oracle_topk_ef
+// chooses within the bucket (key descending, index ascending). The node's
+// output is the concatenation over buckets of each bucket's selection in
+// ascending index order, so it is ascending overall; bucket j's pairs start
+// at j * min(k_per_bucket, bucket), and a node has K = sum_j k_j pairs (rows
+// of K).
+// The residual is a with +0 at every selected position.
+// Pinned by: brute force per bucket with numpy lexsort, the bucket >= N case
+// that is oracle_topk_ef itself, and the exact EF identity.
+// ---------------------------------------------------------------------------
+uint64_t oracle_bucketed_count(uint64_t N, uint32_t bucket, uint32_t kb) {
+  if (N == 0) return 0;
+  const uint64_t nb = (N + bucket - 1) / bucket;
+  const uint64_t last = N - (nb - 1) * bucket;
+  return (nb - 1) * (uint64_t)std::min<uint64_t>(kb, bucket) + std::min<uint64_t>(kb, last);
+}
+
+void oracle_topk_ef_bucketed(uint32_t P, uint64_t N, uint32_t bucket, uint32_t kb, const float* grad,
+                             float* residual, uint32_t* out_idx, float* out_val) {
+  const uint64_t K = oracle_bucketed_count(N, bucket, kb);
+  const uint64_t nb = (N + bucket - 1) / bucket;
+  const uint64_t kfull = std::min<uint64_t>(kb, bucket);  // pairs of a whole bucket
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t p = 0; p < (int64_t)P; ++p) {
+    const float* g = grad + (uint64_t)p * N;
+    float* r = residual + (uint64_t)p * N;
+    std::vector<float> a(N);
+    for (uint64_t i = 0; i < N; ++i) a[i] = g[i] + r[i];
+    for (uint64_t i = 0; i < N; ++i) r[i] = a[i];
+    auto before = [&](uint32_t x, uint32_t y) {
+      uint32_t kx = mag_key(a[x]), ky = mag_key(a[y]);
+      if (kx != ky) return kx > ky;
+      return x < y;
+    };
+    for (uint64_t j = 0; j < nb; ++j) {
+      const uint64_t lo = j * bucket, hi = std::min<uint64_t>(lo + bucket, N);
+      const uint64_t kj = std::min<uint64_t>(kb, hi - lo);
+      std::vector<uint32_t> order;
+      for (uint64_t i = lo; i < hi; ++i) order.push_back((uint32_t)i);
+      if (kj > 0 && kj < order.size())
+        std::nth_element(order.begin(), order.begin() + kj, order.end(), before);
+      std::vector<uint32_t> sel(order.begin(), order.begin() + kj);
+      std::sort(sel.begin(), sel.end());
+      for (uint64_t t = 0; t < kj; ++t) {
+        const uint64_t o = (uint64_t)p * K + j * kfull + t;
+        out_idx[o] = sel[t];
+        out_val[o] = a[sel[t]];
+        r[sel[t]] = +0.0f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Philox-4x32-10 block function, written from [Philox] (SC'11): four 32-bit
 // counter words, two 32-bit key words; each round multiplies counter words 0
 // and 2 by the two Philox-4x32 multipliers into 64-bit products, and builds

@@ -38,8 +38,10 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
 #pragma unroll
   for (int round = 0; round < 10; ++round) {
-    const uint32_t hi_a = __umulhi(kMulA, c0), lo_a = kMulA * c0;
-    const uint32_t hi_b = __umulhi(kMulB, c2), lo_b = kMulB * c2;
+    // one 32x32->64 multiply (v_mad_u64_u32) gives both halves
+    const uint64_t prod_a = (uint64_t)kMulA * c0, prod_b = (uint64_t)kMulB * c2;
+    const uint32_t hi_a = (uint32_t)(prod_a >> 32), lo_a = (uint32_t)prod_a;
+    const uint32_t hi_b = (uint32_t)(prod_b >> 32), lo_b = (uint32_t)prod_b;
     const uint32_t n0 = hi_b ^ c1 ^ k0;
     const uint32_t n2 = hi_a ^ c3 ^ k1;
     c0 = n0;
@@ -135,27 +137,36 @@ __global__ __launch_bounds__(256) void k_qsgd(const float* __restrict__ val, uin
   const uint64_t b0 = j * A.bucket;
   const uint64_t b1 = std::min<uint64_t>(b0 + A.bucket, A.n);
 
-  float vals[8];
+  // buckets of up to kHeld chunks stay in registers between the max and the
+  // quantization; longer ones are read twice
+  constexpr int kHeld = 2;
+  float held[kHeld][8];
   float m = 0.0f;
-  const bool single = (b1 - b0) <= (uint64_t)kChunk;
-  for (uint64_t c = b0; c < b1; c += kChunk) {
-    float v[8];
-    load8(row, c + lane * kPerLane, b1, vec_ok, v);
+  const bool fits = (b1 - b0) <= (uint64_t)kHeld * kChunk;
+  if (fits) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      m = fmaxf(m, fabsf(v[i]));
-      vals[i] = v[i];
+    for (int h = 0; h < kHeld; ++h) {
+      load8(row, b0 + (uint64_t)h * kChunk + lane * kPerLane, b1, vec_ok, held[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(held[h][i]));
+    }
+  } else {
+    for (uint64_t c = b0; c < b1; c += kChunk) {
+      float v[8];
+      load8(row, c + lane * kPerLane, b1, vec_ok, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     }
   }
   const float scale = wave_max(m);
   if (lane == 0) scales[(uint64_t)p * A.nb + j] = scale;
 
-  for (uint64_t c = b0; c < b1; c += kChunk) {
+  for (uint64_t c = b0, h = 0; c < b1; c += kChunk, ++h) {
     const uint64_t e = c + lane * kPerLane;
     float v[8];
-    if (single) {
+    if (fits) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = vals[i];
+      for (int i = 0; i < 8; ++i) v[i] = h == 0 ? held[0][i] : held[1][i];
     } else {
       load8(row, e, b1, vec_ok, v);
     }

@@ -398,6 +398,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   // these loads and the run table's go out together: one round trip
   const bool dense = MODE == kDenseFirst ? true : R.state->is_dense != 0u;
+  if (MODE == kSparseOnly && dense) return;  // the dense-first pass already wrote the result
   const uint32_t seg_cnt = MODE == kDenseFirst ? 1u : R.cnt[s];
   const uint32_t seg_off = MODE == kDenseFirst ? 0u : R.off[s];
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
@@ -405,7 +406,6 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
   const uint32_t total = load_runs<NT, BITS ? MAXP : 1>(R, s, pre, start, scr, BITS ? &qruns : nullptr);
-  if (MODE == kSparseOnly && dense) return;
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
   constexpr int kBatch = 8;

@@ -57,3 +57,25 @@ def reduce(offsets, idx, val, N, delta):
     if K >= T:
         return K, True, np.zeros(0, np.uint32), sums.astype(np.float32)
     return K, False, union.astype(np.uint32), sums[union].astype(np.float32)
+
+
+def topk_ef_bucketed(g, r, bucket, kb):
+    """Per bucket of `bucket` positions: the min(kb, len) first under (key
+    desc, index asc) by a library lexsort; output rows concatenate buckets."""
+    a = (np.asarray(g, np.float32) + np.asarray(r, np.float32)).astype(np.float32)
+    P, N = a.shape
+    idx_rows, val_rows = [], []
+    r_new = a.copy()
+    for p in range(P):
+        ii, vv = [], []
+        for lo in range(0, N, bucket):
+            hi = min(lo + bucket, N)
+            kk = keys(a[p, lo:hi])
+            order = np.lexsort((np.arange(hi - lo), -kk))
+            sel = np.sort(order[:min(kb, hi - lo)]) + lo
+            ii.append(sel)
+            vv.append(a[p, sel])
+            r_new[p, sel] = 0.0
+        idx_rows.append(np.concatenate(ii).astype(np.uint32) if ii else np.zeros(0, np.uint32))
+        val_rows.append(np.concatenate(vv).astype(np.float32) if vv else np.zeros(0, np.float32))
+    return np.stack(idx_rows), np.stack(val_rows), r_new
