@@ -254,6 +254,18 @@ def main():
                                                        1)}
     del red_idx_d, dcodes, dscales
 
+    # ---- bucketed Top-k (16 of every 512) on the same gradients and residual --
+    if w.has_topk:
+        Kb = sg.topk_bucketed_count(N, 512, 16)
+        b_idx = torch.empty((P, Kb), dtype=torch.int32, device=dev)
+        b_val = torch.empty((P, Kb), dtype=torch.float32, device=dev)
+        t_b = time_ops(lambda: sg.topk_ef_bucketed(pool[0], residual, 512, 16, out_idx=b_idx, out_val=b_val), reps=5)
+        b_bytes = 12 * P * N + 8 * P * Kb
+        extra["bucketed_topk_16_of_512"] = {"ms": round(t_b, 4), "gelem_per_s": round(P * N / (t_b * 1e-3) / 1e9, 1),
+                                           "gb_per_s": round(b_bytes / (t_b * 1e-3) / 1e9, 1),
+                                           "frac_hbm_peak": round(b_bytes / (t_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del b_idx, b_val
+
     # ---- attainable-bandwidth ceiling: plain torch streaming kernels on [P][N]
     scratch = torch.empty_like(residual)
     def time_torch(fn, reps=5):

@@ -3,7 +3,8 @@
  *
  * Three operations of SparCML's data-parallel gradient reduction, run on one
  * GPU whose HBM holds the contributions of P nodes:
- *   - error-feedback Top-k sparsification      (sparcml_topk_ef)
+ *   - error-feedback Top-k sparsification      (sparcml_topk_ef; per bucket of
+ *                                               positions: sparcml_topk_ef_bucketed)
  *   - 2-, 4- and 8-bit stochastic quantization and back
  *                              (sparcml_qsgd, sparcml_dqsgd; sparcml_q4, sparcml_dq4)
  *   - sum of P sparse contributions with a switch to a dense result
@@ -91,6 +92,35 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k,
                                const float* grad, float* residual,
                                uint32_t* out_idx, float* out_val,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Bucketed error-feedback Top-k (paper section 8.3: k entries kept out of
+ * every 512, e.g. 16/512; sections 2.2 and 4 for the selection and the
+ * residual).
+ *
+ * Per node p, the N positions form buckets of `bucket` consecutive positions
+ * (the last one partial, restarting per node). With a = grad + residual and
+ * the key and order of sparcml_topk_ef, bucket j with len_j positions keeps
+ * k_j = min(k_per_bucket, len_j) positions: the first k_j of the bucket
+ * under (key descending, index ascending). Node p's output row holds
+ * K = sparcml_topk_bucketed_count(N, bucket, k_per_bucket) = sum_j k_j pairs:
+ * bucket j's selection, ascending, starts at j * min(k_per_bucket, bucket),
+ * so the row is ascending. The residual becomes a, with +0 at every kept
+ * position (in place).
+ *
+ *   P, N      1 <= P <= 65535, N < 2^32, P*N < 2^40
+ *   bucket    64, 128, 256, 512 or 1024
+ *   grad      device, [P][N] fp32, read only
+ *   residual  device, [P][N] fp32, read and overwritten
+ *   out_idx   device, [P][K] uint32 node-relative indices (NULL if K == 0)
+ *   out_val   device, [P][K] fp32                          (NULL if K == 0)
+ * No workspace. grad and residual must not overlap each other or the outputs.
+ * ---------------------------------------------------------------------- */
+uint64_t sparcml_topk_bucketed_count(uint64_t N, uint32_t bucket, uint32_t k_per_bucket);
+
+sparcml_status sparcml_topk_ef_bucketed(uint32_t P, uint64_t N, uint32_t bucket, uint32_t k_per_bucket,
+                                        const float* grad, float* residual, uint32_t* out_idx,
+                                        float* out_val, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * 4-bit stochastic quantization (paper section 6, "Supporting Low-Precision

@@ -49,6 +49,10 @@ def _load():
     L.sparcml_topk_ef_workspace.restype = sz
     L.sparcml_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, vp]
     L.sparcml_topk_ef.restype = st
+    L.sparcml_topk_bucketed_count.argtypes = [u64, u32, u32]
+    L.sparcml_topk_bucketed_count.restype = u64
+    L.sparcml_topk_ef_bucketed.argtypes = [u32, u64, u32, u32, vp, vp, vp, vp, vp]
+    L.sparcml_topk_ef_bucketed.restype = st
     L.sparcml_q4.argtypes = [u32, u64, u32, u64, u32, vp, vp, vp, vp]
     L.sparcml_q4.restype = st
     L.sparcml_dq4.argtypes = [u32, u64, u32, vp, vp, vp, vp]
@@ -122,6 +126,32 @@ def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optiona
     st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_topk_ef")
+    return out_idx, out_val
+
+
+def topk_bucketed_count(N: int, bucket: int, k_per_bucket: int) -> int:
+    return int(_load().sparcml_topk_bucketed_count(N, bucket, k_per_bucket))
+
+
+def topk_ef_bucketed(grad: torch.Tensor, residual: torch.Tensor, bucket: int, k_per_bucket: int,
+                     out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None):
+    """Error-feedback Top-k within every bucket of `bucket` positions (64 ..
+    1024, a power of two); `residual` is updated in place. Returns (idx [P, K]
+    int32 holding uint32 indices, val [P, K] float32), K = topk_bucketed_count."""
+    _check_dev(grad, torch.float32, "grad")
+    _check_dev(residual, torch.float32, "residual")
+    if grad.dim() != 2 or grad.shape != residual.shape:
+        raise ValueError("grad and residual must both be [P, N]")
+    P, N = grad.shape
+    K = topk_bucketed_count(N, bucket, k_per_bucket)
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty((P, K), dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty((P, K), dtype=torch.float32, device=dev)
+    st = _load().sparcml_topk_ef_bucketed(P, N, bucket, k_per_bucket, _ptr(grad), _ptr(residual), _ptr(out_idx),
+                                          _ptr(out_val), ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_topk_ef_bucketed")
     return out_idx, out_val
 
 

@@ -68,6 +68,30 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
 }
 
 // --------------------------------------------------------------------------
+static bool bucket_ok(uint32_t bucket) {
+  return bucket == 64 || bucket == 128 || bucket == 256 || bucket == 512 || bucket == 1024;
+}
+
+uint64_t sparcml_topk_bucketed_count(uint64_t N, uint32_t bucket, uint32_t k_per_bucket) {
+  if (!bucket_ok(bucket) || N > kMaxN) return 0;
+  return sparcml::topk_bucketed_count(N, bucket, k_per_bucket);
+}
+
+sparcml_status sparcml_topk_ef_bucketed(uint32_t P, uint64_t N, uint32_t bucket, uint32_t k_per_bucket,
+                                        const float* grad, float* residual, uint32_t* out_idx, float* out_val,
+                                        hipStream_t stream) {
+  if (P == 0 || P > 65535u || N > kMaxN || !bucket_ok(bucket)) return SPARCML_ERR_INVALID_ARG;
+  if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
+  if (N == 0) return SPARCML_OK;
+  if (!grad || !residual) return SPARCML_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(grad) | reinterpret_cast<uintptr_t>(residual)) & 3u) return SPARCML_ERR_INVALID_ARG;
+  if (sparcml::topk_bucketed_count(N, bucket, k_per_bucket) > 0 && (!out_idx || !out_val))
+    return SPARCML_ERR_INVALID_ARG;
+  return from_hip(sparcml::topk_bucketed_launch(P, N, bucket, k_per_bucket, grad, residual, out_idx, out_val,
+                                                stream));
+}
+
+// --------------------------------------------------------------------------
 static bool qsgd_args_ok(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket) {
   if (bits != 2 && bits != 4 && bits != 8) return false;
   if (P == 0 || P > 65535u) return false;

@@ -14,6 +14,11 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
                           uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// ---- bucketed error-feedback Top-k (bucket = 64, 128, 256, 512 or 1024) -----
+uint64_t topk_bucketed_count(uint64_t N, uint32_t bucket, uint32_t k);
+hipError_t topk_bucketed_launch(uint32_t P, uint64_t N, uint32_t bucket, uint32_t k, const float* grad,
+                                float* residual, uint32_t* out_idx, float* out_val, hipStream_t stream);
+
 // ---- b-bit stochastic quantization (b = 2, 4, 8) ----------------------------
 // gate: null, or a device word that must be nonzero for the quantizer to run
 hipError_t qsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,

@@ -104,6 +104,20 @@ def test_reduce_argument_checks():
     assert call(wb=ws - 1) == sg.ERR_WORKSPACE
 
 
+def test_bucketed_argument_checks():
+    L = sg.lib()
+    for b in (0, 32, 100, 2048):
+        assert L.sparcml_topk_ef_bucketed(2, 1000, b, 16, FAKE, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+        assert L.sparcml_topk_bucketed_count(1000, b, 16) == 0
+    assert L.sparcml_topk_ef_bucketed(0, 1000, 512, 16, FAKE, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_topk_ef_bucketed(2, 1000, 512, 16, None, FAKE, FAKE, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_topk_ef_bucketed(2, 1000, 512, 16, FAKE, FAKE, None, FAKE, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_topk_ef_bucketed(2, 0, 512, 16, None, None, None, None, None) == sg.OK
+    assert L.sparcml_topk_bucketed_count(1000, 512, 16) == 32
+    assert L.sparcml_topk_bucketed_count(1000, 512, 600) == 1000
+    assert L.sparcml_topk_bucketed_count(1000, 64, 3) == 15 * 3 + 3
+
+
 def test_qsgd_argument_checks():
     L = sg.lib()
     for bits in (0, 1, 3, 16):
