@@ -59,7 +59,8 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   g_prof_start = g_prof_stop = nullptr;
   if (P == 0 || P > 65535u || N > kMaxTopkN || k > N) return SPARCML_ERR_INVALID_ARG;
   if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
-  if ((uint64_t)P * ((N + 3 + 1023) / 1024) > 0x7FFFFFFFull) return SPARCML_ERR_INVALID_ARG;  // one workgroup per tile
+  // one 256-thread workgroup per 1024-element tile, in one grid dimension of < 2^32 work-items
+  if ((uint64_t)P * ((N + 3 + 1023) / 1024) >= (1ull << 24)) return SPARCML_ERR_INVALID_ARG;
   if (N == 0) return SPARCML_OK;
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
@@ -98,7 +99,6 @@ static bool qsgd_args_ok(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket)
   if (bucket < 8 || bucket > (1u << 20) || (bucket % 8) != 0) return false;
   if (n >= (1ull << 34)) return false;
   const uint64_t nb = (n + bucket - 1) / bucket;
-  if ((nb + 3) / 4 > 0x7FFFFFFFull || (n + 2047) / 2048 > 0x7FFFFFFFull) return false;
   return true;
 }
 

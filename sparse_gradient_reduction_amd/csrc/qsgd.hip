@@ -127,63 +127,63 @@ __global__ __launch_bounds__(256) void k_qsgd(const float* __restrict__ val, uin
                                               float* __restrict__ scales, QArgs A, const uint32_t* gate) {
   if (gate != nullptr && *gate == 0u) return;  // the result this would quantize is not dense
   const uint32_t p = blockIdx.y;
-  const uint64_t j = (uint64_t)blockIdx.x * 4 + threadIdx.x / kWave;  // bucket
-  if (j >= A.nb) return;
   const uint32_t lane = lane_id();
-  const uint32_t node = A.node0 + p;
-  const float* row = val + (uint64_t)p * A.n;
-  uint8_t* crow = codes + (uint64_t)p * A.row_bytes;
-  const bool vec_ok = (((uint64_t)p * A.n) & 3u) == 0;
-  const uint64_t b0 = j * A.bucket;
-  const uint64_t b1 = std::min<uint64_t>(b0 + A.bucket, A.n);
+  for (uint64_t j = (uint64_t)blockIdx.x * 4 + threadIdx.x / kWave; j < A.nb; j += (uint64_t)gridDim.x * 4) {  // bucket
+    const uint32_t node = A.node0 + p;
+    const float* row = val + (uint64_t)p * A.n;
+    uint8_t* crow = codes + (uint64_t)p * A.row_bytes;
+    const bool vec_ok = (((uint64_t)p * A.n) & 3u) == 0;
+    const uint64_t b0 = j * A.bucket;
+    const uint64_t b1 = std::min<uint64_t>(b0 + A.bucket, A.n);
 
-  // buckets of up to kHeld chunks stay in registers between the max and the
-  // quantization; longer ones are read twice
-  constexpr int kHeld = 2;
-  float held[kHeld][8];
-  float m = 0.0f;
-  const bool fits = (b1 - b0) <= (uint64_t)kHeld * kChunk;
-  if (fits) {
-#pragma unroll
-    for (int h = 0; h < kHeld; ++h) {
-      load8(row, b0 + (uint64_t)h * kChunk + lane * kPerLane, b1, vec_ok, held[h]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(held[h][i]));
-    }
-  } else {
-    for (uint64_t c = b0; c < b1; c += kChunk) {
-      float v[8];
-      load8(row, c + lane * kPerLane, b1, vec_ok, v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    }
-  }
-  const float scale = wave_max(m);
-  if (lane == 0) scales[(uint64_t)p * A.nb + j] = scale;
-
-  for (uint64_t c = b0, h = 0; c < b1; c += kChunk, ++h) {
-    const uint64_t e = c + lane * kPerLane;
-    float v[8];
+    // buckets of up to kHeld chunks stay in registers between the max and the
+    // quantization; longer ones are read twice
+    constexpr int kHeld = 2;
+    float held[kHeld][8];
+    float m = 0.0f;
+    const bool fits = (b1 - b0) <= (uint64_t)kHeld * kChunk;
     if (fits) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = h == 0 ? held[0][i] : held[1][i];
-    } else {
-      load8(row, e, b1, vec_ok, v);
-    }
-    if (e >= b1) continue;
-    const uint32_t ctr = (uint32_t)(e >> 2);
-    const Philox4 r0 = philox4x32_10(ctr, node, A.step, 0u, A.key0, A.key1);
-    const Philox4 r1 = philox4x32_10(ctr + 1u, node, A.step, 0u, A.key0, A.key1);
-    uint64_t packed = 0u;
+      for (int h = 0; h < kHeld; ++h) {
+        load8(row, b0 + (uint64_t)h * kChunk + lane * kPerLane, b1, vec_ok, held[h]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (e + i < b1) {
-        const uint32_t rnd = i < 4 ? r0.w[i] : r1.w[i - 4];
-        packed |= (uint64_t)quantize_one<BITS>(v[i], scale, rnd) << (BITS * i);
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(held[h][i]));
+      }
+    } else {
+      for (uint64_t c = b0; c < b1; c += kChunk) {
+        float v[8];
+        load8(row, c + lane * kPerLane, b1, vec_ok, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
       }
     }
-    store_lane<BITS>(crow, e / 8 * BITS, A.row_bytes, packed, e + 8 <= A.n);
-  }
+    const float scale = wave_max(m);
+    if (lane == 0) scales[(uint64_t)p * A.nb + j] = scale;
+
+    for (uint64_t c = b0, h = 0; c < b1; c += kChunk, ++h) {
+      const uint64_t e = c + lane * kPerLane;
+      float v[8];
+      if (fits) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = h == 0 ? held[0][i] : held[1][i];
+      } else {
+        load8(row, e, b1, vec_ok, v);
+      }
+      if (e >= b1) continue;
+      const uint32_t ctr = (uint32_t)(e >> 2);
+      const Philox4 r0 = philox4x32_10(ctr, node, A.step, 0u, A.key0, A.key1);
+      const Philox4 r1 = philox4x32_10(ctr + 1u, node, A.step, 0u, A.key0, A.key1);
+      uint64_t packed = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (e + i < b1) {
+          const uint32_t rnd = i < 4 ? r0.w[i] : r1.w[i - 4];
+          packed |= (uint64_t)quantize_one<BITS>(v[i], scale, rnd) << (BITS * i);
+        }
+      }
+      store_lane<BITS>(crow, e / 8 * BITS, A.row_bytes, packed, e + 8 <= A.n);
+    }
+  }  // buckets of this wave
 }
 
 template <int BITS>
@@ -232,7 +232,8 @@ hipError_t qsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, u
                        hipStream_t stream) {
   const QArgs A = make_args(bits, P, n, bucket, seed, step, node0);
   if (n == 0) return hipSuccess;
-  const dim3 grid((uint32_t)((A.nb + 3) / 4), P);
+  // a wave per bucket, up to the 2^32 work-items a grid dimension allows
+  const dim3 grid((uint32_t)std::min<uint64_t>((A.nb + 3) / 4, 1u << 22), P);
   switch (bits) {
     case 2: hipLaunchKernelGGL(k_qsgd<2>, grid, dim3(256), 0, stream, val, codes, scales, A, gate); break;
     case 4: hipLaunchKernelGGL(k_qsgd<4>, grid, dim3(256), 0, stream, val, codes, scales, A, gate); break;
