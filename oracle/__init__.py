@@ -8,6 +8,9 @@ module only marshals numpy arrays through ctypes.
 
 Parity status per function (what pins it is in each C function's header):
   topk_ef   pinned (brute force, characterisation, special cases, EF identity)
+  topk_ef_layers
+            pinned (brute force per layer, the one-layer case equals topk_ef,
+            EF identity)
   topk_ef_bucketed
             pinned (brute force per bucket, the one-bucket case equals topk_ef,
             EF identity)
@@ -38,6 +41,8 @@ def lib():
         u32, u64, f64, vp = ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double, ctypes.c_void_p
         L.oracle_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp]
         L.oracle_topk_ef.restype = None
+        L.oracle_topk_ef_layers.argtypes = [u32, u64, u32, vp, vp, vp, vp, vp, vp]
+        L.oracle_topk_ef_layers.restype = None
         L.oracle_bucketed_count.argtypes = [u64, u32, u32]
         L.oracle_bucketed_count.restype = u64
         L.oracle_topk_ef_bucketed.argtypes = [u32, u64, u32, u32, vp, vp, vp, vp]
@@ -85,6 +90,23 @@ def topk_ef(grad, residual, k):
     idx = np.zeros((P, k), np.uint32)
     val = np.zeros((P, k), np.float32)
     lib().oracle_topk_ef(P, N, k, _ptr(g), _ptr(r), _ptr(idx), _ptr(val))
+    return idx, val, r
+
+
+def topk_ef_layers(grad, residual, layer_offsets, ks):
+    """Top-k of every layer [off[l], off[l+1]) of every node. grad, residual:
+    [P, N] float32. Returns (idx [P, sum k] u32, val, r_new [P, N])."""
+    g = _c(grad, np.float32)
+    r = _c(residual, np.float32).copy()
+    P, N = g.shape
+    off = _c(layer_offsets, np.uint64)
+    kk = _c(ks, np.uint64)
+    nl = kk.size
+    assert off.size == nl + 1 and off[0] == 0 and off[-1] == N
+    K = int(kk.sum())
+    idx = np.zeros((P, K), np.uint32)
+    val = np.zeros((P, K), np.float32)
+    lib().oracle_topk_ef_layers(P, N, nl, _ptr(off), _ptr(kk), _ptr(g), _ptr(r), _ptr(idx), _ptr(val))
     return idx, val, r
 
 

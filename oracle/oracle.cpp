@@ -85,6 +85,52 @@ void oracle_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad,
 }
 
 // ---------------------------------------------------------------------------
+// Per-layer error-feedback Top-k ([SparCML] §8.4: the ResNet50 runs sparsify
+// each layer; §2.2 and §4 as above).
+//
+// Every node's vector is cut into layers [off[l], off[l+1]); oracle_topk_ef's
+// selection runs on each layer of each node by itself, keeping k[l]
+// positions. Node p's output row is the concatenation over layers of each
+// layer's selection (node-relative indices, ascending), so it is ascending;
+// layer l starts at sum_{l'<l} k[l']. The residual is a with +0 at every
+// kept position.
+// Pinned by: brute force with numpy lexsort per layer, the one-layer case
+// that is oracle_topk_ef itself, and the exact EF identity.
+// ---------------------------------------------------------------------------
+void oracle_topk_ef_layers(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k,
+                           const float* grad, float* residual, uint32_t* out_idx, float* out_val) {
+  uint64_t K = 0;
+  for (uint32_t l = 0; l < nl; ++l) K += k[l];
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t p = 0; p < (int64_t)P; ++p) {
+    const float* g = grad + (uint64_t)p * N;
+    float* r = residual + (uint64_t)p * N;
+    std::vector<float> a(N);
+    for (uint64_t i = 0; i < N; ++i) a[i] = g[i] + r[i];
+    for (uint64_t i = 0; i < N; ++i) r[i] = a[i];
+    auto before = [&](uint32_t x, uint32_t y) {
+      uint32_t kx = mag_key(a[x]), ky = mag_key(a[y]);
+      if (kx != ky) return kx > ky;
+      return x < y;
+    };
+    uint64_t o = (uint64_t)p * K;
+    for (uint32_t l = 0; l < nl; ++l) {
+      std::vector<uint32_t> order;
+      for (uint64_t i = off[l]; i < off[l + 1]; ++i) order.push_back((uint32_t)i);
+      const uint64_t kl = k[l];
+      if (kl > 0 && kl < order.size()) std::nth_element(order.begin(), order.begin() + kl, order.end(), before);
+      std::vector<uint32_t> sel(order.begin(), order.begin() + kl);
+      std::sort(sel.begin(), sel.end());
+      for (uint64_t t = 0; t < kl; ++t, ++o) {
+        out_idx[o] = sel[t];
+        out_val[o] = a[sel[t]];
+        r[sel[t]] = +0.0f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Bucketed error-feedback Top-k ([SparCML] §8.3: the CIFAR-10 runs keep k
 // entries out of every 512, e.g. 16/512; §2.2 and §4 as above for the
 // selection rule and the residual).

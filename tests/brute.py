@@ -79,3 +79,24 @@ def topk_ef_bucketed(g, r, bucket, kb):
         idx_rows.append(np.concatenate(ii).astype(np.uint32) if ii else np.zeros(0, np.uint32))
         val_rows.append(np.concatenate(vv).astype(np.float32) if vv else np.zeros(0, np.float32))
     return np.stack(idx_rows), np.stack(val_rows), r_new
+
+
+def topk_ef_layers(g, r, off, ks):
+    """Per layer [off[l], off[l+1]): the k[l] first under (key desc, index asc)
+    by a library lexsort; rows concatenate the layers."""
+    a = (np.asarray(g, np.float32) + np.asarray(r, np.float32)).astype(np.float32)
+    P, N = a.shape
+    r_new = a.copy()
+    idx_rows, val_rows = [], []
+    for p in range(P):
+        ii = []
+        for l in range(len(ks)):
+            lo, hi = int(off[l]), int(off[l + 1])
+            kk = keys(a[p, lo:hi])
+            order = np.lexsort((np.arange(hi - lo), -kk))
+            ii.append(np.sort(order[:int(ks[l])]) + lo)
+        sel = np.concatenate(ii).astype(np.int64) if ii else np.zeros(0, np.int64)
+        idx_rows.append(sel.astype(np.uint32))
+        val_rows.append(a[p, sel])
+        r_new[p, sel] = 0.0
+    return np.stack(idx_rows), np.stack(val_rows), r_new
