@@ -266,6 +266,23 @@ def main():
                                            "frac_hbm_peak": round(b_bytes / (t_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del b_idx, b_val
 
+    # ---- per-layer Top-k (1% of each of 160 layers) on the same arrays ------
+    if w.has_topk:
+        off_l = W.layer_offsets(N, 160)
+        ks_l = W.layer_ks(off_l, 1, 100)
+        Kl = int(ks_l.sum())
+        l_idx = torch.empty((P, Kl), dtype=torch.int32, device=dev)
+        l_val = torch.empty((P, Kl), dtype=torch.float32, device=dev)
+        l_ws = torch.empty(sg.topk_ef_layers_workspace_bytes(P, N, off_l, ks_l), dtype=torch.uint8, device=dev)
+        t_l = time_ops(lambda: sg.topk_ef_layers(pool[1], residual, off_l, ks_l, out_idx=l_idx, out_val=l_val,
+                                                 workspace=l_ws), reps=5)
+        l_bytes = 12 * P * N + 8 * P * Kl
+        extra["layers_topk_1pct_of_160"] = {"ms": round(t_l, 4), "gelem_per_s": round(P * N / (t_l * 1e-3) / 1e9, 1),
+                                            "gb_per_s": round(l_bytes / (t_l * 1e-3) / 1e9, 1),
+                                            "frac_hbm_peak": round(l_bytes / (t_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                            "rescan_rows": int(l_ws[: 4 * P * 160].view(torch.int32).sum())}
+        del l_idx, l_val, l_ws
+
     # ---- attainable-bandwidth ceiling: plain torch streaming kernels on [P][N]
     scratch = torch.empty_like(residual)
     def time_torch(fn, reps=5):

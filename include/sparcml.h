@@ -3,8 +3,9 @@
  *
  * Three operations of SparCML's data-parallel gradient reduction, run on one
  * GPU whose HBM holds the contributions of P nodes:
- *   - error-feedback Top-k sparsification      (sparcml_topk_ef; per bucket of
- *                                               positions: sparcml_topk_ef_bucketed)
+ *   - error-feedback Top-k sparsification      (sparcml_topk_ef; per layer:
+ *                sparcml_topk_ef_layers; per bucket of positions:
+ *                sparcml_topk_ef_bucketed)
  *   - 2-, 4- and 8-bit stochastic quantization and back
  *                              (sparcml_qsgd, sparcml_dqsgd; sparcml_q4, sparcml_dq4)
  *   - sum of P sparse contributions with a switch to a dense result
@@ -69,7 +70,7 @@ const char* sparcml_status_string(sparcml_status status);
  *   residual_i = a_i, except +0.0 at the positions in S      (in place)
  * Hence residual_new + scatter(out_val) == grad + residual_old exactly.
  *
- *   P, N      nodes and elements per node; 1 <= P <= 65535, N <= 2^32 - 2^17,
+ *   P, N      nodes and elements per node; 1 <= P <= 65535, N <= 2^32 - 2^19,
  *             P * ceil((N+3)/1024) < 2^24 (about P*N < 2^34: one workgroup
  *             per 1024-element tile in one launch dimension)
  *   k         0 <= k <= N (k == 0 only folds grad into residual)
@@ -93,6 +94,40 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k,
                                const float* grad, float* residual,
                                uint32_t* out_idx, float* out_val,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-layer error-feedback Top-k (paper section 8.4: the ResNet50 runs
+ * sparsify layer by layer; sections 2.2 and 4 as for sparcml_topk_ef).
+ *
+ * Every node's vector is cut into nlayers layers: layer l is positions
+ * [off[l], off[l+1]). The selection of sparcml_topk_ef runs on each layer of
+ * each node by itself, keeping k[l] positions of layer l. Node p's output
+ * row holds K = sum_l k[l] pairs: layer l's selection, ascending, starts at
+ * sum_{l'<l} k[l'], with node-relative indices (off[l] + position in the
+ * layer), so the row is ascending. The residual becomes a with +0 at every
+ * kept position (in place).
+ *
+ *   P, N       1 <= P, P * nlayers <= 65535, N <= 2^32 - 2^19, P*N < 2^40;
+ *              about P*N + 1024*P*nlayers < 2^34 (one workgroup per
+ *              1024-element tile of every layer, in one launch dimension)
+ *   h_layer_offsets  host, [nlayers+1] uint64: 0 = off[0] <= ... <= off[nlayers] = N
+ *   h_k        host, [nlayers] uint64, k[l] <= off[l+1] - off[l]
+ *   grad, residual   device, [P][N] fp32, 16-byte aligned (as sparcml_topk_ef)
+ *   out_idx, out_val device, [P][K] (may be NULL when K == 0)
+ *   ws         device workspace of sparcml_topk_ef_layers_workspace(...) bytes,
+ *              256-byte aligned; afterwards its first 4*P*nlayers bytes hold
+ *              the path of every (node, layer) row (row p*nlayers + l), the
+ *              next 4*P*nlayers bytes its consistency flag, as for
+ *              sparcml_topk_ef
+ * sparcml_topk_ef_layers_workspace returns 0 for arguments the call rejects.
+ * ---------------------------------------------------------------------- */
+size_t sparcml_topk_ef_layers_workspace(uint32_t P, uint64_t N, uint32_t nlayers,
+                                        const uint64_t* h_layer_offsets, const uint64_t* h_k);
+
+sparcml_status sparcml_topk_ef_layers(uint32_t P, uint64_t N, uint32_t nlayers,
+                                      const uint64_t* h_layer_offsets, const uint64_t* h_k,
+                                      const float* grad, float* residual, uint32_t* out_idx,
+                                      float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Bucketed error-feedback Top-k (paper section 8.3: k entries kept out of

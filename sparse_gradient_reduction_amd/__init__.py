@@ -49,6 +49,10 @@ def _load():
     L.sparcml_topk_ef_workspace.restype = sz
     L.sparcml_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, vp]
     L.sparcml_topk_ef.restype = st
+    L.sparcml_topk_ef_layers_workspace.argtypes = [u32, u64, u32, vp, vp]
+    L.sparcml_topk_ef_layers_workspace.restype = sz
+    L.sparcml_topk_ef_layers.argtypes = [u32, u64, u32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sparcml_topk_ef_layers.restype = st
     L.sparcml_topk_bucketed_count.argtypes = [u64, u32, u32]
     L.sparcml_topk_bucketed_count.restype = u64
     L.sparcml_topk_ef_bucketed.argtypes = [u32, u64, u32, u32, vp, vp, vp, vp, vp]
@@ -126,6 +130,42 @@ def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optiona
     st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
                            _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_topk_ef")
+    return out_idx, out_val
+
+
+def _u64s(xs):
+    xs = [int(x) for x in xs]
+    return (ctypes.c_uint64 * len(xs))(*xs)
+
+
+def topk_ef_layers_workspace_bytes(P: int, N: int, layer_offsets: Sequence[int], ks: Sequence[int]) -> int:
+    return int(_load().sparcml_topk_ef_layers_workspace(P, N, len(ks), _u64s(layer_offsets), _u64s(ks)))
+
+
+def topk_ef_layers(grad: torch.Tensor, residual: torch.Tensor, layer_offsets: Sequence[int], ks: Sequence[int],
+                   out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """Error-feedback Top-k of every layer [off[l], off[l+1]) of every node,
+    keeping ks[l] of layer l; `residual` is updated in place. Returns (idx
+    [P, sum ks] int32 holding node-relative uint32 indices, val [P, sum ks])."""
+    _check_dev(grad, torch.float32, "grad")
+    _check_dev(residual, torch.float32, "residual")
+    if grad.dim() != 2 or grad.shape != residual.shape:
+        raise ValueError("grad and residual must both be [P, N]")
+    P, N = grad.shape
+    K = sum(int(x) for x in ks)
+    dev = grad.device
+    if out_idx is None:
+        out_idx = torch.empty((P, K), dtype=torch.int32, device=dev)
+    if out_val is None:
+        out_val = torch.empty((P, K), dtype=torch.float32, device=dev)
+    need = topk_ef_layers_workspace_bytes(P, N, layer_offsets, ks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = _load().sparcml_topk_ef_layers(P, N, len(ks), _u64s(layer_offsets), _u64s(ks), _ptr(grad), _ptr(residual),
+                                        _ptr(out_idx), _ptr(out_val), _ptr(workspace), workspace.numel(),
+                                        ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_topk_ef_layers")
     return out_idx, out_val
 
 

@@ -17,7 +17,7 @@ bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) 
 sparcml_status from_hip(hipError_t e) { return e == hipSuccess ? SPARCML_OK : SPARCML_ERR_HIP; }
 
 constexpr uint64_t kMaxN = 0xFFFFFFFFull;       // indices are uint32
-constexpr uint64_t kMaxTopkN = 0xFFFE0000ull;   // candidate slots stay below 2^32
+constexpr uint64_t kMaxTopkN = 0xFFF80000ull;   // 2^32 - 2^19: candidate slot offsets stay below 2^32 - 2^18
 
 // T = ceil(delta * N) in double, clamped to [0, N + 1]
 uint64_t dense_threshold(double delta, uint64_t N) {
@@ -66,6 +66,40 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
   return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));
+}
+
+// --------------------------------------------------------------------------
+// layers: off[0] = 0 < ... nondecreasing ... off[nl] = N, k[l] <= off[l+1] - off[l]
+static bool layers_ok(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {
+  if (P == 0 || P > 65535u || nl == 0 || (uint64_t)P * nl > 65535u || N > kMaxTopkN) return false;
+  if (!off || !k || off[0] != 0 || off[nl] != N) return false;
+  for (uint32_t l = 0; l < nl; ++l)
+    if (off[l + 1] < off[l] || k[l] > off[l + 1] - off[l]) return false;
+  if ((uint64_t)P * N >= (1ull << 40)) return false;
+  // one 256-thread workgroup per tile of every layer, in one grid dimension
+  return sparcml::topk_layers_stream_blocks(P, N, nl, off, k) < (1ull << 24);
+}
+
+size_t sparcml_topk_ef_layers_workspace(uint32_t P, uint64_t N, uint32_t nlayers, const uint64_t* h_layer_offsets,
+                                        const uint64_t* h_k) {
+  if (!layers_ok(P, N, nlayers, h_layer_offsets, h_k)) return 0;
+  return sparcml::topk_layers_workspace_bytes(P, N, nlayers, h_layer_offsets, h_k);
+}
+
+sparcml_status sparcml_topk_ef_layers(uint32_t P, uint64_t N, uint32_t nlayers, const uint64_t* h_layer_offsets,
+                                      const uint64_t* h_k, const float* grad, float* residual, uint32_t* out_idx,
+                                      float* out_val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!layers_ok(P, N, nlayers, h_layer_offsets, h_k)) return SPARCML_ERR_INVALID_ARG;
+  if (N == 0) return SPARCML_OK;
+  if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
+  uint64_t K = 0;
+  for (uint32_t l = 0; l < nlayers; ++l) K += h_k[l];
+  if (K > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
+  if (!ws || !aligned256(ws) ||
+      ws_bytes < sparcml::topk_layers_workspace_bytes(P, N, nlayers, h_layer_offsets, h_k))
+    return SPARCML_ERR_WORKSPACE;
+  return from_hip(sparcml::topk_layers_launch(P, N, nlayers, h_layer_offsets, h_k, grad, residual, out_idx, out_val,
+                                              ws, stream));
 }
 
 // --------------------------------------------------------------------------

@@ -130,6 +130,37 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return excl;
 }
 
+// 64-bit exclusive prefix sum across a workgroup of NT threads; every
+// thread gets `total`. scratch holds NT / kWave + 1 values.
+template <int NT>
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* scratch, uint64_t& total) {
+  constexpr int NW = NT / kWave;
+  const uint32_t lane = lane_id();
+  const uint32_t wid = threadIdx.x / kWave;
+  uint64_t inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t t = __shfl_up(inc, d, kWave);
+    if (lane >= (uint32_t)d) inc += t;
+  }
+  if (lane == kWave - 1) scratch[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const uint64_t t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[NW] = run;
+  }
+  __syncthreads();
+  const uint64_t excl = scratch[wid] + inc - v;
+  total = scratch[NW];
+  __syncthreads();
+  return excl;
+}
+
 // Radix-select step over a histogram `hist` of `nbins` bins (LDS or global):
 // finds the highest bin b such that the count of items in bins >= b reaches
 // `rank` (1-based, rank >= 1), and the count in bins strictly above b. If the

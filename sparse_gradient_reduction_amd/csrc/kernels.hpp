@@ -14,6 +14,13 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
                           uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// ---- per-layer error-feedback Top-k (layers [off[l], off[l+1]) of every node)
+size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);
+uint64_t topk_layers_stream_blocks(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);
+hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k,
+                              const float* grad, float* residual, uint32_t* out_idx, float* out_val, void* ws,
+                              hipStream_t stream);
+
 // ---- bucketed error-feedback Top-k (bucket = 64, 128, 256, 512 or 1024) -----
 uint64_t topk_bucketed_count(uint64_t N, uint32_t bucket, uint32_t k);
 hipError_t topk_bucketed_launch(uint32_t P, uint64_t N, uint32_t bucket, uint32_t k, const float* grad,

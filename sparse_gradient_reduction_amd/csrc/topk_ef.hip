@@ -40,6 +40,11 @@
 //            residual fixed where the guess `mid` was wrong (selected below
 //            mid: zeroed; not selected at or above mid: restored).
 //
+// A selection row is either a node's whole vector (the [P][N] call) or one
+// layer of one node (the per-layer call); every kernel is templated on which,
+// the first computing a row's geometry from (P, N, k), the second reading it
+// from a per-row table, with a tile-to-row table for the stream kernel.
+//
 // Every element with key >= T* is a candidate whenever the list holds at
 // least k of them, so both paths give the same exact result; the sample only
 // decides how much the candidate work costs.
@@ -67,6 +72,7 @@ constexpr int kChunkThreads = 256;
 constexpr int kChunkIt = 16;
 constexpr int kChunk = kChunkThreads * kChunkIt;          // 4096 candidates per chunk
 constexpr uint32_t kNotStored = 0xFFFFFFFFu;
+constexpr uint32_t kSmallLayer = 16384;  // per-layer call: rows this small skip the sampled prediction
 
 struct NodeState {
   uint32_t lo;      // candidate threshold on the key
@@ -79,51 +85,160 @@ struct NodeState {
   uint32_t pad;
 };
 
+// Sizes of one row's slices of the workspace arrays (integer formulas shared
+// by the host, which sizes the workspace and the grids, and the device, which
+// lays out the per-layer row table).
+struct RowSize {
+  uint64_t nt;      // tiles (stream workgroups)
+  uint64_t groups;  // groups of kGroup tiles
+  uint64_t chunks;  // chunk slots (rescan worst case)
+  uint64_t capS;    // candidate slots per counter region
+  uint32_t nsub;    // counter regions
+  uint32_t schunks; // sample chunks
+  uint32_t npass;   // blocks of the select / count / emit grids
+};
+constexpr size_t kRowBytes = 12 * sizeof(uint64_t);
+
+// A whole node: kSub regions with a whole tile of slack each. A layer: as
+// many regions as it has runs of kTilesPerSlot tiles (at most kSub), with the
+// slack of its largest possible run.
+__host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t k, bool layer) {
+  RowSize z;
+  z.nt = (n + (base & 3u) + kTile - 1) / kTile;
+  z.groups = (z.nt + kGroup - 1) / kGroup;
+  z.chunks = (n + kChunk - 1) / kChunk;
+  if (z.chunks == 0) z.chunks = 1;
+  const uint64_t want = n < 2 * k + 65536 ? n : 2 * k + 65536;
+  if (!layer) {
+    z.nsub = kSub;
+    z.capS = (want + kSub - 1) / kSub + kTile;
+    z.schunks = kSampleChunks;
+    z.npass = 0;
+  } else {
+    uint64_t ns = (z.nt + kTilesPerSlot - 1) / kTilesPerSlot;
+    ns = ns < 1 ? 1 : (ns > (uint64_t)kSub ? (uint64_t)kSub : ns);
+    z.nsub = (uint32_t)ns;
+    z.capS = (want + ns - 1) / ns + (n < (uint64_t)kTile ? n : (uint64_t)kTile);
+    // a sample of about one element in 16 (16 to 1024 chunks): small layers
+    // are cheap to sample and their candidate lists are short anyway
+    uint64_t sc = n / (16 * kSampleChunk);
+    z.schunks = (uint32_t)(sc < 16 ? 16 : (sc > (uint64_t)kSampleChunks ? (uint64_t)kSampleChunks : sc));
+    // select / count / emit blocks: one per 8192 expected candidates, 1..64
+    const uint64_t est = n < 2 * k + 4096 ? n : 2 * k + 4096;
+    uint64_t np = (est + 8191) / 8192;
+    z.npass = (uint32_t)(np < 1 ? 1 : (np > 64 ? 64 : np));
+  }
+  return z;
+}
+
+// Totals over the rows: what the workspace holds.
+struct Plan {
+  uint64_t rows;
+  uint64_t cand;    // candidate slots
+  uint64_t tiles;   // tile words
+  uint64_t groups;  // group words
+  uint64_t chunks;  // chunk words
+  uint64_t passes;  // per-layer call: select / count / emit blocks
+  bool layers;      // per-layer call: row table and block-to-row tables too
+};
+
 struct Layout {
-  uint64_t capS;  // candidate slots per counter region
-  uint64_t cap;   // candidate slots per node (kSub * capS)
-  uint64_t MT;    // tiles per node (slots)
-  uint64_t MG;    // tile groups per node
-  uint64_t MC;    // chunks per node (slots, rescan worst case)
+  uint64_t capS;  // whole-node call: candidate slots per counter region
+  uint64_t cap;   // whole-node call: candidate slots per node (kSub * capS)
+  uint64_t MT;    // whole-node call: tiles per node (slots)
+  uint64_t MG;    // whole-node call: tile groups per node
+  uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
   size_t info, err, state, h0, h1, h2, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
-      cout, total;
+      cout, rows, tile_row, group_row, pass_row, loff, lk, lkoff, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Layout make_layout(uint32_t P, uint64_t N, uint64_t k) {
+Layout make_layout(const Plan& Q, uint64_t nlayers) {
   Layout L{};
-  const uint64_t want = std::min<uint64_t>(N, 2 * k + 65536);
-  L.capS = (want + kSub - 1) / kSub + kTile;  // + one whole tile of slack per region
-  L.cap = kSub * L.capS;
-  L.MT = (N + 3 + kTile - 1) / kTile;
-  L.MG = (L.MT + kGroup - 1) / kGroup;
-  L.MC = std::max<uint64_t>(1, (N + kChunk - 1) / kChunk);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
     o = align_up(o + bytes, 256);
     return at;
   };
-  L.info = take(8ull * P);  // [P] path per node, then [P] consistency flags
-  L.err = L.info + 4ull * P;
-  L.state = take(sizeof(NodeState) * P);
-  L.h0 = take(4ull * P * kH0);
-  L.h1 = take(4ull * P * kH1);
-  L.h2 = take(4ull * P * kH2);
-  L.sub = take(128ull * P * kSub);  // one counter per 128-byte line
-  L.cand = take(8ull * P * L.cap);
-  L.oidx = take(4ull * P * L.cap);
-  L.oval = take(4ull * P * L.cap);
-  L.tmeta = take(8ull * P * L.MT);
-  L.gsum = take(4ull * P * L.MG);
-  L.gbase = take(4ull * P * L.MG);
-  L.cgt = take(4ull * P * L.MC);
-  L.ceq = take(4ull * P * L.MC);
-  L.ceqoff = take(4ull * P * L.MC);
-  L.cout = take(4ull * P * L.MC);
+  const uint64_t R = Q.rows;
+  L.info = take(8ull * R);  // [rows] path per row, then [rows] consistency flags
+  L.err = L.info + 4ull * R;
+  L.state = take(sizeof(NodeState) * R);
+  L.h0 = take(4ull * R * kH0);
+  L.h1 = take(4ull * R * kH1);
+  L.h2 = take(4ull * R * kH2);
+  L.sub = take(128ull * R * kSub);  // one counter per 128-byte line
+  L.cand = take(8ull * Q.cand);
+  L.oidx = take(4ull * Q.cand);
+  L.oval = take(4ull * Q.cand);
+  L.tmeta = take(8ull * Q.tiles);
+  L.gsum = take(4ull * Q.groups);
+  L.gbase = take(4ull * Q.groups);
+  L.cgt = take(4ull * Q.chunks);
+  L.ceq = take(4ull * Q.chunks);
+  L.ceqoff = take(4ull * Q.chunks);
+  L.cout = take(4ull * Q.chunks);
+  if (Q.layers) {
+    L.rows = take(kRowBytes * R);
+    L.tile_row = take(4ull * Q.tiles);
+    L.group_row = take(4ull * Q.groups);
+    L.pass_row = take(4ull * Q.passes);
+    L.loff = take(8ull * (nlayers + 1));
+    L.lk = take(8ull * nlayers);
+    L.lkoff = take(8ull * nlayers);
+  }
   L.total = o;
   return L;
+}
+
+Layout make_node_layout(uint32_t P, uint64_t N, uint64_t k) {
+  const RowSize z = row_size(0, N, k, false);
+  Plan Q;
+  Q.rows = P;
+  Q.cand = (uint64_t)P * kSub * z.capS;
+  // tile slots: a node whose first element is not float4-aligned may straddle one more tile
+  const uint64_t MT = (N + 3 + kTile - 1) / kTile;
+  const uint64_t MG = (MT + kGroup - 1) / kGroup;
+  Q.tiles = (uint64_t)P * MT;
+  Q.groups = (uint64_t)P * MG;
+  Q.chunks = (uint64_t)P * z.chunks;
+  Q.passes = 0;
+  Q.layers = false;
+  Layout L = make_layout(Q, 0);
+  L.capS = z.capS;
+  L.cap = kSub * z.capS;
+  L.MT = MT;
+  L.MG = MG;
+  L.MC = z.chunks;
+  return L;
+}
+
+// per-layer call: node p, layer l is row p * nlayers + l
+struct LayerPlan {
+  Plan Q;
+  uint64_t max_groups, max_cap, max_tiles, K;
+};
+
+LayerPlan plan_layers(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {
+  LayerPlan lp{};
+  lp.Q.rows = (uint64_t)P * nl;
+  lp.Q.layers = true;
+  for (uint32_t l = 0; l < nl; ++l) lp.K += k[l];
+  for (uint32_t p = 0; p < P; ++p)
+    for (uint32_t l = 0; l < nl; ++l) {
+      const RowSize z = row_size((uint64_t)p * N + off[l], off[l + 1] - off[l], k[l], true);
+      lp.Q.cand += (uint64_t)z.nsub * z.capS;
+      lp.Q.tiles += z.nt;
+      lp.Q.groups += z.groups;
+      lp.Q.chunks += z.chunks;
+      lp.Q.passes += z.npass;
+      lp.max_groups = std::max<uint64_t>(lp.max_groups, z.groups);
+      lp.max_cap = std::max<uint64_t>(lp.max_cap, (uint64_t)z.nsub * z.capS);
+      lp.max_tiles = std::max<uint64_t>(lp.max_tiles, z.nt);
+    }
+  return lp;
 }
 
 struct Dev {
@@ -155,22 +270,80 @@ struct Dev {
   uint32_t* ceq;
   uint32_t* ceqoff;
   uint32_t* cout;
+  const struct Row* rows;     // per-layer call: row table
+  const uint32_t* tile_row;   // per-layer call: row of every stream workgroup
+  const uint32_t* group_row;  // per-layer call: row of every tile group
+  const uint32_t* pass_row;   // per-layer call: row of every select / count / emit block
 };
 
-__device__ __forceinline__ uint32_t node_tiles(const Dev& D, uint32_t p) {
-  const uint32_t phi = (uint32_t)(((uint64_t)p * D.N) & 3u);
-  return (uint32_t)(((uint64_t)D.N + phi + kTile - 1) / kTile);
+// Geometry of one selection row. For the [P][N] call it follows from (P, N,
+// k); for the per-layer call it is read from a table in the workspace.
+struct Row {
+  uint64_t base;    // first element in grad / residual
+  uint64_t cand;    // first slot of the row's candidate regions (cand, oidx, oval)
+  uint64_t tile0;   // first tile word (tmeta); in the per-layer call also the first stream workgroup
+  uint64_t group0;  // first group word (gsum, gbase)
+  uint64_t chunk0;  // first chunk word (cgt, ceq, ceqoff, cout)
+  uint64_t out0;    // first output pair
+  uint32_t n;       // elements
+  uint32_t k;       // pairs to select
+  uint32_t capS;    // candidate slots per counter region
+  uint32_t nsub;    // counter regions in use (<= kSub)
+  uint32_t rs_lo;   // sample rank of the candidate threshold
+  uint32_t rs_mid;  // sample rank of the zeroing threshold
+  uint32_t idx_off; // added to row-local indices in the output
+  uint32_t schunks; // sample chunks of kSampleChunk elements
+  uint32_t pass0;   // per-layer call: first block of the row in the select / count / emit grids
+  uint32_t npass;   // blocks of those grids for the row
+  uint32_t pad[2];
+};
+
+static_assert(sizeof(Row) == kRowBytes, "row table entry size used by the workspace layout");
+
+template <bool ROWS>
+__device__ __forceinline__ Row row_of(const Dev& D, uint32_t p) {
+  if constexpr (ROWS) {
+    return D.rows[p];
+  } else {
+    Row R;
+    R.base = (uint64_t)p * D.N;
+    R.cand = (uint64_t)p * D.cap;
+    R.tile0 = (uint64_t)p * D.MT;
+    R.group0 = (uint64_t)p * D.MG;
+    R.chunk0 = (uint64_t)p * D.MC;
+    R.out0 = (uint64_t)p * D.k;
+    R.n = D.N;
+    R.k = D.k;
+    R.capS = (uint32_t)D.capS;
+    R.nsub = kSub;
+    R.rs_lo = D.rs_lo;
+    R.rs_mid = D.rs_mid;
+    R.idx_off = 0u;
+    R.schunks = kSampleChunks;
+    R.pass0 = 0u;
+    R.npass = 0u;
+    R.pad[0] = R.pad[1] = 0u;
+    return R;
+  }
+}
+
+// tiles of a row: its first tile starts at the float4 group holding its first
+// element
+__device__ __forceinline__ uint32_t row_tiles(const Row& R) {
+  const uint32_t phi = (uint32_t)(R.base & 3u);
+  return (uint32_t)(((uint64_t)R.n + phi + kTile - 1) / kTile);
 }
 
 // Source of the select, count and emit kernels: the ordered candidate list,
-// or the whole node (residual holds a) on the rescan path.
-__device__ __forceinline__ uint64_t source_len(const Dev& D, uint32_t p, bool rescan) {
-  return rescan ? (uint64_t)D.N : (uint64_t)D.state[p].count;
+// or the whole row (residual holds a) on the rescan path.
+__device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint32_t p, bool rescan) {
+  return rescan ? (uint64_t)R.n : (uint64_t)D.state[p].count;
 }
 
 // ---------------------------------------------------------------------------
 // predict: reset the node's state and choose the two key thresholds.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __restrict__ g,
                                                              const float* __restrict__ r, Dev D) {
   __shared__ uint32_t h1[4096];
@@ -178,33 +351,38 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
   __shared__ uint32_t h2mid[2048];
   __shared__ uint32_t scr[kPredictThreads / kWave + 3];
   const uint32_t p = blockIdx.x;
+  const Row R = row_of<ROWS>(D, p);
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < kH0; i += kPredictThreads) D.h0[(size_t)p * kH0 + i] = 0u;
   for (uint32_t i = tid; i < kH1; i += kPredictThreads) D.h1[(size_t)p * kH1 + i] = 0u;
   for (uint32_t i = tid; i < kH2; i += kPredictThreads) D.h2[(size_t)p * kH2 + i] = 0u;
   for (uint32_t i = tid; i < kSub; i += kPredictThreads) D.sub[((size_t)p * kSub + i) * 32] = 0u;
-  for (uint32_t i = tid; i < 4096; i += kPredictThreads) h1[i] = 0u;
-  for (uint32_t i = tid; i < 2048; i += kPredictThreads) h2lo[i] = h2mid[i] = 0u;
 
   uint32_t lo, mid;
-  if (D.k == 0) {
+  if (R.k == 0) {
     lo = mid = 0xFFFFFFFFu;  // keys are < 2^31: no candidate
-  } else if (D.k == D.N) {
+  } else if (R.k == R.n) {
     lo = mid = 0u;  // everything is selected
+  } else if (ROWS && R.n <= kSmallLayer) {
+    lo = 0u;            // a small layer is its own candidate list
+    mid = 0xFFFFFFFFu;  // and nothing is zeroed before the selection
   } else {
+    for (uint32_t i = tid; i < 4096; i += kPredictThreads) h1[i] = 0u;
+    for (uint32_t i = tid; i < 2048; i += kPredictThreads) h2lo[i] = h2mid[i] = 0u;
     __syncthreads();
-    const uint64_t base = (uint64_t)p * D.N;
-    const bool whole = D.N <= (uint32_t)kSample;
+    const uint64_t base = R.base;
+    const uint32_t nsamp = R.schunks * kSampleChunk;  // <= kSample
+    const bool whole = R.n <= nsamp;
     uint32_t keys[kSample / kPredictThreads];
 #pragma unroll
     for (int j = 0; j < kSample / kPredictThreads; ++j) {
       const uint32_t i = j * kPredictThreads + tid;
       uint32_t key = 0xFFFFFFFFu;  // marks "no sample"
       if (whole) {
-        if (i < D.N) key = mag_key(g[base + i] + r[base + i]);
-      } else {
+        if (i < R.n) key = mag_key(g[base + i] + r[base + i]);
+      } else if (i < nsamp) {
         const uint32_t c = i / kSampleChunk, o = i % kSampleChunk;
-        const uint64_t start = (uint64_t)c * (D.N - kSampleChunk) / (kSampleChunks - 1);
+        const uint64_t start = (uint64_t)c * (R.n - kSampleChunk) / (R.schunks - 1);
         key = mag_key(g[base + start + o] + r[base + start + o]);
       }
       keys[j] = key;
@@ -214,8 +392,8 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
       if (keys[j] != 0xFFFFFFFFu) atomicAdd(&h1[keys[j] >> 19], 1u);
     __syncthreads();
     uint32_t b_lo, a_lo, b_mid, a_mid;
-    block_find_suffix<kPredictThreads>(h1, 4096, D.rs_lo, scr, b_lo, a_lo);
-    block_find_suffix<kPredictThreads>(h1, 4096, D.rs_mid, scr, b_mid, a_mid);
+    block_find_suffix<kPredictThreads>(h1, 4096, R.rs_lo, scr, b_lo, a_lo);
+    block_find_suffix<kPredictThreads>(h1, 4096, R.rs_mid, scr, b_mid, a_mid);
 #pragma unroll
     for (int j = 0; j < kSample / kPredictThreads; ++j) {
       const uint32_t key = keys[j];
@@ -225,8 +403,8 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
     }
     __syncthreads();
     uint32_t c_lo, x_lo, c_mid, x_mid;
-    block_find_suffix<kPredictThreads>(h2lo, 2048, D.rs_lo - a_lo, scr, c_lo, x_lo);
-    block_find_suffix<kPredictThreads>(h2mid, 2048, D.rs_mid - a_mid, scr, c_mid, x_mid);
+    block_find_suffix<kPredictThreads>(h2lo, 2048, R.rs_lo - a_lo, scr, c_lo, x_lo);
+    block_find_suffix<kPredictThreads>(h2mid, 2048, R.rs_mid - a_mid, scr, c_mid, x_mid);
     lo = (b_lo << 19) | (c_lo << 8);
     mid = (b_mid << 19) | (c_mid << 8);
   }
@@ -243,6 +421,7 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
 // ---------------------------------------------------------------------------
 // stream: a = g + r, per-tile candidate compaction, residual write-back.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restrict__ g,
                                                            float* __restrict__ r, Dev D) {
   __shared__ uint32_t s_cnt[kNW];
@@ -251,14 +430,23 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
   // each XCD streams one contiguous stretch of tiles (steadier than the
   // default round-robin of consecutive tiles over the 8 XCDs)
   const uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
-  const uint32_t p = w / (uint32_t)D.MT;
-  const uint32_t t = w % (uint32_t)D.MT;
-  if (t >= node_tiles(D, p)) return;
+  uint32_t p, t;
+  Row R;
+  if constexpr (ROWS) {
+    p = D.tile_row[w];
+    R = row_of<true>(D, p);
+    t = w - (uint32_t)R.tile0;
+  } else {
+    p = w / (uint32_t)D.MT;
+    t = w % (uint32_t)D.MT;
+    R = row_of<false>(D, p);
+    if (t >= row_tiles(R)) return;
+  }
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id();
   const uint32_t wid = tid / kWave;
-  const uint32_t N = D.N;
-  const uint64_t pN = (uint64_t)p * N;
+  const uint32_t N = R.n;
+  const uint64_t pN = R.base;
   const int64_t e0 = (int64_t)t * kTile - (int64_t)(pN & 3u) + 4 * (int64_t)tid;  // node-local index
   const uint64_t grp = (pN >> 2) + (uint64_t)t * (kTile / 4) + tid;               // float4 group
   const uint32_t lo = D.state[p].lo;
@@ -311,19 +499,19 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
       s_cnt[i] = run;
       run += c;
     }
-    const uint32_t sc = (t / kTilesPerSlot) % kSub;
+    const uint32_t sc = (t / kTilesPerSlot) % R.nsub;
     uint32_t off = run ? atomicAdd(&D.sub[((size_t)p * kSub + sc) * 32], run) : 0u;
-    const bool stored = (uint64_t)off + run <= D.capS;
-    D.tmeta[(size_t)p * D.MT + t] = ((uint64_t)run << 32) | (stored ? (uint32_t)(sc * D.capS + off) : kNotStored);
+    const bool stored = (uint64_t)off + run <= R.capS;
+    D.tmeta[R.tile0 + t] = ((uint64_t)run << 32) | (stored ? (uint32_t)(sc * R.capS + off) : kNotStored);
     if (!stored) atomicOr(&D.state[p].fail, 1u);
-    s_base = (uint32_t)(sc * D.capS + off);
+    s_base = (uint32_t)(sc * R.capS + off);
     s_stored = stored ? 1u : 0u;
   }
   __syncthreads();
   const bool stored = s_stored != 0u;
   if (stored && flags) {
     uint32_t pos = s_base + s_cnt[wid] + pre;
-    uint64_t* cd = D.cand + (size_t)p * D.cap;
+    uint64_t* cd = D.cand + R.cand;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       if ((flags >> c) & 1u) {
@@ -350,41 +538,48 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
 // ---------------------------------------------------------------------------
 // tsum: candidate count of every group of 1024 tiles.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(256) void k_tsum(Dev D) {
   __shared__ uint32_t scr[256 / kWave + 3];
-  const uint32_t p = blockIdx.y;
-  const uint64_t gidx = blockIdx.x;
-  const uint32_t nt = node_tiles(D, p);
+  // per-layer call: one block per group of every row (1D grid)
+  const uint32_t p = ROWS ? D.group_row[blockIdx.x] : blockIdx.y;
+  const Row R = row_of<ROWS>(D, p);
+  const uint64_t gidx = ROWS ? blockIdx.x - R.group0 : blockIdx.x;
+  const uint32_t nt = row_tiles(R);
+  if (gidx * kGroup >= nt) return;
   uint32_t s = 0;
 #pragma unroll
   for (int i = 0; i < kGroup / 256; ++i) {
     const uint64_t t = gidx * kGroup + (uint64_t)i * 256 + threadIdx.x;
-    if (t < nt) s += (uint32_t)(D.tmeta[(size_t)p * D.MT + t] >> 32);
+    if (t < nt) s += (uint32_t)(D.tmeta[R.tile0 + t] >> 32);
   }
   uint32_t tot;
   block_exclusive_scan<256>(s, scr, tot);
-  if (threadIdx.x == 0) D.gsum[(size_t)p * D.MG + gidx] = tot;
+  if (threadIdx.x == 0) D.gsum[R.group0 + gidx] = tot;
 }
 
 // ---------------------------------------------------------------------------
 // gscan: group offsets, candidate count and the path of the node.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(1024) void k_gscan(Dev D) {
   __shared__ uint32_t scr[1024 / kWave + 3];
   const uint32_t p = blockIdx.x;
-  const uint64_t ng = (node_tiles(D, p) + kGroup - 1) / kGroup;
+  const Row R = row_of<ROWS>(D, p);
+  const uint64_t ng = (row_tiles(R) + kGroup - 1) / kGroup;
   uint64_t carry = 0;
   for (uint64_t g0 = 0; g0 < ng; g0 += 1024) {
     const uint64_t gi = g0 + threadIdx.x;
-    const uint32_t v = gi < ng ? D.gsum[(size_t)p * D.MG + gi] : 0u;
+    const uint32_t v = gi < ng ? D.gsum[R.group0 + gi] : 0u;
     uint32_t tot;
     const uint32_t ex = block_exclusive_scan<1024>(v, scr, tot);
-    if (gi < ng) D.gbase[(size_t)p * D.MG + gi] = (uint32_t)(carry + ex);
+    if (gi < ng) D.gbase[R.group0 + gi] = (uint32_t)(carry + ex);
     carry += tot;
   }
   if (threadIdx.x == 0) {
-    const bool rescan = D.state[p].fail != 0u || carry < D.k || carry > D.cap;
-    D.state[p].count = (uint32_t)std::min<uint64_t>(carry, D.cap);
+    const uint64_t cap = (uint64_t)R.nsub * R.capS;
+    const bool rescan = D.state[p].fail != 0u || carry < R.k || carry > cap;
+    D.state[p].count = (uint32_t)std::min<uint64_t>(carry, cap);
     D.state[p].mode = rescan ? 1u : 0u;
     D.info[p] = rescan ? 1u : 0u;
   }
@@ -393,19 +588,21 @@ __global__ __launch_bounds__(1024) void k_gscan(Dev D) {
 // ---------------------------------------------------------------------------
 // restore: rescan path only - zeroed candidates go back into residual.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(256) void k_restore(float* __restrict__ r, Dev D) {
   const uint32_t p = blockIdx.y;
   if (D.state[p].mode == 0u) return;
+  const Row R = row_of<ROWS>(D, p);
   const uint32_t mid = D.state[p].mid;
-  const uint32_t nt = node_tiles(D, p);
-  const uint64_t pN = (uint64_t)p * D.N;
+  const uint32_t nt = row_tiles(R);
+  const uint64_t pN = R.base;
   for (uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x; t < nt; t += (uint64_t)gridDim.x * 256) {
-    const uint64_t meta = D.tmeta[(size_t)p * D.MT + t];
+    const uint64_t meta = D.tmeta[R.tile0 + t];
     const uint32_t off = (uint32_t)meta;
     const uint32_t cnt = (uint32_t)(meta >> 32);
     if (off == kNotStored) continue;
     for (uint32_t j = 0; j < cnt; ++j) {
-      const uint64_t c = D.cand[(size_t)p * D.cap + off + j];
+      const uint64_t c = D.cand[R.cand + off + j];
       const float v = __uint_as_float((uint32_t)c);
       if (mag_key(v) >= mid) r[pN + (uint32_t)(c >> 32)] = v;
     }
@@ -419,28 +616,30 @@ __global__ __launch_bounds__(256) void k_restore(float* __restrict__ r, Dev D) {
 // binary search over the block's prefix of run lengths in LDS, so loads and
 // stores stay spread over the whole block.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
   constexpr int kU = 8;
   __shared__ uint32_t h[kH0];
   __shared__ uint32_t s_excl[kGroup + 1];
   __shared__ uint32_t s_toff[kGroup];
   __shared__ uint32_t scr[kGroup / kWave + 3];
-  const uint32_t p = blockIdx.y;
+  const uint32_t p = ROWS ? D.group_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid over groups
   if (D.state[p].mode != 0u) return;
-  const uint64_t gidx = blockIdx.x;
-  const uint32_t nt = node_tiles(D, p);
+  const Row R = row_of<ROWS>(D, p);
+  const uint64_t gidx = ROWS ? blockIdx.x - R.group0 : blockIdx.x;
+  const uint32_t nt = row_tiles(R);
   if (gidx * kGroup >= nt) return;
   for (uint32_t i = threadIdx.x; i < kH0; i += kGroup) h[i] = 0u;
   const uint64_t t = gidx * kGroup + threadIdx.x;
-  const uint64_t meta = t < nt ? D.tmeta[(size_t)p * D.MT + t] : 0ull;
+  const uint64_t meta = t < nt ? D.tmeta[R.tile0 + t] : 0ull;
   const uint32_t cnt = (uint32_t)(meta >> 32);
   s_toff[threadIdx.x] = cnt ? (uint32_t)meta : 0u;
   uint32_t tot;
   s_excl[threadIdx.x] = block_exclusive_scan<kGroup>(cnt, scr, tot);
   if (threadIdx.x == 0) s_excl[kGroup] = tot;
   __syncthreads();
-  const size_t nbase = (size_t)p * D.cap;
-  const size_t out = nbase + D.gbase[(size_t)p * D.MG + gidx];
+  const size_t nbase = R.cand;
+  const size_t out = nbase + D.gbase[R.group0 + gidx];
   for (uint32_t i0 = threadIdx.x; i0 < tot; i0 += kGroup * kU) {
     uint32_t src[kU];
 #pragma unroll
@@ -481,9 +680,9 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
 // Digits chosen so far, recomputed from the global histograms of the levels
 // below `level` (each block does it; they all agree).
 template <int NT>
-__device__ __forceinline__ void decide(const Dev& D, uint32_t p, int level, uint32_t* scr,
+__device__ __forceinline__ void decide(const Dev& D, uint32_t p, uint32_t k, int level, uint32_t* scr,
                                        uint32_t& prefix, uint32_t& krem) {
-  krem = D.k;
+  krem = k;
   prefix = 0;
   uint32_t bin, above;
   if (level >= 1) {
@@ -507,23 +706,28 @@ __device__ __forceinline__ void decide(const Dev& D, uint32_t p, int level, uint
 // hist: one radix level of T*. Level 0 runs only on the rescan path (the
 // gather kernel builds it for the candidate path).
 // ---------------------------------------------------------------------------
-template <int LEVEL>
+template <int LEVEL, bool ROWS>
 __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D) {
   constexpr int NB = LEVEL == 0 ? kH0 : (LEVEL == 1 ? kH1 : kH2);
   constexpr int kU = 16;
   __shared__ uint32_t h[NB];
   __shared__ uint32_t scr[256 / kWave + 3];
-  const uint32_t p = blockIdx.y;
+  // per-layer call: a 1D grid, each row owning npass consecutive blocks
+  const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;
   const bool rescan = D.state[p].mode != 0u;
   if (LEVEL == 0 && !rescan) return;
+  const Row R = row_of<ROWS>(D, p);
+  if (R.k == 0) return;
+  const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
+  const uint64_t nbx = ROWS ? R.npass : gridDim.x;
   for (uint32_t i = threadIdx.x; i < NB; i += 256) h[i] = 0u;
   uint32_t prefix, krem;
-  decide<256>(D, p, LEVEL, scr, prefix, krem);
+  decide<256>(D, p, R.k, LEVEL, scr, prefix, krem);
   __syncthreads();
-  const uint64_t n = source_len(D, p, rescan);
-  const float* src = rescan ? r + (uint64_t)p * D.N : D.oval + (size_t)p * D.cap;
-  const uint64_t stride = (uint64_t)gridDim.x * 256 * kU;
-  for (uint64_t i0 = (uint64_t)blockIdx.x * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
+  const uint64_t n = source_len(D, R, p, rescan);
+  const float* src = rescan ? r + R.base : D.oval + R.cand;
+  const uint64_t stride = nbx * 256 * kU;
+  for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
     uint32_t key[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -563,21 +767,26 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
 // ---------------------------------------------------------------------------
 // count: per chunk of the source, elements above and equal to T*.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict__ r, Dev D) {
   __shared__ uint32_t scr[kChunkThreads / kWave + 3];
   __shared__ uint32_t s_sum[2 * (kChunkThreads / kWave)];
-  const uint32_t p = blockIdx.y;
+  const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid
+  const Row R = row_of<ROWS>(D, p);
+  if (R.k == 0) return;
+  const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
+  const uint64_t nbx = ROWS ? R.npass : gridDim.x;
   uint32_t T, m;
-  decide<kChunkThreads>(D, p, 3, scr, T, m);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
+  decide<kChunkThreads>(D, p, R.k, 3, scr, T, m);
+  if (bx == 0 && threadIdx.x == 0) {
     D.state[p].T = T;
     D.state[p].m = m;
   }
   const bool rescan = D.state[p].mode != 0u;
-  const uint64_t n = source_len(D, p, rescan);
+  const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
-  const float* src = rescan ? r + (uint64_t)p * D.N : D.oval + (size_t)p * D.cap;
-  for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+  const float* src = rescan ? r + R.base : D.oval + R.cand;
+  for (uint64_t c = bx; c < nchunks; c += nbx) {
     uint32_t gt = 0, eq = 0;
     float v[kChunkIt];
 #pragma unroll
@@ -595,8 +804,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
     uint32_t tgt, teq;
     block_sum2<kChunkThreads>(gt, eq, s_sum, tgt, teq);
     if (threadIdx.x == 0) {
-      D.cgt[(size_t)p * D.MC + c] = tgt;
-      D.ceq[(size_t)p * D.MC + c] = teq;
+      D.cgt[R.chunk0 + c] = tgt;
+      D.ceq[R.chunk0 + c] = teq;
     }
   }
 }
@@ -604,19 +813,22 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
 // ---------------------------------------------------------------------------
 // scan: tie quota in index order, then each chunk's output offset.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(1024) void k_scan(Dev D) {
   __shared__ uint32_t scr[1024 / kWave + 3];
   const uint32_t p = blockIdx.x;
+  const Row R = row_of<ROWS>(D, p);
+  if (R.k == 0) return;
   const uint32_t m = D.state[p].m;
   const bool rescan = D.state[p].mode != 0u;
-  const uint64_t n = source_len(D, p, rescan);
+  const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
   uint32_t eq_carry = 0, out_carry = 0;
   for (uint64_t c0 = 0; c0 < nchunks; c0 += 1024) {
     const uint64_t c = c0 + threadIdx.x;
     const bool in = c < nchunks;
-    const uint32_t gt = in ? D.cgt[(size_t)p * D.MC + c] : 0u;
-    const uint32_t eq = in ? D.ceq[(size_t)p * D.MC + c] : 0u;
+    const uint32_t gt = in ? D.cgt[R.chunk0 + c] : 0u;
+    const uint32_t eq = in ? D.ceq[R.chunk0 + c] : 0u;
     uint32_t tot;
     const uint32_t eq_off = eq_carry + block_exclusive_scan<1024>(eq, scr, tot);
     eq_carry += tot;
@@ -625,38 +837,44 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
     const uint32_t out_off = out_carry + block_exclusive_scan<1024>(sel, scr, tot);
     out_carry += tot;
     if (in) {
-      D.ceqoff[(size_t)p * D.MC + c] = eq_off;
-      D.cout[(size_t)p * D.MC + c] = out_off;
+      D.ceqoff[R.chunk0 + c] = eq_off;
+      D.cout[R.chunk0 + c] = out_off;
     }
   }
-  if (threadIdx.x == 0 && out_carry != D.k) D.err[p] = 1u;
+  if (threadIdx.x == 0 && out_carry != R.k) D.err[p] = 1u;
 }
 
 // ---------------------------------------------------------------------------
 // emit: selected pairs in index order; residual finished.
 // ---------------------------------------------------------------------------
+template <bool ROWS>
 __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, uint32_t* __restrict__ out_idx,
                                                         float* __restrict__ out_val, Dev D) {
   constexpr int NW = kChunkThreads / kWave;
   __shared__ uint32_t s_eq[kChunkIt * NW];
   __shared__ uint32_t s_sel[kChunkIt * NW];
-  const uint32_t p = blockIdx.y;
+  const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid
+  const Row R = row_of<ROWS>(D, p);
+  if (R.k == 0) return;
+  const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
+  const uint64_t nbx = ROWS ? R.npass : gridDim.x;
   const bool rescan = D.state[p].mode != 0u;
   const uint32_t T = D.state[p].T;
   const uint32_t m = D.state[p].m;
   const uint32_t mid = D.state[p].mid;
   const uint32_t lane = lane_id();
   const uint32_t wid = threadIdx.x / kWave;
-  const uint64_t n = source_len(D, p, rescan);
+  const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
-  const uint64_t pN = (uint64_t)p * D.N;
-  const float* vsrc = rescan ? r + pN : D.oval + (size_t)p * D.cap;
-  const uint32_t* isrc = D.oidx + (size_t)p * D.cap;
-  uint32_t* oi = out_idx + (uint64_t)p * D.k;
-  float* ov = out_val + (uint64_t)p * D.k;
-  for (uint64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
-    const uint32_t eq_base = D.ceqoff[(size_t)p * D.MC + c];
-    const uint32_t out_base = D.cout[(size_t)p * D.MC + c];
+  const uint64_t pN = R.base;
+  const uint32_t K = R.k;
+  const float* vsrc = rescan ? r + pN : D.oval + R.cand;
+  const uint32_t* isrc = D.oidx + R.cand;
+  uint32_t* oi = out_idx + R.out0;
+  float* ov = out_val + R.out0;
+  for (uint64_t c = bx; c < nchunks; c += nbx) {
+    const uint32_t eq_base = D.ceqoff[R.chunk0 + c];
+    const uint32_t out_base = D.cout[R.chunk0 + c];
     float v[kChunkIt];
     uint32_t e[kChunkIt];
 #pragma unroll
@@ -719,8 +937,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
       const bool high = mag_key(v[it]) >= mid;  // written as +0 by the stream kernel
       if ((sel_bits >> it) & 1u) {
         const uint32_t pos = out_base + s_sel[it * NW + wid] + sel_pre[it];
-        if (pos < D.k) {
-          oi[pos] = e[it];
+        if (pos < K) {
+          oi[pos] = e[it] + R.idx_off;
           ov[pos] = v[it];
         }
         if (rescan || !high) r[pN + e[it]] = 0.0f;
@@ -732,27 +950,152 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
   }
 }
 
-}  // namespace
+// ---------------------------------------------------------------------------
+// per-layer call: layer offsets and k's in, row table and tile-to-row out.
+// ---------------------------------------------------------------------------
+constexpr int kLayersPerSetup = 120;
 
-size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k) { return make_layout(P, N, k).total; }
+struct LayerChunk {
+  uint64_t off[kLayersPerSetup + 1];
+  uint64_t k[kLayersPerSetup];
+  uint64_t koff[kLayersPerSetup];  // output offset of the layer within a node's row
+};
 
-hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const Layout L = make_layout(P, N, k);
-  char* w = static_cast<char*>(ws);
-  Dev D;
-  D.P = P;
-  D.N = (uint32_t)N;
-  D.k = (uint32_t)k;
-  if (N <= (uint64_t)kSample) {
-    D.rs_lo = D.rs_mid = (uint32_t)k;
-  } else {
-    const double qs = (double)k / (double)N * kSample;
-    D.rs_lo = (uint32_t)std::min<double>(std::ceil(qs + 4.0 * std::sqrt(qs) + 16.0), (double)kSample);
-    D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
+__global__ void k_layers_in(uint64_t* loff, uint64_t* lk, uint64_t* lkoff, uint32_t first, uint32_t count,
+                            LayerChunk in) {
+  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    lk[first + i] = in.k[i];
+    lkoff[first + i] = in.koff[i];
+    loff[first + i] = in.off[i];
   }
-  D.pad = 0;
+  if (threadIdx.x == 0) loff[first + count] = in.off[count];
+}
+
+// One workgroup: every row's sizes (row_size, as the host computed them),
+// exclusive scans of their slices, the sample ranks of its thresholds.
+__global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, const uint64_t* loff, const uint64_t* lk,
+                                                    const uint64_t* lkoff, uint32_t P, uint64_t N, uint32_t nl,
+                                                    uint64_t K) {
+  __shared__ uint64_t scr[1024 / kWave + 1];
+  uint64_t c_cand = 0, c_tiles = 0, c_groups = 0, c_chunks = 0, c_pass = 0;  // carries over rounds
+  const uint64_t nrows = (uint64_t)P * nl;
+  for (uint64_t r0 = 0; r0 < nrows; r0 += 1024) {
+    const uint64_t ri = r0 + threadIdx.x;
+    const bool in = ri < nrows;
+    uint64_t base = 0, n = 0, k = 0, koff = 0, xoff = 0;
+    uint32_t p = 0;
+    if (in) {
+      p = (uint32_t)(ri / nl);
+      const uint32_t l = (uint32_t)(ri % nl);
+      xoff = loff[l];
+      n = loff[l + 1] - xoff;
+      k = lk[l];
+      koff = lkoff[l];
+      base = (uint64_t)p * N + xoff;
+    }
+    const RowSize z = row_size(base, n, k, true);
+    uint64_t t;
+    const uint64_t cand = c_cand + block_exclusive_scan_u64<1024>(in ? (uint64_t)z.nsub * z.capS : 0, scr, t);
+    c_cand += t;
+    const uint64_t tile0 = c_tiles + block_exclusive_scan_u64<1024>(in ? z.nt : 0, scr, t);
+    c_tiles += t;
+    const uint64_t group0 = c_groups + block_exclusive_scan_u64<1024>(in ? z.groups : 0, scr, t);
+    c_groups += t;
+    const uint64_t chunk0 = c_chunks + block_exclusive_scan_u64<1024>(in ? z.chunks : 0, scr, t);
+    c_chunks += t;
+    const uint64_t pass0 = c_pass + block_exclusive_scan_u64<1024>(in ? z.npass : 0, scr, t);
+    c_pass += t;
+    if (in) {
+      Row R{};
+      R.base = base;
+      R.cand = cand;
+      R.tile0 = tile0;
+      R.group0 = group0;
+      R.chunk0 = chunk0;
+      R.out0 = (uint64_t)p * K + koff;
+      R.n = (uint32_t)n;
+      R.k = (uint32_t)k;
+      R.capS = (uint32_t)z.capS;
+      R.nsub = z.nsub;
+      const uint64_t S = (uint64_t)z.schunks * kSampleChunk;
+      if (n <= S) {
+        R.rs_lo = R.rs_mid = (uint32_t)k;
+      } else {
+        const double qs = (double)k / (double)n * (double)S;
+        R.rs_lo = (uint32_t)fmin(ceil(qs + 4.0 * sqrt(qs) + 16.0), (double)S);
+        R.rs_mid = (uint32_t)fmin(fmax(1.0, ceil(qs)), (double)S);
+      }
+      R.idx_off = (uint32_t)xoff;
+      R.schunks = z.schunks;
+      R.pass0 = (uint32_t)pass0;
+      R.npass = z.npass;
+      rows[ri] = R;
+    }
+  }
+}
+
+// block-to-row tables of the per-layer grids
+__global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* tile_row, uint32_t* group_row,
+                                                   uint32_t* pass_row) {
+  const uint32_t p = blockIdx.x;
+  const Row R = rows[p];
+  const uint32_t nt = row_tiles(R);
+  for (uint32_t t = threadIdx.x; t < nt; t += 256) tile_row[R.tile0 + t] = p;
+  const uint32_t ng = (nt + kGroup - 1) / kGroup;
+  for (uint32_t t = threadIdx.x; t < ng; t += 256) group_row[R.group0 + t] = p;
+  for (uint32_t t = threadIdx.x; t < R.npass; t += 256) pass_row[R.pass0 + t] = p;
+}
+
+// The launch sequence shared by both calls. nrows rows; the stream grid has
+// one workgroup per tile slot; `tile_slots`, `groups`, `max_cap` size the
+// other grids.
+template <bool ROWS>
+hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t groups, uint64_t max_tiles,
+               uint64_t max_cap, uint64_t passes, bool any_k, const float* grad, float* residual,
+               uint32_t* out_idx, float* out_val, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const uint32_t R = (uint32_t)nrows;
+  hipLaunchKernelGGL(k_predict<ROWS>, dim3(R), dim3(kPredictThreads), 0, stream, grad, residual, D);
+  hipError_t e = hipSuccess;
+  if (ev_start) e = hipEventRecord(ev_start, stream);
+  if (stream_blocks > 0)
+    hipLaunchKernelGGL(k_stream<ROWS>, dim3((uint32_t)stream_blocks), dim3(kStreamThreads), 0, stream, grad,
+                       residual, D);
+  if (ev_stop && e == hipSuccess) e = hipEventRecord(ev_stop, stream);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess || !any_k) return e;
+
+  // per-row block counts sized for the candidate list; the rescan path loops
+  // over more work with the same grids
+  const uint64_t per_row = std::max<uint64_t>(1, 8192 / nrows);
+  const uint32_t tile_blocks = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_tiles + 255) / 256, per_row));
+  // select / count / emit passes: enough blocks to fill the chip once, each
+  // looping over several chunks, so the per-block digit decisions are amortised
+  const uint64_t pass_row = std::max<uint64_t>(1, 2048 / nrows);
+  const uint32_t hist_blocks =
+      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_cap + 16383) / 16384, pass_row));
+  const uint32_t chunk_blocks =
+      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_cap + kChunk - 1) / kChunk, pass_row));
+  // per-layer call: 1D grids over all groups / all pass blocks of all rows
+  const dim3 gG = ROWS ? dim3((uint32_t)groups) : dim3((uint32_t)std::max<uint64_t>(1, groups), R);
+  const dim3 gH = ROWS ? dim3((uint32_t)passes) : dim3(hist_blocks, R);
+  const dim3 gC = ROWS ? dim3((uint32_t)passes) : dim3(chunk_blocks, R);
+  if (ROWS && groups > 0) hipLaunchKernelGGL(k_tsum<ROWS>, gG, dim3(256), 0, stream, D);
+  if (!ROWS) hipLaunchKernelGGL(k_tsum<ROWS>, gG, dim3(256), 0, stream, D);
+  hipLaunchKernelGGL(k_gscan<ROWS>, dim3(R), dim3(1024), 0, stream, D);
+  hipLaunchKernelGGL(k_restore<ROWS>, dim3(tile_blocks, R), dim3(256), 0, stream, residual, D);
+  if (!ROWS || groups > 0) hipLaunchKernelGGL(k_gather<ROWS>, gG, dim3(kGroup), 0, stream, D);
+  hipLaunchKernelGGL((k_hist<0, ROWS>), gH, dim3(256), 0, stream, residual, D);
+  hipLaunchKernelGGL((k_hist<1, ROWS>), gH, dim3(256), 0, stream, residual, D);
+  hipLaunchKernelGGL((k_hist<2, ROWS>), gH, dim3(256), 0, stream, residual, D);
+  hipLaunchKernelGGL(k_count<ROWS>, gC, dim3(kChunkThreads), 0, stream, residual, D);
+  hipLaunchKernelGGL(k_scan<ROWS>, dim3(R), dim3(1024), 0, stream, D);
+  hipLaunchKernelGGL(k_emit<ROWS>, gC, dim3(kChunkThreads), 0, stream, residual, out_idx, out_val, D);
+  return hipGetLastError();
+}
+
+Dev make_dev(const Layout& L, char* w, uint32_t P) {
+  Dev D{};
+  D.P = P;
   D.capS = L.capS;
   D.cap = L.cap;
   D.MT = L.MT;
@@ -775,39 +1118,78 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
   D.ceq = reinterpret_cast<uint32_t*>(w + L.ceq);
   D.ceqoff = reinterpret_cast<uint32_t*>(w + L.ceqoff);
   D.cout = reinterpret_cast<uint32_t*>(w + L.cout);
+  D.rows = nullptr;
+  D.tile_row = nullptr;
+  return D;
+}
 
-  hipLaunchKernelGGL(k_predict, dim3(P), dim3(kPredictThreads), 0, stream, grad, residual, D);
-  hipError_t e = hipSuccess;
-  if (ev_start) e = hipEventRecord(ev_start, stream);
-  hipLaunchKernelGGL(k_stream, dim3((uint32_t)(L.MT * P)), dim3(kStreamThreads), 0, stream, grad, residual, D);
-  if (ev_stop && e == hipSuccess) e = hipEventRecord(ev_stop, stream);
-  if (e == hipSuccess) e = hipGetLastError();
-  if (e != hipSuccess || k == 0) return e;
+}  // namespace
 
-  // per-node block counts sized for the candidate list; the rescan path
-  // loops over more work with the same grids
-  const uint64_t per_node = std::max<uint64_t>(1, 8192 / P);
-  const uint32_t groups = (uint32_t)L.MG;
-  const uint32_t tile_blocks = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((L.MT + 255) / 256, per_node));
-  // select / count / emit passes: enough blocks to fill the chip once, each
-  // looping over several chunks, so the per-block digit decisions are amortised
-  const uint64_t pass_node = std::max<uint64_t>(1, 2048 / P);
-  const uint32_t hist_blocks =
-      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((L.cap + 16383) / 16384, pass_node));
-  const uint32_t chunk_blocks =
-      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((L.cap + kChunk - 1) / kChunk, pass_node));
-  hipLaunchKernelGGL(k_tsum, dim3(groups, P), dim3(256), 0, stream, D);
-  hipLaunchKernelGGL(k_gscan, dim3(P), dim3(1024), 0, stream, D);
-  hipLaunchKernelGGL(k_restore, dim3(tile_blocks, P), dim3(256), 0, stream, residual, D);
-  hipLaunchKernelGGL(k_gather, dim3(groups, P), dim3(kGroup), 0, stream, D);
-  hipLaunchKernelGGL(k_hist<0>, dim3(hist_blocks, P), dim3(256), 0, stream, residual, D);
-  hipLaunchKernelGGL(k_hist<1>, dim3(hist_blocks, P), dim3(256), 0, stream, residual, D);
-  hipLaunchKernelGGL(k_hist<2>, dim3(hist_blocks, P), dim3(256), 0, stream, residual, D);
-  hipLaunchKernelGGL(k_count, dim3(chunk_blocks, P), dim3(kChunkThreads), 0, stream, residual, D);
-  hipLaunchKernelGGL(k_scan, dim3(P), dim3(1024), 0, stream, D);
-  hipLaunchKernelGGL(k_emit, dim3(chunk_blocks, P), dim3(kChunkThreads), 0, stream, residual, out_idx, out_val,
-                     D);
-  return hipGetLastError();
+size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k) { return make_node_layout(P, N, k).total; }
+
+hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
+                          hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const Layout L = make_node_layout(P, N, k);
+  Dev D = make_dev(L, static_cast<char*>(ws), P);
+  D.N = (uint32_t)N;
+  D.k = (uint32_t)k;
+  if (N <= (uint64_t)kSample) {
+    D.rs_lo = D.rs_mid = (uint32_t)k;
+  } else {
+    const double qs = (double)k / (double)N * kSample;
+    D.rs_lo = (uint32_t)std::min<double>(std::ceil(qs + 4.0 * std::sqrt(qs) + 16.0), (double)kSample);
+    D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
+  }
+  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, k > 0, grad, residual, out_idx, out_val, stream,
+                    ev_start, ev_stop);
+}
+
+size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {
+  const LayerPlan lp = plan_layers(P, N, nl, off, k);
+  return make_layout(lp.Q, nl).total;
+}
+
+uint64_t topk_layers_stream_blocks(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {
+  return plan_layers(P, N, nl, off, k).Q.tiles;
+}
+
+hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k,
+                              const float* grad, float* residual, uint32_t* out_idx, float* out_val, void* ws,
+                              hipStream_t stream) {
+  const LayerPlan lp = plan_layers(P, N, nl, off, k);
+  const Layout L = make_layout(lp.Q, nl);
+  char* w = static_cast<char*>(ws);
+  Dev D = make_dev(L, w, (uint32_t)lp.Q.rows);
+  Row* rows = reinterpret_cast<Row*>(w + L.rows);
+  uint32_t* tile_row = reinterpret_cast<uint32_t*>(w + L.tile_row);
+  uint64_t* loff = reinterpret_cast<uint64_t*>(w + L.loff);
+  uint64_t* lk = reinterpret_cast<uint64_t*>(w + L.lk);
+  uint32_t* group_row = reinterpret_cast<uint32_t*>(w + L.group_row);
+  uint32_t* pass_row = reinterpret_cast<uint32_t*>(w + L.pass_row);
+  uint64_t* lkoff = reinterpret_cast<uint64_t*>(w + L.lkoff);
+  D.rows = rows;
+  D.tile_row = tile_row;
+  D.group_row = group_row;
+  D.pass_row = pass_row;
+  uint64_t koff = 0;
+  for (uint32_t first = 0; first < nl; first += kLayersPerSetup) {
+    LayerChunk in{};
+    const uint32_t count = std::min<uint32_t>(kLayersPerSetup, nl - first);
+    for (uint32_t i = 0; i < count; ++i) {
+      in.off[i] = off[first + i];
+      in.k[i] = k[first + i];
+      in.koff[i] = koff;
+      koff += k[first + i];
+    }
+    in.off[count] = off[first + count];
+    hipLaunchKernelGGL(k_layers_in, dim3(1), dim3(128), 0, stream, loff, lk, lkoff, first, count, in);
+  }
+  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, loff, lk, lkoff, P, N, nl, lp.K);
+  hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_row, group_row,
+                     pass_row);
+  return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.K > 0, grad,
+                   residual, out_idx, out_val, stream, nullptr, nullptr);
 }
 
 }  // namespace sparcml

@@ -161,3 +161,24 @@ def zipf_sparse(w: Workload):
     offsets = np.zeros(w.P + 1, np.uint64)
     offsets[1:] = np.cumsum([len(a) for a in idx_parts])
     return offsets, np.concatenate(idx_parts), np.concatenate(val_parts)
+
+
+def layer_offsets(N: int, nlayers: int, seed: int = 50):
+    """Synthetic layer boundaries for per-layer Top-k: sizes log-uniform between
+    64 and N/8 (a few large layers among many small ones, as in a convolutional
+    network), scaled to sum to N; returns [nlayers + 1] offsets from 0 to N."""
+    rng = np.random.default_rng(seed)
+    sizes = np.exp(rng.uniform(np.log(64), np.log(max(65, N // 8)), size=nlayers))
+    sizes = np.maximum(1, np.floor(sizes / sizes.sum() * N)).astype(np.int64)
+    sizes[-1] += N - sizes.sum()
+    while sizes[-1] < 1:  # keep every layer non-empty
+        j = int(np.argmax(sizes[:-1]))
+        sizes[j] -= 1
+        sizes[-1] += 1
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.uint64)
+
+
+def layer_ks(offsets, num: int, den: int):
+    """k of every layer: floor(num/den * size) in integer arithmetic."""
+    sizes = np.diff(np.asarray(offsets, np.uint64).astype(np.int64))
+    return (sizes * num // den).astype(np.uint64)

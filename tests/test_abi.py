@@ -104,6 +104,32 @@ def test_reduce_argument_checks():
     assert call(wb=ws - 1) == sg.ERR_WORKSPACE
 
 
+def test_layers_argument_checks():
+    L = sg.lib()
+    u64 = lambda *xs: (ctypes.c_uint64 * len(xs))(*xs)
+    off, ks = u64(0, 10, 100), u64(2, 5)
+    ws = L.sparcml_topk_ef_layers_workspace(2, 100, 2, off, ks)
+    assert ws > 0
+
+    def call(P=2, N=100, nl=2, o=off, k=ks, g=FAKE, w=FAKE, wb=ws):
+        return L.sparcml_topk_ef_layers(P, N, nl, o, k, g, FAKE, FAKE, FAKE, w, wb, None)
+
+    assert call(P=0) == sg.ERR_INVALID_ARG
+    assert call(nl=0) == sg.ERR_INVALID_ARG
+    assert call(P=70000) == sg.ERR_INVALID_ARG
+    assert call(o=u64(0, 10, 99)) == sg.ERR_INVALID_ARG      # does not end at N
+    assert call(o=u64(1, 10, 100)) == sg.ERR_INVALID_ARG     # does not start at 0
+    assert call(o=u64(0, 50, 40)) == sg.ERR_INVALID_ARG      # decreasing
+    assert call(k=u64(11, 5)) == sg.ERR_INVALID_ARG          # k above the layer size
+    assert call(g=None) == sg.ERR_INVALID_ARG
+    assert call(g=FAKE_ODD) == sg.ERR_INVALID_ARG
+    assert call(w=None) == sg.ERR_WORKSPACE
+    assert call(w=FAKE_WS_ODD) == sg.ERR_WORKSPACE
+    assert call(wb=ws - 1) == sg.ERR_WORKSPACE
+    assert L.sparcml_topk_ef_layers_workspace(0, 100, 2, off, ks) == 0
+    assert L.sparcml_topk_ef_layers_workspace(40000, 100, 2, off, ks) == 0   # rows above 65535
+
+
 def test_bucketed_argument_checks():
     L = sg.lib()
     for b in (0, 32, 100, 2048):
