@@ -23,7 +23,7 @@
 //            not interleave inside a region);
 //            residual is written back as a, with stored candidates whose key
 //            is >= mid written as +0 (they are almost surely selected).
-//   tsum     candidate counts summed per group of 1024 tiles.
+//   tsum     candidate counts summed per group of 512 tiles.
 //   gscan    per node: group offsets, candidate count, and the path: the
 //            candidate list when every tile was stored and it holds >= k
 //            candidates, else an exact rescan of the whole node.
@@ -67,7 +67,7 @@ constexpr int kSampleChunk = 64;
 constexpr int kSample = kSampleChunks * kSampleChunk;     // 65536
 constexpr int kPredictThreads = 1024;
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
-constexpr int kGroup = 1024;                              // tiles per gather group
+constexpr int kGroup = 512;                              // tiles per gather group
 constexpr int kChunkThreads = 256;
 constexpr int kChunkIt = 16;
 constexpr int kChunk = kChunkThreads * kChunkIt;          // 4096 candidates per chunk
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
-// tsum: candidate count of every group of 1024 tiles.
+// tsum: candidate count of every group of kGroup tiles.
 // ---------------------------------------------------------------------------
 template <bool ROWS>
 __global__ __launch_bounds__(256) void k_tsum(Dev D) {
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256) void k_restore(float* __restrict__ r, Dev D) {
 
 // ---------------------------------------------------------------------------
 // gather: candidate runs into index order, first radix level on the way.
-// A block owns 1024 consecutive tiles, whose runs land contiguously in the
+// A block owns kGroup consecutive tiles, whose runs land contiguously in the
 // ordered list; each thread walks output positions and finds its tile by a
 // binary search over the block's prefix of run lengths in LDS, so loads and
 // stores stay spread over the whole block.
@@ -897,13 +897,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
       if (lane == 0) s_eq[it * NW + wid] = popc64(em);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t run = 0;
-      for (int i = 0; i < kChunkIt * NW; ++i) {
-        const uint32_t x = s_eq[i];
-        s_eq[i] = run;
-        run += x;
-      }
+    static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
+    if (threadIdx.x < kWave) {
+      const uint32_t x = s_eq[threadIdx.x];
+      s_eq[threadIdx.x] = wave_inclusive_scan(x) - x;
     }
     __syncthreads();
     uint32_t sel_bits = 0;
@@ -921,13 +918,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
       if (lane == 0) s_sel[it * NW + wid] = popc64(sm);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t run = 0;
-      for (int i = 0; i < kChunkIt * NW; ++i) {
-        const uint32_t x = s_sel[i];
-        s_sel[i] = run;
-        run += x;
-      }
+    static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
+    if (threadIdx.x < kWave) {
+      const uint32_t x = s_sel[threadIdx.x];
+      s_sel[threadIdx.x] = wave_inclusive_scan(x) - x;
     }
     __syncthreads();
 #pragma unroll
