@@ -331,10 +331,12 @@ sparcml_status sparcml_qsgd_dense_result(uint32_t bits, uint64_t N, uint32_t buc
 double sparcml_estimate_nnz(uint32_t P, uint64_t N, const uint64_t* h_offsets);
 
 /* ------------------------------------------------------------------------
- * Profiling hook (measurement only). Records `start` on the stream right
- * before, and `stop` right after, the streaming error-feedback kernel of the
- * next sparcml_topk_ef call made by the calling thread; the events are then
- * forgotten. Pass NULL, NULL to cancel. The events belong to the caller.
+ * Profiling hook (measurement only). Attaches `start` and `stop` to the
+ * dispatch of the streaming error-feedback kernel of the next
+ * sparcml_topk_ef call made by the calling thread (hipExtLaunchKernel), so
+ * that hipEventElapsedTime(start, stop) is that kernel's own duration; the
+ * events are then forgotten. Pass NULL, NULL to cancel. The events belong to
+ * the caller and must have been created on the current device.
  * ---------------------------------------------------------------------- */
 void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop);
 
