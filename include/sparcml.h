@@ -340,6 +340,18 @@ double sparcml_estimate_nnz(uint32_t P, uint64_t N, const uint64_t* h_offsets);
  * ---------------------------------------------------------------------- */
 void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop);
 
+/* ------------------------------------------------------------------------
+ * Attainable-bandwidth reference (measurement only, not part of the method):
+ * r[i] += g[i] for i < n with exactly the stream kernel's access pattern
+ * (one 1024-element tile per workgroup, non-temporal float4 loads and
+ * stores). `start` / `stop` (may be NULL) are attached to the kernel's
+ * dispatch, as for sparcml_profile_next_topk.
+ *   g, r   device, n fp32 each, 16-byte aligned, not overlapping
+ *   n      < 1024 * 2^24
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_reference_stream(uint64_t n, const float* g, float* r, hipEvent_t start,
+                                        hipEvent_t stop, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,6 +75,8 @@ def _load():
     L.sparcml_sparse_reduce.restype = st
     L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
     L.sparcml_estimate_nnz.restype = f64
+    L.sparcml_reference_stream.argtypes = [u64, vp, vp, vp, vp, vp]
+    L.sparcml_reference_stream.restype = st
     L.sparcml_profile_next_topk.argtypes = [vp, vp]
     L.sparcml_profile_next_topk.restype = None
     _lib = L

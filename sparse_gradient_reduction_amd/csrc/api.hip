@@ -41,6 +41,13 @@ const char* sparcml_status_string(sparcml_status status) {
   return "SPARCML: unknown status";
 }
 
+sparcml_status sparcml_reference_stream(uint64_t n, const float* g, float* r, hipEvent_t start, hipEvent_t stop,
+                                        hipStream_t stream) {
+  if (n >= (1ull << 42) || (n > 0 && (!g || !r || !aligned16(g) || !aligned16(r)))) return SPARCML_ERR_INVALID_ARG;
+  if ((n + 1023) / 1024 >= (1ull << 24)) return SPARCML_ERR_INVALID_ARG;  // one launch dimension
+  return from_hip(sparcml::reference_add_launch(n, g, r, stream, start, stop));
+}
+
 void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop) {
   g_prof_start = start;
   g_prof_stop = stop;

@@ -55,4 +55,8 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
                                 bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream);
 
+// ---- measurement only: plain streaming add with the stream kernel's access pattern
+hipError_t reference_add_launch(uint64_t n, const float* g, float* r, hipStream_t stream, hipEvent_t ev_start,
+                                hipEvent_t ev_stop);
+
 }  // namespace sparcml
