@@ -171,3 +171,34 @@ def test_dense_result_quantized_only_when_dense(dev, bits):
     torch.cuda.synchronize()
     assert not out2.read()[1]
     assert bool((codes2 == 0xAB).all()) and bool((scales2 == -1.0).all())
+
+
+def test_reduce_qsgd_invalid_input_sets_flags(dev):
+    """Descending and out-of-range indices set the flags; the code and scale
+    loads stay inside each node's rows even with a run table left over from
+    an earlier call in the same workspace."""
+    P, N, bits, bucket = 3, 300000, 4, 64
+    ws = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, 60000), dtype=torch.uint8, device=dev)
+    rng = np.random.default_rng(61)
+    off, idx, codes, scales, _ = _ragged_quantized(rng, P, N, 20000, bits, bucket, seed=1, step=0)
+    it = torch.from_numpy(idx.view(np.int32)).to(dev)
+    out = sg.sparse_reduce_qsgd([int(x) for x in off], it, torch.from_numpy(codes).to(dev),
+                                torch.from_numpy(scales).to(dev), bits, bucket, N, 0.25, workspace=ws)
+    torch.cuda.synchronize()
+    assert out.read()[2] == 0
+    parts = [np.array([100000, 50000, 10], np.uint32), np.array([5, N + 3], np.uint32), np.array([7, 8], np.uint32)]
+    c_parts, s_parts = [], []
+    for p, ids in enumerate(parts):
+        c, s = oracle.qsgd(np.ones((1, ids.size), np.float32), bits, bucket, 2, 0, node0=p)
+        c_parts.append(c[0])
+        s_parts.append(s[0])
+    bad_off = [0, 3, 5, 7]
+    bad_idx = torch.from_numpy(np.concatenate(parts).view(np.int32)).to(dev)
+    bc = torch.from_numpy(np.concatenate(c_parts)).to(dev)
+    bs = torch.from_numpy(np.concatenate(s_parts)).to(dev)
+    for hint in (1, N):
+        out = sg.sparse_reduce_qsgd(bad_off, bad_idx, bc, bs, bits, bucket, N, 0.25, expected_nnz_hint=hint,
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        flags = out.read()[2]
+        assert flags & sg.FLAG_NOT_ASCENDING and flags & sg.FLAG_INDEX_RANGE, flags
