@@ -121,9 +121,10 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
     ns = ns < 1 ? 1 : (ns > (uint64_t)kSub ? (uint64_t)kSub : ns);
     z.nsub = (uint32_t)ns;
     z.capS = (want + ns - 1) / ns + (n < (uint64_t)kTile ? n : (uint64_t)kTile);
-    // a sample of about one element in 16 (16 to 1024 chunks): small layers
-    // are cheap to sample and their candidate lists are short anyway
-    uint64_t sc = n / (16 * kSampleChunk);
+    // a sample of about one element in 64 (16 to 1024 chunks): the wider
+    // margin of a small sample costs little, as a layer's candidate list is
+    // short next to its stream pass
+    uint64_t sc = n / (64 * kSampleChunk);
     z.schunks = (uint32_t)(sc < 16 ? 16 : (sc > (uint64_t)kSampleChunks ? (uint64_t)kSampleChunks : sc));
     // select / count / emit blocks: one per 8192 expected candidates, 1..64
     const uint64_t est = n < 2 * k + 4096 ? n : 2 * k + 4096;
@@ -345,20 +346,20 @@ __device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint3
 // ---------------------------------------------------------------------------
 // predict: reset the node's state and choose the two key thresholds.
 // ---------------------------------------------------------------------------
-template <bool ROWS>
-__global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __restrict__ g,
+template <bool ROWS, int NT>
+__global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
                                                              const float* __restrict__ r, Dev D) {
   __shared__ uint32_t h1[4096];
   __shared__ uint32_t h2lo[2048];
   __shared__ uint32_t h2mid[2048];
-  __shared__ uint32_t scr[kPredictThreads / kWave + 3];
+  __shared__ uint32_t scr[NT / kWave + 3];
   const uint32_t p = blockIdx.x;
   const Row R = row_of<ROWS>(D, p);
   const uint32_t tid = threadIdx.x;
-  for (uint32_t i = tid; i < kH0; i += kPredictThreads) D.h0[(size_t)p * kH0 + i] = 0u;
-  for (uint32_t i = tid; i < kH1; i += kPredictThreads) D.h1[(size_t)p * kH1 + i] = 0u;
-  for (uint32_t i = tid; i < kH2; i += kPredictThreads) D.h2[(size_t)p * kH2 + i] = 0u;
-  for (uint32_t i = tid; i < kSub; i += kPredictThreads) D.sub[((size_t)p * kSub + i) * 32] = 0u;
+  for (uint32_t i = tid; i < kH0; i += NT) D.h0[(size_t)p * kH0 + i] = 0u;
+  for (uint32_t i = tid; i < kH1; i += NT) D.h1[(size_t)p * kH1 + i] = 0u;
+  for (uint32_t i = tid; i < kH2; i += NT) D.h2[(size_t)p * kH2 + i] = 0u;
+  for (uint32_t i = tid; i < kSub; i += NT) D.sub[((size_t)p * kSub + i) * 32] = 0u;
 
   uint32_t lo, mid;
   if (R.k == 0) {
@@ -369,35 +370,31 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
     lo = 0u;            // a small layer is its own candidate list
     mid = 0xFFFFFFFFu;  // and nothing is zeroed before the selection
   } else {
-    for (uint32_t i = tid; i < 4096; i += kPredictThreads) h1[i] = 0u;
-    for (uint32_t i = tid; i < 2048; i += kPredictThreads) h2lo[i] = h2mid[i] = 0u;
+    for (uint32_t i = tid; i < 4096; i += NT) h1[i] = 0u;
+    for (uint32_t i = tid; i < 2048; i += NT) h2lo[i] = h2mid[i] = 0u;
     __syncthreads();
     const uint64_t base = R.base;
     const uint32_t nsamp = R.schunks * kSampleChunk;  // <= kSample
     const bool whole = R.n <= nsamp;
-    uint32_t keys[kSample / kPredictThreads];
+    auto sample_key = [&](uint32_t i) -> uint32_t {  // 0xFFFFFFFF marks "no sample"
+      if (whole) return i < R.n ? mag_key(g[base + i] + r[base + i]) : 0xFFFFFFFFu;
+      if (i >= nsamp) return 0xFFFFFFFFu;
+      const uint32_t c = i / kSampleChunk, o = i % kSampleChunk;
+      const uint64_t start = (uint64_t)c * (R.n - kSampleChunk) / (R.schunks - 1);
+      return mag_key(g[base + start + o] + r[base + start + o]);
+    };
+    uint32_t keys[kSample / NT];
 #pragma unroll
-    for (int j = 0; j < kSample / kPredictThreads; ++j) {
-      const uint32_t i = j * kPredictThreads + tid;
-      uint32_t key = 0xFFFFFFFFu;  // marks "no sample"
-      if (whole) {
-        if (i < R.n) key = mag_key(g[base + i] + r[base + i]);
-      } else if (i < nsamp) {
-        const uint32_t c = i / kSampleChunk, o = i % kSampleChunk;
-        const uint64_t start = (uint64_t)c * (R.n - kSampleChunk) / (R.schunks - 1);
-        key = mag_key(g[base + start + o] + r[base + start + o]);
-      }
-      keys[j] = key;
-    }
+    for (int j = 0; j < kSample / NT; ++j) keys[j] = sample_key(j * NT + tid);
 #pragma unroll
-    for (int j = 0; j < kSample / kPredictThreads; ++j)
+    for (int j = 0; j < kSample / NT; ++j)
       if (keys[j] != 0xFFFFFFFFu) atomicAdd(&h1[keys[j] >> 19], 1u);
     __syncthreads();
     uint32_t b_lo, a_lo, b_mid, a_mid;
-    block_find_suffix<kPredictThreads>(h1, 4096, R.rs_lo, scr, b_lo, a_lo);
-    block_find_suffix<kPredictThreads>(h1, 4096, R.rs_mid, scr, b_mid, a_mid);
+    block_find_suffix<NT>(h1, 4096, R.rs_lo, scr, b_lo, a_lo);
+    block_find_suffix<NT>(h1, 4096, R.rs_mid, scr, b_mid, a_mid);
 #pragma unroll
-    for (int j = 0; j < kSample / kPredictThreads; ++j) {
+    for (int j = 0; j < kSample / NT; ++j) {
       const uint32_t key = keys[j];
       if (key == 0xFFFFFFFFu) continue;
       if ((key >> 19) == b_lo) atomicAdd(&h2lo[(key >> 8) & 2047u], 1u);
@@ -405,8 +402,8 @@ __global__ __launch_bounds__(kPredictThreads) void k_predict(const float* __rest
     }
     __syncthreads();
     uint32_t c_lo, x_lo, c_mid, x_mid;
-    block_find_suffix<kPredictThreads>(h2lo, 2048, R.rs_lo - a_lo, scr, c_lo, x_lo);
-    block_find_suffix<kPredictThreads>(h2mid, 2048, R.rs_mid - a_mid, scr, c_mid, x_mid);
+    block_find_suffix<NT>(h2lo, 2048, R.rs_lo - a_lo, scr, c_lo, x_lo);
+    block_find_suffix<NT>(h2mid, 2048, R.rs_mid - a_mid, scr, c_mid, x_mid);
     lo = (b_lo << 19) | (c_lo << 8);
     mid = (b_mid << 19) | (c_mid << 8);
   }
@@ -1050,7 +1047,8 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
                uint64_t max_cap, uint64_t passes, bool any_k, const float* grad, float* residual,
                uint32_t* out_idx, float* out_val, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const uint32_t R = (uint32_t)nrows;
-  hipLaunchKernelGGL(k_predict<ROWS>, dim3(R), dim3(kPredictThreads), 0, stream, grad, residual, D);
+  hipLaunchKernelGGL((k_predict<ROWS, kPredictThreads>), dim3(R), dim3(kPredictThreads), 0, stream, grad, residual,
+                     D);
   hipError_t e = hipSuccess;
   if (stream_blocks > 0) {
     if (ev_start || ev_stop) {
