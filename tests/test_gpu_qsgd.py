@@ -202,3 +202,9 @@ def test_reduce_qsgd_invalid_input_sets_flags(dev):
         torch.cuda.synchronize()
         flags = out.read()[2]
         assert flags & sg.FLAG_NOT_ASCENDING and flags & sg.FLAG_INDEX_RANGE, flags
+
+
+def test_qsgd_max_nodes(dev):
+    rng = np.random.default_rng(15)
+    v = rng.standard_normal((65535, 9)).astype(np.float32)
+    _check_qsgd(v, 4, 8, seed=5, step=1, node0=0, dev=dev)

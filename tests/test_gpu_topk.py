@@ -142,3 +142,12 @@ def test_topk_laplace_full_size_sampled_nodes(dev):
     min_sel = val.abs().min(dim=1).values
     unsel_max = r.abs().max(dim=1).values
     assert bool((unsel_max <= min_sel).all())
+
+
+def test_topk_max_nodes(dev):
+    """65535 nodes (the largest second launch dimension) of 5 elements."""
+    rng = np.random.default_rng(14)
+    P, N, k = 65535, 5, 2
+    g = rng.standard_normal((P, N)).astype(np.float32)
+    r = np.zeros_like(g)
+    _check(g, r, k, dev)
