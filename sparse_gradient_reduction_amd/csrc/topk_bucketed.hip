@@ -223,6 +223,180 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed(const float* _
   }  // buckets of this wave
 }
 
+// Sum / max over aligned groups of LG = 16 or 32 lanes, the result in every
+// lane of the group: DPP within each row of 16 lanes (quad swaps, then row
+// rotations by 4 and 8), and for 32-lane groups a swap of rows 0<->1 and
+// 2<->3. Every lane of the group must be active.
+template <uint32_t LG>
+__device__ __forceinline__ uint32_t group_sum(uint32_t v) {
+  static_assert(LG == 16 || LG == 32, "group of 16 or 32 lanes");
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  if constexpr (LG == 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = s[0] + s[1];
+  }
+  return v;
+}
+template <uint32_t LG>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  static_assert(LG == 16 || LG == 32, "group of 16 or 32 lanes");
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+  if constexpr (LG == 32) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(s[0], s[1]);
+  }
+  return v;
+}
+
+// Buckets of 64 and 128: a wave takes 256 consecutive positions, G = 256 / B
+// buckets at once, lane l holding positions 4l..4l+3 (one float4 of each
+// array). The lanes of one bucket form a group of 64 / G; each group runs its
+// own threshold search, with counts summed across the group, and ranks come
+// from ballots restricted to the group's lanes. Every cross-lane step runs
+// with the whole wave active: the search loop runs while any group is still
+// searching, and a finished group's lanes join its counts without using them.
+template <int G>
+__global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed_small(const float* __restrict__ g,
+                                                                        float* __restrict__ r,
+                                                                        uint32_t* __restrict__ out_idx,
+                                                                        float* __restrict__ out_val, BArgs A,
+                                                                        uint64_t chunks_per_node,
+                                                                        uint64_t total_chunks) {
+  constexpr uint32_t B = 256 / G;     // bucket size
+  constexpr uint32_t LG = kWave / G;  // lanes per bucket
+  const uint32_t lane = lane_id();
+  const uint32_t grp = lane / LG;
+  const uint64_t gmask = ((1ull << LG) - 1ull) << (grp * LG);
+  const uint64_t stride = (uint64_t)gridDim.x * kBucketWaves;
+  for (uint64_t w = (uint64_t)blockIdx.x * kBucketWaves + uniform(threadIdx.x / kWave); w < total_chunks;
+       w += stride) {
+    const uint64_t p = w / chunks_per_node, c = w % chunks_per_node;
+    const uint64_t j = c * G + grp;  // this lane's bucket
+    const uint64_t cpos = c * 256;   // chunk start within the node
+    const uint32_t clen = (uint32_t)std::min<uint64_t>(256, A.N - cpos);
+    const float* gb = g + p * A.N + cpos;
+    float* rb = r + p * A.N + cpos;
+    const bool vec = ((reinterpret_cast<uintptr_t>(gb) | reinterpret_cast<uintptr_t>(rb)) & 15u) == 0;
+    const uint32_t pos0 = lane * 4;  // within the chunk
+    float a[4];
+    uint32_t key[4];
+    bool in[4];
+    if (vec && pos0 + 4 <= clen) {
+      const f32x4 x = load_nt(reinterpret_cast<const f32x4*>(gb + pos0));
+      const f32x4 y = load_nt(reinterpret_cast<const f32x4*>(rb + pos0));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] = x[q] + y[q];
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        a[q] = pos0 + q < clen ? __builtin_nontemporal_load(gb + pos0 + q) + __builtin_nontemporal_load(rb + pos0 + q)
+                               : 0.0f;
+    }
+    uint32_t lmax = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      in[q] = pos0 + q < clen;
+      key[q] = in[q] ? mag_key(a[q]) : 0u;
+      lmax = max(lmax, key[q]);
+    }
+    // the group's bucket: its length (0 past the node's end) and kept count
+    const uint64_t bstart = j * B;
+    const uint32_t len = bstart < A.N ? (uint32_t)std::min<uint64_t>(B, A.N - bstart) : 0u;
+    const uint32_t kj = std::min<uint32_t>(A.kb, len);
+    auto count_ge = [&](uint32_t t) {  // keys >= t in the group; t >= 1 leaves out padding
+      uint32_t n = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) n += key[q] >= t ? 1u : 0u;
+      return group_sum<LG>(n);
+    };
+    const uint32_t M = group_max<LG>(lmax);
+    // T = the kj-th largest key of the group, by binary search over [lo_t,
+    // hi_t) with count(>= lo_t) >= kj > count(>= hi_t), first bracketed by
+    // M - 2^24 (about a factor of four below the largest magnitude); it
+    // stops at a threshold with exactly kj keys at or above it
+    uint32_t lo_t = 0u, hi_t = M + 1u;
+    bool exact = kj == 0u || len == kj;
+    {
+      const bool try_guess = !exact && M > (1u << 24);
+      const uint32_t guess = try_guess ? M - (1u << 24) : 1u;
+      const uint32_t n = count_ge(guess);
+      if (try_guess) {
+        if (n >= kj) {
+          lo_t = guess;
+          exact = n == kj;
+        } else {
+          hi_t = guess;
+        }
+      }
+    }
+    bool done = exact || hi_t - lo_t <= 1u;
+    while (ballot(!done) != 0ull) {
+      const uint32_t mid = lo_t + ((hi_t - lo_t) >> 1);  // >= 1 while searching
+      const uint32_t n = count_ge(done ? 1u : mid);
+      // a finished group keeps its bracket (no branch: the wave stays converged)
+      const bool up = !done && n >= kj, down = !done && n < kj;
+      lo_t = up ? mid : lo_t;
+      hi_t = down ? mid : hi_t;
+      exact = exact || (up && n == kj);
+      done = exact || hi_t - lo_t <= 1u;
+    }
+    const uint32_t T = lo_t;
+    // kept: with an exact count every key >= T (all of the bucket when T = 0);
+    // otherwise T is the kj-th largest key, every key above it is kept and
+    // the m ties at T at the lowest positions
+    uint32_t ngt = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ngt += key[q] > T ? 1u : 0u;
+    const uint32_t m = kj - std::min(kj, group_sum<LG>(ngt));
+    uint64_t em[4];
+    uint32_t tie_rank = 0;  // ties at T in lower lanes of the group
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      em[q] = ballot(in[q] && key[q] == T) & gmask;
+      tie_rank += lanes_below(em[q]);
+    }
+    uint64_t sel[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool eq = (em[q] >> lane) & 1ull;
+      const bool keep = exact ? (kj > 0u && in[q] && key[q] >= T) : (key[q] > T || (eq && tie_rank < m));
+      sel[q] = ballot(keep) & gmask;
+      tie_rank += eq ? 1u : 0u;
+    }
+    uint32_t rank = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rank += lanes_below(sel[q]);
+    const uint64_t out0 = p * A.K + j * A.kb;
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool s_q = (sel[q] >> lane) & 1ull;
+      if (s_q) {
+        out_idx[out0 + rank] = (uint32_t)(cpos + pos0 + q);
+        out_val[out0 + rank] = a[q];
+        ++rank;
+      }
+      o[q] = s_q ? 0.0f : a[q];
+    }
+    if (vec && pos0 + 4 <= clen) {
+      f32x4 v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = o[q];
+      store_nt(v, reinterpret_cast<f32x4*>(rb + pos0));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (in[q]) __builtin_nontemporal_store(o[q], rb + pos0 + q);
+    }
+  }  // chunks of this wave
+}
+
 }  // namespace
 
 uint64_t topk_bucketed_count(uint64_t N, uint32_t bucket, uint32_t k) {
@@ -246,9 +420,18 @@ hipError_t topk_bucketed_launch(uint32_t P, uint64_t N, uint32_t bucket, uint32_
   // beyond that the waves loop
   const dim3 grid((uint32_t)std::min<uint64_t>((A.total_buckets + kBucketWaves - 1) / kBucketWaves, 1u << 23));
   const dim3 block(kBucketThreads);
+  // buckets of 64 and 128: one wave per 256 positions
+  const uint64_t cpn = (N + 255) / 256, chunks = (uint64_t)P * cpn;
+  const dim3 grid_small((uint32_t)std::min<uint64_t>((chunks + kBucketWaves - 1) / kBucketWaves, 1u << 23));
   switch (bucket) {
-    case 64: hipLaunchKernelGGL(k_topk_bucketed<1>, grid, block, 0, stream, grad, residual, out_idx, out_val, A); break;
-    case 128: hipLaunchKernelGGL(k_topk_bucketed<2>, grid, block, 0, stream, grad, residual, out_idx, out_val, A); break;
+    case 64:
+      hipLaunchKernelGGL(k_topk_bucketed_small<4>, grid_small, block, 0, stream, grad, residual, out_idx, out_val, A,
+                         cpn, chunks);
+      break;
+    case 128:
+      hipLaunchKernelGGL(k_topk_bucketed_small<2>, grid_small, block, 0, stream, grad, residual, out_idx, out_val, A,
+                         cpn, chunks);
+      break;
     case 256: hipLaunchKernelGGL(k_topk_bucketed<4>, grid, block, 0, stream, grad, residual, out_idx, out_val, A); break;
     case 512: hipLaunchKernelGGL(k_topk_bucketed<8>, grid, block, 0, stream, grad, residual, out_idx, out_val, A); break;
     case 1024: hipLaunchKernelGGL(k_topk_bucketed<16>, grid, block, 0, stream, grad, residual, out_idx, out_val, A); break;

@@ -42,7 +42,7 @@ def test_bucketed_shapes(dev, bucket, P, N, kb):
     _check(g, r, bucket, kb, dev)
 
 
-@pytest.mark.parametrize("bucket", [64, 512])
+@pytest.mark.parametrize("bucket", [64, 128, 512])
 def test_bucketed_ties_zeros_and_subnormals(dev, bucket):
     rng = np.random.default_rng(bucket)
     P, N = 4, 6000
@@ -71,16 +71,18 @@ def test_bucketed_error_feedback_steps(dev):
         assert_bits_equal(rd.cpu().numpy(), r_o, f"residual step {step}")
 
 
-def test_bucketed_wideresnet_size_sampled_nodes(dev):
-    """P = 64, N = 2^27, 16 of every 512: oracle on two nodes, properties on all."""
+@pytest.mark.parametrize("bucket,kb", [(512, 16), (128, 4), (64, 2)])
+def test_bucketed_wideresnet_size_sampled_nodes(dev, bucket, kb):
+    """P = 64, N = 2^27, one in 32 kept: oracle on two nodes, properties on all."""
     w = W.workload(4)
-    P, N, bucket, kb = w.P, w.N, 512, 16
+    P, N = w.P, w.N
+    print(f"bucketed wide-ResNet size bucket={bucket} kb={kb}", flush=True)
     g = W.gradients(w, 0, device=dev)
     r = torch.zeros_like(g)
     idx, val = sg.topk_ef_bucketed(g, r, bucket, kb)
     torch.cuda.synchronize()
     K = sg.topk_bucketed_count(N, bucket, kb)
-    assert idx.shape == (P, K) and K == N // 512 * 16
+    assert idx.shape == (P, K) and K == N // bucket * kb
     for p in (0, P - 1):
         gp = g[p:p + 1].cpu().numpy()
         oi, ov, orr = oracle.topk_ef_bucketed(gp, np.zeros_like(gp), bucket, kb)
