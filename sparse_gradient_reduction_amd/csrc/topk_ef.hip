@@ -68,6 +68,9 @@ constexpr int kSampleChunks = 1024;
 constexpr int kSampleChunk = 64;
 constexpr int kSample = kSampleChunks * kSampleChunk;     // 65536
 constexpr int kPredictThreads = 1024;
+constexpr int kPredictKeys = 64;                            // sample keys per predict thread (registers)
+constexpr int kSmallPredictThreads = 256;
+constexpr int kSmallSample = kSmallPredictThreads * kPredictKeys;  // 16384
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
 constexpr int kGroup = 512;                              // tiles per gather group
 constexpr int kChunkThreads = 256;
@@ -134,6 +137,12 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
   return z;
 }
 
+// Per-layer call: rows whose sample exceeds what a 256-thread predict block
+// holds; they get 1024-thread blocks of their own.
+__host__ __device__ inline bool big_predict(uint64_t n, uint64_t k, uint32_t schunks) {
+  return k != 0 && k != n && n > kSmallLayer && (uint64_t)schunks * kSampleChunk > (uint64_t)kSmallSample;
+}
+
 // Totals over the rows: what the workspace holds.
 struct Plan {
   uint64_t rows;
@@ -142,6 +151,7 @@ struct Plan {
   uint64_t groups;  // group words
   uint64_t chunks;  // chunk words
   uint64_t passes;  // per-layer call: select / count / emit blocks
+  uint64_t big;     // per-layer call: rows with big_predict
   bool layers;      // per-layer call: row table and block-to-row tables too
 };
 
@@ -152,7 +162,7 @@ struct Layout {
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
   size_t info, err, state, h0, h1, h2, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
-      cout, rows, tile_row, group_row, pass_row, loff, lk, lkoff, total;
+      cout, rows, tile_row, group_row, pass_row, big_rows, loff, lk, lkoff, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -188,6 +198,7 @@ Layout make_layout(const Plan& Q, uint64_t nlayers) {
     L.tile_row = take(4ull * Q.tiles);
     L.group_row = take(4ull * Q.groups);
     L.pass_row = take(4ull * Q.passes);
+    L.big_rows = take(4ull * std::max<uint64_t>(1, Q.big));
     L.loff = take(8ull * (nlayers + 1));
     L.lk = take(8ull * nlayers);
     L.lkoff = take(8ull * nlayers);
@@ -208,6 +219,7 @@ Layout make_node_layout(uint32_t P, uint64_t N, uint64_t k) {
   Q.groups = (uint64_t)P * MG;
   Q.chunks = (uint64_t)P * z.chunks;
   Q.passes = 0;
+  Q.big = 0;
   Q.layers = false;
   Layout L = make_layout(Q, 0);
   L.capS = z.capS;
@@ -237,6 +249,7 @@ LayerPlan plan_layers(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, 
       lp.Q.groups += z.groups;
       lp.Q.chunks += z.chunks;
       lp.Q.passes += z.npass;
+      lp.Q.big += big_predict(off[l + 1] - off[l], k[l], z.schunks) ? 1 : 0;
       lp.max_groups = std::max<uint64_t>(lp.max_groups, z.groups);
       lp.max_cap = std::max<uint64_t>(lp.max_cap, (uint64_t)z.nsub * z.capS);
       lp.max_tiles = std::max<uint64_t>(lp.max_tiles, z.nt);
@@ -277,6 +290,7 @@ struct Dev {
   const uint32_t* tile_row;   // per-layer call: row of every stream workgroup
   const uint32_t* group_row;  // per-layer call: row of every tile group
   const uint32_t* pass_row;   // per-layer call: row of every select / count / emit block
+  const uint32_t* big_rows;   // per-layer call: the rows with big_predict, in row order
 };
 
 // Geometry of one selection row. For the [P][N] call it follows from (P, N,
@@ -346,20 +360,29 @@ __device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint3
 // ---------------------------------------------------------------------------
 // predict: reset the node's state and choose the two key thresholds.
 // ---------------------------------------------------------------------------
-template <bool ROWS, int NT>
+// One block per row, holding kPredictKeys sample keys per thread in
+// registers, so a block takes samples of up to NT * kPredictKeys keys. The
+// whole-node call runs 1024-thread blocks; the per-layer call runs 256-thread
+// blocks over every row (skipping the big_predict rows) and 1024-thread blocks
+// over the big_predict rows (BIG: block b takes row big_rows[b]).
+template <bool ROWS, int NT, bool BIG>
 __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
                                                              const float* __restrict__ r, Dev D) {
+  static_assert(!BIG || ROWS, "the row list exists in the per-layer call only");
+  static_assert(ROWS ? (NT * kPredictKeys == (BIG ? kSample : kSmallSample)) : NT * kPredictKeys == kSample,
+                "a block holds the largest sample of its rows");
   __shared__ uint32_t h1[4096];
   __shared__ uint32_t h2lo[2048];
   __shared__ uint32_t h2mid[2048];
   __shared__ uint32_t scr[NT / kWave + 3];
-  const uint32_t p = blockIdx.x;
+  const uint32_t p = BIG ? D.big_rows[blockIdx.x] : blockIdx.x;
   const Row R = row_of<ROWS>(D, p);
+  if (ROWS && !BIG && big_predict(R.n, R.k, R.schunks)) return;  // the 1024-thread launch takes it
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < kH0; i += NT) D.h0[(size_t)p * kH0 + i] = 0u;
   for (uint32_t i = tid; i < kH1; i += NT) D.h1[(size_t)p * kH1 + i] = 0u;
   for (uint32_t i = tid; i < kH2; i += NT) D.h2[(size_t)p * kH2 + i] = 0u;
-  for (uint32_t i = tid; i < kSub; i += NT) D.sub[((size_t)p * kSub + i) * 32] = 0u;
+  for (uint32_t i = tid; i < R.nsub; i += NT) D.sub[((size_t)p * kSub + i) * 32] = 0u;  // the counters in use
 
   uint32_t lo, mid;
   if (R.k == 0) {
@@ -374,7 +397,7 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
     for (uint32_t i = tid; i < 2048; i += NT) h2lo[i] = h2mid[i] = 0u;
     __syncthreads();
     const uint64_t base = R.base;
-    const uint32_t nsamp = R.schunks * kSampleChunk;  // <= kSample
+    const uint32_t nsamp = R.schunks * kSampleChunk;  // <= NT * kPredictKeys
     const bool whole = R.n <= nsamp;
     auto sample_key = [&](uint32_t i) -> uint32_t {  // 0xFFFFFFFF marks "no sample"
       if (whole) return i < R.n ? mag_key(g[base + i] + r[base + i]) : 0xFFFFFFFFu;
@@ -383,18 +406,18 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
       const uint64_t start = (uint64_t)c * (R.n - kSampleChunk) / (R.schunks - 1);
       return mag_key(g[base + start + o] + r[base + start + o]);
     };
-    uint32_t keys[kSample / NT];
+    uint32_t keys[kPredictKeys];
 #pragma unroll
-    for (int j = 0; j < kSample / NT; ++j) keys[j] = sample_key(j * NT + tid);
+    for (int j = 0; j < kPredictKeys; ++j) keys[j] = sample_key(j * NT + tid);
 #pragma unroll
-    for (int j = 0; j < kSample / NT; ++j)
+    for (int j = 0; j < kPredictKeys; ++j)
       if (keys[j] != 0xFFFFFFFFu) atomicAdd(&h1[keys[j] >> 19], 1u);
     __syncthreads();
     uint32_t b_lo, a_lo, b_mid, a_mid;
     block_find_suffix<NT>(h1, 4096, R.rs_lo, scr, b_lo, a_lo);
     block_find_suffix<NT>(h1, 4096, R.rs_mid, scr, b_mid, a_mid);
 #pragma unroll
-    for (int j = 0; j < kSample / NT; ++j) {
+    for (int j = 0; j < kPredictKeys; ++j) {
       const uint32_t key = keys[j];
       if (key == 0xFFFFFFFFu) continue;
       if ((key >> 19) == b_lo) atomicAdd(&h2lo[(key >> 8) & 2047u], 1u);
@@ -966,11 +989,11 @@ __global__ void k_layers_in(uint64_t* loff, uint64_t* lk, uint64_t* lkoff, uint3
 
 // One workgroup: every row's sizes (row_size, as the host computed them),
 // exclusive scans of their slices, the sample ranks of its thresholds.
-__global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, const uint64_t* loff, const uint64_t* lk,
-                                                    const uint64_t* lkoff, uint32_t P, uint64_t N, uint32_t nl,
-                                                    uint64_t K) {
+__global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_rows, const uint64_t* loff,
+                                                    const uint64_t* lk, const uint64_t* lkoff, uint32_t P, uint64_t N,
+                                                    uint32_t nl, uint64_t K) {
   __shared__ uint64_t scr[1024 / kWave + 1];
-  uint64_t c_cand = 0, c_tiles = 0, c_groups = 0, c_chunks = 0, c_pass = 0;  // carries over rounds
+  uint64_t c_cand = 0, c_tiles = 0, c_groups = 0, c_chunks = 0, c_pass = 0, c_big = 0;  // carries over rounds
   const uint64_t nrows = (uint64_t)P * nl;
   for (uint64_t r0 = 0; r0 < nrows; r0 += 1024) {
     const uint64_t ri = r0 + threadIdx.x;
@@ -998,6 +1021,10 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, const uint64_t* l
     c_chunks += t;
     const uint64_t pass0 = c_pass + block_exclusive_scan_u64<1024>(in ? z.npass : 0, scr, t);
     c_pass += t;
+    const bool big = in && big_predict(n, k, z.schunks);
+    const uint64_t big0 = c_big + block_exclusive_scan_u64<1024>(big ? 1 : 0, scr, t);
+    c_big += t;
+    if (big) big_rows[big0] = (uint32_t)ri;
     if (in) {
       Row R{};
       R.base = base;
@@ -1044,11 +1071,19 @@ __global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* ti
 // other grids.
 template <bool ROWS>
 hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t groups, uint64_t max_tiles,
-               uint64_t max_cap, uint64_t passes, bool any_k, const float* grad, float* residual,
+               uint64_t max_cap, uint64_t passes, uint64_t big_rows, bool any_k, const float* grad, float* residual,
                uint32_t* out_idx, float* out_val, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const uint32_t R = (uint32_t)nrows;
-  hipLaunchKernelGGL((k_predict<ROWS, kPredictThreads>), dim3(R), dim3(kPredictThreads), 0, stream, grad, residual,
-                     D);
+  if constexpr (ROWS) {
+    hipLaunchKernelGGL((k_predict<true, kSmallPredictThreads, false>), dim3(R), dim3(kSmallPredictThreads), 0, stream,
+                       grad, residual, D);
+    if (big_rows > 0)
+      hipLaunchKernelGGL((k_predict<true, kPredictThreads, true>), dim3((uint32_t)big_rows), dim3(kPredictThreads), 0,
+                         stream, grad, residual, D);
+  } else {
+    hipLaunchKernelGGL((k_predict<false, kPredictThreads, false>), dim3(R), dim3(kPredictThreads), 0, stream, grad,
+                       residual, D);
+  }
   hipError_t e = hipSuccess;
   if (stream_blocks > 0) {
     if (ev_start || ev_stop) {
@@ -1144,7 +1179,7 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
     D.rs_lo = (uint32_t)std::min<double>(std::ceil(qs + 4.0 * std::sqrt(qs) + 16.0), (double)kSample);
     D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
   }
-  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, k > 0, grad, residual, out_idx, out_val, stream,
+  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, k > 0, grad, residual, out_idx, out_val, stream,
                     ev_start, ev_stop);
 }
 
@@ -1171,6 +1206,8 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
   uint32_t* group_row = reinterpret_cast<uint32_t*>(w + L.group_row);
   uint32_t* pass_row = reinterpret_cast<uint32_t*>(w + L.pass_row);
   uint64_t* lkoff = reinterpret_cast<uint64_t*>(w + L.lkoff);
+  uint32_t* big_rows = reinterpret_cast<uint32_t*>(w + L.big_rows);
+  D.big_rows = big_rows;
   D.rows = rows;
   D.tile_row = tile_row;
   D.group_row = group_row;
@@ -1188,11 +1225,11 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
     in.off[count] = off[first + count];
     hipLaunchKernelGGL(k_layers_in, dim3(1), dim3(128), 0, stream, loff, lk, lkoff, first, count, in);
   }
-  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, loff, lk, lkoff, P, N, nl, lp.K);
+  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, loff, lk, lkoff, P, N, nl, lp.K);
   hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_row, group_row,
                      pass_row);
-  return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.K > 0, grad,
-                   residual, out_idx, out_val, stream, nullptr, nullptr);
+  return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.K > 0,
+                   grad, residual, out_idx, out_val, stream, nullptr, nullptr);
 }
 
 }  // namespace sparcml
