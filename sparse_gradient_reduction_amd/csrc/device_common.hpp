@@ -74,7 +74,7 @@ __device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool
   uint64_t todo = ballot(valid);
   while (todo) {
     const int leader = __ffsll((long long)todo) - 1;
-    const uint32_t b = (uint32_t)__shfl((int)bin, leader, kWave);
+    const uint32_t b = __builtin_amdgcn_readlane(bin, leader);  // leader is wave-uniform
     const uint64_t same = ballot(valid && bin == b) & todo;
     if (lane_id() == (uint32_t)leader) atomicAdd(&hist[b], popc64(same));
     todo &= ~same;
@@ -161,44 +161,66 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
   return excl;
 }
 
-// Radix-select step over a histogram `hist` of `nbins` bins (LDS or global):
-// finds the highest bin b such that the count of items in bins >= b reaches
-// `rank` (1-based, rank >= 1), and the count in bins strictly above b. If the
-// histogram holds fewer than `rank` items, returns bin 0 with `above` = total
-// of bins > 0. `scratch` holds NT/64 + 3 words of LDS. All threads call it;
-// all receive the result.
-template <int NT>
-__device__ __forceinline__ void block_find_suffix(const uint32_t* hist, int nbins, uint32_t rank,
-                                                  uint32_t* scratch, uint32_t& bin, uint32_t& above) {
-  const int per = nbins / NT;  // bins per thread, nbins is a multiple of NT
-  // thread t owns bins [nbins-1-t*per-(per-1), nbins-1-t*per], walked top down
-  const int top = nbins - 1 - (int)threadIdx.x * per;
+// Radix-select step over a histogram of NB bins whose counts each thread
+// holds: c[i] is bin NB-1-t*per-i for thread t (per = NB/NT), the layout
+// load_suffix_bins reads. Finds the highest bin b such that the count of items
+// in bins >= b reaches `rank` (1-based, rank >= 1), and the count in bins
+// strictly above b. If the histogram holds fewer than `rank` items, returns
+// bin 0 with `above` = total of bins > 0. `scratch` holds NT/64 + 3 words of
+// LDS. All threads call it; all receive the result.
+template <int NT, int NB>
+__device__ __forceinline__ void block_find_suffix_held(const uint32_t (&c)[NB / NT], uint32_t rank,
+                                                       uint32_t* scratch, uint32_t& bin, uint32_t& above) {
+  static_assert(NB % NT == 0, "whole bins per thread");
+  constexpr int per = NB / NT;
+  const int top = NB - 1 - (int)threadIdx.x * per;
   uint32_t s = 0;
-  for (int i = 0; i < per; ++i) s += hist[top - i];
+#pragma unroll
+  for (int i = 0; i < per; ++i) s += c[i];
   uint32_t total;
-  uint32_t before = block_exclusive_scan<NT>(s, scratch, total);
+  const uint32_t before = block_exclusive_scan<NT>(s, scratch, total);
   constexpr int NW = NT / kWave;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == NT - 1) {  // holds bin 0 as c[per - 1]
     scratch[NW + 1] = 0u;
-    scratch[NW + 2] = total - hist[0];
+    scratch[NW + 2] = total - c[per - 1];
   }
   __syncthreads();
   if (before < rank && before + s >= rank) {
     uint32_t run = before;
+    bool found = false;
+#pragma unroll
     for (int i = 0; i < per; ++i) {
-      uint32_t c = hist[top - i];
-      if (run + c >= rank) {
+      if (!found && run + c[i] >= rank) {
         scratch[NW + 1] = (uint32_t)(top - i);
         scratch[NW + 2] = run;
-        break;
+        found = true;
       }
-      run += c;
+      run += c[i];
     }
   }
   __syncthreads();
   bin = scratch[NW + 1];
   above = scratch[NW + 2];
   __syncthreads();
+}
+
+// This thread's bins of an NB-bin histogram in the block_find_suffix_held
+// layout (all loads issued at once).
+template <int NT, int NB>
+__device__ __forceinline__ void load_suffix_bins(const uint32_t* hist, uint32_t (&c)[NB / NT]) {
+  constexpr int per = NB / NT;
+  const int top = NB - 1 - (int)threadIdx.x * per;
+#pragma unroll
+  for (int i = 0; i < per; ++i) c[i] = hist[top - i];
+}
+
+// block_find_suffix_held over a histogram in memory (LDS or global).
+template <int NT, int NB>
+__device__ __forceinline__ void block_find_suffix(const uint32_t* hist, uint32_t rank, uint32_t* scratch,
+                                                  uint32_t& bin, uint32_t& above) {
+  uint32_t c[NB / NT];
+  load_suffix_bins<NT, NB>(hist, c);
+  block_find_suffix_held<NT, NB>(c, rank, scratch, bin, above);
 }
 
 }  // namespace sparcml

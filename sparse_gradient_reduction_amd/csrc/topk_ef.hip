@@ -414,8 +414,8 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
       if (keys[j] != 0xFFFFFFFFu) atomicAdd(&h1[keys[j] >> 19], 1u);
     __syncthreads();
     uint32_t b_lo, a_lo, b_mid, a_mid;
-    block_find_suffix<NT>(h1, 4096, R.rs_lo, scr, b_lo, a_lo);
-    block_find_suffix<NT>(h1, 4096, R.rs_mid, scr, b_mid, a_mid);
+    block_find_suffix<NT, 4096>(h1, R.rs_lo, scr, b_lo, a_lo);
+    block_find_suffix<NT, 4096>(h1, R.rs_mid, scr, b_mid, a_mid);
 #pragma unroll
     for (int j = 0; j < kPredictKeys; ++j) {
       const uint32_t key = keys[j];
@@ -425,8 +425,8 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
     }
     __syncthreads();
     uint32_t c_lo, x_lo, c_mid, x_mid;
-    block_find_suffix<NT>(h2lo, 2048, R.rs_lo - a_lo, scr, c_lo, x_lo);
-    block_find_suffix<NT>(h2mid, 2048, R.rs_mid - a_mid, scr, c_mid, x_mid);
+    block_find_suffix<NT, 2048>(h2lo, R.rs_lo - a_lo, scr, c_lo, x_lo);
+    block_find_suffix<NT, 2048>(h2mid, R.rs_mid - a_mid, scr, c_mid, x_mid);
     lo = (b_lo << 19) | (c_lo << 8);
     mid = (b_mid << 19) | (c_mid << 8);
   }
@@ -700,29 +700,38 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
 }
 
 // Digits chosen so far, recomputed from the global histograms of the levels
-// below `level` (each block does it; they all agree).
+// below `level` (each block does it; they all agree). The bins are loaded
+// first (DigitBins::load) and decided on later, so that a kernel can issue
+// its first data loads in between and wait for the bins alone.
 template <int NT>
-__device__ __forceinline__ void decide(const Dev& D, uint32_t p, uint32_t k, int level, uint32_t* scr,
-                                       uint32_t& prefix, uint32_t& krem) {
-  krem = k;
-  prefix = 0;
-  uint32_t bin, above;
-  if (level >= 1) {
-    block_find_suffix<NT>(D.h0 + (size_t)p * kH0, kH0, krem, scr, bin, above);
-    krem -= above;
-    prefix = bin;
+struct DigitBins {
+  uint32_t c0[kH0 / NT], c1[kH1 / NT], c2[kH2 / NT];
+  __device__ __forceinline__ void load(const Dev& D, uint32_t p, int level) {
+    if (level >= 1) load_suffix_bins<NT, kH0>(D.h0 + (size_t)p * kH0, c0);
+    if (level >= 2) load_suffix_bins<NT, kH1>(D.h1 + (size_t)p * kH1, c1);
+    if (level >= 3) load_suffix_bins<NT, kH2>(D.h2 + (size_t)p * kH2, c2);
   }
-  if (level >= 2) {
-    block_find_suffix<NT>(D.h1 + (size_t)p * kH1, kH1, krem, scr, bin, above);
-    krem -= above;
-    prefix = (prefix << 10) | bin;
+  __device__ __forceinline__ void decide(uint32_t k, int level, uint32_t* scr, uint32_t& prefix, uint32_t& krem) {
+    krem = k;
+    prefix = 0;
+    uint32_t bin, above;
+    if (level >= 1) {
+      block_find_suffix_held<NT, kH0>(c0, krem, scr, bin, above);
+      krem -= above;
+      prefix = bin;
+    }
+    if (level >= 2) {
+      block_find_suffix_held<NT, kH1>(c1, krem, scr, bin, above);
+      krem -= above;
+      prefix = (prefix << 10) | bin;
+    }
+    if (level >= 3) {
+      block_find_suffix_held<NT, kH2>(c2, krem, scr, bin, above);
+      krem -= above;
+      prefix = (prefix << 10) | bin;
+    }
   }
-  if (level >= 3) {
-    block_find_suffix<NT>(D.h2 + (size_t)p * kH2, kH2, krem, scr, bin, above);
-    krem -= above;
-    prefix = (prefix << 10) | bin;
-  }
-}
+};
 
 // ---------------------------------------------------------------------------
 // hist: one radix level of T*. Level 0 runs only on the rescan path (the
@@ -743,19 +752,30 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
   const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
   const uint64_t nbx = ROWS ? R.npass : gridDim.x;
   for (uint32_t i = threadIdx.x; i < NB; i += 256) h[i] = 0u;
-  uint32_t prefix, krem;
-  decide<256>(D, p, R.k, LEVEL, scr, prefix, krem);
-  __syncthreads();
   const uint64_t n = source_len(D, R, p, rescan);
   const float* src = rescan ? r + R.base : D.oval + R.cand;
   const uint64_t stride = nbx * 256 * kU;
-  for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
-    uint32_t key[kU];
+  // keys of the pass starting at i0 (0xFFFFFFFF past the end, where the
+  // load rereads the last element: no branch around the loads)
+  const uint64_t last = n ? n - 1 : 0;
+  auto load = [&](uint64_t i0, uint32_t (&key)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const uint64_t i = i0 + (uint64_t)u * 256;
-      key[u] = i < n ? mag_key(src[i]) : 0xFFFFFFFFu;
+      const float x = src[i < n ? i : last];
+      key[u] = i < n ? mag_key(x) : 0xFFFFFFFFu;
     }
+  };
+  DigitBins<256> bins;
+  bins.load(D, p, LEVEL);
+  uint32_t key[kU];
+  load(bx * 256 * kU + threadIdx.x, key);  // in flight while the digits are decided
+  uint32_t prefix, krem;
+  bins.decide(R.k, LEVEL, scr, prefix, krem);
+  __syncthreads();
+  for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
+    uint32_t nkey[kU];
+    load(i0 + stride, nkey);  // the block's next pass, in flight during this one
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const uint32_t kk = key[u];
@@ -779,6 +799,8 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
         atomicAdd(&h[bin], 1u);
       }
     }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) key[u] = nkey[u];
   }
   __syncthreads();
   uint32_t* gh = (LEVEL == 0 ? D.h0 : (LEVEL == 1 ? D.h1 : D.h2)) + (size_t)p * NB;
@@ -798,24 +820,34 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
   if (R.k == 0) return;
   const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
   const uint64_t nbx = ROWS ? R.npass : gridDim.x;
-  uint32_t T, m;
-  decide<kChunkThreads>(D, p, R.k, 3, scr, T, m);
-  if (bx == 0 && threadIdx.x == 0) {
-    D.state[p].T = T;
-    D.state[p].m = m;
-  }
   const bool rescan = D.state[p].mode != 0u;
   const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
   const float* src = rescan ? r + R.base : D.oval + R.cand;
-  for (uint64_t c = bx; c < nchunks; c += nbx) {
-    uint32_t gt = 0, eq = 0;
-    float v[kChunkIt];
+  // chunk c's values; positions past the end reread the last element (no
+  // branch around the loads) and are masked where used
+  const uint64_t last = n ? n - 1 : 0;
+  auto load = [&](uint64_t c, float (&v)[kChunkIt]) {
 #pragma unroll
     for (int it = 0; it < kChunkIt; ++it) {
       const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
-      v[it] = j < n ? src[j] : 0.0f;
+      v[it] = src[j < n ? j : last];
     }
+  };
+  DigitBins<kChunkThreads> bins;
+  bins.load(D, p, 3);
+  float v[kChunkIt];
+  load(bx, v);  // in flight while the digits are decided
+  uint32_t T, m;
+  bins.decide(R.k, 3, scr, T, m);
+  if (bx == 0 && threadIdx.x == 0) {
+    D.state[p].T = T;
+    D.state[p].m = m;
+  }
+  for (uint64_t c = bx; c < nchunks; c += nbx) {
+    float nv[kChunkIt];
+    load(c + nbx, nv);  // the block's next chunk, in flight during this one
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int it = 0; it < kChunkIt; ++it) {
       const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
@@ -829,6 +861,8 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
       D.cgt[R.chunk0 + c] = tgt;
       D.ceq[R.chunk0 + c] = teq;
     }
+#pragma unroll
+    for (int it = 0; it < kChunkIt; ++it) v[it] = nv[it];
   }
 }
 
@@ -894,18 +928,36 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
   const uint32_t* isrc = D.oidx + R.cand;
   uint32_t* oi = out_idx + R.out0;
   float* ov = out_val + R.out0;
+  // chunk c's values and row-local indices; positions past the end reread
+  // the last element (no branch around the loads) and are masked where used
+  const uint64_t last = n ? n - 1 : 0;
+  auto load = [&](uint64_t c, float (&v)[kChunkIt], uint32_t (&e)[kChunkIt]) {
+    if (rescan) {  // the source is the row itself: the position is the index
+#pragma unroll
+      for (int it = 0; it < kChunkIt; ++it) {
+        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+        v[it] = vsrc[j < n ? j : last];
+        e[it] = (uint32_t)j;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < kChunkIt; ++it) {
+        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+        const uint64_t jj = j < n ? j : last;
+        v[it] = vsrc[jj];
+        e[it] = isrc[jj];
+      }
+    }
+  };
+  float v[kChunkIt];
+  uint32_t e[kChunkIt];
+  load(bx, v, e);
   for (uint64_t c = bx; c < nchunks; c += nbx) {
     const uint32_t eq_base = D.ceqoff[R.chunk0 + c];
     const uint32_t out_base = D.cout[R.chunk0 + c];
-    float v[kChunkIt];
-    uint32_t e[kChunkIt];
-#pragma unroll
-    for (int it = 0; it < kChunkIt; ++it) {
-      const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
-      const bool valid = j < n;
-      v[it] = valid ? vsrc[j] : 0.0f;
-      e[it] = valid ? (rescan ? (uint32_t)j : isrc[j]) : 0u;
-    }
+    float nv[kChunkIt];
+    uint32_t ne[kChunkIt];
+    load(c + nbx, nv, ne);  // the block's next chunk, in flight during this one
     // per (it, wave): ranks of equal keys, then of selected elements
     uint32_t eq_pre[kChunkIt];
     uint32_t eq_bits = 0;
@@ -961,6 +1013,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
       } else if (!rescan && high) {
         r[pN + e[it]] = v[it];  // zeroed on the guess but not selected: restore
       }
+    }
+#pragma unroll
+    for (int it = 0; it < kChunkIt; ++it) {
+      v[it] = nv[it];
+      e[it] = ne[it];
     }
     __syncthreads();  // s_eq / s_sel are reused by the next chunk
   }
