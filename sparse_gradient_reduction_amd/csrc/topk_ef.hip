@@ -167,7 +167,7 @@ struct Layout {
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
   size_t info, err, state, h0, h1, h2, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
-      cout, rows, tile_rec, group_row, pass_row, big_rows, loff, lk, lkoff, total;
+      cout, rows, tile_row, group_row, pass_row, big_rows, loff, lk, lkoff, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -200,7 +200,7 @@ Layout make_layout(const Plan& Q, uint64_t nlayers) {
   L.cout = take(4ull * Q.chunks);
   if (Q.layers) {
     L.rows = take(kRowBytes * R);
-    L.tile_rec = take(16ull * Q.tiles);
+    L.tile_row = take(4ull * Q.tiles);
     L.group_row = take(4ull * Q.groups);
     L.pass_row = take(4ull * Q.passes);
     L.big_rows = take(4ull * std::max<uint64_t>(1, Q.big));
@@ -292,7 +292,7 @@ struct Dev {
   uint32_t* ceqoff;
   uint32_t* cout;
   const struct Row* rows;     // per-layer call: row table
-  const struct TileRec* tile_rec;  // per-layer call: row and place of every stream workgroup
+  const uint32_t* tile_row;   // per-layer call: row of every stream workgroup
   const uint32_t* group_row;  // per-layer call: row of every tile group
   const uint32_t* pass_row;   // per-layer call: row of every select / count / emit block
   const uint32_t* big_rows;   // per-layer call: the rows with big_predict, in row order
@@ -321,17 +321,6 @@ struct Row {
 };
 
 static_assert(sizeof(Row) == kRowBytes, "row table entry size used by the workspace layout");
-
-// Per-layer call: one record per stream workgroup, read with one scalar load,
-// so that a tile inside its row issues its data loads before the row's fields
-// arrive.
-struct alignas(16) TileRec {
-  uint32_t row;
-  uint32_t tile;  // tile within the row; bit 31: every float4 group of the tile lies inside the row
-  uint64_t grp0;  // float4 group of the tile's first element
-};
-constexpr uint32_t kInterior = 0x80000000u;
-static_assert(sizeof(TileRec) == 16, "read as one uint4");
 
 template <bool ROWS>
 __device__ __forceinline__ Row row_of(const Dev& D, uint32_t p) {
@@ -468,30 +457,19 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
   // each XCD streams one contiguous stretch of tiles (steadier than the
   // default round-robin of consecutive tiles over the 8 XCDs)
   const uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
-  const uint32_t tid = threadIdx.x;
   uint32_t p, t;
   Row R;
-  bool interior = false;
-  f32x4 gv, rv;
   if constexpr (ROWS) {
-    // the whole record in one 16-byte load
-    const uint4 rec = *reinterpret_cast<const uint4*>(D.tile_rec + w);
-    p = rec.x;
-    t = rec.y & ~kInterior;
-    interior = (rec.y & kInterior) != 0u;
-    const uint64_t grp0 = ((uint64_t)rec.w << 32) | rec.z;
-    // in flight while the row's fields load; an edge tile loads its first
-    // group (inside the arrays) and reloads below
-    const uint64_t gi = interior ? grp0 + tid : grp0;
-    gv = load_nt(reinterpret_cast<const f32x4*>(g) + gi);
-    rv = load_nt(reinterpret_cast<const f32x4*>(r) + gi);
+    p = D.tile_row[w];
     R = row_of<true>(D, p);
+    t = w - (uint32_t)R.tile0;
   } else {
     p = w / (uint32_t)D.MT;
     t = w % (uint32_t)D.MT;
     R = row_of<false>(D, p);
     if (t >= row_tiles(R)) return;
   }
+  const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id();
   const uint32_t wid = tid / kWave;
   const uint32_t N = R.n;
@@ -501,15 +479,13 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
   const uint64_t grp = ((pN - phi) >> 2) + (uint64_t)t * (kTile / 4) + tid;   // float4 group
   const uint32_t lo = D.state[p].lo;
   const uint32_t mid = D.state[p].mid;
-  const bool full = interior || (e0 >= 0 && e0 + 4 <= (int64_t)N);
+  const bool full = e0 >= 0 && e0 + 4 <= (int64_t)N;
 
   float a[4];
   uint32_t own = 0xFu;
   if (full) {
-    if (!interior) {
-      gv = load_nt(reinterpret_cast<const f32x4*>(g) + grp);
-      rv = load_nt(reinterpret_cast<const f32x4*>(r) + grp);
-    }
+    const f32x4 gv = load_nt(reinterpret_cast<const f32x4*>(g) + grp);
+    const f32x4 rv = load_nt(reinterpret_cast<const f32x4*>(r) + grp);
     a[0] = gv.x + rv.x;
     a[1] = gv.y + rv.y;
     a[2] = gv.z + rv.z;
@@ -1142,21 +1118,12 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_row
 }
 
 // block-to-row tables of the per-layer grids
-__global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, TileRec* tile_rec, uint32_t* group_row,
+__global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* tile_row, uint32_t* group_row,
                                                    uint32_t* pass_row) {
   const uint32_t p = blockIdx.x;
   const Row R = rows[p];
   const uint32_t nt = row_tiles(R);
-  const uint32_t phi = tile_phase(R.base);
-  for (uint32_t t = threadIdx.x; t < nt; t += 256) {
-    // tile t covers row elements [t * kTile - phi, (t + 1) * kTile - phi)
-    const bool interior = (t > 0 || phi == 0) && (uint64_t)(t + 1) * kTile - phi <= R.n;
-    TileRec rec;
-    rec.row = p;
-    rec.tile = t | (interior ? kInterior : 0u);
-    rec.grp0 = ((R.base - phi) >> 2) + (uint64_t)t * (kTile / 4);
-    tile_rec[R.tile0 + t] = rec;
-  }
+  for (uint32_t t = threadIdx.x; t < nt; t += 256) tile_row[R.tile0 + t] = p;
   const uint32_t ng = (nt + kGroup - 1) / kGroup;
   for (uint32_t t = threadIdx.x; t < ng; t += 256) group_row[R.group0 + t] = p;
   for (uint32_t t = threadIdx.x; t < R.npass; t += 256) pass_row[R.pass0 + t] = p;
@@ -1253,7 +1220,7 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
   D.ceqoff = reinterpret_cast<uint32_t*>(w + L.ceqoff);
   D.cout = reinterpret_cast<uint32_t*>(w + L.cout);
   D.rows = nullptr;
-  D.tile_rec = nullptr;
+  D.tile_row = nullptr;
   return D;
 }
 
@@ -1296,7 +1263,7 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
   char* w = static_cast<char*>(ws);
   Dev D = make_dev(L, w, (uint32_t)lp.Q.rows);
   Row* rows = reinterpret_cast<Row*>(w + L.rows);
-  TileRec* tile_rec = reinterpret_cast<TileRec*>(w + L.tile_rec);
+  uint32_t* tile_row = reinterpret_cast<uint32_t*>(w + L.tile_row);
   uint64_t* loff = reinterpret_cast<uint64_t*>(w + L.loff);
   uint64_t* lk = reinterpret_cast<uint64_t*>(w + L.lk);
   uint32_t* group_row = reinterpret_cast<uint32_t*>(w + L.group_row);
@@ -1305,7 +1272,7 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
   uint32_t* big_rows = reinterpret_cast<uint32_t*>(w + L.big_rows);
   D.big_rows = big_rows;
   D.rows = rows;
-  D.tile_rec = tile_rec;
+  D.tile_row = tile_row;
   D.group_row = group_row;
   D.pass_row = pass_row;
   uint64_t koff = 0;
@@ -1322,7 +1289,7 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
     hipLaunchKernelGGL(k_layers_in, dim3(1), dim3(128), 0, stream, loff, lk, lkoff, first, count, in);
   }
   hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, loff, lk, lkoff, P, N, nl, lp.K);
-  hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_rec, group_row,
+  hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_row, group_row,
                      pass_row);
   return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.K > 0,
                    grad, residual, out_idx, out_val, stream, nullptr, nullptr);
