@@ -67,18 +67,24 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// hist[bin] += 1 for every active lane with `valid`, issuing one LDS atomic
-// per distinct bin in the wave instead of one per lane: keys near a selection
-// threshold crowd into a few bins, where per-lane atomics would serialise.
-__device__ __forceinline__ void wave_hist_add(uint32_t* hist, uint32_t bin, bool valid) {
+// hist[bin] += 1 for every active lane with `valid`. The bins of the first
+// CAP distinct bins met (lowest lanes first) take one LDS atomic each for all
+// their lanes; the lanes left over add one by one. Keys near a selection
+// threshold crowd into a few bins, where per-lane atomics would serialise;
+// where they spread, a leader loop over every distinct bin would cost more.
+template <int CAP>
+__device__ __forceinline__ void wave_hist_add_capped(uint32_t* hist, uint32_t bin, bool valid) {
   uint64_t todo = ballot(valid);
-  while (todo) {
+#pragma unroll
+  for (int i = 0; i < CAP; ++i) {
+    if (!todo) return;
     const int leader = __ffsll((long long)todo) - 1;
     const uint32_t b = __builtin_amdgcn_readlane(bin, leader);  // leader is wave-uniform
     const uint64_t same = ballot(valid && bin == b) & todo;
     if (lane_id() == (uint32_t)leader) atomicAdd(&hist[b], popc64(same));
     todo &= ~same;
   }
+  if ((todo >> lane_id()) & 1ull) atomicAdd(&hist[bin], 1u);
 }
 
 // Sum of (a, b) over the block. `scratch` holds 2 * NT/64 words of LDS.

@@ -675,12 +675,12 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
       const uint32_t i = i0 + u * kGroup;
       src[u] = 0xFFFFFFFFu;
       if (i < tot) {
-        uint32_t lo = 0, hi = kGroup;  // s_excl[lo] <= i < s_excl[hi]
-        while (hi - lo > 1) {
-          const uint32_t mid = (lo + hi) >> 1;
-          if (s_excl[mid] <= i) lo = mid;
-          else hi = mid;
-        }
+        // the last tile whose run starts at or before i (a fixed number of
+        // branch-free steps, so the kU searches interleave)
+        uint32_t lo = 0;
+#pragma unroll
+        for (uint32_t step = kGroup / 2; step > 0; step >>= 1)
+          lo = s_excl[lo + step] <= i ? lo + step : lo;
         src[u] = s_toff[lo] + (i - s_excl[lo]);
       }
     }
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
         D.oval[out + i] = v;
         D.oidx[out + i] = (uint32_t)(c[u] >> 32);
       }
-      wave_hist_add(h, mag_key(v) >> 20, valid);
+      wave_hist_add_capped<2>(h, mag_key(v) >> 20, valid);
     }
   }
   __syncthreads();
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
       // level 0 keys crowd into a few bins: aggregate per wave; the lower
       // digits spread out, where plain LDS atomics are cheaper
       if (LEVEL == 0) {
-        wave_hist_add(h, bin, hit);
+        wave_hist_add_capped<2>(h, bin, hit);
       } else if (hit) {
         atomicAdd(&h[bin], 1u);
       }
