@@ -961,37 +961,41 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
   for (uint64_t c = bx; c < nchunks; c += nbx) {
     const uint32_t eq_base = D.ceqoff[R.chunk0 + c];
     const uint32_t out_base = D.cout[R.chunk0 + c];
+    const uint32_t teq = D.ceq[R.chunk0 + c];
     float nv[kChunkIt];
     uint32_t ne[kChunkIt];
     load(c + nbx, nv, ne);  // the block's next chunk, in flight during this one
-    // per (it, wave): ranks of equal keys, then of selected elements
+    // per (it, wave): ranks of equal keys, needed only where some key of the
+    // chunk equals T* with tie quota left (usually one chunk of the row)
     uint32_t eq_pre[kChunkIt];
     uint32_t eq_bits = 0;
+    if (teq != 0u && eq_base < m) {
 #pragma unroll
-    for (int it = 0; it < kChunkIt; ++it) {
-      const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
-      const bool is_eq = j < n && mag_key(v[it]) == T;
-      const uint64_t em = ballot(is_eq);
-      eq_bits |= (is_eq ? 1u : 0u) << it;
-      eq_pre[it] = lanes_below(em);
-      if (lane == 0) s_eq[it * NW + wid] = popc64(em);
+      for (int it = 0; it < kChunkIt; ++it) {
+        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+        const bool is_eq = j < n && mag_key(v[it]) == T;
+        const uint64_t em = ballot(is_eq);
+        eq_bits |= (is_eq ? 1u : 0u) << it;
+        eq_pre[it] = lanes_below(em);
+        if (lane == 0) s_eq[it * NW + wid] = popc64(em);
+      }
+      __syncthreads();
+      static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
+      if (threadIdx.x < kWave) {
+        const uint32_t x = s_eq[threadIdx.x];
+        s_eq[threadIdx.x] = wave_inclusive_scan(x) - x;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
-    if (threadIdx.x < kWave) {
-      const uint32_t x = s_eq[threadIdx.x];
-      s_eq[threadIdx.x] = wave_inclusive_scan(x) - x;
-    }
-    __syncthreads();
+    // then ranks of the selected elements
     uint32_t sel_bits = 0;
     uint32_t sel_pre[kChunkIt];
 #pragma unroll
     for (int it = 0; it < kChunkIt; ++it) {
       const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
       const uint32_t key = mag_key(v[it]);
-      const bool is_eq = (eq_bits >> it) & 1u;
-      const uint32_t eq_rank = eq_base + s_eq[it * NW + wid] + eq_pre[it];
-      const bool sel = j < n && (key > T || (is_eq && eq_rank < m));
+      const bool is_eq = (eq_bits >> it) & 1u;  // set only on the tie path above
+      const bool sel = j < n && (key > T || (is_eq && eq_base + s_eq[it * NW + wid] + eq_pre[it] < m));
       sel_bits |= (sel ? 1u : 0u) << it;
       const uint64_t sm = ballot(sel);
       sel_pre[it] = lanes_below(sm);
