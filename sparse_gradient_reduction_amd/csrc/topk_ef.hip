@@ -111,7 +111,10 @@ constexpr size_t kRowBytes = 12 * sizeof(uint64_t);
 
 // A whole node: kSub regions with a whole tile of slack each. A layer: as
 // many regions as it has runs of kTilesPerSlot tiles (at most kSub), with the
-// slack of its largest possible run.
+// slack of its largest possible run. Where every element is a candidate (k =
+// n, or a layer small enough to skip the prediction), a region takes whole
+// slot groups of tiles, and regions may hold one group more than others: each
+// holds the most groups any region gets.
 __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t k, bool layer) {
   RowSize z;
   z.nt = (n + tile_phase(base) + kTile - 1) / kTile;
@@ -138,6 +141,14 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
     const uint64_t est = n < 2 * k + 4096 ? n : 2 * k + 4096;
     uint64_t np = (est + 8191) / 8192;
     z.npass = (uint32_t)(np < 1 ? 1 : (np > 64 ? 64 : np));
+  }
+  if (k >= n || (layer && n <= kSmallLayer)) {
+    const uint64_t slots = (z.nt + kTilesPerSlot - 1) / kTilesPerSlot;
+    const uint64_t most = (slots + z.nsub - 1) / z.nsub * kTilesPerSlot * kTile;
+    const uint64_t need = ((most < n ? most : n) + 3) / 4 * 4;
+    // (candidate slots are 32-bit: where the total would not fit, such a row
+    // takes the exact rescan path instead)
+    if (need > z.capS && (uint64_t)z.nsub * need < (1ull << 32) - (1ull << 18)) z.capS = need;
   }
   return z;
 }

@@ -58,6 +58,22 @@ def test_layers_random(dev, P, N, nl):
     _check(g, r, off, ks, dev)
 
 
+def test_layers_prediction_size_classes(dev):
+    """Layers on both sides of each prediction size class: whole-row
+    candidates (<= 16384), samples held by 256-thread blocks (<= 16384
+    keys, n < 257 * 4096) and by 1024-thread blocks (up to 65536 keys), at
+    1%, with line-misaligned starts; every row stays on the candidate path."""
+    sizes = [16384, 16385, 777, 1048575, 1052672, 1052671 + 4096, 4194305, 123457]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.uint64)
+    ks = np.array([max(1, s // 100) for s in sizes], np.uint64)
+    P, N = 3, int(off[-1])
+    rng = np.random.default_rng(2718)
+    g = rng.standard_normal((P, N)).astype(np.float32)
+    r = (rng.standard_normal((P, N)) * 0.5).astype(np.float32)
+    print(f"layers size classes P={P} N={N}", flush=True)
+    _check(g, r, off, ks, dev, expect_rescan_rows=[])
+
+
 def test_layers_one_layer_equals_whole_vector(dev):
     rng = np.random.default_rng(3)
     P, N, k = 4, 300001, 3000
