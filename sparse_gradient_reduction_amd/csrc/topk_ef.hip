@@ -76,6 +76,10 @@ constexpr int kPredictThreads = 1024;
 constexpr int kPredictKeys = 64;                            // sample keys per predict thread (registers)
 constexpr int kSmallPredictThreads = 256;
 constexpr int kSmallSample = kSmallPredictThreads * kPredictKeys;  // 16384
+// per-layer call: the largest sample a row gets (512 chunks), held by
+// 512-thread blocks, two of which fit a compute unit at once
+constexpr int kLayerPredictThreads = 512;
+constexpr int kLayerSampleChunks = kLayerPredictThreads * kPredictKeys / kSampleChunk;  // 512
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
 constexpr int kGroup = 512;                              // tiles per gather group
 constexpr int kChunkThreads = 256;
@@ -132,11 +136,11 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
     ns = ns < 1 ? 1 : (ns > (uint64_t)kSub ? (uint64_t)kSub : ns);
     z.nsub = (uint32_t)ns;
     z.capS = (want + ns - 1) / ns + (n < (uint64_t)kTile ? n : (uint64_t)kTile);
-    // a sample of about one element in 64 (16 to 1024 chunks): the wider
+    // a sample of about one element in 64 (16 to 512 chunks): the wider
     // margin of a small sample costs little, as a layer's candidate list is
     // short next to its stream pass
     uint64_t sc = n / (64 * kSampleChunk);
-    z.schunks = (uint32_t)(sc < 16 ? 16 : (sc > (uint64_t)kSampleChunks ? (uint64_t)kSampleChunks : sc));
+    z.schunks = (uint32_t)(sc < 16 ? 16 : (sc > (uint64_t)kLayerSampleChunks ? (uint64_t)kLayerSampleChunks : sc));
     // select / count / emit blocks: one per 8192 expected candidates, 1..64
     const uint64_t est = n < 2 * k + 4096 ? n : 2 * k + 4096;
     uint64_t np = (est + 8191) / 8192;
@@ -154,7 +158,7 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
 }
 
 // Per-layer call: rows whose sample exceeds what a 256-thread predict block
-// holds; they get 1024-thread blocks of their own.
+// holds; they get 512-thread blocks of their own.
 __host__ __device__ inline bool big_predict(uint64_t n, uint64_t k, uint32_t schunks) {
   return k != 0 && k != n && n > kSmallLayer && (uint64_t)schunks * kSampleChunk > (uint64_t)kSmallSample;
 }
@@ -379,13 +383,14 @@ __device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint3
 // One block per row, holding kPredictKeys sample keys per thread in
 // registers, so a block takes samples of up to NT * kPredictKeys keys. The
 // whole-node call runs 1024-thread blocks; the per-layer call runs 256-thread
-// blocks over every row (skipping the big_predict rows) and 1024-thread blocks
+// blocks over every row (skipping the big_predict rows) and 512-thread blocks
 // over the big_predict rows (BIG: block b takes row big_rows[b]).
 template <bool ROWS, int NT, bool BIG>
 __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
                                                              const float* __restrict__ r, Dev D) {
   static_assert(!BIG || ROWS, "the row list exists in the per-layer call only");
-  static_assert(ROWS ? (NT * kPredictKeys == (BIG ? kSample : kSmallSample)) : NT * kPredictKeys == kSample,
+  static_assert(ROWS ? (NT * kPredictKeys == (BIG ? kLayerSampleChunks * kSampleChunk : kSmallSample))
+                     : NT * kPredictKeys == kSample,
                 "a block holds the largest sample of its rows");
   __shared__ uint32_t h1[4096];
   __shared__ uint32_t h2lo[2048];
@@ -1156,7 +1161,8 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
     hipLaunchKernelGGL((k_predict<true, kSmallPredictThreads, false>), dim3(R), dim3(kSmallPredictThreads), 0, stream,
                        grad, residual, D);
     if (big_rows > 0)
-      hipLaunchKernelGGL((k_predict<true, kPredictThreads, true>), dim3((uint32_t)big_rows), dim3(kPredictThreads), 0,
+      hipLaunchKernelGGL((k_predict<true, kLayerPredictThreads, true>), dim3((uint32_t)big_rows),
+                         dim3(kLayerPredictThreads), 0,
                          stream, grad, residual, D);
   } else {
     hipLaunchKernelGGL((k_predict<false, kPredictThreads, false>), dim3(R), dim3(kPredictThreads), 0, stream, grad,
