@@ -349,25 +349,30 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed_small(const fl
     const uint32_t T = lo_t;
     // kept: with an exact count every key >= T (all of the bucket when T = 0);
     // otherwise T is the kj-th largest key, every key above it is kept and
-    // the m ties at T at the lowest positions
-    uint32_t ngt = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) ngt += key[q] > T ? 1u : 0u;
-    const uint32_t m = kj - std::min(kj, group_sum<LG>(ngt));
-    uint64_t em[4];
-    uint32_t tie_rank = 0;  // ties at T in lower lanes of the group
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      em[q] = ballot(in[q] && key[q] == T) & gmask;
-      tie_rank += lanes_below(em[q]);
-    }
+    // the m ties at T at the lowest positions (a group ends that way only on
+    // ties, so the wave usually skips that part)
+    const uint64_t ex_lanes = ballot(exact);  // lanes of the groups with an exact count
     uint64_t sel[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool eq = (em[q] >> lane) & 1ull;
-      const bool keep = exact ? (kj > 0u && in[q] && key[q] >= T) : (key[q] > T || (eq && tie_rank < m));
-      sel[q] = ballot(keep) & gmask;
-      tie_rank += eq ? 1u : 0u;
+    for (int q = 0; q < 4; ++q) sel[q] = ballot(kj > 0u && in[q] && key[q] >= T) & ex_lanes & gmask;
+    if (ex_lanes != ~0ull) {
+      uint32_t ngt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ngt += key[q] > T ? 1u : 0u;
+      const uint32_t m = kj - std::min(kj, group_sum<LG>(ngt));
+      uint64_t em[4];
+      uint32_t tie_rank = 0;  // ties at T in lower lanes of the group
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        em[q] = ballot(in[q] && key[q] == T) & gmask;
+        tie_rank += lanes_below(em[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool eq = (em[q] >> lane) & 1ull;
+        sel[q] |= ballot(key[q] > T || (eq && tie_rank < m)) & ~ex_lanes & gmask;
+        tie_rank += eq ? 1u : 0u;
+      }
     }
     uint32_t rank = 0;
 #pragma unroll
