@@ -157,10 +157,13 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
   return z;
 }
 
-// Per-layer call: rows whose sample exceeds what a 256-thread predict block
-// holds; they get 512-thread blocks of their own.
+// Per-layer call: rows whose thresholds come from a sample (the others keep
+// no candidate, keep everything, or are small enough to be their own
+// candidate list), and among them those whose sample exceeds what a
+// 256-thread predict block holds, which get 512-thread blocks.
+__host__ __device__ inline bool layer_sampled(uint64_t n, uint64_t k) { return k != 0 && k != n && n > kSmallLayer; }
 __host__ __device__ inline bool big_predict(uint64_t n, uint64_t k, uint32_t schunks) {
-  return k != 0 && k != n && n > kSmallLayer && (uint64_t)schunks * kSampleChunk > (uint64_t)kSmallSample;
+  return layer_sampled(n, k) && (uint64_t)schunks * kSampleChunk > (uint64_t)kSmallSample;
 }
 
 // Totals over the rows: what the workspace holds.
@@ -172,6 +175,7 @@ struct Plan {
   uint64_t chunks;  // chunk words
   uint64_t passes;  // per-layer call: select / count / emit blocks
   uint64_t big;     // per-layer call: rows with big_predict
+  uint64_t mid;     // per-layer call: sampled rows without big_predict
   bool layers;      // per-layer call: row table and block-to-row tables too
 };
 
@@ -182,7 +186,7 @@ struct Layout {
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
   size_t info, err, state, h0, h1, h2, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
-      cout, rows, tile_row, group_row, pass_row, big_rows, loff, lk, lkoff, total;
+      cout, rows, tile_row, group_row, pass_row, big_rows, mid_rows, loff, lk, lkoff, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -219,6 +223,7 @@ Layout make_layout(const Plan& Q, uint64_t nlayers) {
     L.group_row = take(4ull * Q.groups);
     L.pass_row = take(4ull * Q.passes);
     L.big_rows = take(4ull * std::max<uint64_t>(1, Q.big));
+    L.mid_rows = take(4ull * std::max<uint64_t>(1, Q.mid));
     L.loff = take(8ull * (nlayers + 1));
     L.lk = take(8ull * nlayers);
     L.lkoff = take(8ull * nlayers);
@@ -240,6 +245,7 @@ Layout make_node_layout(uint32_t P, uint64_t N, uint64_t k) {
   Q.chunks = (uint64_t)P * z.chunks;
   Q.passes = 0;
   Q.big = 0;
+  Q.mid = 0;
   Q.layers = false;
   Layout L = make_layout(Q, 0);
   L.capS = z.capS;
@@ -269,7 +275,9 @@ LayerPlan plan_layers(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, 
       lp.Q.groups += z.groups;
       lp.Q.chunks += z.chunks;
       lp.Q.passes += z.npass;
-      lp.Q.big += big_predict(off[l + 1] - off[l], k[l], z.schunks) ? 1 : 0;
+      const bool big = big_predict(off[l + 1] - off[l], k[l], z.schunks);
+      lp.Q.big += big ? 1 : 0;
+      lp.Q.mid += layer_sampled(off[l + 1] - off[l], k[l]) && !big ? 1 : 0;
       lp.max_groups = std::max<uint64_t>(lp.max_groups, z.groups);
       lp.max_cap = std::max<uint64_t>(lp.max_cap, (uint64_t)z.nsub * z.capS);
       lp.max_tiles = std::max<uint64_t>(lp.max_tiles, z.nt);
@@ -311,6 +319,7 @@ struct Dev {
   const uint32_t* group_row;  // per-layer call: row of every tile group
   const uint32_t* pass_row;   // per-layer call: row of every select / count / emit block
   const uint32_t* big_rows;   // per-layer call: the rows with big_predict, in row order
+  const uint32_t* mid_rows;   // per-layer call: the other sampled rows, in row order
 };
 
 // Geometry of one selection row. For the [P][N] call it follows from (P, N,
@@ -380,40 +389,64 @@ __device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint3
 // ---------------------------------------------------------------------------
 // predict: reset the node's state and choose the two key thresholds.
 // ---------------------------------------------------------------------------
-// One block per row, holding kPredictKeys sample keys per thread in
-// registers, so a block takes samples of up to NT * kPredictKeys keys. The
-// whole-node call runs 1024-thread blocks; the per-layer call runs 256-thread
-// blocks over every row (skipping the big_predict rows) and 512-thread blocks
-// over the big_predict rows (BIG: block b takes row big_rows[b]).
-template <bool ROWS, int NT, bool BIG>
-__global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
-                                                             const float* __restrict__ r, Dev D) {
-  static_assert(!BIG || ROWS, "the row list exists in the per-layer call only");
-  static_assert(ROWS ? (NT * kPredictKeys == (BIG ? kLayerSampleChunks * kSampleChunk : kSmallSample))
-                     : NT * kPredictKeys == kSample,
-                "a block holds the largest sample of its rows");
-  __shared__ uint32_t h1[4096];
-  __shared__ uint32_t h2lo[2048];
-  __shared__ uint32_t h2mid[2048];
-  __shared__ uint32_t scr[NT / kWave + 3];
-  const uint32_t p = BIG ? D.big_rows[blockIdx.x] : blockIdx.x;
-  const Row R = row_of<ROWS>(D, p);
-  if (ROWS && !BIG && big_predict(R.n, R.k, R.schunks)) return;  // the 1024-thread launch takes it
+// Clears a row's histograms, the reservation counters its stream uses, and
+// (with its thresholds) its state and flags.
+template <int NT>
+__device__ __forceinline__ void reset_row(const Dev& D, uint32_t p, const Row& R) {
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < kH0; i += NT) D.h0[(size_t)p * kH0 + i] = 0u;
   for (uint32_t i = tid; i < kH1; i += NT) D.h1[(size_t)p * kH1 + i] = 0u;
   for (uint32_t i = tid; i < kH2; i += NT) D.h2[(size_t)p * kH2 + i] = 0u;
   for (uint32_t i = tid; i < R.nsub; i += NT) D.sub[((size_t)p * kSub + i) * 32] = 0u;  // the counters in use
-
-  uint32_t lo, mid;
+}
+__device__ __forceinline__ void set_state(const Dev& D, uint32_t p, uint32_t lo, uint32_t mid) {
+  NodeState s{};
+  s.lo = lo;
+  s.mid = mid;
+  D.state[p] = s;
+  D.err[p] = 0u;
+  D.info[p] = 0u;
+}
+// Thresholds that need no sample; false where the row is sampled.
+__device__ __forceinline__ bool fixed_thresholds(const Row& R, bool layer, uint32_t& lo, uint32_t& mid) {
   if (R.k == 0) {
     lo = mid = 0xFFFFFFFFu;  // keys are < 2^31: no candidate
   } else if (R.k == R.n) {
     lo = mid = 0u;  // everything is selected
-  } else if (ROWS && R.n <= kSmallLayer) {
+  } else if (layer && R.n <= kSmallLayer) {
     lo = 0u;            // a small layer is its own candidate list
     mid = 0xFFFFFFFFu;  // and nothing is zeroed before the selection
   } else {
+    return false;
+  }
+  return true;
+}
+
+// One block per row, holding kPredictKeys sample keys per thread in
+// registers, so a block takes samples of up to NT * kPredictKeys keys. The
+// whole-node call runs 1024-thread blocks over the nodes (LIST = 0) and
+// resets each node first. The per-layer call, whose rows the tile-table
+// kernel has reset, runs 256-thread blocks over the sampled rows without
+// big_predict (LIST = 1: block b takes row mid_rows[b]) and 512-thread blocks
+// over the big_predict rows (LIST = 2: row big_rows[b]).
+template <bool ROWS, int NT, int LIST>
+__global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
+                                                             const float* __restrict__ r, Dev D) {
+  static_assert((LIST != 0) == ROWS, "the row lists exist in the per-layer call only");
+  static_assert(NT * kPredictKeys ==
+                    (LIST == 0 ? kSample : (LIST == 2 ? kLayerSampleChunks * kSampleChunk : kSmallSample)),
+                "a block holds the largest sample of its rows");
+  __shared__ uint32_t h1[4096];
+  __shared__ uint32_t h2lo[2048];
+  __shared__ uint32_t h2mid[2048];
+  __shared__ uint32_t scr[NT / kWave + 3];
+  const uint32_t p = LIST == 0 ? blockIdx.x : (LIST == 1 ? D.mid_rows[blockIdx.x] : D.big_rows[blockIdx.x]);
+  const Row R = row_of<ROWS>(D, p);
+  const uint32_t tid = threadIdx.x;
+  if constexpr (!ROWS) reset_row<NT>(D, p, R);
+
+  uint32_t lo, mid;
+  if (!fixed_thresholds(R, ROWS, lo, mid)) {
     for (uint32_t i = tid; i < 4096; i += NT) h1[i] = 0u;
     for (uint32_t i = tid; i < 2048; i += NT) h2lo[i] = h2mid[i] = 0u;
     __syncthreads();
@@ -451,14 +484,7 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
     lo = (b_lo << 19) | (c_lo << 8);
     mid = (b_mid << 19) | (c_mid << 8);
   }
-  if (tid == 0) {
-    NodeState s{};
-    s.lo = lo;
-    s.mid = mid;
-    D.state[p] = s;
-    D.err[p] = 0u;
-    D.info[p] = 0u;
-  }
+  if (tid == 0) set_state(D, p, lo, mid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1071,12 +1097,13 @@ __global__ void k_layers_in(uint64_t* loff, uint64_t* lk, uint64_t* lkoff, uint3
 }
 
 // One workgroup: every row's sizes (row_size, as the host computed them),
-// exclusive scans of their slices, the sample ranks of its thresholds.
-__global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_rows, const uint64_t* loff,
-                                                    const uint64_t* lk, const uint64_t* lkoff, uint32_t P, uint64_t N,
-                                                    uint32_t nl, uint64_t K) {
+// exclusive scans of their slices, the sample ranks of its thresholds, and
+// the lists of sampled rows for the two prediction block sizes.
+__global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_rows, uint32_t* mid_rows,
+                                                    const uint64_t* loff, const uint64_t* lk, const uint64_t* lkoff,
+                                                    uint32_t P, uint64_t N, uint32_t nl, uint64_t K) {
   __shared__ uint64_t scr[1024 / kWave + 1];
-  uint64_t c_cand = 0, c_tiles = 0, c_groups = 0, c_chunks = 0, c_pass = 0, c_big = 0;  // carries over rounds
+  uint64_t c_cand = 0, c_tiles = 0, c_groups = 0, c_chunks = 0, c_pass = 0, c_big = 0, c_mid = 0;  // carried
   const uint64_t nrows = (uint64_t)P * nl;
   for (uint64_t r0 = 0; r0 < nrows; r0 += 1024) {
     const uint64_t ri = r0 + threadIdx.x;
@@ -1108,6 +1135,10 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_row
     const uint64_t big0 = c_big + block_exclusive_scan_u64<1024>(big ? 1 : 0, scr, t);
     c_big += t;
     if (big) big_rows[big0] = (uint32_t)ri;
+    const bool sampled = in && layer_sampled(n, k) && !big;
+    const uint64_t mid0 = c_mid + block_exclusive_scan_u64<1024>(sampled ? 1 : 0, scr, t);
+    c_mid += t;
+    if (sampled) mid_rows[mid0] = (uint32_t)ri;
     if (in) {
       Row R{};
       R.base = base;
@@ -1137,11 +1168,15 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_row
   }
 }
 
-// block-to-row tables of the per-layer grids
+// block-to-row tables of the per-layer grids; each row reset for the call
 __global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* tile_row, uint32_t* group_row,
-                                                   uint32_t* pass_row) {
+                                                   uint32_t* pass_row, Dev D) {
   const uint32_t p = blockIdx.x;
   const Row R = rows[p];
+  // every row reset here; the rows that need no sample get their thresholds
+  reset_row<256>(D, p, R);
+  uint32_t lo, mid;
+  if (threadIdx.x == 0 && fixed_thresholds(R, true, lo, mid)) set_state(D, p, lo, mid);
   const uint32_t nt = row_tiles(R);
   for (uint32_t t = threadIdx.x; t < nt; t += 256) tile_row[R.tile0 + t] = p;
   const uint32_t ng = (nt + kGroup - 1) / kGroup;
@@ -1154,18 +1189,19 @@ __global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* ti
 // other grids.
 template <bool ROWS>
 hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t groups, uint64_t max_tiles,
-               uint64_t max_cap, uint64_t passes, uint64_t big_rows, bool any_k, const float* grad, float* residual,
+               uint64_t max_cap, uint64_t passes, uint64_t big_rows, uint64_t mid_rows, bool any_k, const float* grad,
+               float* residual,
                uint32_t* out_idx, float* out_val, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const uint32_t R = (uint32_t)nrows;
   if constexpr (ROWS) {
-    hipLaunchKernelGGL((k_predict<true, kSmallPredictThreads, false>), dim3(R), dim3(kSmallPredictThreads), 0, stream,
-                       grad, residual, D);
+    if (mid_rows > 0)
+      hipLaunchKernelGGL((k_predict<true, kSmallPredictThreads, 1>), dim3((uint32_t)mid_rows),
+                         dim3(kSmallPredictThreads), 0, stream, grad, residual, D);
     if (big_rows > 0)
-      hipLaunchKernelGGL((k_predict<true, kLayerPredictThreads, true>), dim3((uint32_t)big_rows),
-                         dim3(kLayerPredictThreads), 0,
-                         stream, grad, residual, D);
+      hipLaunchKernelGGL((k_predict<true, kLayerPredictThreads, 2>), dim3((uint32_t)big_rows),
+                         dim3(kLayerPredictThreads), 0, stream, grad, residual, D);
   } else {
-    hipLaunchKernelGGL((k_predict<false, kPredictThreads, false>), dim3(R), dim3(kPredictThreads), 0, stream, grad,
+    hipLaunchKernelGGL((k_predict<false, kPredictThreads, 0>), dim3(R), dim3(kPredictThreads), 0, stream, grad,
                        residual, D);
   }
   hipError_t e = hipSuccess;
@@ -1263,7 +1299,7 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
     D.rs_lo = (uint32_t)std::min<double>(std::ceil(qs + 4.0 * std::sqrt(qs) + 16.0), (double)kSample);
     D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
   }
-  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, k > 0, grad, residual, out_idx, out_val, stream,
+  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, 0, k > 0, grad, residual, out_idx, out_val, stream,
                     ev_start, ev_stop);
 }
 
@@ -1291,7 +1327,9 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
   uint32_t* pass_row = reinterpret_cast<uint32_t*>(w + L.pass_row);
   uint64_t* lkoff = reinterpret_cast<uint64_t*>(w + L.lkoff);
   uint32_t* big_rows = reinterpret_cast<uint32_t*>(w + L.big_rows);
+  uint32_t* mid_rows = reinterpret_cast<uint32_t*>(w + L.mid_rows);
   D.big_rows = big_rows;
+  D.mid_rows = mid_rows;
   D.rows = rows;
   D.tile_row = tile_row;
   D.group_row = group_row;
@@ -1309,10 +1347,12 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
     in.off[count] = off[first + count];
     hipLaunchKernelGGL(k_layers_in, dim3(1), dim3(128), 0, stream, loff, lk, lkoff, first, count, in);
   }
-  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, loff, lk, lkoff, P, N, nl, lp.K);
+  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, mid_rows, loff, lk, lkoff, P, N, nl,
+                     lp.K);
   hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_row, group_row,
-                     pass_row);
-  return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.K > 0,
+                     pass_row, D);
+  return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.Q.mid,
+                   lp.K > 0,
                    grad, residual, out_idx, out_val, stream, nullptr, nullptr);
 }
 
