@@ -88,7 +88,7 @@ def _run_fused(off, idx, codes, scales, bits, bucket, N, delta, dev, hint=0):
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("P,N,nnz,bucket,delta", [
     (1, 100, 30, 8, 0.5), (3, 8191, 501, 8, 0.25), (5, 30000, 4001, 512, 0.25), (8, 30000, 9000, 64, 0.25),
-    (16, 100003, 2003, 512, 0.05), (300, 20000, 77, 16, 0.3),
+    (16, 100003, 2003, 512, 0.05), (200, 30000, 150, 32, 0.25), (300, 20000, 77, 16, 0.3),
 ])
 def test_reduce_qsgd_matches_oracle(dev, bits, P, N, nnz, bucket, delta):
     rng = np.random.default_rng(P * 31 + N + nnz + bits)

@@ -54,7 +54,8 @@ def _random_sparse(rng, P, N, nnz_max):
 @pytest.mark.parametrize("P,N,nnz,delta", [
     (1, 1, 1, 0.25), (1, 100, 30, 0.5), (3, 8191, 500, 0.25), (4, 8192, 3000, 0.25),
     (5, 8193, 2000, 0.3), (8, 30000, 4000, 0.25), (8, 30000, 9000, 0.25), (16, 100003, 2000, 0.05),
-    (2, 1 << 20, 5000, 0.3), (64, 65536, 800, 0.25),
+    (2, 1 << 20, 5000, 0.3), (64, 65536, 800, 0.25), (65, 70001, 700, 0.25), (200, 70000, 300, 0.25),
+    (256, 40000, 100, 0.3), (257, 20000, 60, 0.3),
 ])
 @pytest.mark.parametrize("hint", ["estimate", "count_first", "dense_first"])
 def test_reduce_random(dev, P, N, nnz, delta, hint):
