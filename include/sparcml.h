@@ -26,6 +26,10 @@
  *   - Calls are asynchronous on `stream` and stream-ordered, in the spirit of
  *     the non-blocking collectives of the paper (section 7, "Non-Blocking
  *     Operations"): results are valid once the stream has reached them.
+ *   - A call only launches kernels on `stream`: no allocation, copy, fill or
+ *     host synchronisation, so a sequence of calls may be captured into a HIP
+ *     graph and replayed (host arguments such as offsets and layer lists are
+ *     taken by value into the launches at capture time).
  *   - The return value reports argument errors (nothing is launched) and
  *     launch errors. The library never aborts, throws or prints. Errors in
  *     the contents of device buffers are reported in device-written flags.
