@@ -75,7 +75,7 @@ const char* sparcml_status_string(sparcml_status status);
  * Hence residual_new + scatter(out_val) == grad + residual_old exactly.
  *
  *   P, N      nodes and elements per node; 1 <= P <= 65535, N <= 2^32 - 2^19,
- *             P * ceil((N+3)/1024) < 2^24 (about P*N < 2^34: one workgroup
+ *             P * ceil((N+31)/1024) < 2^24 (about P*N < 2^34: one workgroup
  *             per 1024-element tile in one launch dimension)
  *   k         0 <= k <= N (k == 0 only folds grad into residual)
  *   grad      device, [P][N] fp32, read only, 16-byte aligned

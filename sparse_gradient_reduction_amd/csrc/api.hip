@@ -66,8 +66,9 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   g_prof_start = g_prof_stop = nullptr;
   if (P == 0 || P > 65535u || N > kMaxTopkN || k > N) return SPARCML_ERR_INVALID_ARG;
   if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
-  // one 256-thread workgroup per 1024-element tile, in one grid dimension of < 2^32 work-items
-  if ((uint64_t)P * ((N + 3 + 1023) / 1024) >= (1ull << 24)) return SPARCML_ERR_INVALID_ARG;
+  // one 256-thread workgroup per 1024-element tile slot (a node's tiles start at
+  // the 128-byte line of its first element), in one grid dimension of < 2^32 work-items
+  if ((uint64_t)P * ((N + 31 + 1023) / 1024) >= (1ull << 24)) return SPARCML_ERR_INVALID_ARG;
   if (N == 0) return SPARCML_OK;
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;

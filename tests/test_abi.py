@@ -57,6 +57,9 @@ def test_topk_argument_checks():
     assert call(0, 1000, 10) == sg.ERR_INVALID_ARG
     assert call(4, 1000, 1001) == sg.ERR_INVALID_ARG
     assert call(4, 1 << 32, 10) == sg.ERR_INVALID_ARG
+    # tile slots: P * ceil((N + 31) / 1024) must stay below 2^24 (one launch dimension)
+    assert call(16384, 1024 * 1023 - 30, 10) == sg.ERR_INVALID_ARG  # 1024 slots per node: 2^24 in all
+    assert call(16384, 1024 * 1023 - 31, 10, w=None) == sg.ERR_WORKSPACE  # 1023 slots: within the limit
     assert call(4, 1000, 10, g=None) == sg.ERR_INVALID_ARG
     assert call(4, 1000, 10, r=FAKE_ODD) == sg.ERR_INVALID_ARG
     assert call(4, 1000, 10, oi=None) == sg.ERR_INVALID_ARG
