@@ -190,3 +190,24 @@ def test_dense_threshold_reading():
     assert sg.dense_threshold(0.0, 10) == 0
     assert sg.dense_threshold(-1.0, 10) == 0
     assert sg.dense_threshold(1.5, 10) == 11
+
+
+def test_header_is_plain_c_and_links():
+    """include/sparcml.h compiles as C99 and a C program links the library and
+    gets answers from the calls that need no device (tests/c_abi_client.c)."""
+    import shutil
+    import subprocess
+    import tempfile
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("gcc or the HIP headers are not available")
+    sg.lib()  # the library is built
+    libdir = os.path.dirname(sg.LIB_PATH)
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "client")
+        subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration", "-D__HIP_PLATFORM_AMD__",
+                        "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c_abi_client.c"), "-o", exe, "-L" + libdir, "-lsparcml",
+                        "-Wl,-rpath," + libdir, "-lm"], check=True, capture_output=True)
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+        assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout + out.stderr
