@@ -29,6 +29,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-nodes", type=int, default=8, help="nodes in the oracle's timed sample")
     ap.add_argument("--seed", type=int, default=987654321)
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the other workloads' timings (profiling runs: their kernels would mix into the averages)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device once before warmup (reference for PMC byte counters)")
     return ap.parse_args()
@@ -367,7 +369,99 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pool[0], args, sg)
+    if not args.no_other_configs:
+        del pool, residual, ws_topk, idx, val, red_idx, red_val, ws_red
+        if B:
+            del codes, scales, dval
+        torch.cuda.synchronize()
+        out["other_configs"] = other_configs(sg, W, dev, w.wid)
     print(json.dumps(out), flush=True)
+
+
+def other_configs(sg, W, dev, skip_wid):
+    """The other workloads at their full sizes, outside the timed steps: the
+    median per-step time of Top-k EF and of the reduce of its pairs over the
+    workload's error-feedback steps (from a zero residual), or of the reduce
+    alone for the already-sparse workload, each with its algorithmic bytes."""
+    import numpy as np
+    import torch
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    res = {}
+    for wi in range(5):
+        w = W.workload(wi)
+        if w.wid == skip_wid:
+            continue
+        P, N, k = w.P, w.N, w.k
+        T = sg.dense_threshold(w.delta, N)
+        if not w.has_topk:  # already-sparse contributions: the reduce alone
+            o, i_np, v_np = W.zipf_sparse(w)
+            off = [int(x) for x in o]
+            ii = torch.from_numpy(i_np.view(np.int32)).to(dev)
+            vv = torch.from_numpy(v_np).to(dev)
+            ri = torch.empty(max(1, min(N, T - 1)), dtype=torch.int32, device=dev)
+            rv = torch.empty(N, dtype=torch.float32, device=dev)
+            rr = torch.zeros(16, dtype=torch.uint8, device=dev)
+            wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, off[-1]), dtype=torch.uint8, device=dev)
+            run = lambda: sg.sparse_reduce(off, ii, vv, N, w.delta, out_idx=ri, out_val=rv, result=rr, workspace=wr)
+            run()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+            for a, b in ev:
+                a.record()
+                run()
+                b.record()
+            torch.cuda.synchronize()
+            t = med([a.elapsed_time(b) for a, b in ev])
+            K, dense, flags = sg.ReduceOutput(rr, ri, rv, N).read()
+            b_in, b_out = 8 * off[-1], (4 * N if dense else 8 * K)
+            res[w.name] = {"reduce_ms": round(t, 4), "pairs": off[-1], "nnz": K, "dense": dense,
+                           "reduce_input_gb_per_s": round(b_in / (t * 1e-3) / 1e9, 1),
+                           "reduce_frac_hbm_peak": round((b_in + b_out) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            continue
+        grads = [W.gradients(w, t, device=dev) for t in range(w.steps)]
+        r = torch.zeros((P, N), dtype=torch.float32, device=dev)
+        ws = torch.empty(sg.topk_ef_workspace_bytes(P, N, k), dtype=torch.uint8, device=dev)
+        idx = torch.empty((P, k), dtype=torch.int32, device=dev)
+        val = torch.empty((P, k), dtype=torch.float32, device=dev)
+        off = [p * k for p in range(P + 1)]
+        ri = torch.empty(max(1, min(N, T - 1)), dtype=torch.int32, device=dev)
+        rv = torch.empty(N, dtype=torch.float32, device=dev)
+        rr = torch.zeros(16, dtype=torch.uint8, device=dev)
+        wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
+        t_topk, t_red, per_step = [], [], []
+        for rep in range(2):  # the first pass warms up; the second is timed
+            r.zero_()
+            for t in range(w.steps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record()
+                sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws)
+                e[1].record()
+                sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
+                                 workspace=wr)
+                e[2].record()
+                if rep == 1:
+                    torch.cuda.synchronize()
+                    K, dense, flags = sg.ReduceOutput(rr, ri, rv, N).read()
+                    t_topk.append(e[0].elapsed_time(e[1]))
+                    t_red.append(e[1].elapsed_time(e[2]))
+                    per_step.append({"nnz": K, "dense": dense})
+        torch.cuda.synchronize()
+        tk, tr = med(t_topk), med(t_red)
+        b_topk = 12 * P * N + 8 * P * k
+        b_in = 8 * P * k
+        b_out = [4 * N if s["dense"] else 8 * s["nnz"] for s in per_step]
+        res[w.name] = {"steps": w.steps, "topk_ms": round(tk, 4), "reduce_ms": round(tr, 4),
+                       "topk_gelem_per_s": round(P * N / (tk * 1e-3) / 1e9, 1),
+                       "topk_frac_hbm_peak": round(b_topk / (tk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "reduce_input_gb_per_s": round(b_in / (tr * 1e-3) / 1e9, 1),
+                       "reduce_frac_hbm_peak": round((b_in + med(b_out)) / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "per_step": per_step}
+        del grads, r, ws, idx, val, ri, rv, rr, wr
+        torch.cuda.synchronize()
+    return res
 
 
 def cpu_baseline(w, g_dev, args, sg):
