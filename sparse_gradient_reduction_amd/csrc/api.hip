@@ -140,8 +140,7 @@ static bool qsgd_args_ok(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket)
   if (P == 0 || P > 65535u) return false;
   if (bucket < 8 || bucket > (1u << 20) || (bucket % 8) != 0) return false;
   if (n >= (1ull << 34)) return false;
-  const uint64_t nb = (n + bucket - 1) / bucket;
-  return true;
+  return true;  // any number of buckets: the kernels loop over them
 }
 
 sparcml_status sparcml_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
