@@ -267,6 +267,19 @@ def main():
                                            "gb_per_s": round(b_bytes / (t_b * 1e-3) / 1e9, 1),
                                            "frac_hbm_peak": round(b_bytes / (t_b * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del b_idx, b_val
+        # the same density (1 in 32) in the smallest buckets, several buckets per wave
+        for bs, kb in ((64, 2), (128, 4)):
+            Kb = sg.topk_bucketed_count(N, bs, kb)
+            b_idx = torch.empty((P, Kb), dtype=torch.int32, device=dev)
+            b_val = torch.empty((P, Kb), dtype=torch.float32, device=dev)
+            t_b = time_ops(lambda: sg.topk_ef_bucketed(pool[0], residual, bs, kb, out_idx=b_idx, out_val=b_val),
+                           reps=5)
+            b_bytes = 12 * P * N + 8 * P * Kb
+            extra[f"bucketed_topk_{kb}_of_{bs}"] = {"ms": round(t_b, 4),
+                                                    "gb_per_s": round(b_bytes / (t_b * 1e-3) / 1e9, 1),
+                                                    "frac_hbm_peak": round(b_bytes / (t_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                                                           4)}
+            del b_idx, b_val
 
     # ---- per-layer Top-k (1% of each of 160 layers) on the same arrays ------
     if w.has_topk:

@@ -15,11 +15,13 @@
 // One wave per bucket of B = 64 * E positions, held in registers: one HBM
 // pass, 12 bytes per element plus 8 per kept pair. The bucket's threshold is
 // found by binary search over key values, counting with wave ballots (a
-// vector compare and a scalar popcount per element slot), first within a
-// factor of four below the bucket's largest magnitude; it stops as soon as
+// vector compare and a scalar popcount per element slot), first bracketed
+// below the bucket's largest magnitude (within half a binade when at most one
+// in 16 is kept, else within a factor of about four); it stops as soon as
 // some threshold has exactly k_j keys at or above it, else it ends on the
 // k_j-th largest key itself and ties at it go to the lowest indices. Ranks of
-// ties and output positions are mbcnt prefixes in index order.
+// ties and output positions are mbcnt prefixes in index order. Buckets of 64
+// and 128 share a wave (see k_topk_bucketed_small).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -119,8 +121,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed(const float* _
       // T = the kj-th largest key, by binary search over [lo_t, hi_t) with
       // count(key >= lo_t) >= kj > count(key >= hi_t); it stops early at a
       // threshold with exactly kj keys at or above it. The first bracket is
-      // [M - 2^24, M]: a factor of about four below the largest key M, which
-      // usually holds the kj-th largest; otherwise the whole key range.
+      // [M - 2^22, M] or [M - 2^24, M] below the largest key M, which usually
+      // holds the kj-th largest; otherwise the whole key range.
       uint32_t mloc = 0;
 #pragma unroll
       for (int c = 0; c < C; ++c)
@@ -129,7 +131,19 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed(const float* _
       const uint32_t M = wave_max_u32(mloc);
       uint32_t lo_t = 0u, hi_t = M + 1u;  // count(key >= 0) = len >= kj; none is above M
       bool exact = (len == kj);
-      if (!exact && M > (1u << 24)) {
+      // keeping at most 1 in 16, first try half a binade below M (2^22 key
+      // units); then, or otherwise, about a factor of four (2^24)
+      if (!exact && kj * 16u <= len && M > (1u << 22)) {
+        const uint32_t guess = M - (1u << 22);
+        const uint32_t n = count_ge(guess);
+        if (n >= kj) {
+          lo_t = guess;
+          exact = (n == kj);
+        } else {
+          hi_t = guess;
+        }
+      }
+      if (!exact && lo_t == 0u && M > (1u << 24)) {  // not tried, or held too few keys
         const uint32_t guess = M - (1u << 24);
         const uint32_t n = count_ge(guess);
         if (n >= kj) {
@@ -322,9 +336,16 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucketed_small(const fl
     // stops at a threshold with exactly kj keys at or above it
     uint32_t lo_t = 0u, hi_t = M + 1u;
     bool exact = kj == 0u || len == kj;
-    {
-      const bool try_guess = !exact && M > (1u << 24);
-      const uint32_t guess = try_guess ? M - (1u << 24) : 1u;
+    // a group keeping at most 1 in 16 first tries half a binade below M
+    // (2^22 key units), then about a factor of four (2^24) if that holds
+    // too few keys
+    const uint32_t span1 = kj * 16u <= len ? (1u << 22) : (1u << 24);
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const uint32_t span = pass == 0 ? span1 : (1u << 24);
+      const bool try_guess = !exact && M > span && (pass == 0 || (span1 < span && hi_t == M - span1));
+      if (pass == 1 && ballot(try_guess) == 0ull) break;  // no group's first guess held too few keys
+      const uint32_t guess = try_guess ? M - span : 1u;
       const uint32_t n = count_ge(guess);
       if (try_guess) {
         if (n >= kj) {
