@@ -150,53 +150,79 @@ __global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
   }
 }
 
-// Node-major pass: start[s][p] = absolute index of node p's first pair with
+// Node-major pass: start[p][s] = absolute index of node p's first pair with
 // index >= s*4096 (s = S stands for N), written by the pair where the run
-// crosses into segment s. The table is segment-major, so a segment's
-// workgroup reads its P run starts from consecutive words.
-// Lanes load consecutive pairs (coalesced); a pair's left neighbour comes from
+// crosses into segment s. The table is node-major, so the entries one node
+// writes are consecutive words (a segment's workgroup later gathers its P
+// run starts, one word per node).
+// Each lane loads four consecutive pairs as one 16-byte-aligned quad (quad q
+// holds elements 4q - shift .. 4q - shift + 3, shift placing the quads on
+// 16-byte boundaries of the index array); a quad's left neighbour comes from
 // the lane below through a cross-lane shift, and only lane 0 loads its own.
-__global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R) {
-  constexpr int kPer = 4;
+__global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift) {
+  constexpr int kQuads = 4;  // quads per thread and pass
   const uint32_t p = blockIdx.y;
-  const uint64_t o0 = R.offs[p];
-  const uint64_t nnz = R.offs[p + 1] - o0;
+  const uint64_t o0 = R.offs[p], o1 = R.offs[p + 1];
   const uint64_t S = R.S;
-  uint32_t* b = R.bounds + p;  // entry s at b[s * P]
-  const uint64_t P = R.P;
+  uint32_t* b = R.bounds + (uint64_t)p * (S + 1);
   uint32_t bad = 0u;
-  if (nnz == 0) {  // an empty node starts every segment at its offset
+  if (o1 == o0) {  // an empty node starts every segment at its offset
     if (blockIdx.x == 0)
-      for (uint64_t s = threadIdx.x; s <= S; s += kThreads) b[s * P] = (uint32_t)o0;
+      for (uint64_t s = threadIdx.x; s <= S; s += kThreads) b[s] = (uint32_t)o0;
     return;
   }
+  const uint64_t q0 = (o0 + shift) >> 2, q1 = (o1 + shift + 3) >> 2;  // quads meeting [o0, o1)
+  const uint64_t nq = q1 - q0;
+  const int64_t total = R.total;
   const bool lane0 = lane_id() == 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kPer;
-  for (uint64_t j0 = (uint64_t)blockIdx.x * kThreads * kPer; j0 < nnz; j0 += stride) {
-    uint32_t v[kPer], w[kPer];
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kQuads;
+  for (uint64_t j0 = (uint64_t)blockIdx.x * kThreads * kQuads; j0 < nq; j0 += stride) {
+    uint32_t v[kQuads][4], w[kQuads];
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint64_t j = j0 + (uint64_t)u * kThreads + threadIdx.x;
-      v[u] = j < nnz ? idx[o0 + j] : 0u;
-      w[u] = (lane0 && j > 0 && j < nnz) ? idx[o0 + j - 1] : 0u;
+    for (int u = 0; u < kQuads; ++u) {
+      const uint64_t jq = j0 + (uint64_t)u * kThreads + threadIdx.x;
+      const int64_t e0 = (int64_t)(4 * (q0 + jq)) - (int64_t)shift;
+      w[u] = 0u;
+      if (jq < nq) {
+        if (e0 >= 0 && e0 + 4 <= total) {
+          const uint4 x = *reinterpret_cast<const uint4*>(idx + e0);
+          v[u][0] = x.x;
+          v[u][1] = x.y;
+          v[u][2] = x.z;
+          v[u][3] = x.w;
+        } else {  // a quad at either end of the array: elements inside it only
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[u][t] = e0 + t >= 0 && e0 + t < total ? idx[e0 + t] : 0u;
+        }
+        if (lane0 && e0 > (int64_t)o0) w[u] = idx[e0 - 1];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[u][t] = 0u;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const uint32_t up = __shfl_up(v[u], 1);
-      const uint64_t j = j0 + (uint64_t)u * kThreads + threadIdx.x;
-      if (j >= nnz) continue;
-      const uint32_t i = v[u];
-      const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
-      if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
-      int64_t s_prev = -1;
-      if (j > 0) {
-        const uint32_t ip = lane0 ? w[u] : up;
-        if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
-        s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
+    for (int u = 0; u < kQuads; ++u) {
+      const uint32_t up = __shfl_up(v[u][3], 1);
+      const uint64_t jq = j0 + (uint64_t)u * kThreads + threadIdx.x;
+      if (jq >= nq) continue;
+      const int64_t e0 = (int64_t)(4 * (q0 + jq)) - (int64_t)shift;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t e = e0 + t;
+        if (e < (int64_t)o0 || e >= (int64_t)o1) continue;
+        const uint32_t i = v[u][t];
+        const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
+        if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
+        int64_t s_prev = -1;
+        if (e > (int64_t)o0) {
+          const uint32_t ip = t > 0 ? v[u][t > 0 ? t - 1 : 0] : (lane0 ? w[u] : up);
+          if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
+          s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
+        }
+        for (int64_t sx = s_prev + 1; sx <= (int64_t)s_cur; ++sx) b[sx] = (uint32_t)e;
+        if ((uint64_t)e + 1 == o1)
+          for (uint64_t sx = s_cur + 1; sx <= S; ++sx) b[sx] = (uint32_t)o1;
       }
-      for (int64_t s = s_prev + 1; s <= (int64_t)s_cur; ++s) b[(uint64_t)s * P] = (uint32_t)(o0 + j);
-      if (j + 1 == nnz)
-        for (uint64_t s = s_cur + 1; s <= S; ++s) b[s * P] = (uint32_t)(o0 + nnz);
     }
   }
   if (bad) atomicOr(&R.state->flags, bad);
@@ -219,11 +245,12 @@ struct QRuns {
 template <int NT, int MAXP>
 __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
                                               uint32_t* scr, QRuns<MAXP>* q) {
-  const uint32_t* b = R.bounds + s * R.P;
+  const uint64_t rows = R.S + 1;  // entries per node in the run-start table
   auto run = [&](uint32_t p) -> uint32_t {
+    const uint32_t* b = R.bounds + p * rows + s;
     const uint32_t lo = (uint32_t)R.offs[p], hi = (uint32_t)R.offs[p + 1];
-    const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[p], lo), hi);
-    const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[R.P + p], lo), hi);
+    const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[0], lo), hi);
+    const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[1], lo), hi);
     start[p] = b0;
     if (q != nullptr) {
       q->rel[p] = b0 - lo;
@@ -257,15 +284,26 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
   return carry;
 }
 
-// largest p with pre[p] <= f (pre is nondecreasing, pre[0] = 0, f < pre[P])
-__device__ __forceinline__ uint32_t find_node(const uint32_t* pre, uint32_t P, uint32_t f) {
-  uint32_t lo = 0, hi = P;  // invariant: pre[lo] <= f < pre[hi]
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (pre[mid] <= f) lo = mid;
-    else hi = mid;
+// For every batch slot b with f = f0 + b * NT + threadIdx.x < total: node[b]
+// = the largest p with pre[p] <= f (pre is nondecreasing, pre[0] = 0 and
+// pre[P] = total > f). Binary lifting with one uniform step sequence for all
+// slots, so the slots' LDS reads overlap instead of forming one dependent
+// chain per slot. Steps never pass p = P, and pre[P] > f stops them there.
+template <int NT, int B>
+__device__ __forceinline__ void find_nodes(const uint32_t* pre, uint32_t P, uint32_t f0, uint32_t total,
+                                           uint32_t (&node)[B]) {
+#pragma unroll
+  for (int b = 0; b < B; ++b) node[b] = 0u;
+  const uint32_t top = P > 1u ? 1u << (31 - __clz(P - 1u)) : 0u;  // largest power of two <= P - 1
+  for (uint32_t step = top; step != 0u; step >>= 1) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      if (f0 + b * NT >= total) break;  // no thread has this slot or a later one (uniform)
+      const uint32_t f = f0 + b * NT + threadIdx.x;
+      const uint32_t c = node[b] + step;
+      if (c <= P && pre[c] <= f) node[b] = c;
+    }
   }
-  return lo;
 }
 
 // One workgroup per segment: short, independent workgroups kept more
@@ -290,14 +328,15 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
   const uint32_t total = load_runs<NT, MAXP>(R, s, pre, start, scr, (QRuns<MAXP>*)nullptr);
-  constexpr int kBatch = 24;
+  constexpr int kBatch = 12;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch];
+    uint32_t ii[kBatch], node[kBatch];
+    find_nodes<NT>(pre, R.P, f0, total, node);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
-        const uint32_t p = find_node(pre, R.P, f);
+        const uint32_t p = node[b];
         ii[b] = idx[start[p] + (f - pre[p])];
       }
     }
@@ -410,13 +449,14 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 
   constexpr int kBatch = 8;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch];
+    uint32_t ii[kBatch], node[kBatch];
     float vv[kBatch];
+    find_nodes<NT>(pre, R.P, f0, total, node);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
-        const uint32_t p = find_node(pre, R.P, f);
+        const uint32_t p = node[b];
         const uint32_t j = start[p] + (f - pre[p]);
         ii[b] = idx[j];
         if constexpr (BITS == 0) {
@@ -562,7 +602,8 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   }
   if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
-  hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R);
+  const uint32_t shift = (uint32_t)((reinterpret_cast<uintptr_t>(idx) >> 2) & 3u);
+  hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R, shift);
   const dim3 segs((uint32_t)L.S);
   const bool small_p = P <= 256;
   if (dense_first) {

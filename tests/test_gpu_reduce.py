@@ -176,6 +176,31 @@ def test_zipf_workload_full_size(dev):
     assert not dense and 0.1 * w.N < K < 0.3 * w.N
 
 
+@pytest.mark.parametrize("shift", [1, 2, 3])
+def test_unaligned_index_array(dev, shift):
+    """Pair arrays that start 4, 8 or 12 bytes past a 16-byte boundary (views
+    into a larger buffer): the bounds pass reads indices in aligned quads, with
+    partial quads at both ends of the array and at node edges."""
+    rng = np.random.default_rng(40 + shift)
+    N, delta = 70001, 0.25
+    off, idx, val = _random_sparse(rng, 7, N, 9000)
+    K, dense, oi, ov = oracle.reduce(off, idx, val, N, delta)
+    n = idx.size
+    bi = torch.zeros(n + 8, dtype=torch.int32, device=dev)
+    bv = torch.zeros(n + 8, dtype=torch.float32, device=dev)
+    bi[shift:shift + n] = torch.from_numpy(idx.view(np.int32)).to(dev)
+    bv[shift:shift + n] = torch.from_numpy(val).to(dev)
+    it, vt = bi[shift:shift + n], bv[shift:shift + n]
+    assert it.data_ptr() % 16 == 4 * shift
+    for hint in (1, N):
+        gK, gdense, flags, gi, gv = sg.sparse_reduce([int(x) for x in off], it, vt, N, delta,
+                                                     expected_nnz_hint=hint).host()
+        assert flags == 0 and gK == K and gdense == dense
+        if not dense:
+            np.testing.assert_array_equal(gi.numpy().astype(np.uint32), oi)
+        assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= reduce_tolerance(7, val)
+
+
 def test_reduce_deterministic(dev):
     rng = np.random.default_rng(21)
     off, idx, val = _random_sparse(rng, 32, 1 << 18, 20000)
