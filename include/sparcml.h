@@ -248,8 +248,9 @@ sparcml_status sparcml_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t buc
  *   P          1 <= P <= 1024 nodes
  *   N          index space, 1 <= N < 2^32
  *   delta      finite; delta <= 0 is always dense, T > N never dense
- *   h_offsets  host, [P+1] uint64, nondecreasing, h_offsets[0] == 0: node p
- *              owns pairs [h_offsets[p], h_offsets[p+1])
+ *   h_offsets  host, [P+1] uint64, nondecreasing, h_offsets[0] == 0,
+ *              h_offsets[P] <= 2^32 - 16: node p owns pairs
+ *              [h_offsets[p], h_offsets[p+1])
  *   idx, val   device, [h_offsets[P]] uint32 / fp32; each node's indices
  *              strictly ascending and < N
  *   expected_nnz_hint  0: estimate K from the nonzero counts (uniform model

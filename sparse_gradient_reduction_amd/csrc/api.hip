@@ -210,7 +210,7 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
   for (uint32_t p = 0; p < P; ++p)
     if (h_offsets[p + 1] < h_offsets[p]) return SPARCML_ERR_INVALID_ARG;
   const uint64_t total = h_offsets[P];
-  if (total > kMaxN) return SPARCML_ERR_INVALID_ARG;
+  if (total > kMaxN - 15) return SPARCML_ERR_INVALID_ARG;  // positions and quad ends fit in 32 bits
   if (total > 0 && (!idx || (quant ? (!quant->codes || !quant->scales) : !val))) return SPARCML_ERR_INVALID_ARG;
   const uint64_t T = dense_threshold(delta, N);
   const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);

@@ -162,29 +162,31 @@ __global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift) {
   constexpr int kQuads = 4;  // quads per thread and pass
   const uint32_t p = blockIdx.y;
-  const uint64_t o0 = R.offs[p], o1 = R.offs[p + 1];
-  const uint64_t S = R.S;
+  // positions fit in 32 bits (total < 2^32) and so do segment numbers
+  const uint32_t o0 = (uint32_t)R.offs[p], o1 = (uint32_t)R.offs[p + 1];
+  const uint32_t S = (uint32_t)R.S, N = R.N;
   uint32_t* b = R.bounds + (uint64_t)p * (S + 1);
   uint32_t bad = 0u;
   if (o1 == o0) {  // an empty node starts every segment at its offset
     if (blockIdx.x == 0)
-      for (uint64_t s = threadIdx.x; s <= S; s += kThreads) b[s] = (uint32_t)o0;
+      for (uint32_t s = threadIdx.x; s <= S; s += kThreads) b[s] = o0;
     return;
   }
-  const uint64_t q0 = (o0 + shift) >> 2, q1 = (o1 + shift + 3) >> 2;  // quads meeting [o0, o1)
-  const uint64_t nq = q1 - q0;
-  const int64_t total = R.total;
+  const uint32_t q0 = (uint32_t)(((uint64_t)o0 + shift) >> 2);
+  const uint32_t nq = (uint32_t)((((uint64_t)o1 + shift + 3) >> 2) - q0);  // quads meeting [o0, o1)
   const bool lane0 = lane_id() == 0;
-  const uint64_t stride = (uint64_t)gridDim.x * kThreads * kQuads;
-  for (uint64_t j0 = (uint64_t)blockIdx.x * kThreads * kQuads; j0 < nq; j0 += stride) {
+  const uint32_t stride = gridDim.x * kThreads * kQuads;
+  for (uint32_t j0 = blockIdx.x * kThreads * kQuads; j0 < nq; j0 += stride) {
     uint32_t v[kQuads][4], w[kQuads];
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
-      const uint64_t jq = j0 + (uint64_t)u * kThreads + threadIdx.x;
-      const int64_t e0 = (int64_t)(4 * (q0 + jq)) - (int64_t)shift;
+      const uint32_t jq = j0 + u * kThreads + threadIdx.x;
+      // first element of the quad; below 0 (wrapped) only for the array's first quad
+      const uint32_t e0 = 4u * (q0 + jq) - shift;
+      const bool first_quad = q0 + jq == 0u && shift != 0u;
       w[u] = 0u;
       if (jq < nq) {
-        if (e0 >= 0 && e0 + 4 <= total) {
+        if (!first_quad && (uint64_t)e0 + 4u <= R.total) {
           const uint4 x = *reinterpret_cast<const uint4*>(idx + e0);
           v[u][0] = x.x;
           v[u][1] = x.y;
@@ -192,9 +194,13 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
           v[u][3] = x.w;
         } else {  // a quad at either end of the array: elements inside it only
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[u][t] = e0 + t >= 0 && e0 + t < total ? idx[e0 + t] : 0u;
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t e = e0 + t;
+            const bool in = (!first_quad || (uint32_t)t >= shift) && e < R.total;
+            v[u][t] = in ? idx[e] : 0u;
+          }
         }
-        if (lane0 && e0 > (int64_t)o0) w[u] = idx[e0 - 1];
+        if (lane0 && !first_quad && e0 > o0) w[u] = idx[e0 - 1];
       } else {
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[u][t] = 0u;
@@ -203,25 +209,29 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
 #pragma unroll
     for (int u = 0; u < kQuads; ++u) {
       const uint32_t up = __shfl_up(v[u][3], 1);
-      const uint64_t jq = j0 + (uint64_t)u * kThreads + threadIdx.x;
+      const uint32_t jq = j0 + u * kThreads + threadIdx.x;
       if (jq >= nq) continue;
-      const int64_t e0 = (int64_t)(4 * (q0 + jq)) - (int64_t)shift;
+      const uint32_t e0 = 4u * (q0 + jq) - shift;
+      const bool first_quad = q0 + jq == 0u && shift != 0u;
+      uint32_t ip = lane0 ? w[u] : up;  // the element before the current one
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int64_t e = e0 + t;
-        if (e < (int64_t)o0 || e >= (int64_t)o1) continue;
+        const uint32_t e = e0 + t;
         const uint32_t i = v[u][t];
-        const uint64_t s_cur = i >= R.N ? S : (i >> kSegBits);
-        if (i >= R.N) bad |= SPARCML_FLAG_INDEX_RANGE;
-        int64_t s_prev = -1;
-        if (e > (int64_t)o0) {
-          const uint32_t ip = t > 0 ? v[u][t > 0 ? t - 1 : 0] : (lane0 ? w[u] : up);
-          if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
-          s_prev = ip >= R.N ? (int64_t)S : (int64_t)(ip >> kSegBits);
+        const bool live = (!first_quad || (uint32_t)t >= shift) && e >= o0 && e < o1;
+        if (live) {
+          const uint32_t s_cur = i < N ? i >> kSegBits : S;
+          uint32_t s_first = 0u;  // first segment whose run starts here
+          if (e > o0) {
+            if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
+            s_first = (ip < N ? ip >> kSegBits : S) + 1u;
+          }
+          if (i >= N) bad |= SPARCML_FLAG_INDEX_RANGE;
+          for (uint32_t sx = s_first; sx <= s_cur; ++sx) b[sx] = e;
+          if (e + 1u == o1)
+            for (uint32_t sx = s_cur + 1u; sx <= S; ++sx) b[sx] = o1;
         }
-        for (int64_t sx = s_prev + 1; sx <= (int64_t)s_cur; ++sx) b[sx] = (uint32_t)e;
-        if ((uint64_t)e + 1 == o1)
-          for (uint64_t sx = s_cur + 1; sx <= S; ++sx) b[sx] = (uint32_t)o1;
+        ip = i;
       }
     }
   }
@@ -447,7 +457,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   const uint32_t total = load_runs<NT, BITS ? MAXP : 1>(R, s, pre, start, scr, BITS ? &qruns : nullptr);
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 4;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch], node[kBatch];
     float vv[kBatch];

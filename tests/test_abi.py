@@ -99,6 +99,7 @@ def test_reduce_argument_checks():
     assert call(o=None) == sg.ERR_INVALID_ARG
     assert call(o=(ctypes.c_uint64 * 3)(0, 5, 4)) == sg.ERR_INVALID_ARG  # decreasing
     assert call(o=(ctypes.c_uint64 * 3)(1, 5, 9)) == sg.ERR_INVALID_ARG  # not starting at 0
+    assert call(o=(ctypes.c_uint64 * 3)(0, 5, 2**32 - 15)) == sg.ERR_INVALID_ARG  # too many pairs
     assert call(ov=FAKE_ODD) == sg.ERR_INVALID_ARG
     assert call(oi=None) == sg.ERR_INVALID_ARG
     assert call(res=None) == sg.ERR_INVALID_ARG
