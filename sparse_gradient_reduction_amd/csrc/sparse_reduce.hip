@@ -249,9 +249,10 @@ struct QRuns {
 
 // Node runs of segment s: pre[p] = exclusive prefix of their lengths,
 // start[p] = absolute index of the first pair; returns the segment's pair
-// count. Run ends are clamped to the node's own pairs, which keeps every
-// later load inside them even for input whose order check failed. With at
-// most 64 nodes one wave builds the table (no block scan).
+// count. pre[P + 1 .. 2P) are set to all ones (room for find_nodes' steps).
+// Run ends are clamped to the node's own pairs, which keeps every later load
+// inside them even for input whose order check failed. With at most 64 nodes
+// one wave builds the table (no block scan).
 template <int NT, int MAXP>
 __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
                                               uint32_t* scr, QRuns<MAXP>* q) {
@@ -269,6 +270,7 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
     }
     return b1 > b0 ? b1 - b0 : 0u;
   };
+  for (uint32_t i = R.P + 1u + threadIdx.x; i < 2u * R.P; i += NT) pre[i] = ~0u;
   if (R.P <= (uint32_t)kWave) {
     if (threadIdx.x < kWave) {
       const uint32_t p = threadIdx.x;
@@ -297,21 +299,20 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
 // For every batch slot b with f = f0 + b * NT + threadIdx.x < total: node[b]
 // = the largest p with pre[p] <= f (pre is nondecreasing, pre[0] = 0 and
 // pre[P] = total > f). Binary lifting with one uniform step sequence for all
-// slots, so the slots' LDS reads overlap instead of forming one dependent
-// chain per slot. Steps never pass p = P, and pre[P] > f stops them there.
+// slots and no branches, so the slots' LDS reads overlap instead of forming
+// one dependent chain per slot. pre[] holds 2P words, those past P all ones:
+// a step reads at most pre[2P - 1] and never moves past P for f < total.
 template <int NT, int B>
-__device__ __forceinline__ void find_nodes(const uint32_t* pre, uint32_t P, uint32_t f0, uint32_t total,
-                                           uint32_t (&node)[B]) {
+__device__ __forceinline__ void find_nodes(const uint32_t* pre, uint32_t P, uint32_t f0, uint32_t (&node)[B]) {
 #pragma unroll
   for (int b = 0; b < B; ++b) node[b] = 0u;
   const uint32_t top = P > 1u ? 1u << (31 - __clz(P - 1u)) : 0u;  // largest power of two <= P - 1
   for (uint32_t step = top; step != 0u; step >>= 1) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      if (f0 + b * NT >= total) break;  // no thread has this slot or a later one (uniform)
       const uint32_t f = f0 + b * NT + threadIdx.x;
       const uint32_t c = node[b] + step;
-      if (c <= P && pre[c] <= f) node[b] = c;
+      node[b] = pre[c] <= f ? c : node[b];
     }
   }
 }
@@ -330,7 +331,7 @@ template <int MAXP>
 __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R) {
   constexpr int NT = kCountThreads;
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[MAXP + 1];
+  __shared__ uint32_t pre[2 * MAXP];
   __shared__ uint32_t start[MAXP];
   __shared__ uint32_t scr[NT / kWave + 3];
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
@@ -341,7 +342,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   constexpr int kBatch = 12;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch], node[kBatch];
-    find_nodes<NT>(pre, R.P, f0, total, node);
+    find_nodes<NT>(pre, R.P, f0, node);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
@@ -440,7 +441,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   constexpr int NT = kWriteThreads;
   __shared__ double acc[kSeg];
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[MAXP + 1];
+  __shared__ uint32_t pre[2 * MAXP];
   __shared__ uint32_t start[MAXP];
   __shared__ uint32_t scr[NT / kWave + 3];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
     uint32_t ii[kBatch], node[kBatch];
     float vv[kBatch];
-    find_nodes<NT>(pre, R.P, f0, total, node);
+    find_nodes<NT>(pre, R.P, f0, node);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
