@@ -44,21 +44,31 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave (all lanes active):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (DPP row_shr, lanes
+// without a source add 0), then each row adds the totals of the rows below,
+// read from lanes 15, 31 and 47.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const uint32_t lane = lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    uint32_t t = __shfl_up(v, d, kWave);
-    if (lane >= (uint32_t)d) v += t;
-  }
-  return v;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t row = lane_id() >> 4;
+  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
 }
 
+// Sum over the 64 lanes of a wave (all lanes active), the same in every lane:
+// DPP sums within each row of 16, then the four row sums.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -111,29 +121,26 @@ __device__ __forceinline__ void block_sum2(uint32_t a, uint32_t b, uint32_t* scr
 
 // Exclusive prefix sum over the threads of a block (thread order), with the
 // block total. `scratch` holds NT/64 + 1 words of LDS. Contains barriers: all
-// threads of the block must call it.
+// threads of the block must call it. Every wave adds up the wave totals
+// itself, so one barrier separates their writes from the reads, and one more
+// lets the caller reuse `scratch` right away.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
   constexpr int NW = NT / kWave;
-  const uint32_t lane = lane_id();
   const uint32_t wid = threadIdx.x / kWave;
-  uint32_t inc = wave_inclusive_scan(v);
-  if (lane == kWave - 1) scratch[wid] = inc;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane_id() == kWave - 1) scratch[wid] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int w = 0; w < NW; ++w) {
-      uint32_t t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[NW] = run;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = scratch[w];
+    before += (uint32_t)w < wid ? t : 0u;
+    all += t;
   }
+  total = all;
   __syncthreads();
-  uint32_t excl = scratch[wid] + inc - v;
-  total = scratch[NW];
-  __syncthreads();
-  return excl;
+  return before + inc - v;
 }
 
 // 64-bit exclusive prefix sum across a workgroup of NT threads; every

@@ -344,13 +344,13 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
     uint32_t ii[kBatch], node[kBatch];
     find_nodes<NT>(pre, R.P, f0, node);
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const uint32_t f = f0 + b * NT + threadIdx.x;
-      if (f < total) {
-        const uint32_t p = node[b];
-        ii[b] = idx[start[p] + (f - pre[p])];
-      }
+    for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
+      const uint32_t p = std::min(node[b], R.P - 1u);
+      node[b] = start[p] + (f0 + b * NT + threadIdx.x - pre[p]);
     }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+      if (f0 + b * NT + threadIdx.x < total) ii[b] = idx[node[b]];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t local = ii[b] - seg_lo;
@@ -460,21 +460,27 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 
   constexpr int kBatch = 4;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch], node[kBatch];
+    uint32_t ii[kBatch], node[kBatch], jj[kBatch], js[kBatch];
     float vv[kBatch];
     find_nodes<NT>(pre, R.P, f0, node);
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
+      node[b] = std::min(node[b], R.P - 1u);
+      jj[b] = f0 + b * NT + threadIdx.x - pre[node[b]];  // position in the node's run
+      js[b] = start[node[b]] + jj[b];                    // position in the pair arrays
+    }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
         const uint32_t p = node[b];
-        const uint32_t j = start[p] + (f - pre[p]);
+        const uint32_t j = js[b];
         ii[b] = idx[j];
         if constexpr (BITS == 0) {
           vv[b] = val[j];
         } else {  // dequantize on load: position e of node p
           using F = Qsgd<BITS>;
-          const uint32_t e = qruns.rel[p] + (f - pre[p]);
+          const uint32_t e = qruns.rel[p] + jj[b];
           const uint32_t code = F::code_at(R.codes + qruns.cb[p], e);
           vv[b] = F::value(code, F::step(R.scales[qruns.sb[p] + e / R.bucket]));
         }
