@@ -94,6 +94,7 @@ struct RDev {
   // scales at soffs[p]
   uint32_t bits;
   uint32_t bucket;
+  uint64_t bucket_recip;  // ceil(2^64 / bucket) for bucket >= 2, else 0: e / bucket = mulhi(e, bucket_recip)
   const uint8_t* codes;
   const float* scales;
   uint64_t* coffs;
@@ -239,12 +240,15 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
 }
 
 // Per-node tables of a quantized segment, in LDS: node-relative position of
-// the run's first pair and the node's code-byte and scale offsets.
+// the run's first pair and the node's code-byte and scale offsets. Offsets
+// fit in 32 bits (at most 2^32 - 16 pairs of at most 8-bit codes, and fewer
+// scales than pairs plus nodes), which keeps the writer within four
+// workgroups per compute unit.
 template <int MAXP>
 struct QRuns {
   uint32_t rel[MAXP];
-  uint64_t cb[MAXP];
-  uint64_t sb[MAXP];
+  uint32_t cb[MAXP];
+  uint32_t sb[MAXP];
 };
 
 // Node runs of segment s: pre[p] = exclusive prefix of their lengths,
@@ -265,8 +269,8 @@ __device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_
     start[p] = b0;
     if (q != nullptr) {
       q->rel[p] = b0 - lo;
-      q->cb[p] = R.coffs[p];
-      q->sb[p] = R.soffs[p];
+      q->cb[p] = (uint32_t)R.coffs[p];
+      q->sb[p] = (uint32_t)R.soffs[p];
     }
     return b1 > b0 ? b1 - b0 : 0u;
   };
@@ -460,29 +464,36 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 
   constexpr int kBatch = 4;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch], node[kBatch], jj[kBatch], js[kBatch];
+    uint32_t ii[kBatch], node[kBatch], js[kBatch];
+    uint32_t qe[kBatch];              // quantized input: position in the node's code row
+    uint32_t qc[kBatch], qs[kBatch];  // ... and the node's code-byte and scale offsets
     float vv[kBatch];
     find_nodes<NT>(pre, R.P, f0, node);
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
-      node[b] = std::min(node[b], R.P - 1u);
-      jj[b] = f0 + b * NT + threadIdx.x - pre[node[b]];  // position in the node's run
-      js[b] = start[node[b]] + jj[b];                    // position in the pair arrays
+      const uint32_t p = std::min(node[b], R.P - 1u);
+      const uint32_t jr = f0 + b * NT + threadIdx.x - pre[p];  // position in the node's run
+      js[b] = start[p] + jr;                                   // position in the pair arrays
+      if constexpr (BITS != 0) {
+        qe[b] = qruns.rel[p] + jr;
+        qc[b] = qruns.cb[p];
+        qs[b] = qruns.sb[p];
+      }
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t f = f0 + b * NT + threadIdx.x;
       if (f < total) {
-        const uint32_t p = node[b];
         const uint32_t j = js[b];
         ii[b] = idx[j];
         if constexpr (BITS == 0) {
           vv[b] = val[j];
-        } else {  // dequantize on load: position e of node p
+        } else {  // dequantize on load: position e of the node's codes
           using F = Qsgd<BITS>;
-          const uint32_t e = qruns.rel[p] + jj[b];
-          const uint32_t code = F::code_at(R.codes + qruns.cb[p], e);
-          vv[b] = F::value(code, F::step(R.scales[qruns.sb[p] + e / R.bucket]));
+          const uint32_t e = qe[b];
+          const uint32_t bucket_no = R.bucket_recip ? (uint32_t)__umul64hi((uint64_t)e, R.bucket_recip) : e;
+          const uint32_t code = F::code_at(R.codes + qc[b], e);
+          vv[b] = F::value(code, F::step(R.scales[qs[b] + bucket_no]));
         }
       }
     }
@@ -603,6 +614,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.result = d_result;
   R.bits = quant ? quant->bits : 0u;
   R.bucket = quant ? quant->bucket : 1u;
+  R.bucket_recip = R.bucket >= 2u ? UINT64_MAX / R.bucket + 1u : 0u;
   R.codes = quant ? quant->codes : nullptr;
   R.scales = quant ? quant->scales : nullptr;
   R.coffs = reinterpret_cast<uint64_t*>(w + L.qoffs);
