@@ -345,16 +345,16 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   const uint32_t total = load_runs<NT, MAXP>(R, s, pre, start, scr, (QRuns<MAXP>*)nullptr);
   constexpr int kBatch = 12;
   for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch], node[kBatch];
-    find_nodes<NT>(pre, R.P, f0, node);
+    uint32_t ii[kBatch], pos[kBatch];
+    find_nodes<NT>(pre, R.P, f0, pos);  // each slot's node, replaced below by its position
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
-      const uint32_t p = std::min(node[b], R.P - 1u);
-      node[b] = start[p] + (f0 + b * NT + threadIdx.x - pre[p]);
+      const uint32_t p = std::min(pos[b], R.P - 1u);
+      pos[b] = start[p] + (f0 + b * NT + threadIdx.x - pre[p]);
     }
 #pragma unroll
     for (int b = 0; b < kBatch; ++b)
-      if (f0 + b * NT + threadIdx.x < total) ii[b] = idx[node[b]];
+      if (f0 + b * NT + threadIdx.x < total) ii[b] = idx[pos[b]];
 #pragma unroll
     for (int b = 0; b < kBatch; ++b) {
       const uint32_t local = ii[b] - seg_lo;
