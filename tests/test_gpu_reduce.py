@@ -201,6 +201,31 @@ def test_unaligned_index_array(dev, shift):
         assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= reduce_tolerance(7, val)
 
 
+def test_wideresnet_size_dense_result(dev):
+    """Full wide-ResNet size (P = 64, N = 2^27, 671088 pairs per node) with
+    delta = 0.25, where the union (about 0.274 N) passes T: the dense result
+    of both the dense-first and the count-first path against the oracle."""
+    w = W.workload(4)
+    P, N, k, delta = w.P, w.N, w.k, 0.25
+    rng = np.random.default_rng(45)
+    idx = np.empty((P, k), np.uint32)
+    for p in range(P):
+        cand = np.unique(rng.integers(0, N, size=int(k * 1.02)))
+        while cand.size < k:
+            cand = np.unique(np.concatenate([cand, rng.integers(0, N, size=k)]))
+        idx[p] = np.sort(rng.choice(cand, size=k, replace=False))
+    val = (rng.standard_normal((P, k)) * 1e-3).astype(np.float32)
+    off = np.arange(P + 1, dtype=np.uint64) * k
+    K, dense, _, ov = oracle.reduce(off, idx.reshape(-1), val.reshape(-1), N, delta)
+    assert dense and K >= sg.dense_threshold(delta, N)
+    tol = reduce_tolerance(P, val)
+    for hint in (0, 1):  # the estimate (dense-first here), then count-first
+        print(f"wide-ResNet dense result hint={hint}", flush=True)
+        gK, gdense, flags, _, gv = _gpu_reduce(off, idx.reshape(-1), val.reshape(-1), N, delta, dev, hint)
+        assert flags == 0 and gK == K and gdense
+        assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= tol
+
+
 def test_reduce_deterministic(dev):
     rng = np.random.default_rng(21)
     off, idx, val = _random_sparse(rng, 32, 1 << 18, 20000)
