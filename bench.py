@@ -234,6 +234,22 @@ def main():
         fused_in = P * k * 4.5 + 4 * P * ((k + B - 1) // B)
         extra["fused_dq4_reduce"] = {"unfused_ms": round(t_unf, 4), "fused_ms": round(t_fus, 4),
                                      "fused_input_gb_per_s": round(fused_in / (t_fus * 1e-3) / 1e9, 2)}
+        # b-bit QSGD of the same sent values (2, 4 and 8 bits) and the reduce over its codes
+        nsc = (k + B - 1) // B
+        for bits in (2, 4, 8):
+            cb = torch.empty((P, sg.qsgd_row_bytes(bits, k)), dtype=torch.uint8, device=dev)
+            sb = torch.empty((P, nsc), dtype=torch.float32, device=dev)
+            t_q = time_ops(lambda: sg.qsgd(val, bits, B, args.seed, 1, codes=cb, scales=sb))
+            t_r = time_ops(lambda: sg.sparse_reduce_qsgd(offsets, idx.view(-1), cb.view(-1), sb.view(-1), bits, B, N,
+                                                         w.delta, out_idx=red_idx, out_val=red_val, result=red_res,
+                                                         workspace=ws_red))
+            q_bytes = P * k * 4 + P * sg.qsgd_row_bytes(bits, k) + 4 * P * nsc
+            r_in = P * k * 4 + P * sg.qsgd_row_bytes(bits, k) + 4 * P * nsc
+            extra[f"qsgd_{bits}bit"] = {"quantize_ms": round(t_q, 4),
+                                        "quantize_gb_per_s": round(q_bytes / (t_q * 1e-3) / 1e9, 1),
+                                        "fused_reduce_ms": round(t_r, 4),
+                                        "fused_reduce_input_gb_per_s": round(r_in / (t_r * 1e-3) / 1e9, 1)}
+            del cb, sb
     # the dense phase: a reduce whose result turns dense (delta lowered below K / N), then
     # 4-bit quantization of the dense sum in buckets of 1024, gated on the device
     delta_d = 0.25
