@@ -411,13 +411,37 @@ def other_configs(sg, W, dev, skip_wid):
     """The other workloads at their full sizes, outside the timed steps: the
     median per-step time of Top-k EF and of the reduce of its pairs over the
     workload's error-feedback steps (from a zero residual), or of the reduce
-    alone for the already-sparse workload, each with its algorithmic bytes."""
+    alone for the already-sparse workload, each with its algorithmic bytes;
+    and the same step (or reduce) captured once as a HIP graph and replayed,
+    which removes the launch gaps that dominate the small workloads."""
     import numpy as np
     import torch
 
     def med(xs):
         xs = sorted(xs)
         return xs[len(xs) // 2]
+
+    def graph_ms(fn, reps=10):
+        """fn captured once as a HIP graph (after a warm-up on a side stream of
+        default priority), then the median time of a replay."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        graph.replay()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        del graph
+        return med([a.elapsed_time(b) for a, b in ev])
 
     res = {}
     for wi in range(5):
@@ -448,7 +472,8 @@ def other_configs(sg, W, dev, skip_wid):
             b_in, b_out = 8 * off[-1], (4 * N if dense else 8 * K)
             res[w.name] = {"reduce_ms": round(t, 4), "pairs": off[-1], "nnz": K, "dense": dense,
                            "reduce_input_gb_per_s": round(b_in / (t * 1e-3) / 1e9, 1),
-                           "reduce_frac_hbm_peak": round((b_in + b_out) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                           "reduce_frac_hbm_peak": round((b_in + b_out) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "reduce_graph_ms": round(graph_ms(run), 4)}
             continue
         grads = [W.gradients(w, t, device=dev) for t in range(w.steps)]
         r = torch.zeros((P, N), dtype=torch.float32, device=dev)
@@ -479,6 +504,13 @@ def other_configs(sg, W, dev, skip_wid):
                     per_step.append({"nnz": K, "dense": dense})
         torch.cuda.synchronize()
         tk, tr = med(t_topk), med(t_red)
+
+        def one_step():
+            sg.topk_ef(grads[0], r, k, out_idx=idx, out_val=val, workspace=ws)
+            sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
+                             workspace=wr)
+
+        t_graph = graph_ms(one_step)  # the residual keeps accumulating: EF steps on the first gradient
         b_topk = 12 * P * N + 8 * P * k
         b_in = 8 * P * k
         b_out = [4 * N if s["dense"] else 8 * s["nnz"] for s in per_step]
@@ -487,6 +519,7 @@ def other_configs(sg, W, dev, skip_wid):
                        "topk_frac_hbm_peak": round(b_topk / (tk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "reduce_input_gb_per_s": round(b_in / (tr * 1e-3) / 1e9, 1),
                        "reduce_frac_hbm_peak": round((b_in + med(b_out)) / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "step_graph_ms": round(t_graph, 4),
                        "per_step": per_step}
         del grads, r, ws, idx, val, ri, rv, rr, wr
         torch.cuda.synchronize()
