@@ -197,9 +197,13 @@ def topk_ef_bucketed(grad: torch.Tensor, residual: torch.Tensor, bucket: int, k_
     return out_idx, out_val
 
 
+TOPK_ROW_MAX = 1 << 17  # SPARCML_TOPK_ROW_MAX: rows this short (N % 4 == 0) are selected by one workgroup per node
+
+
 def topk_ef_paths(workspace: torch.Tensor, P: int) -> torch.Tensor:
     """Per node, which path the last sparcml_topk_ef in `workspace` took
-    (0 candidates, 1 exact rescan), and its consistency flag: [2, P] int32."""
+    (0 candidates, 1 exact rescan, 2 one workgroup over a short row), and its
+    consistency flag: [2, P] int32."""
     return workspace[: 8 * P].view(torch.int32).view(2, P)
 
 

@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparcml.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "topk_ef.hip", "topk_bucketed.hip", "qsgd.hip", "sparse_reduce.hip", "reference_stream.hip"]
+SOURCES = ["api.hip", "topk_ef.hip", "topk_row.hip", "topk_bucketed.hip", "qsgd.hip", "sparse_reduce.hip",
+           "reference_stream.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -14,6 +14,12 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
                           uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
                           hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// ---- error-feedback Top-k of short rows: one workgroup per node; info holds
+// the [P] path words (2) and the [P] consistency words the workspace reports
+hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                           uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop);
+
 // ---- per-layer error-feedback Top-k (layers [off[l], off[l+1]) of every node)
 size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);
 uint64_t topk_layers_stream_blocks(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);

@@ -1,0 +1,279 @@
+// Error-feedback Top-k of short rows for gfx950: one workgroup per node.
+//
+// SparCML (paperlayer.ai digest of arXiv 1802.08021v3), section 2.2: a node
+// sends the k entries of largest magnitude of its accumulated gradient
+// a = g + r and, section 4, keeps the others as the residual for the next
+// step. Selection order: magnitude key (the IEEE bits with the sign cleared)
+// descending, index ascending; the sent entries are emitted in index order
+// and zeroed in the residual. The result is the one the candidate pipeline of
+// topk_ef.hip computes.
+//
+// That pipeline is a chain of about a dozen dependent kernels, each lasting a
+// few microseconds whatever the row length, which is the whole cost for short
+// rows. Here a 1024-thread workgroup owns one node:
+//   accumulate  a = g + r over the row, written over r, with the histogram of
+//               the keys' top 11 bits in LDS;
+//   refine      two passes over a (in r, now cache-resident) histogram the
+//               next two 10-bit digits among the keys that share the chosen
+//               prefix, which gives T, the k-th largest key, and m, how many
+//               keys equal to T are taken (the lowest indices);
+//   count       each wave counts the keys > T and == T over its own contiguous
+//               stretch of the row; the sixteen totals give each stretch its
+//               output offset and the tie rank it starts from;
+//   emit        each wave walks its stretch again in index order, placing the
+//               selected pairs by ballots and zeroing their residual entries.
+// Rows of a multiple of four elements only (so every row starts on a 16-byte
+// boundary): each thread reads groups of four with 16-byte accesses, its
+// positions clamped into the row and the surplus masked, so that the loads of
+// a pass issue together with no branch between them.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace sparcml {
+namespace {
+
+constexpr int kRowThreads = 1024;
+constexpr int kRowWaves = kRowThreads / kWave;    // 16
+constexpr int kD0 = 2048, kD1 = 1024, kD2 = 1024;  // key digits: 11 + 10 + 10 bits
+constexpr int kUnroll = 4;                         // groups per thread in flight
+
+// Group j (of nq) of the row starting at group q0, as four values; `own` is
+// 0xF for a group of the row and 0 for a position past its end (which reads
+// the row's last group again instead).
+__device__ __forceinline__ void load_group(const float* __restrict__ x, uint64_t q0, uint64_t nq, uint64_t j,
+                                           float (&v)[4], uint32_t& own) {
+  const f32x4 t = reinterpret_cast<const f32x4*>(x)[q0 + (j < nq ? j : nq - 1)];
+  v[0] = t.x;
+  v[1] = t.y;
+  v[2] = t.z;
+  v[3] = t.w;
+  own = j < nq ? 0xFu : 0u;
+}
+
+// Histogram over the row's keys in r of the digit (key >> shift) & (NB - 1),
+// for keys whose bits above shift + 10 equal prefix.
+template <int NB>
+__device__ __forceinline__ void refine_pass(const float* __restrict__ r, uint64_t q0, uint64_t nq, uint32_t* h,
+                                            uint32_t prefix, int shift) {
+  constexpr int NT = kRowThreads;
+  for (uint64_t j0 = 0; j0 < nq; j0 += (uint64_t)NT * kUnroll) {
+    float v[kUnroll][4];
+    uint32_t own[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) load_group(r, q0, nq, j0 + (uint64_t)u * NT + threadIdx.x, v[u], own[u]);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t key = mag_key(v[u][c]);
+        if (own[u] && (key >> (shift + 10)) == prefix) atomicAdd(&h[(key >> shift) & (NB - 1)], 1u);
+      }
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ g, float* __restrict__ r,
+                                                          uint64_t N, uint32_t k, uint32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_val, uint32_t* __restrict__ info) {
+  constexpr int NT = kRowThreads;
+  __shared__ uint32_t h[kD0];
+  __shared__ uint32_t scr[NT / kWave + 3];
+  __shared__ uint32_t s_gt[kRowWaves], s_eq[kRowWaves];
+  const uint64_t base = (uint64_t)blockIdx.x * N;
+  const uint64_t q0 = base >> 2, nq = N >> 2;  // the row's groups of four
+  const uint32_t tid = threadIdx.x;
+  for (uint32_t i = tid; i < kD0; i += NT) h[i] = 0u;
+  __syncthreads();
+
+  // accumulate: a = g + r written over r; histogram of the top 11 key bits
+  for (uint64_t j0 = 0; j0 < nq; j0 += (uint64_t)NT * kUnroll) {
+    float gv[kUnroll][4], rv[kUnroll][4];
+    uint32_t own[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t j = j0 + (uint64_t)u * NT + tid;
+      load_group(g, q0, nq, j, gv[u], own[u]);
+      load_group(r, q0, nq, j, rv[u], own[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float a[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = gv[u][c] + rv[u][c];
+      if (own[u]) {
+        f32x4 t;
+        t.x = a[0];
+        t.y = a[1];
+        t.z = a[2];
+        t.w = a[3];
+        reinterpret_cast<f32x4*>(r)[q0 + j0 + (uint64_t)u * NT + tid] = t;
+        if (k != 0u) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) atomicAdd(&h[mag_key(a[c]) >> 20], 1u);
+        }
+      }
+    }
+  }
+  if (k == 0u) {  // nothing is sent: the residual is a
+    if (tid == 0) {
+      info[blockIdx.x] = 2u;
+      info[gridDim.x + blockIdx.x] = 0u;
+    }
+    return;
+  }
+  __syncthreads();
+
+  // refine: T = the k-th largest key, m = keys equal to T that are taken
+  uint32_t d0, d1, d2, above;
+  block_find_suffix<NT, kD0>(h, k, scr, d0, above);
+  uint32_t rank = k - above;
+  for (uint32_t i = tid; i < kD1; i += NT) h[i] = 0u;
+  __syncthreads();
+  refine_pass<kD1>(r, q0, nq, h, d0, 10);
+  __syncthreads();
+  block_find_suffix<NT, kD1>(h, rank, scr, d1, above);
+  rank -= above;
+  const uint32_t prefix = (d0 << 10) | d1;  // key >> 10
+  for (uint32_t i = tid; i < kD2; i += NT) h[i] = 0u;
+  __syncthreads();
+  refine_pass<kD2>(r, q0, nq, h, prefix, 0);
+  __syncthreads();
+  block_find_suffix<NT, kD2>(h, rank, scr, d2, above);
+  const uint32_t T = (prefix << 10) | d2;
+  const uint32_t m = rank - above;
+
+  // count: keys > T and == T over each wave's stretch of whole steps of 64 groups
+  const uint32_t wid = tid / kWave, lane = lane_id();
+  const uint64_t steps = (nq + kWave - 1) / kWave;
+  const uint64_t per_wave = (steps + kRowWaves - 1) / kRowWaves;
+  const uint64_t s_lo = std::min<uint64_t>((uint64_t)wid * per_wave, steps) * kWave;
+  const uint64_t s_hi = std::min<uint64_t>((uint64_t)(wid + 1) * per_wave, steps) * kWave;
+  auto load_steps = [&](uint64_t s0, float (&v)[kUnroll][4], uint32_t (&own)[kUnroll]) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t j = s0 + (uint64_t)u * kWave + lane;
+      load_group(r, q0, nq, j < s_hi ? j : nq, v[u], own[u]);
+    }
+  };
+  uint32_t gt = 0, eq = 0;  // wave-uniform
+  for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
+    float v[kUnroll][4];
+    uint32_t own[kUnroll];
+    load_steps(s0, v, own);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool in = own[u] != 0u;
+        const uint32_t key = mag_key(v[u][c]);
+        gt += popc64(ballot(in && key > T));
+        eq += popc64(ballot(in && key == T));
+      }
+  }
+  if (lane == 0) {
+    s_gt[wid] = gt;
+    s_eq[wid] = eq;
+  }
+  __syncthreads();
+  uint32_t eq_run = 0, pos = 0;  // ties and selected pairs before this wave's stretch
+  uint32_t all_eq = 0, all_sel = 0;
+  for (uint32_t w = 0; w < (uint32_t)kRowWaves; ++w) {
+    const uint32_t e = s_eq[w];
+    const uint32_t take = all_eq >= m ? 0u : std::min(m - all_eq, e);
+    if (w == wid) {
+      eq_run = all_eq;
+      pos = all_sel;
+    }
+    all_sel += s_gt[w] + take;
+    all_eq += e;
+  }
+  if (tid == 0) {
+    info[blockIdx.x] = 2u;
+    info[gridDim.x + blockIdx.x] = all_sel != k ? 1u : 0u;
+  }
+
+  // emit: the stretch in index order (lane, then element within the group)
+  uint32_t* oi = out_idx + (uint64_t)blockIdx.x * k;
+  float* ov = out_val + (uint64_t)blockIdx.x * k;
+  for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
+    float v[kUnroll][4];
+    uint32_t own[kUnroll];
+    load_steps(s0, v, own);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint64_t q = q0 + s0 + (uint64_t)u * kWave + lane;
+      uint32_t is_eq = 0u, is_gt = 0u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool in = own[u] != 0u;
+        const uint32_t key = mag_key(v[u][c]);
+        if (in && key == T) is_eq |= 1u << c;
+        if (in && key > T) is_gt |= 1u << c;
+      }
+      // tie ranks in index order: ties before this step, in lower lanes, and
+      // earlier in this lane's group
+      uint32_t eq_below = 0, step_eq = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t em = ballot((is_eq >> c) & 1u);
+        eq_below += lanes_below(em);
+        step_eq += popc64(em);
+      }
+      uint32_t rank_t = eq_run + eq_below;
+      uint32_t sel = is_gt;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((is_eq >> c) & 1u) {
+          if (rank_t < m) sel |= 1u << c;
+          ++rank_t;
+        }
+      eq_run += step_eq;
+      uint32_t sel_below = 0, step_sel = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t sm = ballot((sel >> c) & 1u);
+        sel_below += lanes_below(sm);
+        step_sel += popc64(sm);
+      }
+      uint32_t p = pos + sel_below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((sel >> c) & 1u) {
+          const uint64_t e = 4 * q + c;
+          if (p < k) {
+            oi[p] = (uint32_t)(e - base);
+            ov[p] = v[u][c];
+          }
+          r[e] = 0.0f;
+          ++p;
+        }
+      pos += step_sel;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                           uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,
+                           hipEvent_t ev_start, hipEvent_t ev_stop) {
+  if (ev_start || ev_stop) {  // profiling: the events ride on the kernel's own dispatch
+    const float* ga = grad;
+    float* ra = residual;
+    uint64_t n = N;
+    uint32_t kk = (uint32_t)k;
+    uint32_t* oi = out_idx;
+    float* ov = out_val;
+    uint32_t* in = info;
+    void* args[] = {&ga, &ra, &n, &kk, &oi, &ov, &in};
+    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_topk_row), dim3(P), dim3(kRowThreads),
+                                            args, 0, stream, ev_start, ev_stop, 0);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_topk_row, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k, out_idx,
+                     out_val, info);
+  return hipGetLastError();
+}
+
+}  // namespace sparcml

@@ -185,6 +185,14 @@ def test_estimate_matches_uniform_closed_form(P, N, k):
     assert got <= P * k + 1e-9
 
 
+def test_row_limit_matches_header():
+    """The binding's short-row limit mirrors SPARCML_TOPK_ROW_MAX."""
+    import re
+    text = open(os.path.join(ROOT, "include", "sparcml.h")).read()
+    m = re.search(r"#define SPARCML_TOPK_ROW_MAX \(1u << (\d+)\)", text)
+    assert m and sg.TOPK_ROW_MAX == 1 << int(m.group(1))
+
+
 def test_dense_threshold_reading():
     assert sg.dense_threshold(0.25, 65536) == 16384
     assert sg.dense_threshold(0.3, 1 << 27) == 40265319
