@@ -75,9 +75,9 @@ const char* sparcml_status_string(sparcml_status status);
  *   out_idx[p][0..k) = S in ascending order, out_val[p][j] = a[out_idx[p][j]]
  *   residual_i = a_i, except +0.0 at the positions in S      (in place)
  * Hence residual_new + scatter(out_val) == grad + residual_old exactly.
- * Rows of at most SPARCML_TOPK_ROW_MAX elements, N a multiple of 4, are
- * selected by one workgroup per node; other rows by the predicted-threshold
- * candidate pipeline. Both give the result above.
+ * Rows of at most SPARCML_TOPK_ROW_MAX elements are selected by one
+ * workgroup per node; longer rows by the predicted-threshold candidate
+ * pipeline. Both give the result above.
  *
  *   P, N      nodes and elements per node; 1 <= P <= 65535, N <= 2^32 - 2^19,
  *             P * ceil((N+31)/1024) < 2^24 (about P*N < 2^34: one workgroup
@@ -93,8 +93,7 @@ const char* sparcml_status_string(sparcml_status status);
  *             first 4*P bytes hold, per node, which path produced the result
  *             (0: predicted-threshold candidates, 1: exact rescan, 2: one
  *             workgroup over the whole row, taken when N <=
- *             SPARCML_TOPK_ROW_MAX and N % 4 == 0), and the next 4*P bytes
- *             hold a nonzero
+ *             SPARCML_TOPK_ROW_MAX), and the next 4*P bytes hold a nonzero
  *             value for a node whose internal consistency check failed (never
  *             expected).
  * grad and residual must not overlap; neither may overlap the outputs.

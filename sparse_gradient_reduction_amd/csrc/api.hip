@@ -73,8 +73,7 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
-  // short rows of whole 16-byte groups: one workgroup per node beats the candidate pipeline's kernel chain
-  if (N <= SPARCML_TOPK_ROW_MAX && N % 4 == 0)
+  if (N <= SPARCML_TOPK_ROW_MAX)  // short rows: one workgroup per node beats the candidate pipeline's kernel chain
     return from_hip(sparcml::topk_row_launch(P, N, k, grad, residual, out_idx, out_val, static_cast<uint32_t*>(ws),
                                              stream, ev0, ev1));
   return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));

@@ -22,10 +22,13 @@
 //               output offset and the tie rank it starts from;
 //   emit        each wave walks its stretch again in index order, placing the
 //               selected pairs by ballots and zeroing their residual entries.
-// Rows of a multiple of four elements only (so every row starts on a 16-byte
-// boundary): each thread reads groups of four with 16-byte accesses, its
-// positions clamped into the row and the surplus masked, so that the loads of
-// a pass issue together with no branch between them.
+// A row is read as its whole 16-byte groups of four (absolute positions
+// 4q .. 4q+3 inside the row), each thread's positions clamped into the row
+// and the surplus masked, so that the loads of a pass issue together with no
+// branch between them; the at most three elements before the first whole
+// group (the head) and after the last (the tail) are handled one per lane,
+// the head by the first wave before its stretch, the tail by the last wave
+// after its stretch.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -80,9 +83,16 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   __shared__ uint32_t h[kD0];
   __shared__ uint32_t scr[NT / kWave + 3];
   __shared__ uint32_t s_gt[kRowWaves], s_eq[kRowWaves];
-  const uint64_t base = (uint64_t)blockIdx.x * N;
-  const uint64_t q0 = base >> 2, nq = N >> 2;  // the row's groups of four
+  const uint64_t base = (uint64_t)blockIdx.x * N, end = base + N;
+  const uint64_t q0 = (base + 3) >> 2;                                    // first whole group
+  const uint64_t nq = (end >> 2) > q0 ? (end >> 2) - q0 : 0;              // whole groups
+  const uint64_t head_end = std::min<uint64_t>(4 * q0, end);              // head: [base, head_end)
+  const uint64_t tail0 = std::min(std::max<uint64_t>(4 * (q0 + nq), head_end), end);  // tail: [tail0, end)
+  const uint32_t nh = (uint32_t)(head_end - base), ntl = (uint32_t)(end - tail0);  // each at most 3
+  // element of the head (lanes 0..2) or tail (lanes 4..6) this thread takes, if any
   const uint32_t tid = threadIdx.x;
+  const bool edge = (tid < 4 && tid < nh) || (tid >= 4 && tid < 4 + ntl);
+  const uint64_t e_edge = tid < 4 ? base + tid : tail0 + (tid - 4);
   for (uint32_t i = tid; i < kD0; i += NT) h[i] = 0u;
   __syncthreads();
 
@@ -115,6 +125,11 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
       }
     }
   }
+  if (edge) {
+    const float a = g[e_edge] + r[e_edge];
+    r[e_edge] = a;
+    if (k != 0u) atomicAdd(&h[mag_key(a) >> 20], 1u);
+  }
   if (k == 0u) {  // nothing is sent: the residual is a
     if (tid == 0) {
       info[blockIdx.x] = 2u;
@@ -131,6 +146,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   for (uint32_t i = tid; i < kD1; i += NT) h[i] = 0u;
   __syncthreads();
   refine_pass<kD1>(r, q0, nq, h, d0, 10);
+  if (edge) {
+    const uint32_t key = mag_key(r[e_edge]);
+    if ((key >> 20) == d0) atomicAdd(&h[(key >> 10) & (kD1 - 1)], 1u);
+  }
   __syncthreads();
   block_find_suffix<NT, kD1>(h, rank, scr, d1, above);
   rank -= above;
@@ -138,6 +157,10 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   for (uint32_t i = tid; i < kD2; i += NT) h[i] = 0u;
   __syncthreads();
   refine_pass<kD2>(r, q0, nq, h, prefix, 0);
+  if (edge) {
+    const uint32_t key = mag_key(r[e_edge]);
+    if ((key >> 10) == prefix) atomicAdd(&h[key & (kD2 - 1)], 1u);
+  }
   __syncthreads();
   block_find_suffix<NT, kD2>(h, rank, scr, d2, above);
   const uint32_t T = (prefix << 10) | d2;
@@ -157,19 +180,47 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     }
   };
   uint32_t gt = 0, eq = 0;  // wave-uniform
+  auto count_step = [&](const float (&v)[4], uint32_t own) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool in = (own >> c) & 1u;
+      const uint32_t key = mag_key(v[c]);
+      gt += popc64(ballot(in && key > T));
+      eq += popc64(ballot(in && key == T));
+    }
+  };
+  // the head (first wave) or the tail (last wave) as one step, one element per lane
+  auto edge_step = [&](bool head, float (&v)[4], uint32_t& own, uint64_t& e_first) {
+    const uint32_t n = head ? nh : ntl;
+    e_first = (head ? base : tail0) + lane;
+    v[0] = v[1] = v[2] = v[3] = 0.0f;
+    own = 0u;
+    if (lane < n) {
+      v[0] = r[e_first];
+      own = 1u;
+    }
+  };
+  const bool first_wave = wid == 0, last_wave = wid == (uint32_t)kRowWaves - 1;
+  if (first_wave && nh != 0u) {
+    float v[4];
+    uint32_t own;
+    uint64_t e;
+    edge_step(true, v, own, e);
+    count_step(v, own);
+  }
   for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
     float v[kUnroll][4];
     uint32_t own[kUnroll];
     load_steps(s0, v, own);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool in = own[u] != 0u;
-        const uint32_t key = mag_key(v[u][c]);
-        gt += popc64(ballot(in && key > T));
-        eq += popc64(ballot(in && key == T));
-      }
+    for (int u = 0; u < kUnroll; ++u) count_step(v[u], own[u]);
+  }
+  if (last_wave && ntl != 0u) {
+    float v[4];
+    uint32_t own;
+    uint64_t e;
+    edge_step(false, v, own, e);
+    count_step(v, own);
   }
   if (lane == 0) {
     s_gt[wid] = gt;
@@ -196,60 +247,76 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   // emit: the stretch in index order (lane, then element within the group)
   uint32_t* oi = out_idx + (uint64_t)blockIdx.x * k;
   float* ov = out_val + (uint64_t)blockIdx.x * k;
+  // one step: element c of lane l is at e_first + c (own bit c set), in index
+  // order (lane, then c)
+  auto emit_step = [&](const float (&v)[4], uint32_t own, uint64_t e_first) {
+    uint32_t is_eq = 0u, is_gt = 0u;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bool in = (own >> c) & 1u;
+      const uint32_t key = mag_key(v[c]);
+      if (in && key == T) is_eq |= 1u << c;
+      if (in && key > T) is_gt |= 1u << c;
+    }
+    // tie ranks in index order: ties before this step, in lower lanes, and
+    // earlier in this lane
+    uint32_t eq_below = 0, step_eq = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t em = ballot((is_eq >> c) & 1u);
+      eq_below += lanes_below(em);
+      step_eq += popc64(em);
+    }
+    uint32_t rank_t = eq_run + eq_below;
+    uint32_t sel = is_gt;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((is_eq >> c) & 1u) {
+        if (rank_t < m) sel |= 1u << c;
+        ++rank_t;
+      }
+    eq_run += step_eq;
+    uint32_t sel_below = 0, step_sel = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint64_t sm = ballot((sel >> c) & 1u);
+      sel_below += lanes_below(sm);
+      step_sel += popc64(sm);
+    }
+    uint32_t p = pos + sel_below;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if ((sel >> c) & 1u) {
+        const uint64_t e = e_first + c;
+        if (p < k) {
+          oi[p] = (uint32_t)(e - base);
+          ov[p] = v[c];
+        }
+        r[e] = 0.0f;
+        ++p;
+      }
+    pos += step_sel;
+  };
+  if (first_wave && nh != 0u) {
+    float v[4];
+    uint32_t own;
+    uint64_t e;
+    edge_step(true, v, own, e);
+    emit_step(v, own, e);
+  }
   for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
     float v[kUnroll][4];
     uint32_t own[kUnroll];
     load_steps(s0, v, own);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t q = q0 + s0 + (uint64_t)u * kWave + lane;
-      uint32_t is_eq = 0u, is_gt = 0u;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool in = own[u] != 0u;
-        const uint32_t key = mag_key(v[u][c]);
-        if (in && key == T) is_eq |= 1u << c;
-        if (in && key > T) is_gt |= 1u << c;
-      }
-      // tie ranks in index order: ties before this step, in lower lanes, and
-      // earlier in this lane's group
-      uint32_t eq_below = 0, step_eq = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint64_t em = ballot((is_eq >> c) & 1u);
-        eq_below += lanes_below(em);
-        step_eq += popc64(em);
-      }
-      uint32_t rank_t = eq_run + eq_below;
-      uint32_t sel = is_gt;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((is_eq >> c) & 1u) {
-          if (rank_t < m) sel |= 1u << c;
-          ++rank_t;
-        }
-      eq_run += step_eq;
-      uint32_t sel_below = 0, step_sel = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint64_t sm = ballot((sel >> c) & 1u);
-        sel_below += lanes_below(sm);
-        step_sel += popc64(sm);
-      }
-      uint32_t p = pos + sel_below;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((sel >> c) & 1u) {
-          const uint64_t e = 4 * q + c;
-          if (p < k) {
-            oi[p] = (uint32_t)(e - base);
-            ov[p] = v[u][c];
-          }
-          r[e] = 0.0f;
-          ++p;
-        }
-      pos += step_sel;
-    }
+    for (int u = 0; u < kUnroll; ++u) emit_step(v[u], own[u], 4 * (q0 + s0 + (uint64_t)u * kWave + lane));
+  }
+  if (last_wave && ntl != 0u) {
+    float v[4];
+    uint32_t own;
+    uint64_t e;
+    edge_step(false, v, own, e);
+    emit_step(v, own, e);
   }
 }
 
