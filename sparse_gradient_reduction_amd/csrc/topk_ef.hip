@@ -68,7 +68,8 @@ constexpr uint32_t kTileAlign = 32;
 __host__ __device__ inline uint32_t tile_phase(uint64_t base) { return (uint32_t)(base & (kTileAlign - 1)); }
 constexpr int kNW = kStreamThreads / kWave;               // waves per stream block
 constexpr int kSub = 256;                                 // reservation counters per node
-constexpr int kTilesPerSlot = 16;                         // consecutive tiles sharing a counter
+constexpr int kTilesPerSlotLog = 4;
+constexpr int kTilesPerSlot = 1 << kTilesPerSlotLog;      // consecutive tiles sharing a counter
 constexpr int kSampleChunks = 1024;
 constexpr int kSampleChunk = 64;
 constexpr int kSample = kSampleChunks * kSampleChunk;     // 65536
@@ -110,12 +111,16 @@ struct RowSize {
   uint32_t nsub;    // counter regions
   uint32_t schunks; // sample chunks
   uint32_t npass;   // blocks of the select / count / emit grids
+  uint32_t tps_log; // log2 of the consecutive tiles sharing a counter
 };
 constexpr size_t kRowBytes = 12 * sizeof(uint64_t);
 
-// A whole node: kSub regions with a whole tile of slack each. A layer: as
-// many regions as it has runs of kTilesPerSlot tiles (at most kSub), with the
-// slack of its largest possible run. Where every element is a candidate (k =
+// A whole node: kSub regions with a whole tile of slack each; a node of at
+// most kSub runs of kTilesPerSlot tiles deals its tiles to the counters one by
+// one, so that candidates crowded in one stretch of the node (a layer of
+// larger gradients) spread over all regions. A layer: as many regions as it
+// has runs of kTilesPerSlot tiles (at most kSub), with the slack of its
+// largest possible run. Where every element is a candidate (k =
 // n, or a layer small enough to skip the prediction), a region takes whole
 // slot groups of tiles, and regions may hold one group more than others: each
 // holds the most groups any region gets.
@@ -126,8 +131,10 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
   z.chunks = (n + kChunk - 1) / kChunk;
   if (z.chunks == 0) z.chunks = 1;
   const uint64_t want = n < 2 * k + 65536 ? n : 2 * k + 65536;
+  z.tps_log = kTilesPerSlotLog;
   if (!layer) {
     z.nsub = kSub;
+    if (z.nt <= (uint64_t)kSub * kTilesPerSlot) z.tps_log = 0;
     z.capS = (want + kSub - 1) / kSub + kTile;
     z.schunks = kSampleChunks;
     z.npass = 0;
@@ -147,8 +154,9 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
     z.npass = (uint32_t)(np < 1 ? 1 : (np > 64 ? 64 : np));
   }
   if (k >= n || (layer && n <= kSmallLayer)) {
-    const uint64_t slots = (z.nt + kTilesPerSlot - 1) / kTilesPerSlot;
-    const uint64_t most = (slots + z.nsub - 1) / z.nsub * kTilesPerSlot * kTile;
+    const uint64_t tps = 1ull << z.tps_log;
+    const uint64_t slots = (z.nt + tps - 1) / tps;
+    const uint64_t most = (slots + z.nsub - 1) / z.nsub * tps * kTile;
     const uint64_t need = ((most < n ? most : n) + 3) / 4 * 4;
     // (candidate slots are 32-bit: where the total would not fit, such a row
     // takes the exact rescan path instead)
@@ -182,6 +190,7 @@ struct Plan {
 struct Layout {
   uint64_t capS;  // whole-node call: candidate slots per counter region
   uint64_t cap;   // whole-node call: candidate slots per node (kSub * capS)
+  uint32_t tps_log;  // whole-node call: log2 of the consecutive tiles sharing a counter
   uint64_t MT;    // whole-node call: tiles per node (slots)
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
@@ -250,6 +259,7 @@ Layout make_node_layout(uint32_t P, uint64_t N, uint64_t k) {
   Layout L = make_layout(Q, 0);
   L.capS = z.capS;
   L.cap = kSub * z.capS;
+  L.tps_log = z.tps_log;
   L.MT = MT;
   L.MG = MG;
   L.MC = z.chunks;
@@ -291,7 +301,7 @@ struct Dev {
   uint32_t k;
   uint32_t rs_lo;   // sample rank of the candidate threshold
   uint32_t rs_mid;  // sample rank of the zeroing threshold
-  uint32_t pad;
+  uint32_t tps_log; // whole-node call: log2 of the consecutive tiles sharing a counter
   uint64_t capS;
   uint64_t cap;
   uint64_t MT;
@@ -341,7 +351,8 @@ struct Row {
   uint32_t schunks; // sample chunks of kSampleChunk elements
   uint32_t pass0;   // per-layer call: first block of the row in the select / count / emit grids
   uint32_t npass;   // blocks of those grids for the row
-  uint32_t pad[2];
+  uint32_t tps_log; // log2 of the consecutive tiles sharing a counter
+  uint32_t pad;
 };
 
 static_assert(sizeof(Row) == kRowBytes, "row table entry size used by the workspace layout");
@@ -368,7 +379,8 @@ __device__ __forceinline__ Row row_of(const Dev& D, uint32_t p) {
     R.schunks = kSampleChunks;
     R.pass0 = 0u;
     R.npass = 0u;
-    R.pad[0] = R.pad[1] = 0u;
+    R.tps_log = D.tps_log;
+    R.pad = 0u;
     return R;
   }
 }
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const float* __restri
       s_cnt[i] = run;
       run += c;
     }
-    const uint32_t sc = (t / kTilesPerSlot) % R.nsub;
+    const uint32_t sc = (t >> R.tps_log) % R.nsub;
     uint32_t off = run ? atomicAdd(&D.sub[((size_t)p * kSub + sc) * 32], run) : 0u;
     const bool stored = (uint64_t)off + run <= R.capS;
     D.tmeta[R.tile0 + t] = ((uint64_t)run << 32) | (stored ? (uint32_t)(sc * R.capS + off) : kNotStored);
@@ -1151,6 +1163,7 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_row
       R.k = (uint32_t)k;
       R.capS = (uint32_t)z.capS;
       R.nsub = z.nsub;
+      R.tps_log = z.tps_log;
       const uint64_t S = (uint64_t)z.schunks * kSampleChunk;
       if (n <= S) {
         R.rs_lo = R.rs_mid = (uint32_t)k;
@@ -1256,6 +1269,7 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
   D.P = P;
   D.capS = L.capS;
   D.cap = L.cap;
+  D.tps_log = L.tps_log;
   D.MT = L.MT;
   D.MG = L.MG;
   D.MC = L.MC;

@@ -44,10 +44,10 @@ def test_topk_random_shapes(dev, P, N, k):
 
 
 def test_topk_ties_take_lowest_indices_rescan_path(dev):
-    P, N, k = 3, 300000, 777
+    P, N, k = 3, 1 << 20, 777
     g = np.full((P, N), 0.5, np.float32)
     g[1, ::3] = -0.5
-    g[2, 240000:] = 0.25  # 240000 ties: still more than the list holds
+    g[2, 840000:] = 0.25  # 840000 ties: still more than the list holds (256 regions of 1287 slots)
     r = np.zeros_like(g)
     _check(g, r, k, dev, expect_path=1)  # far more candidates than the list holds
 
