@@ -69,7 +69,8 @@ __host__ __device__ inline uint32_t tile_phase(uint64_t base) { return (uint32_t
 constexpr int kNW = kStreamThreads / kWave;               // waves per stream block
 constexpr int kSub = 256;                                 // reservation counters per node
 constexpr int kTilesPerSlotLog = 4;
-constexpr int kTilesPerSlot = 1 << kTilesPerSlotLog;      // consecutive tiles sharing a counter
+constexpr int kTilesPerSlot = 1 << kTilesPerSlotLog;      // per-layer call: consecutive tiles sharing a counter
+constexpr int kNodeTilesPerSlotLog = 2;                   // whole-node call: 4 consecutive tiles per counter
 constexpr int kSampleChunks = 1024;
 constexpr int kSampleChunk = 64;
 constexpr int kSample = kSampleChunks * kSampleChunk;     // 65536
@@ -115,10 +116,12 @@ struct RowSize {
 };
 constexpr size_t kRowBytes = 12 * sizeof(uint64_t);
 
-// A whole node: kSub regions with a whole tile of slack each; a node of at
-// most kSub runs of kTilesPerSlot tiles deals its tiles to the counters one by
-// one, so that candidates crowded in one stretch of the node (a layer of
-// larger gradients) spread over all regions. A layer: as many regions as it
+// A whole node: kSub regions with a whole tile of slack each, fed by runs of
+// 4 consecutive tiles dealt to the counters in turn (a node of at most
+// kSub * kTilesPerSlot tiles deals single tiles), so that candidates crowded in
+// one stretch of the node (a layer of larger gradients) spread over many
+// regions: with runs of 16 tiles a 2^20-element stretch at 100 times the
+// scale fed 64 regions, overflowed them and forced the exact rescan. A layer: as many regions as it
 // has runs of kTilesPerSlot tiles (at most kSub), with the slack of its
 // largest possible run. Where every element is a candidate (k =
 // n, or a layer small enough to skip the prediction), a region takes whole
@@ -134,7 +137,7 @@ __host__ __device__ inline RowSize row_size(uint64_t base, uint64_t n, uint64_t 
   z.tps_log = kTilesPerSlotLog;
   if (!layer) {
     z.nsub = kSub;
-    if (z.nt <= (uint64_t)kSub * kTilesPerSlot) z.tps_log = 0;
+    z.tps_log = z.nt <= (uint64_t)kSub * kTilesPerSlot ? 0 : kNodeTilesPerSlotLog;
     z.capS = (want + kSub - 1) / kSub + kTile;
     z.schunks = kSampleChunks;
     z.npass = 0;

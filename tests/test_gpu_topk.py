@@ -82,6 +82,19 @@ def test_topk_normal_data_takes_candidate_path(dev):
     _check(g, r, k, dev, expect_path=0)
 
 
+def test_topk_crowded_stretch_stays_on_candidate_path(dev):
+    """Candidates crowded into one stretch of a long node (2^18 elements at 100
+    times the scale of the other 2^23): the tiles of the stretch feed many
+    counter regions, so the node keeps the candidate path."""
+    rng = np.random.default_rng(14)
+    P, N = 2, 1 << 23
+    k = N // 200
+    g = (rng.standard_normal((P, N)) * 1e-3).astype(np.float32)
+    g[:, 3_000_000:3_000_000 + (1 << 18)] *= 100.0
+    r = np.zeros_like(g)
+    _check(g, r, k, dev, expect_path=0)
+
+
 def test_topk_subnormal_and_signed_zero(dev):
     rng = np.random.default_rng(12)
     P, N, k = 3, 40000, 900
