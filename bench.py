@@ -311,7 +311,7 @@ def main():
         extra["layers_topk_1pct_of_160"] = {"ms": round(t_l, 4), "gelem_per_s": round(P * N / (t_l * 1e-3) / 1e9, 1),
                                             "gb_per_s": round(l_bytes / (t_l * 1e-3) / 1e9, 1),
                                             "frac_hbm_peak": round(l_bytes / (t_l * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                            "rescan_rows": int(l_ws[: 4 * P * 160].view(torch.int32).sum())}
+                                            "rescan_rows": int((l_ws[: 4 * P * 160].view(torch.int32) == 1).sum())}
         del l_idx, l_val, l_ws
 
     # ---- attainable-bandwidth ceiling: plain torch streaming kernels on [P][N]
@@ -379,7 +379,7 @@ def main():
                             "cold_input_gb_per_s": round(b_red_in / (med(red_cold) * 1e-3) / 1e9, 2)},
         "reduce_result": {"nnz": K, "dense": is_dense},
         **extra,
-        "topk_rescan_nodes": int(paths[0].sum()),
+        "topk_rescan_nodes": int((paths[0] == 1).sum()),
         "roofline": {"kernel": "k_stream (error-feedback accumulate + candidate compaction)",
                      "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),

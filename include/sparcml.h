@@ -57,7 +57,8 @@ typedef enum sparcml_status {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* sparcml_status_string(sparcml_status status);
 
-#define SPARCML_TOPK_ROW_MAX (1u << 17) /* longest row sparcml_topk_ef selects in one workgroup */
+#define SPARCML_TOPK_ROW_MAX (1u << 17)        /* longest row selected by one workgroup */
+#define SPARCML_TOPK_ROW_TOTAL_MAX (1ull << 24) /* ... when P * N is at most this */
 
 /* ------------------------------------------------------------------------
  * Error-feedback Top-k
@@ -75,9 +76,10 @@ const char* sparcml_status_string(sparcml_status status);
  *   out_idx[p][0..k) = S in ascending order, out_val[p][j] = a[out_idx[p][j]]
  *   residual_i = a_i, except +0.0 at the positions in S      (in place)
  * Hence residual_new + scatter(out_val) == grad + residual_old exactly.
- * Rows of at most SPARCML_TOPK_ROW_MAX elements are selected by one
- * workgroup per node; longer rows by the predicted-threshold candidate
- * pipeline. Both give the result above.
+ * Rows of at most SPARCML_TOPK_ROW_MAX elements, in calls of at most
+ * SPARCML_TOPK_ROW_TOTAL_MAX elements (P * N), are selected by one workgroup
+ * per node; the others by the predicted-threshold candidate pipeline. Both
+ * give the result above.
  *
  *   P, N      nodes and elements per node; 1 <= P <= 65535, N <= 2^32 - 2^19,
  *             P * ceil((N+31)/1024) < 2^24 (about P*N < 2^34: one workgroup
@@ -93,7 +95,8 @@ const char* sparcml_status_string(sparcml_status status);
  *             first 4*P bytes hold, per node, which path produced the result
  *             (0: predicted-threshold candidates, 1: exact rescan, 2: one
  *             workgroup over the whole row, taken when N <=
- *             SPARCML_TOPK_ROW_MAX), and the next 4*P bytes hold a nonzero
+ *             SPARCML_TOPK_ROW_MAX and P * N <= SPARCML_TOPK_ROW_TOTAL_MAX),
+ *             and the next 4*P bytes hold a nonzero
  *             value for a node whose internal consistency check failed (never
  *             expected).
  * grad and residual must not overlap; neither may overlap the outputs.
@@ -129,7 +132,9 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k,
  *              256-byte aligned; afterwards its first 4*P*nlayers bytes hold
  *              the path of every (node, layer) row (row p*nlayers + l), the
  *              next 4*P*nlayers bytes its consistency flag, as for
- *              sparcml_topk_ef
+ *              sparcml_topk_ef (path 2 when every layer holds at most
+ *              SPARCML_TOPK_ROW_MAX elements and P * N is at most
+ *              SPARCML_TOPK_ROW_TOTAL_MAX: one workgroup per row)
  * sparcml_topk_ef_layers_workspace returns 0 for arguments the call rejects.
  * ---------------------------------------------------------------------- */
 size_t sparcml_topk_ef_layers_workspace(uint32_t P, uint64_t N, uint32_t nlayers,

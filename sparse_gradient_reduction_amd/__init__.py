@@ -197,7 +197,8 @@ def topk_ef_bucketed(grad: torch.Tensor, residual: torch.Tensor, bucket: int, k_
     return out_idx, out_val
 
 
-TOPK_ROW_MAX = 1 << 17  # SPARCML_TOPK_ROW_MAX: rows this short are selected by one workgroup per node
+TOPK_ROW_MAX = 1 << 17  # SPARCML_TOPK_ROW_MAX: rows this short are selected by one workgroup per node ...
+TOPK_ROW_TOTAL_MAX = 1 << 24  # SPARCML_TOPK_ROW_TOTAL_MAX: ... in calls of at most this many elements
 
 
 def topk_ef_paths(workspace: torch.Tensor, P: int) -> torch.Tensor:

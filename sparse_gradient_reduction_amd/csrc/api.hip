@@ -2,6 +2,7 @@
 // The declarations and their contracts are in include/sparcml.h.
 #include "sparcml.h"
 
+#include <algorithm>
 #include <cmath>
 
 #include "kernels.hpp"
@@ -73,7 +74,8 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   if (!grad || !residual || !aligned16(grad) || !aligned16(residual)) return SPARCML_ERR_INVALID_ARG;
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
-  if (N <= SPARCML_TOPK_ROW_MAX)  // short rows: one workgroup per node beats the candidate pipeline's kernel chain
+  // short rows in a small call: one workgroup per node beats the candidate pipeline's kernel chain
+  if (N <= SPARCML_TOPK_ROW_MAX && (uint64_t)P * N <= SPARCML_TOPK_ROW_TOTAL_MAX)
     return from_hip(sparcml::topk_row_launch(P, N, k, grad, residual, out_idx, out_val, static_cast<uint32_t*>(ws),
                                              stream, ev0, ev1));
   return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));
@@ -109,6 +111,12 @@ sparcml_status sparcml_topk_ef_layers(uint32_t P, uint64_t N, uint32_t nlayers, 
   if (!ws || !aligned256(ws) ||
       ws_bytes < sparcml::topk_layers_workspace_bytes(P, N, nlayers, h_layer_offsets, h_k))
     return SPARCML_ERR_WORKSPACE;
+  uint64_t longest = 0;
+  for (uint32_t l = 0; l < nlayers; ++l) longest = std::max(longest, h_layer_offsets[l + 1] - h_layer_offsets[l]);
+  if (longest <= SPARCML_TOPK_ROW_MAX && (uint64_t)P * N <= SPARCML_TOPK_ROW_TOTAL_MAX &&
+      ws_bytes >= sparcml::topk_layer_rows_workspace_bytes(P, nlayers))
+    return from_hip(sparcml::topk_layer_rows_launch(P, N, nlayers, h_layer_offsets, h_k, grad, residual, out_idx,
+                                                    out_val, ws, stream));  // only short layers: one workgroup each
   return from_hip(sparcml::topk_layers_launch(P, N, nlayers, h_layer_offsets, h_k, grad, residual, out_idx, out_val,
                                               ws, stream));
 }

@@ -20,6 +20,15 @@ hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad
                            uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,
                            hipEvent_t ev_start, hipEvent_t ev_stop);
 
+// per-layer call whose layers all hold at most SPARCML_TOPK_ROW_MAX elements:
+// one workgroup per (node, layer) row. Uses the first
+// topk_layer_rows_workspace_bytes(P, nl) bytes of the per-layer workspace:
+// the [P * nl] path and consistency words, then the layer tables.
+size_t topk_layer_rows_workspace_bytes(uint32_t P, uint32_t nl);
+hipError_t topk_layer_rows_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k,
+                                  const float* grad, float* residual, uint32_t* out_idx, float* out_val, void* ws,
+                                  hipStream_t stream);
+
 // ---- per-layer error-feedback Top-k (layers [off[l], off[l+1]) of every node)
 size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);
 uint64_t topk_layers_stream_blocks(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k);

@@ -76,14 +76,19 @@ __device__ __forceinline__ void refine_pass(const float* __restrict__ r, uint64_
   }
 }
 
-__global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ g, float* __restrict__ r,
-                                                          uint64_t N, uint32_t k, uint32_t* __restrict__ out_idx,
-                                                          float* __restrict__ out_val, uint32_t* __restrict__ info) {
+// The whole selection of one row by the calling 1024-thread workgroup: the
+// row's N elements start at base in g and r; its k pairs go to oi / ov with
+// idx_off added to the row-local indices; *path = 2 (this path) and *err =
+// nonzero if the selection did not come to k, as the workspace reports for
+// the candidate pipeline.
+__device__ __forceinline__ void select_row(const float* __restrict__ g, float* __restrict__ r, uint64_t base,
+                                           uint64_t N, uint32_t k, uint32_t* __restrict__ oi, float* __restrict__ ov,
+                                           uint32_t idx_off, uint32_t* path, uint32_t* err) {
   constexpr int NT = kRowThreads;
   __shared__ uint32_t h[kD0];
   __shared__ uint32_t scr[NT / kWave + 3];
   __shared__ uint32_t s_gt[kRowWaves], s_eq[kRowWaves];
-  const uint64_t base = (uint64_t)blockIdx.x * N, end = base + N;
+  const uint64_t end = base + N;
   const uint64_t q0 = (base + 3) >> 2;                                    // first whole group
   const uint64_t nq = (end >> 2) > q0 ? (end >> 2) - q0 : 0;              // whole groups
   const uint64_t head_end = std::min<uint64_t>(4 * q0, end);              // head: [base, head_end)
@@ -132,8 +137,8 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   }
   if (k == 0u) {  // nothing is sent: the residual is a
     if (tid == 0) {
-      info[blockIdx.x] = 2u;
-      info[gridDim.x + blockIdx.x] = 0u;
+      *path = 2u;
+      *err = 0u;
     }
     return;
   }
@@ -240,13 +245,11 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
     all_eq += e;
   }
   if (tid == 0) {
-    info[blockIdx.x] = 2u;
-    info[gridDim.x + blockIdx.x] = all_sel != k ? 1u : 0u;
+    *path = 2u;
+    *err = all_sel != k ? 1u : 0u;
   }
 
   // emit: the stretch in index order (lane, then element within the group)
-  uint32_t* oi = out_idx + (uint64_t)blockIdx.x * k;
-  float* ov = out_val + (uint64_t)blockIdx.x * k;
   // one step: element c of lane l is at e_first + c (own bit c set), in index
   // order (lane, then c)
   auto emit_step = [&](const float (&v)[4], uint32_t own, uint64_t e_first) {
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
       if ((sel >> c) & 1u) {
         const uint64_t e = e_first + c;
         if (p < k) {
-          oi[p] = (uint32_t)(e - base);
+          oi[p] = (uint32_t)(e - base) + idx_off;
           ov[p] = v[c];
         }
         r[e] = 0.0f;
@@ -320,7 +323,82 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restric
   }
 }
 
+// whole-node call: row p of [P][N]; info holds the [P] path and [P]
+// consistency words
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ g, float* __restrict__ r,
+                                                          uint64_t N, uint32_t k, uint32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_val, uint32_t* __restrict__ info) {
+  const uint32_t p = blockIdx.x;
+  select_row(g, r, (uint64_t)p * N, N, k, out_idx + (uint64_t)p * k, out_val + (uint64_t)p * k, 0u, info + p,
+             info + gridDim.x + p);
+}
+
+// per-layer call: row p * nl + l is layer l ([loff[l], loff[l+1])) of node p,
+// whose lk[l] pairs go at p * K + lkoff[l]; info holds the [P * nl] path and
+// [P * nl] consistency words
+__global__ __launch_bounds__(kRowThreads) void k_topk_layer_rows(const float* __restrict__ g, float* __restrict__ r,
+                                                                 uint64_t N, uint32_t nl, const uint64_t* loff,
+                                                                 const uint64_t* lk, const uint64_t* lkoff, uint64_t K,
+                                                                 uint32_t* __restrict__ out_idx,
+                                                                 float* __restrict__ out_val,
+                                                                 uint32_t* __restrict__ info) {
+  const uint32_t row = blockIdx.x, p = row / nl, l = row % nl;
+  const uint64_t o = loff[l];
+  const uint64_t out = (uint64_t)p * K + lkoff[l];
+  select_row(g, r, (uint64_t)p * N + o, loff[l + 1] - o, (uint32_t)lk[l], out_idx + out, out_val + out, (uint32_t)o,
+             info + row, info + gridDim.x + row);
+}
+
+// layer tables copied to the device, kRowLayersPerCopy layers per launch
+// (kernel arguments): loff[first .. first+count], lk and lkoff[first ..)
+constexpr uint32_t kRowLayersPerCopy = 64;
+struct RowLayerChunk {
+  uint64_t off[kRowLayersPerCopy + 1];
+  uint64_t k[kRowLayersPerCopy];
+  uint64_t koff[kRowLayersPerCopy];
+};
+
+__global__ void k_row_layers_in(uint64_t* loff, uint64_t* lk, uint64_t* lkoff, uint32_t first, uint32_t count,
+                                RowLayerChunk in) {
+  for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) {
+    loff[first + i] = in.off[i];
+    lk[first + i] = in.k[i];
+    lkoff[first + i] = in.koff[i];
+  }
+  if (threadIdx.x == 0) loff[first + count] = in.off[count];
+}
+
 }  // namespace
+
+size_t topk_layer_rows_workspace_bytes(uint32_t P, uint32_t nl) {
+  return (8ull * P * nl + 255) / 256 * 256 + 24ull * (nl + 1);
+}
+
+hipError_t topk_layer_rows_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k,
+                                  const float* grad, float* residual, uint32_t* out_idx, float* out_val, void* ws,
+                                  hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  uint32_t* info = reinterpret_cast<uint32_t*>(w);  // [P * nl] path words, then [P * nl] consistency words
+  uint64_t* loff = reinterpret_cast<uint64_t*>(w + (8ull * P * nl + 255) / 256 * 256);
+  uint64_t* lk = loff + nl + 1;
+  uint64_t* lkoff = lk + nl;
+  uint64_t koff = 0;
+  for (uint32_t first = 0; first < nl; first += kRowLayersPerCopy) {
+    RowLayerChunk in{};
+    const uint32_t count = std::min<uint32_t>(kRowLayersPerCopy, nl - first);
+    for (uint32_t i = 0; i < count; ++i) {
+      in.off[i] = off[first + i];
+      in.k[i] = k[first + i];
+      in.koff[i] = koff;
+      koff += k[first + i];
+    }
+    in.off[count] = off[first + count];
+    hipLaunchKernelGGL(k_row_layers_in, dim3(1), dim3(64), 0, stream, loff, lk, lkoff, first, count, in);
+  }
+  hipLaunchKernelGGL(k_topk_layer_rows, dim3(P * nl), dim3(kRowThreads), 0, stream, grad, residual, N, nl, loff, lk,
+                     lkoff, koff, out_idx, out_val, info);
+  return hipGetLastError();
+}
 
 hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
                            uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,

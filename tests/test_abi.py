@@ -191,6 +191,8 @@ def test_row_limit_matches_header():
     text = open(os.path.join(ROOT, "include", "sparcml.h")).read()
     m = re.search(r"#define SPARCML_TOPK_ROW_MAX \(1u << (\d+)\)", text)
     assert m and sg.TOPK_ROW_MAX == 1 << int(m.group(1))
+    m = re.search(r"#define SPARCML_TOPK_ROW_TOTAL_MAX \(1ull << (\d+)\)", text)
+    assert m and sg.TOPK_ROW_TOTAL_MAX == 1 << int(m.group(1))
 
 
 def test_dense_threshold_reading():

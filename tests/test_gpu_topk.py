@@ -37,7 +37,7 @@ def test_topk_random_shapes(dev, P, N, k):
     r = (rng.standard_normal((P, N)) * 0.5).astype(np.float32)
     print(f"topk P={P} N={N} k={k}", flush=True)
     paths = _check(g, r, k, dev)
-    if N <= sg.TOPK_ROW_MAX:  # short rows: one workgroup per node
+    if N <= sg.TOPK_ROW_MAX and P * N <= sg.TOPK_ROW_TOTAL_MAX:  # short rows: one workgroup per node
         assert np.all(paths[0] == 2), paths[0]
     elif k > 0:
         assert np.all(paths[0] <= 1), paths[0]

@@ -34,7 +34,11 @@ def _check(g, r, off, ks, dev, expect_rescan_rows=None):
     assert_bits_equal(grr, orr, "residual")
     assert np.all(paths[1] == 0), "consistency flag"
     if expect_rescan_rows is not None:
-        assert set(np.nonzero(paths[0])[0].tolist()) == set(expect_rescan_rows), paths[0]
+        assert set(np.nonzero(paths[0] == 1)[0].tolist()) == set(expect_rescan_rows), paths[0]
+    short = np.max(np.diff(np.asarray(off, np.int64))) <= sg.TOPK_ROW_MAX
+    if short and g.size <= sg.TOPK_ROW_TOTAL_MAX:  # only short layers, small call: one workgroup per row
+        assert np.all(paths[0] == 2), paths[0]
+    return paths
 
 
 def _random_layers(rng, N, nl):
@@ -56,6 +60,25 @@ def test_layers_random(dev, P, N, nl):
     r = (rng.standard_normal((P, N)) * 0.5).astype(np.float32)
     print(f"layers P={P} N={N} nl={nl} K={int(ks.sum())}", flush=True)
     _check(g, r, off, ks, dev)
+
+
+@pytest.mark.parametrize("P,N,nl", [(2, 100, 3), (3, 5003, 9), (4, 70001, 17), (7, 20000, 200)])
+def test_layers_random_with_a_long_layer(dev, P, N, nl):
+    """The random short layers of test_layers_random followed by one layer
+    longer than the one-workgroup limit, which sends every row through the
+    candidate pipeline."""
+    rng = np.random.default_rng(P * 1013 + N + nl)
+    long = sg.TOPK_ROW_MAX + 5
+    off = np.concatenate([_random_layers(rng, N, nl), [N + long]]).astype(np.uint64)
+    sizes = np.diff(off.astype(np.int64))
+    ks = np.array([0 if s == 0 else rng.integers(0, s + 1) for s in sizes], np.uint64)
+    ks[-1] = long // 50
+    N += long
+    g = rng.standard_normal((P, N)).astype(np.float32)
+    r = (rng.standard_normal((P, N)) * 0.5).astype(np.float32)
+    print(f"layers + long layer P={P} N={N} nl={nl + 1}", flush=True)
+    paths = _check(g, r, off, ks, dev)
+    assert np.all(paths[0] <= 1), paths[0]
 
 
 def test_layers_prediction_size_classes(dev):
