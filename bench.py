@@ -511,6 +511,22 @@ def other_configs(sg, W, dev, skip_wid):
                              workspace=wr)
 
         t_graph = graph_ms(one_step)  # the residual keeps accumulating: EF steps on the first gradient
+        # the same rows as 20 layers (sizes log-uniform), the same fraction kept per layer
+        lo = W.layer_offsets(N, 20)
+        lks = W.layer_ks(lo, k, N)
+        wl = torch.empty(sg.topk_ef_layers_workspace_bytes(P, N, lo, lks), dtype=torch.uint8, device=dev)
+        li = torch.empty((P, int(lks.sum())), dtype=torch.int32, device=dev)
+        lv = torch.empty((P, int(lks.sum())), dtype=torch.float32, device=dev)
+        layers_call = lambda: sg.topk_ef_layers(grads[0], r, lo, lks, out_idx=li, out_val=lv, workspace=wl)
+        layers_call()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in ev:
+            a.record()
+            layers_call()
+            b.record()
+        torch.cuda.synchronize()
+        t_layers = med([a.elapsed_time(b) for a, b in ev])
+        del wl, li, lv
         b_topk = 12 * P * N + 8 * P * k
         b_in = 8 * P * k
         b_out = [4 * N if s["dense"] else 8 * s["nnz"] for s in per_step]
@@ -520,6 +536,7 @@ def other_configs(sg, W, dev, skip_wid):
                        "reduce_input_gb_per_s": round(b_in / (tr * 1e-3) / 1e9, 1),
                        "reduce_frac_hbm_peak": round((b_in + med(b_out)) / (tr * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "step_graph_ms": round(t_graph, 4),
+                       "topk_20_layers_ms": round(t_layers, 4),
                        "per_step": per_step}
         del grads, r, ws, idx, val, ri, rv, rr, wr
         torch.cuda.synchronize()
