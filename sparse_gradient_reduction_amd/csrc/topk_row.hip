@@ -29,10 +29,17 @@
 // group (the head) and after the last (the tail) are handled one per lane,
 // the head by the first wave before its stretch, the tail by the last wave
 // after its stretch.
+//
+// Rows of at most kRowRegMax elements (sixteen waves x sixteen steps of 64
+// groups) are also held in registers: every pass uses the waves' stretches,
+// each lane keeping a of its groups in VGPRs from the accumulate pass on, so
+// that the refine, count and emit passes read no memory but the edges. Such a
+// row moves 12 bytes per element (g and r read, a written) instead of 28.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace sparcml {
 namespace {
@@ -41,6 +48,8 @@ constexpr int kRowThreads = 1024;
 constexpr int kRowWaves = kRowThreads / kWave;    // 16
 constexpr int kD0 = 2048, kD1 = 1024, kD2 = 1024;  // key digits: 11 + 10 + 10 bits
 constexpr int kUnroll = 4;                         // groups per thread in flight
+constexpr int kRegSteps = 16;                      // register-resident steps of 64 groups per wave
+constexpr uint64_t kRowRegMax = (uint64_t)kRowWaves * kRegSteps * kWave * 4;  // 65536 elements
 
 // Group j (of nq) of the row starting at group q0, as four values; `own` is
 // 0xF for a group of the row and 0 for a position past its end (which reads
@@ -81,6 +90,7 @@ __device__ __forceinline__ void refine_pass(const float* __restrict__ r, uint64_
 // idx_off added to the row-local indices; *path = 2 (this path) and *err =
 // nonzero if the selection did not come to k, as the workspace reports for
 // the candidate pipeline.
+template <bool kReg>
 __device__ __forceinline__ void select_row(const float* __restrict__ g, float* __restrict__ r, uint64_t base,
                                            uint64_t N, uint32_t k, uint32_t* __restrict__ oi, float* __restrict__ ov,
                                            uint32_t idx_off, uint32_t* path, uint32_t* err) {
@@ -99,10 +109,59 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
   const bool edge = (tid < 4 && tid < nh) || (tid >= 4 && tid < 4 + ntl);
   const uint64_t e_edge = tid < 4 ? base + tid : tail0 + (tid - 4);
   for (uint32_t i = tid; i < kD0; i += NT) h[i] = 0u;
+  // each wave's stretch of whole steps of 64 groups (count and emit, and every
+  // pass of a register-resident row)
+  const uint32_t wid = tid / kWave, lane = lane_id();
+  const uint64_t steps = (nq + kWave - 1) / kWave;
+  const uint64_t per_wave = (steps + kRowWaves - 1) / kRowWaves;
+  const uint64_t s_lo = std::min<uint64_t>((uint64_t)wid * per_wave, steps) * kWave;
+  const uint64_t s_hi = std::min<uint64_t>((uint64_t)(wid + 1) * per_wave, steps) * kWave;
+  const int w_steps = (int)((s_hi - s_lo) / kWave);  // steps of this wave's stretch
+  float a_reg[kReg ? kRegSteps : 1][4];              // register-resident a, step i of the stretch
+  uint32_t own_reg = 0u;                             // bit i: lane's group of step i is in the row
+  if (kReg && per_wave > (uint64_t)kRegSteps) {      // longer than the launch allows: report, select nothing
+    if (tid == 0) {
+      *path = 2u;
+      *err = 1u;
+    }
+    return;
+  }
   __syncthreads();
 
   // accumulate: a = g + r written over r; histogram of the top 11 key bits
-  for (uint64_t j0 = 0; j0 < nq; j0 += (uint64_t)NT * kUnroll) {
+  if constexpr (kReg) {
+#pragma unroll
+    for (int i0 = 0; i0 < kRegSteps; i0 += kUnroll) {
+      if (i0 >= w_steps) continue;  // wave-uniform; the trip count stays constant so a_reg stays in VGPRs
+      float gv[kUnroll][4];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t j = s_lo + (uint64_t)(i0 + u) * kWave + lane;
+        uint32_t own;
+        load_group(g, q0, nq, j < s_hi ? j : nq, gv[u], own);
+        load_group(r, q0, nq, j < s_hi ? j : nq, a_reg[i0 + u], own);
+        own_reg |= (own ? 1u : 0u) << (i0 + u);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a_reg[i0 + u][c] = gv[u][c] + a_reg[i0 + u][c];
+        if ((own_reg >> (i0 + u)) & 1u) {
+          f32x4 t;
+          t.x = a_reg[i0 + u][0];
+          t.y = a_reg[i0 + u][1];
+          t.z = a_reg[i0 + u][2];
+          t.w = a_reg[i0 + u][3];
+          reinterpret_cast<f32x4*>(r)[q0 + s_lo + (uint64_t)(i0 + u) * kWave + lane] = t;
+          if (k != 0u) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) atomicAdd(&h[mag_key(a_reg[i0 + u][c]) >> 20], 1u);
+          }
+        }
+      }
+    }
+  }
+  for (uint64_t j0 = 0; !kReg && j0 < nq; j0 += (uint64_t)NT * kUnroll) {
     float gv[kUnroll][4], rv[kUnroll][4];
     uint32_t own[kUnroll];
 #pragma unroll
@@ -144,13 +203,31 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
   }
   __syncthreads();
 
+  // histogram pass over the register-resident a: digit (key >> shift) & (NB - 1)
+  // of the keys whose bits above shift + 10 equal prefix
+  auto refine_regs = [&](uint32_t prefix, int shift, uint32_t mask) {
+#pragma unroll
+    for (int i = 0; i < kRegSteps; ++i) {
+      if (kReg && i < w_steps && ((own_reg >> i) & 1u)) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t key = mag_key(a_reg[i][c]);
+          if ((key >> (shift + 10)) == prefix) atomicAdd(&h[(key >> shift) & mask], 1u);
+        }
+      }
+    }
+  };
+
   // refine: T = the k-th largest key, m = keys equal to T that are taken
   uint32_t d0, d1, d2, above;
   block_find_suffix<NT, kD0>(h, k, scr, d0, above);
   uint32_t rank = k - above;
   for (uint32_t i = tid; i < kD1; i += NT) h[i] = 0u;
   __syncthreads();
-  refine_pass<kD1>(r, q0, nq, h, d0, 10);
+  if constexpr (kReg)
+    refine_regs(d0, 10, kD1 - 1);
+  else
+    refine_pass<kD1>(r, q0, nq, h, d0, 10);
   if (edge) {
     const uint32_t key = mag_key(r[e_edge]);
     if ((key >> 20) == d0) atomicAdd(&h[(key >> 10) & (kD1 - 1)], 1u);
@@ -161,7 +238,10 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
   const uint32_t prefix = (d0 << 10) | d1;  // key >> 10
   for (uint32_t i = tid; i < kD2; i += NT) h[i] = 0u;
   __syncthreads();
-  refine_pass<kD2>(r, q0, nq, h, prefix, 0);
+  if constexpr (kReg)
+    refine_regs(prefix, 0, kD2 - 1);
+  else
+    refine_pass<kD2>(r, q0, nq, h, prefix, 0);
   if (edge) {
     const uint32_t key = mag_key(r[e_edge]);
     if ((key >> 10) == prefix) atomicAdd(&h[key & (kD2 - 1)], 1u);
@@ -171,27 +251,16 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
   const uint32_t T = (prefix << 10) | d2;
   const uint32_t m = rank - above;
 
-  // count: keys > T and == T over each wave's stretch of whole steps of 64 groups
-  const uint32_t wid = tid / kWave, lane = lane_id();
-  const uint64_t steps = (nq + kWave - 1) / kWave;
-  const uint64_t per_wave = (steps + kRowWaves - 1) / kRowWaves;
-  const uint64_t s_lo = std::min<uint64_t>((uint64_t)wid * per_wave, steps) * kWave;
-  const uint64_t s_hi = std::min<uint64_t>((uint64_t)(wid + 1) * per_wave, steps) * kWave;
+  // Keys equal to T in the row: bin d2 of the last histogram, whose bins are
+  // whole keys. When all of them are taken (the usual case of a unique T) the
+  // selection is simply key >= T and no tie rank is needed.
+  const bool all_ties = h[d2] == m;
+
   auto load_steps = [&](uint64_t s0, float (&v)[kUnroll][4], uint32_t (&own)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint64_t j = s0 + (uint64_t)u * kWave + lane;
       load_group(r, q0, nq, j < s_hi ? j : nq, v[u], own[u]);
-    }
-  };
-  uint32_t gt = 0, eq = 0;  // wave-uniform
-  auto count_step = [&](const float (&v)[4], uint32_t own) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool in = (own >> c) & 1u;
-      const uint32_t key = mag_key(v[c]);
-      gt += popc64(ballot(in && key > T));
-      eq += popc64(ballot(in && key == T));
     }
   };
   // the head (first wave) or the tail (last wave) as one step, one element per lane
@@ -206,136 +275,199 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
     }
   };
   const bool first_wave = wid == 0, last_wave = wid == (uint32_t)kRowWaves - 1;
-  if (first_wave && nh != 0u) {
-    float v[4];
-    uint32_t own;
-    uint64_t e;
-    edge_step(true, v, own, e);
-    count_step(v, own);
-  }
-  for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
-    float v[kUnroll][4];
-    uint32_t own[kUnroll];
-    load_steps(s0, v, own);
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) count_step(v[u], own[u]);
-  }
-  if (last_wave && ntl != 0u) {
-    float v[4];
-    uint32_t own;
-    uint64_t e;
-    edge_step(false, v, own, e);
-    count_step(v, own);
-  }
-  if (lane == 0) {
-    s_gt[wid] = gt;
-    s_eq[wid] = eq;
-  }
-  __syncthreads();
-  uint32_t eq_run = 0, pos = 0;  // ties and selected pairs before this wave's stretch
-  uint32_t all_eq = 0, all_sel = 0;
-  for (uint32_t w = 0; w < (uint32_t)kRowWaves; ++w) {
-    const uint32_t e = s_eq[w];
-    const uint32_t take = all_eq >= m ? 0u : std::min(m - all_eq, e);
-    if (w == wid) {
-      eq_run = all_eq;
-      pos = all_sel;
-    }
-    all_sel += s_gt[w] + take;
-    all_eq += e;
-  }
-  if (tid == 0) {
-    *path = 2u;
-    *err = all_sel != k ? 1u : 0u;
-  }
 
-  // emit: the stretch in index order (lane, then element within the group)
-  // one step: element c of lane l is at e_first + c (own bit c set), in index
-  // order (lane, then c)
-  auto emit_step = [&](const float (&v)[4], uint32_t own, uint64_t e_first) {
-    uint32_t is_eq = 0u, is_gt = 0u;
+  // count, then emit; kAll: every key equal to T is taken
+  auto finish = [&](auto take_all) {
+    constexpr bool kAll = decltype(take_all)::value;
+    // count: over each wave's stretch, the keys >= T (kAll), else the keys > T and == T
+    uint32_t gt = 0, eq = 0;  // wave-uniform
+    auto count_step = [&](const float (&v)[4], uint32_t own) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const bool in = (own >> c) & 1u;
-      const uint32_t key = mag_key(v[c]);
-      if (in && key == T) is_eq |= 1u << c;
-      if (in && key > T) is_gt |= 1u << c;
-    }
-    // tie ranks in index order: ties before this step, in lower lanes, and
-    // earlier in this lane
-    uint32_t eq_below = 0, step_eq = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint64_t em = ballot((is_eq >> c) & 1u);
-      eq_below += lanes_below(em);
-      step_eq += popc64(em);
-    }
-    uint32_t rank_t = eq_run + eq_below;
-    uint32_t sel = is_gt;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if ((is_eq >> c) & 1u) {
-        if (rank_t < m) sel |= 1u << c;
-        ++rank_t;
-      }
-    eq_run += step_eq;
-    uint32_t sel_below = 0, step_sel = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint64_t sm = ballot((sel >> c) & 1u);
-      sel_below += lanes_below(sm);
-      step_sel += popc64(sm);
-    }
-    uint32_t p = pos + sel_below;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if ((sel >> c) & 1u) {
-        const uint64_t e = e_first + c;
-        if (p < k) {
-          oi[p] = (uint32_t)(e - base) + idx_off;
-          ov[p] = v[c];
+      for (int c = 0; c < 4; ++c) {
+        const bool in = (own >> c) & 1u;
+        const uint32_t key = mag_key(v[c]);
+        if constexpr (kAll) {
+          gt += popc64(ballot(in && key >= T));
+        } else {
+          gt += popc64(ballot(in && key > T));
+          eq += popc64(ballot(in && key == T));
         }
-        r[e] = 0.0f;
-        ++p;
       }
-    pos += step_sel;
-  };
-  if (first_wave && nh != 0u) {
-    float v[4];
-    uint32_t own;
-    uint64_t e;
-    edge_step(true, v, own, e);
-    emit_step(v, own, e);
-  }
-  for (uint64_t s0 = s_lo; s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
-    float v[kUnroll][4];
-    uint32_t own[kUnroll];
-    load_steps(s0, v, own);
+    };
+    if (first_wave && nh != 0u) {
+      float v[4];
+      uint32_t own;
+      uint64_t e;
+      edge_step(true, v, own, e);
+      count_step(v, own);
+    }
+    if constexpr (kReg) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) emit_step(v[u], own[u], 4 * (q0 + s0 + (uint64_t)u * kWave + lane));
-  }
-  if (last_wave && ntl != 0u) {
-    float v[4];
-    uint32_t own;
-    uint64_t e;
-    edge_step(false, v, own, e);
-    emit_step(v, own, e);
-  }
-}
+      for (int i = 0; i < kRegSteps; ++i) {
+        if (i >= w_steps) continue;
+        count_step(a_reg[i], ((own_reg >> i) & 1u) ? 0xFu : 0u);
+      }
+    }
+    for (uint64_t s0 = s_lo; !kReg && s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
+      float v[kUnroll][4];
+      uint32_t own[kUnroll];
+      load_steps(s0, v, own);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) count_step(v[u], own[u]);
+    }
+    if (last_wave && ntl != 0u) {
+      float v[4];
+      uint32_t own;
+      uint64_t e;
+      edge_step(false, v, own, e);
+      count_step(v, own);
+    }
+    if (lane == 0) {
+      s_gt[wid] = gt;
+      s_eq[wid] = eq;
+    }
+    __syncthreads();
+    uint32_t eq_run = 0, pos = 0;  // ties and selected pairs before this wave's stretch
+    uint32_t all_eq = 0, all_sel = 0;
+    for (uint32_t w = 0; w < (uint32_t)kRowWaves; ++w) {
+      const uint32_t e = s_eq[w];
+      const uint32_t take = all_eq >= m ? 0u : std::min(m - all_eq, e);
+      if (w == wid) {
+        eq_run = all_eq;
+        pos = all_sel;
+      }
+      all_sel += s_gt[w] + take;
+      all_eq += e;
+    }
+    if (tid == 0) {
+      *path = 2u;
+      *err = all_sel != k ? 1u : 0u;
+    }
 
+    // emit: the stretch in index order (lane, then element within the group);
+    // element c of lane l is at e_first + c (own bit c set)
+    auto emit_step = [&](const float (&v)[4], uint32_t own, uint64_t e_first) {
+      uint32_t sel = 0u;
+      if constexpr (kAll) {
+        uint64_t sm[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool s = ((own >> c) & 1u) && mag_key(v[c]) >= T;
+          sel |= s ? 1u << c : 0u;
+          sm[c] = ballot(s);
+        }
+        if ((sm[0] | sm[1] | sm[2] | sm[3]) == 0u) return;  // nothing selected in this step
+        uint32_t p = pos + lanes_below(sm[0]) + lanes_below(sm[1]) + lanes_below(sm[2]) + lanes_below(sm[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if ((sel >> c) & 1u) {
+            const uint64_t e = e_first + c;
+            if (p < k) {
+              oi[p] = (uint32_t)(e - base) + idx_off;
+              ov[p] = v[c];
+            }
+            r[e] = 0.0f;
+            ++p;
+          }
+        pos += popc64(sm[0]) + popc64(sm[1]) + popc64(sm[2]) + popc64(sm[3]);
+        return;
+      }
+      uint32_t is_eq = 0u, is_gt = 0u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bool in = (own >> c) & 1u;
+        const uint32_t key = mag_key(v[c]);
+        if (in && key == T) is_eq |= 1u << c;
+        if (in && key > T) is_gt |= 1u << c;
+      }
+      // tie ranks in index order: ties before this step, in lower lanes, and
+      // earlier in this lane
+      uint32_t eq_below = 0, step_eq = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t em = ballot((is_eq >> c) & 1u);
+        eq_below += lanes_below(em);
+        step_eq += popc64(em);
+      }
+      uint32_t rank_t = eq_run + eq_below;
+      sel = is_gt;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((is_eq >> c) & 1u) {
+          if (rank_t < m) sel |= 1u << c;
+          ++rank_t;
+        }
+      eq_run += step_eq;
+      uint32_t sel_below = 0, step_sel = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t sm = ballot((sel >> c) & 1u);
+        sel_below += lanes_below(sm);
+        step_sel += popc64(sm);
+      }
+      uint32_t p = pos + sel_below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if ((sel >> c) & 1u) {
+          const uint64_t e = e_first + c;
+          if (p < k) {
+            oi[p] = (uint32_t)(e - base) + idx_off;
+            ov[p] = v[c];
+          }
+          r[e] = 0.0f;
+          ++p;
+        }
+      pos += step_sel;
+    };
+    if (first_wave && nh != 0u) {
+      float v[4];
+      uint32_t own;
+      uint64_t e;
+      edge_step(true, v, own, e);
+      emit_step(v, own, e);
+    }
+    if constexpr (kReg) {
+#pragma unroll
+      for (int i = 0; i < kRegSteps; ++i) {
+        if (i >= w_steps) continue;
+        emit_step(a_reg[i], ((own_reg >> i) & 1u) ? 0xFu : 0u, 4 * (q0 + s_lo + (uint64_t)i * kWave + lane));
+      }
+    }
+    for (uint64_t s0 = s_lo; !kReg && s0 < s_hi; s0 += (uint64_t)kWave * kUnroll) {
+      float v[kUnroll][4];
+      uint32_t own[kUnroll];
+      load_steps(s0, v, own);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) emit_step(v[u], own[u], 4 * (q0 + s0 + (uint64_t)u * kWave + lane));
+    }
+    if (last_wave && ntl != 0u) {
+      float v[4];
+      uint32_t own;
+      uint64_t e;
+      edge_step(false, v, own, e);
+      emit_step(v, own, e);
+    }
+  };
+  if (all_ties)
+    finish(std::true_type{});
+  else
+    finish(std::false_type{});
+}
 // whole-node call: row p of [P][N]; info holds the [P] path and [P]
 // consistency words
+template <bool kReg>
 __global__ __launch_bounds__(kRowThreads) void k_topk_row(const float* __restrict__ g, float* __restrict__ r,
                                                           uint64_t N, uint32_t k, uint32_t* __restrict__ out_idx,
                                                           float* __restrict__ out_val, uint32_t* __restrict__ info) {
   const uint32_t p = blockIdx.x;
-  select_row(g, r, (uint64_t)p * N, N, k, out_idx + (uint64_t)p * k, out_val + (uint64_t)p * k, 0u, info + p,
+  select_row<kReg>(g, r, (uint64_t)p * N, N, k, out_idx + (uint64_t)p * k, out_val + (uint64_t)p * k, 0u, info + p,
              info + gridDim.x + p);
 }
 
 // per-layer call: row p * nl + l is layer l ([loff[l], loff[l+1])) of node p,
 // whose lk[l] pairs go at p * K + lkoff[l]; info holds the [P * nl] path and
 // [P * nl] consistency words
+template <bool kReg>
 __global__ __launch_bounds__(kRowThreads) void k_topk_layer_rows(const float* __restrict__ g, float* __restrict__ r,
                                                                  uint64_t N, uint32_t nl, const uint64_t* loff,
                                                                  const uint64_t* lk, const uint64_t* lkoff, uint64_t K,
@@ -345,7 +477,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_layer_rows(const float* __
   const uint32_t row = blockIdx.x, p = row / nl, l = row % nl;
   const uint64_t o = loff[l];
   const uint64_t out = (uint64_t)p * K + lkoff[l];
-  select_row(g, r, (uint64_t)p * N + o, loff[l + 1] - o, (uint32_t)lk[l], out_idx + out, out_val + out, (uint32_t)o,
+  select_row<kReg>(g, r, (uint64_t)p * N + o, loff[l + 1] - o, (uint32_t)lk[l], out_idx + out, out_val + out, (uint32_t)o,
              info + row, info + gridDim.x + row);
 }
 
@@ -395,8 +527,14 @@ hipError_t topk_layer_rows_launch(uint32_t P, uint64_t N, uint32_t nl, const uin
     in.off[count] = off[first + count];
     hipLaunchKernelGGL(k_row_layers_in, dim3(1), dim3(64), 0, stream, loff, lk, lkoff, first, count, in);
   }
-  hipLaunchKernelGGL(k_topk_layer_rows, dim3(P * nl), dim3(kRowThreads), 0, stream, grad, residual, N, nl, loff, lk,
-                     lkoff, koff, out_idx, out_val, info);
+  uint64_t longest = 0;
+  for (uint32_t l = 0; l < nl; ++l) longest = std::max(longest, off[l + 1] - off[l]);
+  if (longest <= kRowRegMax)
+    hipLaunchKernelGGL(k_topk_layer_rows<true>, dim3(P * nl), dim3(kRowThreads), 0, stream, grad, residual, N, nl,
+                       loff, lk, lkoff, koff, out_idx, out_val, info);
+  else
+    hipLaunchKernelGGL(k_topk_layer_rows<false>, dim3(P * nl), dim3(kRowThreads), 0, stream, grad, residual, N, nl,
+                       loff, lk, lkoff, koff, out_idx, out_val, info);
   return hipGetLastError();
 }
 
@@ -412,12 +550,18 @@ hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad
     float* ov = out_val;
     uint32_t* in = info;
     void* args[] = {&ga, &ra, &n, &kk, &oi, &ov, &in};
-    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_topk_row), dim3(P), dim3(kRowThreads),
+    const void* fn = N <= kRowRegMax ? reinterpret_cast<const void*>(&k_topk_row<true>)
+                                     : reinterpret_cast<const void*>(&k_topk_row<false>);
+    const hipError_t e = hipExtLaunchKernel(fn, dim3(P), dim3(kRowThreads),
                                             args, 0, stream, ev_start, ev_stop, 0);
     return e != hipSuccess ? e : hipGetLastError();
   }
-  hipLaunchKernelGGL(k_topk_row, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k, out_idx,
-                     out_val, info);
+  if (N <= kRowRegMax)
+    hipLaunchKernelGGL(k_topk_row<true>, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k,
+                       out_idx, out_val, info);
+  else
+    hipLaunchKernelGGL(k_topk_row<false>, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k,
+                       out_idx, out_val, info);
   return hipGetLastError();
 }
 

@@ -60,6 +60,24 @@ def test_topk_ties_mixed_with_distinct(dev):
     _check(g, r, k, dev)
 
 
+@pytest.mark.parametrize("N", [65536, 65533, 70001])
+@pytest.mark.parametrize("cut", [0, -5])
+def test_topk_row_ties_at_the_boundary(dev, N, cut):
+    """One-workgroup rows with 41 value levels, every node a permutation of the
+    same multiset: k ends exactly at a level (every key equal to the k-th
+    largest is taken, many of them) or five short of it (only the lowest
+    indices among them). Rows of 65536 or fewer elements are held in
+    registers; 65533 leaves every row but the first unaligned."""
+    rng = np.random.default_rng(N + 17)
+    P = 4
+    base = (rng.integers(-20, 21, size=N) * 0.125).astype(np.float32)
+    g = np.stack([rng.permutation(base) for _ in range(P)])
+    r = np.zeros_like(g)
+    k = int(np.count_nonzero(np.abs(base) >= 1.5)) + cut
+    print(f"topk row ties N={N} k={k}", flush=True)
+    _check(g, r, k, dev, expect_path=2)
+
+
 def test_topk_sample_underestimate_takes_rescan_path(dev):
     """Large values placed exactly on the sampled chunks make the predicted
     threshold too high: fewer than k candidates, exact rescan."""

@@ -112,6 +112,20 @@ def test_layers_one_layer_equals_whole_vector(dev):
     assert_bits_equal(lr, rd.cpu().numpy(), "residual")
 
 
+def test_layers_short_rows_with_ties(dev):
+    """Short layers of 41 value levels: ties at the k-th largest key in most
+    rows, partly or wholly taken, on the one-workgroup row path."""
+    rng = np.random.default_rng(11)
+    P, N = 3, 200003
+    off = np.array([0, 5, 65541, 65542, 130000, 170001, N], np.uint64)
+    sizes = np.diff(off.astype(np.int64))
+    ks = np.array([2, 3000, 1, 65536 // 8, 4000, 555], np.uint64)
+    assert np.all(ks <= sizes)
+    g = (rng.integers(-20, 21, size=(P, N)) * 0.125).astype(np.float32)
+    r = np.zeros_like(g)
+    _check(g, r, off, ks, dev)
+
+
 def test_layers_rescan_row(dev):
     """A large layer of equal values far exceeds its candidate capacity: that
     row alone takes the exact rescan path."""
