@@ -49,6 +49,7 @@ constexpr int kRowWaves = kRowThreads / kWave;    // 16
 constexpr int kD0 = 2048, kD1 = 1024, kD2 = 1024;  // key digits: 11 + 10 + 10 bits
 constexpr int kUnroll = 4;                         // groups per thread in flight
 constexpr int kRegSteps = 16;                      // register-resident steps of 64 groups per wave
+constexpr int kRegChunk = 4;                       // steps loaded together into the registers
 constexpr uint64_t kRowRegMax = (uint64_t)kRowWaves * kRegSteps * kWave * 4;  // 65536 elements
 
 // Group j (of nq) of the row starting at group q0, as four values; `own` is
@@ -131,11 +132,11 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
   // accumulate: a = g + r written over r; histogram of the top 11 key bits
   if constexpr (kReg) {
 #pragma unroll
-    for (int i0 = 0; i0 < kRegSteps; i0 += kUnroll) {
+    for (int i0 = 0; i0 < kRegSteps; i0 += kRegChunk) {
       if (i0 >= w_steps) continue;  // wave-uniform; the trip count stays constant so a_reg stays in VGPRs
-      float gv[kUnroll][4];
+      float gv[kRegChunk][4];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kRegChunk; ++u) {
         const uint64_t j = s_lo + (uint64_t)(i0 + u) * kWave + lane;
         uint32_t own;
         load_group(g, q0, nq, j < s_hi ? j : nq, gv[u], own);
@@ -143,7 +144,7 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
         own_reg |= (own ? 1u : 0u) << (i0 + u);
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kRegChunk; ++u) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) a_reg[i0 + u][c] = gv[u][c] + a_reg[i0 + u][c];
         if ((own_reg >> (i0 + u)) & 1u) {
@@ -327,18 +328,16 @@ __device__ __forceinline__ void select_row(const float* __restrict__ g, float* _
       s_eq[wid] = eq;
     }
     __syncthreads();
-    uint32_t eq_run = 0, pos = 0;  // ties and selected pairs before this wave's stretch
-    uint32_t all_eq = 0, all_sel = 0;
-    for (uint32_t w = 0; w < (uint32_t)kRowWaves; ++w) {
-      const uint32_t e = s_eq[w];
-      const uint32_t take = all_eq >= m ? 0u : std::min(m - all_eq, e);
-      if (w == wid) {
-        eq_run = all_eq;
-        pos = all_sel;
-      }
-      all_sel += s_gt[w] + take;
-      all_eq += e;
-    }
+    // lane w < 16 of every wave takes wave w's totals: ties before it, ties it
+    // takes (the lowest indices first), and selected pairs before it
+    const uint32_t e_w = lane < (uint32_t)kRowWaves ? s_eq[lane] : 0u;
+    const uint32_t g_w = lane < (uint32_t)kRowWaves ? s_gt[lane] : 0u;
+    const uint32_t eq_before = wave_inclusive_scan(e_w) - e_w;
+    const uint32_t sel_w = g_w + (eq_before >= m ? 0u : std::min(m - eq_before, e_w));
+    const uint32_t sel_incl = wave_inclusive_scan(sel_w);
+    uint32_t eq_run = __builtin_amdgcn_readlane(eq_before, wid);  // ties and selected pairs before
+    uint32_t pos = __builtin_amdgcn_readlane(sel_incl - sel_w, wid);  // this wave's stretch
+    const uint32_t all_sel = __builtin_amdgcn_readlane(sel_incl, kRowWaves - 1);
     if (tid == 0) {
       *path = 2u;
       *err = all_sel != k ? 1u : 0u;
