@@ -78,6 +78,19 @@ def test_topk_row_ties_at_the_boundary(dev, N, cut):
     _check(g, r, k, dev, expect_path=2)
 
 
+@pytest.mark.parametrize("N", [65536, 65531])
+def test_topk_row_crowded_first_digit(dev, N):
+    """Every key of a register-held row in one bin of the first 11-bit digit
+    (values in [1, 1.125)): both refining passes see the whole row, and the
+    histogram's atomics all land on a few bins."""
+    rng = np.random.default_rng(N)
+    P, k = 3, 655
+    g = (1.0 + rng.random((P, N)) * 0.125).astype(np.float32)
+    g[:, ::7] *= -1.0
+    r = np.zeros_like(g)
+    _check(g, r, k, dev, expect_path=2)
+
+
 def test_topk_sample_underestimate_takes_rescan_path(dev):
     """Large values placed exactly on the sampled chunks make the predicted
     threshold too high: fewer than k candidates, exact rescan."""
