@@ -126,6 +126,20 @@ def test_layers_short_rows_with_ties(dev):
     _check(g, r, off, ks, dev)
 
 
+def test_layers_rows_longer_than_registers(dev):
+    """A per-layer call whose longest layer (100003 elements) is beyond what a
+    workgroup holds in registers but within the one-workgroup row limit: every
+    row streams its passes from memory, unaligned layers included."""
+    rng = np.random.default_rng(12)
+    P, N = 2, 200001
+    off = np.array([0, 100003, 100004, 165000, N], np.uint64)
+    ks = np.array([1000, 1, 650, 350], np.uint64)
+    g = rng.standard_normal((P, N)).astype(np.float32)
+    r = (rng.standard_normal((P, N)) * 0.5).astype(np.float32)
+    assert np.max(np.diff(off.astype(np.int64))) > 65536
+    _check(g, r, off, ks, dev)
+
+
 def test_layers_rescan_row(dev):
     """A large layer of equal values far exceeds its candidate capacity: that
     row alone takes the exact rescan path."""
