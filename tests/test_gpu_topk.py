@@ -200,3 +200,55 @@ def test_topk_max_nodes(dev):
     g = rng.standard_normal((P, N)).astype(np.float32)
     r = np.zeros_like(g)
     _check(g, r, k, dev)
+
+
+def test_topk_wideresnet_full_size_two_ef_steps(dev):
+    """The wide-ResNet-sized call as the bench makes it: P = 64 nodes of
+    N = 2^27, k = 0.5% (671 088), two error-feedback steps with the residual
+    carried on the device. Nodes 0 and 63 bit for bit against the oracle's
+    own residual chain, with the 4-bit codes of their sent values; on all 64
+    nodes the exact EF identity, strictly ascending indices and no unselected
+    magnitude above a selected one."""
+    w = W.workload(4)
+    P, N, k, B = w.P, w.N, w.k, w.q4_bucket
+    seed = 987654321
+    r = torch.zeros((P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(sg.topk_ef_workspace_bytes(P, N, k), dtype=torch.uint8, device=dev)
+    idx = torch.empty((P, k), dtype=torch.int32, device=dev)
+    val = torch.empty((P, k), dtype=torch.float32, device=dev)
+    sample = (0, P - 1)
+    r_o = {p: np.zeros((1, N), np.float32) for p in sample}
+    for step in range(2):
+        print(f"wide-ResNet Top-k step {step}", flush=True)
+        g = W.gradients(w, step, device=dev)
+        r_old = r.clone()
+        sg.topk_ef(g, r, k, out_idx=idx, out_val=val, workspace=ws)
+        codes, scales = sg.q4(val, B, seed, step)
+        torch.cuda.synchronize()
+        paths = sg.topk_ef_paths(ws, P).cpu().numpy()
+        assert np.all(paths[1] == 0), "consistency flag"
+        assert np.all(paths[0] <= 1), paths[0]  # the candidate pipeline (or its exact rescan)
+        for p in sample:
+            oi, ov, orr = oracle.topk_ef(g[p:p + 1].cpu().numpy(), r_o[p], k)
+            assert_bits_equal(idx[p:p + 1].cpu().numpy().view(np.uint32), oi, f"idx node {p} step {step}")
+            assert_bits_equal(val[p:p + 1].cpu().numpy(), ov, f"val node {p} step {step}")
+            assert_bits_equal(r[p:p + 1].cpu().numpy(), orr, f"residual node {p} step {step}")
+            oc, osc = oracle.qsgd(ov, 4, B, seed, step, node0=p)
+            assert_bits_equal(codes[p:p + 1].cpu().numpy(), oc, f"q4 codes node {p} step {step}")
+            assert_bits_equal(scales[p:p + 1].cpu().numpy(), osc, f"q4 scales node {p} step {step}")
+            r_o[p] = orr
+        for c0 in range(0, P, 8):  # properties on every node, 8 nodes at a time
+            c = slice(c0, c0 + 8)
+            il = idx[c].to(torch.int64) & 0xFFFFFFFF
+            assert bool((il[:, 1:] > il[:, :-1]).all()), f"ascending, nodes {c0}.."
+            a = g[c] + r_old[c]
+            recon = r[c].clone()
+            assert bool((torch.gather(recon, 1, il) == 0).all()), f"sent positions zeroed, nodes {c0}.."
+            recon.scatter_add_(1, il, val[c])
+            assert torch.equal(recon, a), f"EF identity, nodes {c0}.."
+            min_sel = val[c].abs().min(dim=1).values
+            unsel_max = r[c].abs().max(dim=1).values
+            assert bool((unsel_max <= min_sel).all()), f"magnitude split, nodes {c0}.."
+            del il, a, recon
+        del g, r_old, codes, scales
+        torch.cuda.empty_cache()
