@@ -51,7 +51,8 @@ typedef enum sparcml_status {
   SPARCML_OK = 0,
   SPARCML_ERR_INVALID_ARG = 1, /* a null pointer, size, alignment or value out of range */
   SPARCML_ERR_WORKSPACE = 2,   /* workspace null, not 256-byte aligned, or smaller than the *_workspace size */
-  SPARCML_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+  SPARCML_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  SPARCML_ERR_SCRATCH_LIMIT = 4 /* the allocation-free call needs more than its static scratch */
 } sparcml_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -298,6 +299,34 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
                                      uint32_t* out_idx, float* out_val,
                                      sparcml_reduce_result* d_result,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Allocation-free sparse reduction, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * The operation, arguments, outputs and errors of sparcml_sparse_reduce,
+ * without the workspace: its scratch is a static device array of
+ * SPARCML_REDUCE_SCRATCH_BYTES in the library, one copy per GPU, kept until
+ * the process ends. The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress); no call allocates or frees memory. Returns
+ * SPARCML_ERR_SCRATCH_LIMIT, launching nothing, when
+ * sparcml_sparse_reduce_workspace(P, N, h_offsets[P]) exceeds
+ * SPARCML_REDUCE_SCRATCH_BYTES (16 MiB: for instance 64 nodes over an index
+ * space of 2^27 take 8.4 MB).
+ * Every call on one GPU uses the same scratch: calls that may overlap in time
+ * on one GPU (different streams without ordering between them) race and
+ * give unspecified results. Calls ordered on one stream are safe; each clears
+ * what it needs.
+ * ---------------------------------------------------------------------- */
+#define SPARCML_REDUCE_SCRATCH_BYTES (16u << 20)
+
+sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delta,
+                                             const uint64_t* h_offsets,
+                                             const uint32_t* idx, const float* val,
+                                             uint64_t expected_nnz_hint,
+                                             uint32_t* out_idx, float* out_val,
+                                             sparcml_reduce_result* d_result, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Sparse reduction of quantized contributions (paper section 6: the values

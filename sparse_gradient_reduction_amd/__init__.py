@@ -19,7 +19,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparcml.so")
 
-OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
+REDUCE_SCRATCH_BYTES = 16 << 20  # SPARCML_REDUCE_SCRATCH_BYTES: static scratch of sparse_reduce_noalloc
 FLAG_INDEX_RANGE, FLAG_NOT_ASCENDING = 1, 2
 
 _lib = None
@@ -73,6 +74,8 @@ def _load():
     L.sparcml_sparse_reduce_workspace.restype = sz
     L.sparcml_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
     L.sparcml_sparse_reduce.restype = st
+    L.sparcml_sparse_reduce_noalloc.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp]
+    L.sparcml_sparse_reduce_noalloc.restype = st
     L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
     L.sparcml_estimate_nnz.restype = f64
     L.sparcml_reference_stream.argtypes = [u64, vp, vp, vp, vp, vp]
@@ -388,4 +391,31 @@ def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, 
                                        _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
                                        workspace.numel(), ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_sparse_reduce")
+    return ReduceOutput(result, out_idx, out_val, N)
+
+
+def sparse_reduce_noalloc(offsets, idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
+                          out_idx: torch.Tensor, out_val: torch.Tensor, result: torch.Tensor,
+                          expected_nnz_hint: int = 0) -> ReduceOutput:
+    """sparse_reduce through the allocation-free entry point: the library's
+    static per-GPU scratch replaces the workspace, and the caller passes every
+    output (out_idx with capacity min(N, T-1), out_val [N], result 16 bytes),
+    so nothing is allocated on the device. `offsets` may be a sequence or a
+    prepared (ctypes.c_uint64 * (P+1)) array. Calls that overlap in time on
+    one GPU share the scratch and race."""
+    _check_dev(idx, torch.int32, "idx")
+    _check_dev(val, torch.float32, "val")
+    _check_dev(out_idx, torch.int32, "out_idx")
+    _check_dev(out_val, torch.float32, "out_val")
+    _check_dev(result, torch.uint8, "result")
+    if isinstance(offsets, ctypes.Array):
+        off, P = offsets, len(offsets) - 1
+    else:
+        P = len(offsets) - 1
+        off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
+    dev = idx.device
+    st = _load().sparcml_sparse_reduce_noalloc(P, N, float(delta), off, _ptr(idx), _ptr(val),
+                                               int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
+                                               _ptr(result), ctypes.c_void_p(_stream(dev)))
+    _raise(st, "sparcml_sparse_reduce_noalloc")
     return ReduceOutput(result, out_idx, out_val, N)

@@ -3,11 +3,43 @@
 #include "sparcml.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "kernels.hpp"
 
+// Scratch of the allocation-free reduce: one copy per GPU, held until the
+// process ends. Host code never passes this name to a kernel; it uses the
+// device address that hipGetSymbolAddress gives on each device.
+static __device__ __align__(256) unsigned char scratch[SPARCML_REDUCE_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> g_scratch[kMaxDevices];  // device address of `scratch`, per device ordinal
+std::mutex g_scratch_mu;
+
+// Device address of the current device's `scratch`, looked up once per device.
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
@@ -38,6 +70,8 @@ const char* sparcml_status_string(sparcml_status status) {
     case SPARCML_ERR_INVALID_ARG: return "SPARCML_ERR_INVALID_ARG: invalid argument";
     case SPARCML_ERR_WORKSPACE: return "SPARCML_ERR_WORKSPACE: workspace missing or too small";
     case SPARCML_ERR_HIP: return "SPARCML_ERR_HIP: HIP runtime or launch error";
+    case SPARCML_ERR_SCRATCH_LIMIT:
+      return "SPARCML_ERR_SCRATCH_LIMIT: the call needs more than SPARCML_REDUCE_SCRATCH_BYTES of scratch";
   }
   return "SPARCML: unknown status";
 }
@@ -240,6 +274,20 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
   return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
                        ws_bytes, stream);
+}
+
+sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                             const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
+                                             uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
+                                             hipStream_t stream) {
+  if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !h_offsets) return SPARCML_ERR_INVALID_ARG;
+  if (h_offsets[P] > kMaxN) return SPARCML_ERR_INVALID_ARG;
+  if (sparcml::reduce_workspace_bytes(P, N, h_offsets[P]) > SPARCML_REDUCE_SCRATCH_BYTES)
+    return SPARCML_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return SPARCML_ERR_HIP;
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
+                       SPARCML_REDUCE_SCRATCH_BYTES, stream);
 }
 
 sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N, double delta,

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     L = sg.lib()
-    for st in range(4):
+    for st in range(5):
         s = L.sparcml_status_string(st).decode()
         assert s.startswith("SPARCML")
     assert L.sparcml_status_string(99).decode()
@@ -106,6 +106,31 @@ def test_reduce_argument_checks():
     assert call(w=None) == sg.ERR_WORKSPACE
     assert call(w=FAKE_WS_ODD) == sg.ERR_WORKSPACE
     assert call(wb=ws - 1) == sg.ERR_WORKSPACE
+
+
+def test_reduce_noalloc_rejects_what_exceeds_its_scratch():
+    """The allocation-free reduce refuses, before touching any device, a call
+    whose workspace would exceed SPARCML_REDUCE_SCRATCH_BYTES, and takes one
+    that fits up to its other argument checks."""
+    L = sg.lib()
+    L.sparcml_sparse_reduce_noalloc.argtypes = [ctypes.c_uint32, ctypes.c_uint64, ctypes.c_double,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+    assert sg.REDUCE_SCRATCH_BYTES == 16 << 20
+    big_P, big_N = 1024, 1 << 27  # the run-start table alone is 4 * 1024 * 32769 bytes
+    assert sg.sparse_reduce_workspace_bytes(big_P, big_N, 1000) > sg.REDUCE_SCRATCH_BYTES
+    off = (ctypes.c_uint64 * (big_P + 1))(*([0] * (big_P + 1)))
+    st = L.sparcml_sparse_reduce_noalloc(big_P, big_N, 0.3, off, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None)
+    assert st == sg.ERR_SCRATCH_LIMIT
+    assert "SCRATCH" in L.sparcml_status_string(st).decode()
+    # the wide-ResNet-sized reduce (64 nodes over 2^27 indices) fits
+    assert sg.sparse_reduce_workspace_bytes(64, 1 << 27, 64 * 671088) <= sg.REDUCE_SCRATCH_BYTES
+    off = (ctypes.c_uint64 * 2)(0, 10)
+    assert L.sparcml_sparse_reduce_noalloc(0, 100, 0.3, off, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None) == \
+        sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_noalloc(1, 100, 0.3, None, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None) == \
+        sg.ERR_INVALID_ARG
 
 
 def test_layers_argument_checks():
