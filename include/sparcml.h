@@ -312,14 +312,14 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
  * (hipGetSymbolAddress); no call allocates or frees memory. Returns
  * SPARCML_ERR_SCRATCH_LIMIT, launching nothing, when
  * sparcml_sparse_reduce_workspace(P, N, h_offsets[P]) exceeds
- * SPARCML_REDUCE_SCRATCH_BYTES (16 MiB: for instance 64 nodes over an index
- * space of 2^27 take 8.4 MB).
+ * SPARCML_REDUCE_SCRATCH_BYTES (32 MiB: for instance 64 nodes over an index
+ * space of 2^27 take 25.2 MB).
  * Every call on one GPU uses the same scratch: calls that may overlap in time
  * on one GPU (different streams without ordering between them) race and
  * give unspecified results. Calls ordered on one stream are safe; each clears
  * what it needs.
  * ---------------------------------------------------------------------- */
-#define SPARCML_REDUCE_SCRATCH_BYTES (16u << 20)
+#define SPARCML_REDUCE_SCRATCH_BYTES (32u << 20)
 
 sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delta,
                                              const uint64_t* h_offsets,

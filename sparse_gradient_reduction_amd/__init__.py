@@ -20,7 +20,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparcml.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
-REDUCE_SCRATCH_BYTES = 16 << 20  # SPARCML_REDUCE_SCRATCH_BYTES: static scratch of sparse_reduce_noalloc
+REDUCE_SCRATCH_BYTES = 32 << 20  # SPARCML_REDUCE_SCRATCH_BYTES: static scratch of sparse_reduce_noalloc
 FLAG_INDEX_RANGE, FLAG_NOT_ASCENDING = 1, 2
 
 _lib = None

@@ -52,7 +52,7 @@ struct State {
 
 struct Layout {
   uint64_t S;  // segments
-  size_t state, offs, qoffs, bounds, cnt, off, total;
+  size_t state, offs, qoffs, bounds, cnt, off, bitmaps, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -72,6 +72,7 @@ Layout make_layout(uint32_t P, uint64_t N) {
   L.bounds = take(4ull * P * (L.S + 1));
   L.cnt = take(4ull * L.S);
   L.off = take(4ull * L.S);
+  L.bitmaps = take(4ull * kWords * L.S);  // union bitmap of every segment
   L.total = o;
   return L;
 }
@@ -89,6 +90,7 @@ struct RDev {
   uint32_t* bounds;
   uint32_t* cnt;
   uint32_t* off;
+  uint32_t* bitmaps;  // [S][128]: bit i of segment s set iff s * 4096 + i is in the union
   ReduceResultDev* result;
   // quantized input only: node p's codes start at byte coffs[p], its
   // scales at soffs[p]
@@ -251,120 +253,106 @@ struct QRuns {
   uint32_t sb[MAXP];
 };
 
-// Node runs of segment s: pre[p] = exclusive prefix of their lengths,
-// start[p] = absolute index of the first pair; returns the segment's pair
-// count. pre[P + 1 .. 2P) are set to all ones (room for find_nodes' steps).
-// Run ends are clamped to the node's own pairs, which keeps every later load
-// inside them even for input whose order check failed. With at most 64 nodes
-// one wave builds the table (no block scan).
+// Run of node p in segment s: (absolute position of the node's first pair
+// in the segment, number of its pairs there). Run ends are clamped to the
+// node's own pairs, which keeps every later load inside them even for input
+// whose order check failed.
+__device__ __forceinline__ uint2 node_run(const RDev& R, uint64_t s, uint32_t p) {
+  const uint32_t* b = R.bounds + p * (R.S + 1) + s;  // node-major run-start table
+  const uint32_t lo = (uint32_t)R.offs[p], hi = (uint32_t)R.offs[p + 1];
+  const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[0], lo), hi);
+  const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[1], lo), hi);
+  return make_uint2(b0, b1 > b0 ? b1 - b0 : 0u);
+}
+
+// The run table of segment s in LDS (node p's run at runs[p]), and for
+// quantized input the node's code tables. All loads of a thread go out
+// before it waits; the caller's barrier publishes the table.
 template <int NT, int MAXP>
-__device__ __forceinline__ uint32_t load_runs(const RDev& R, uint64_t s, uint32_t* pre, uint32_t* start,
-                                              uint32_t* scr, QRuns<MAXP>* q) {
-  const uint64_t rows = R.S + 1;  // entries per node in the run-start table
-  auto run = [&](uint32_t p) -> uint32_t {
-    const uint32_t* b = R.bounds + p * rows + s;
-    const uint32_t lo = (uint32_t)R.offs[p], hi = (uint32_t)R.offs[p + 1];
-    const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[0], lo), hi);
-    const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[1], lo), hi);
-    start[p] = b0;
+__device__ __forceinline__ void store_run_table(const RDev& R, uint64_t s, uint2* runs, QRuns<MAXP>* q) {
+  for (uint32_t p = threadIdx.x; p < R.P; p += NT) {
+    const uint2 rn = node_run(R, s, p);
+    runs[p] = rn;
     if (q != nullptr) {
-      q->rel[p] = b0 - lo;
+      q->rel[p] = rn.x - (uint32_t)R.offs[p];
       q->cb[p] = (uint32_t)R.coffs[p];
       q->sb[p] = (uint32_t)R.soffs[p];
     }
-    return b1 > b0 ? b1 - b0 : 0u;
-  };
-  for (uint32_t i = R.P + 1u + threadIdx.x; i < 2u * R.P; i += NT) pre[i] = ~0u;
-  if (R.P <= (uint32_t)kWave) {
-    if (threadIdx.x < kWave) {
-      const uint32_t p = threadIdx.x;
-      const uint32_t len = p < R.P ? run(p) : 0u;
-      const uint32_t inc = wave_inclusive_scan(len);
-      if (p < R.P) pre[p] = inc - len;
-      if (p == R.P - 1) pre[R.P] = inc;
-    }
-    __syncthreads();
-    return pre[R.P];
-  }
-  uint32_t carry = 0;
-  for (uint32_t p0 = 0; p0 < R.P; p0 += NT) {
-    const uint32_t p = p0 + threadIdx.x;
-    const uint32_t len = p < R.P ? run(p) : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<NT>(len, scr, tot);
-    if (p < R.P) pre[p] = carry + ex;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) pre[R.P] = carry;
-  __syncthreads();
-  return carry;
-}
-
-// For every batch slot b with f = f0 + b * NT + threadIdx.x < total: node[b]
-// = the largest p with pre[p] <= f (pre is nondecreasing, pre[0] = 0 and
-// pre[P] = total > f). Binary lifting with one uniform step sequence for all
-// slots and no branches, so the slots' LDS reads overlap instead of forming
-// one dependent chain per slot. pre[] holds 2P words, those past P all ones:
-// a step reads at most pre[2P - 1] and never moves past P for f < total.
-template <int NT, int B>
-__device__ __forceinline__ void find_nodes(const uint32_t* pre, uint32_t P, uint32_t f0, uint32_t (&node)[B]) {
-#pragma unroll
-  for (int b = 0; b < B; ++b) node[b] = 0u;
-  const uint32_t top = P > 1u ? 1u << (31 - __clz(P - 1u)) : 0u;  // largest power of two <= P - 1
-  for (uint32_t step = top; step != 0u; step >>= 1) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const uint32_t f = f0 + b * NT + threadIdx.x;
-      const uint32_t c = node[b] + step;
-      node[b] = pre[c] <= f ? c : node[b];
-    }
   }
 }
 
-// One workgroup per segment: short, independent workgroups kept more
-// segments in flight than long ones walking several segments (measured).
-// Counting needs only the bitmap's 128 words, held by the first two waves;
-// the others leave once the merge is done. The sparse compaction stages the
-// segment's pairs in LDS so that its global stores are coalesced.
+// Slots of a pass: the threads are cut into groups of `lanes` consecutive
+// lanes (lanes = 2^lane_bits); group g of NT / lanes takes nodes
+// p0 + b * (NT / lanes) + g for b < B, lane l of the group the node's pair
+// l. Each node's pairs are consecutive in memory, so a group's loads are
+// contiguous and no thread searches for its node. Pairs past the first
+// `lanes` of a run are taken by a later loop.
+struct Slots {
+  uint32_t lane;     // l
+  uint32_t group;    // g
+  uint32_t groups;   // NT / lanes: nodes per row of the pass
+};
+
+__device__ __forceinline__ Slots make_slots(uint32_t lane_bits, int NT) {
+  Slots sl;
+  sl.lane = threadIdx.x & ((1u << lane_bits) - 1u);
+  sl.group = threadIdx.x >> lane_bits;
+  sl.groups = (uint32_t)NT >> lane_bits;
+  return sl;
+}
+
 constexpr int kCountThreads = 128;
 constexpr int kWriteThreads = 512;
 constexpr int kWordWaves = kWords / kWave;  // 2
 static_assert(kWords % kWave == 0 && kWords <= kCountThreads, "bitmap words cover whole waves");
 
+// One workgroup per segment: short, independent workgroups kept more
+// segments in flight than long ones walking several segments (measured).
+// Counting needs only the bitmap's 128 words, held by the first two waves;
+// the others leave once the merge is done.
 template <int MAXP>
-__global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R) {
+__global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R,
+                                                         uint32_t lane_bits) {
   constexpr int NT = kCountThreads;
+  constexpr int kB = 16;  // node rows per pass: 16 index loads in flight per thread
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[2 * MAXP];
-  __shared__ uint32_t start[MAXP];
-  __shared__ uint32_t scr[NT / kWave + 3];
+  __shared__ uint2 runs[MAXP];
+  __shared__ uint32_t scr[NT / kWave];
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<NT, MAXP>(R, s, pre, start, scr, (QRuns<MAXP>*)nullptr);
-  constexpr int kBatch = 12;
-  for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch], pos[kBatch];
-    find_nodes<NT>(pre, R.P, f0, pos);  // each slot's node, replaced below by its position
+  const Slots sl = make_slots(lane_bits, NT);
+  store_run_table<NT, MAXP>(R, s, runs, nullptr);
+  __syncthreads();
+  auto mark = [&](uint32_t i) {
+    const uint32_t local = i - seg_lo;
+    if (local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
+  };
+  for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
+    uint2 rn[kB];
+    uint32_t ii[kB];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
-      const uint32_t p = std::min(pos[b], R.P - 1u);
-      pos[b] = start[p] + (f0 + b * NT + threadIdx.x - pre[p]);
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t p = p0 + b * sl.groups + sl.group;
+      rn[b] = p < R.P ? runs[p] : make_uint2(0u, 0u);
     }
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b)
-      if (f0 + b * NT + threadIdx.x < total) ii[b] = idx[pos[b]];
+    for (int b = 0; b < kB; ++b)
+      if (sl.lane < rn[b].y) ii[b] = idx[rn[b].x + sl.lane];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const uint32_t local = ii[b] - seg_lo;
-      if (f0 + b * NT + threadIdx.x < total && local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
-    }
+    for (int b = 0; b < kB; ++b)
+      if (sl.lane < rn[b].y) mark(ii[b]);
+    const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
+    for (int b = 0; b < kB; ++b)
+      for (uint32_t j = sl.lane + step; j < rn[b].y; j += step) mark(idx[rn[b].x + j]);
   }
   __syncthreads();
   const uint32_t wid = threadIdx.x / kWave;
   if (wid >= (uint32_t)kWordWaves) return;
-  const uint32_t c = wave_sum((uint32_t)__popc(bits[threadIdx.x]));
+  const uint32_t word = bits[threadIdx.x];
+  R.bitmaps[s * kWords + threadIdx.x] = word;  // the ranked writer places pairs by it
+  const uint32_t c = wave_sum((uint32_t)__popc(word));
   if (lane_id() == 0) scr[wid] = c;
   __syncthreads();  // only the word waves are left
   if (threadIdx.x == 0) {
@@ -441,12 +429,12 @@ template <int MODE, int MAXP, int BITS>
 __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restrict__ idx,
                                                          const float* __restrict__ val,
                                                          uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                                                         RDev R) {
+                                                         RDev R, uint32_t lane_bits) {
   constexpr int NT = kWriteThreads;
+  constexpr int kB = 4;  // node rows per pass
   __shared__ double acc[kSeg];
   __shared__ uint32_t bits[kWords];
-  __shared__ uint32_t pre[2 * MAXP];
-  __shared__ uint32_t start[MAXP];
+  __shared__ uint2 runs[MAXP];
   __shared__ uint32_t scr[NT / kWave + 3];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
@@ -459,50 +447,56 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
   if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
-  const uint32_t total = load_runs<NT, BITS ? MAXP : 1>(R, s, pre, start, scr, BITS ? &qruns : nullptr);
+  const Slots sl = make_slots(lane_bits, NT);
+  store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
+  __syncthreads();
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
-  constexpr int kBatch = 4;
-  for (uint32_t f0 = 0; f0 < total; f0 += NT * kBatch) {
-    uint32_t ii[kBatch], node[kBatch], js[kBatch];
-    uint32_t qe[kBatch];              // quantized input: position in the node's code row
-    uint32_t qc[kBatch], qs[kBatch];  // ... and the node's code-byte and scale offsets
-    float vv[kBatch];
-    find_nodes<NT>(pre, R.P, f0, node);
+  // value of node p's pair at absolute position j, run-relative position jr
+  auto value_at = [&](uint32_t p, uint32_t j, uint32_t jr) -> float {
+    if constexpr (BITS == 0) {
+      return val[j];
+    } else {  // dequantize on load: position e of the node's codes
+      using F = Qsgd<BITS>;
+      const uint32_t e = qruns.rel[p] + jr;
+      const uint32_t bucket_no = R.bucket_recip ? (uint32_t)__umul64hi((uint64_t)e, R.bucket_recip) : e;
+      const uint32_t code = F::code_at(R.codes + qruns.cb[p], e);
+      return F::value(code, F::step(R.scales[qruns.sb[p] + bucket_no]));
+    }
+  };
+  auto add = [&](uint32_t i, float v) {
+    const uint32_t local = i - seg_lo;
+    if (local < seg_len) {
+      atomicAdd(&acc[local], (double)v);
+      atomicOr(&bits[local >> 5], 1u << (local & 31));
+    }
+  };
+  for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
+    uint2 rn[kB];
+    uint32_t ii[kB];
+    float vv[kB];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {  // positions first, so the LDS reads are not behind branches
-      const uint32_t p = std::min(node[b], R.P - 1u);
-      const uint32_t jr = f0 + b * NT + threadIdx.x - pre[p];  // position in the node's run
-      js[b] = start[p] + jr;                                   // position in the pair arrays
-      if constexpr (BITS != 0) {
-        qe[b] = qruns.rel[p] + jr;
-        qc[b] = qruns.cb[p];
-        qs[b] = qruns.sb[p];
-      }
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t p = p0 + b * sl.groups + sl.group;
+      rn[b] = p < R.P ? runs[p] : make_uint2(0u, 0u);
     }
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const uint32_t f = f0 + b * NT + threadIdx.x;
-      if (f < total) {
-        const uint32_t j = js[b];
+    for (int b = 0; b < kB; ++b) {
+      if (sl.lane < rn[b].y) {
+        const uint32_t j = rn[b].x + sl.lane;
         ii[b] = idx[j];
-        if constexpr (BITS == 0) {
-          vv[b] = val[j];
-        } else {  // dequantize on load: position e of the node's codes
-          using F = Qsgd<BITS>;
-          const uint32_t e = qe[b];
-          const uint32_t bucket_no = R.bucket_recip ? (uint32_t)__umul64hi((uint64_t)e, R.bucket_recip) : e;
-          const uint32_t code = F::code_at(R.codes + qc[b], e);
-          vv[b] = F::value(code, F::step(R.scales[qs[b] + bucket_no]));
-        }
+        vv[b] = value_at(p0 + b * sl.groups + sl.group, j, sl.lane);
       }
     }
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const uint32_t local = ii[b] - seg_lo;
-      if (f0 + b * NT + threadIdx.x < total && local < seg_len) {
-        atomicAdd(&acc[local], (double)vv[b]);
-        atomicOr(&bits[local >> 5], 1u << (local & 31));
+    for (int b = 0; b < kB; ++b)
+      if (sl.lane < rn[b].y) add(ii[b], vv[b]);
+    const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
+    for (int b = 0; b < kB; ++b) {
+      const uint32_t p = p0 + b * sl.groups + sl.group;
+      for (uint32_t jr = sl.lane + step; jr < rn[b].y; jr += step) {
+        const uint32_t j = rn[b].x + jr;
+        add(idx[j], value_at(p, j, jr));
       }
     }
   }
@@ -564,6 +558,160 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
   }
 }
 
+// Writer placing pairs by their rank in the segment's union, for results
+// expected sparse. The count pass left each segment's union bitmap; a word
+// table (ranks before each 32-index word, and the word) gives every pair its
+// rank r in the segment with one LDS read and a popcount, so the sums
+// accumulate directly in output order: acc[r] (fp64) and sidx[r] (the index)
+// hold the segment's part of the result, which is stored as it stands: no
+// clearing or compaction of a 4096-entry tile, and a quarter of its LDS,
+// which lets more workgroups share a compute unit. Ranks come in windows of
+// kRankCap; a segment with more union entries takes one pass over its pairs
+// per window. A dense result (the count crossed T) writes every index of the
+// segment: the sum at its rank, or 0 outside the union.
+constexpr int kRankThreads = 256;
+constexpr uint32_t kRankCap = 1536;
+
+template <int MAXP, int BITS>
+__global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* __restrict__ idx,
+                                                               const float* __restrict__ val,
+                                                               uint32_t* __restrict__ out_idx,
+                                                               float* __restrict__ out_val, RDev R,
+                                                               uint32_t lane_bits) {
+  constexpr int NT = kRankThreads;
+  constexpr int kB = 8;  // node rows per pass
+  __shared__ double acc[kRankCap];
+  __shared__ uint32_t sidx[kRankCap];
+  __shared__ uint2 words[kWords];  // (ranks before the word, the word)
+  __shared__ uint2 runs[MAXP];
+  __shared__ QRuns<BITS ? MAXP : 1> qruns;
+  __shared__ uint32_t head[3];     // is_dense, the segment's union count, its output offset
+  const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
+  const uint32_t seg_lo = (uint32_t)(s << kSegBits);
+  const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
+  const Slots sl = make_slots(lane_bits, NT);
+  // every load of the prologue goes out before any wait: the bitmap (wave 0),
+  // the decision, count and offset (vector loads by the last thread, so that
+  // no scalar load sits in front of them), and the run table
+  uint2 wpair = make_uint2(0u, 0u);
+  if (threadIdx.x < kWords / 2) wpair = reinterpret_cast<const uint2*>(R.bitmaps + s * kWords)[threadIdx.x];
+  uint32_t h0 = 0, h1 = 0, h2 = 0;
+  if (threadIdx.x == NT - 1) {  // non-temporal loads stay vector loads
+    h0 = __builtin_nontemporal_load(&R.state->is_dense);
+    h1 = __builtin_nontemporal_load(&R.cnt[s]);
+    h2 = __builtin_nontemporal_load(&R.off[s]);
+  }
+  for (uint32_t r = threadIdx.x; r < kRankCap; r += NT) acc[r] = 0.0;
+  store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
+  if (threadIdx.x < kWave) {  // word table: wave 0, two words per lane
+    const uint32_t c0 = (uint32_t)__popc(wpair.x), c1 = (uint32_t)__popc(wpair.y);
+    const uint32_t inc = wave_inclusive_scan(c0 + c1);
+    words[2 * threadIdx.x] = make_uint2(inc - c0 - c1, wpair.x);
+    words[2 * threadIdx.x + 1] = make_uint2(inc - c1, wpair.y);
+  }
+  if (threadIdx.x == NT - 1) {
+    head[0] = h0;
+    head[1] = h1;
+    head[2] = h2;
+  }
+  __syncthreads();
+  const bool dense = head[0] != 0u;
+  const uint32_t seg_cnt = head[1];
+  const uint32_t seg_off = head[2];
+  if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
+
+  auto value_at = [&](uint32_t p, uint32_t j, uint32_t jr) -> float {
+    if constexpr (BITS == 0) {
+      return val[j];
+    } else {  // dequantize on load: position e of the node's codes
+      using F = Qsgd<BITS>;
+      const uint32_t e = qruns.rel[p] + jr;
+      const uint32_t bucket_no = R.bucket_recip ? (uint32_t)__umul64hi((uint64_t)e, R.bucket_recip) : e;
+      const uint32_t code = F::code_at(R.codes + qruns.cb[p], e);
+      return F::value(code, F::step(R.scales[qruns.sb[p] + bucket_no]));
+    }
+  };
+  const uint32_t windows = std::max<uint32_t>(1u, (seg_cnt + kRankCap - 1) / kRankCap);
+  for (uint32_t w0 = 0, win = 0; win < windows; ++win, w0 += kRankCap) {
+    if (win > 0) {  // the previous window is stored: clear for this one
+      __syncthreads();
+      for (uint32_t r = threadIdx.x; r < kRankCap; r += NT) acc[r] = 0.0;
+      __syncthreads();
+    }
+    auto add = [&](uint32_t i, float v) {
+      const uint32_t local = i - seg_lo;
+      if (local < seg_len) {
+        const uint2 wd = words[local >> 5];
+        const uint32_t bit = 1u << (local & 31);
+        const uint32_t r = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - w0;
+        if ((wd.y & bit) && r < kRankCap) {
+          atomicAdd(&acc[r], (double)v);
+          sidx[r] = i;
+        }
+      }
+    };
+    for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
+      uint2 rn[kB];
+      uint32_t ii[kB];
+      float vv[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const uint32_t p = p0 + b * sl.groups + sl.group;
+        rn[b] = p < R.P ? runs[p] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (sl.lane < rn[b].y) {
+          const uint32_t j = rn[b].x + sl.lane;
+          ii[b] = idx[j];
+          vv[b] = value_at(p0 + b * sl.groups + sl.group, j, sl.lane);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (sl.lane < rn[b].y) add(ii[b], vv[b]);
+      const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
+      for (int b = 0; b < kB; ++b) {
+        const uint32_t p = p0 + b * sl.groups + sl.group;
+        for (uint32_t jr = sl.lane + step; jr < rn[b].y; jr += step) {
+          const uint32_t j = rn[b].x + jr;
+          add(idx[j], value_at(p, j, jr));
+        }
+      }
+    }
+    __syncthreads();
+    if (dense) {  // every index of the segment: its sum, or 0 outside the union
+      float* out = out_val + seg_lo;
+      const bool whole = windows == 1u && seg_len == kSeg;
+      for (uint32_t q = threadIdx.x; q < (seg_len + 3) / 4; q += NT) {
+        const uint2 wd = words[q >> 3];
+        float o[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t local = 4 * q + t;
+          const uint32_t bit = 1u << (local & 31);
+          const uint32_t r = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - w0;
+          o[t] = (wd.y & bit) && r < kRankCap ? (float)acc[r] : 0.0f;
+          if (!whole && local < seg_len) {
+            const bool mine = (wd.y & bit) ? r < kRankCap : win == 0u;
+            if (mine) out[local] = o[t];
+          }
+        }
+        if (whole) reinterpret_cast<float4*>(out)[q] = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      const uint32_t n = std::min(seg_cnt - w0, kRankCap);
+      for (uint32_t r = threadIdx.x; r < n; r += NT) {
+        const uint64_t pos = (uint64_t)seg_off + w0 + r;
+        if (pos < R.out_idx_cap) {
+          out_idx[pos] = sidx[r];
+          out_val[pos] = (float)acc[r];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t /*total_nnz*/) { return make_layout(P, N).total; }
@@ -572,22 +720,44 @@ namespace {
 
 template <int MODE, int MAXP>
 void launch_write(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                  uint32_t* out_idx, float* out_val, const RDev& R) {
+                  uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
   const dim3 block(kWriteThreads);
   switch (bits) {
-    case 0: hipLaunchKernelGGL((k_write<MODE, MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
-    case 2: hipLaunchKernelGGL((k_write<MODE, MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
-    case 4: hipLaunchKernelGGL((k_write<MODE, MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
-    default: hipLaunchKernelGGL((k_write<MODE, MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R); break;
+    case 0: hipLaunchKernelGGL((k_write<MODE, MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 2: hipLaunchKernelGGL((k_write<MODE, MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 4: hipLaunchKernelGGL((k_write<MODE, MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    default: hipLaunchKernelGGL((k_write<MODE, MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
   }
 }
 
 template <int MODE>
 void launch_write(bool small_p, uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                  uint32_t* out_idx, float* out_val, const RDev& R) {
+                  uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
   // run tables sized for up to 256 nodes keep the write workgroups small
-  if (small_p) launch_write<MODE, 256>(bits, grid, stream, idx, val, out_idx, out_val, R);
-  else launch_write<MODE, kMaxP>(bits, grid, stream, idx, val, out_idx, out_val, R);
+  if (small_p) launch_write<MODE, 256>(bits, grid, stream, idx, val, out_idx, out_val, R, lb);
+  else launch_write<MODE, kMaxP>(bits, grid, stream, idx, val, out_idx, out_val, R, lb);
+}
+
+template <int MAXP>
+void launch_write_ranked(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
+                         uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
+  const dim3 block(kRankThreads);
+  switch (bits) {
+    case 0: hipLaunchKernelGGL((k_write_ranked<MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 2: hipLaunchKernelGGL((k_write_ranked<MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 4: hipLaunchKernelGGL((k_write_ranked<MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    default: hipLaunchKernelGGL((k_write_ranked<MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+  }
+}
+
+// Lanes per node in the count and write passes (as a power of two): about
+// 1.5 times the mean run length of a node in a segment, so that few runs
+// spill past their lanes while lanes stay mostly busy; 16 to 128.
+uint32_t lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
+  const double mean = (double)total / ((double)P * (double)S);
+  uint32_t lb = 4;
+  while (lb < 7 && (double)(1u << lb) < 1.5 * mean) ++lb;
+  return lb;
 }
 
 }  // namespace
@@ -611,6 +781,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.bounds = reinterpret_cast<uint32_t*>(w + L.bounds);
   R.cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
   R.off = reinterpret_cast<uint32_t*>(w + L.off);
+  R.bitmaps = reinterpret_cast<uint32_t*>(w + L.bitmaps);
   R.result = d_result;
   R.bits = quant ? quant->bits : 0u;
   R.bucket = quant ? quant->bucket : 1u;
@@ -635,15 +806,17 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R, shift);
   const dim3 segs((uint32_t)L.S);
   const bool small_p = P <= 256;
+  const uint32_t lb = lanes_log2(P, L.S, R.total);
   if (dense_first) {
-    launch_write<kDenseFirst>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
+    launch_write<kDenseFirst>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    launch_write<kSparseOnly>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
+    launch_write<kSparseOnly>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
   } else {
-    if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R);
-    else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R);
+    if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
+    else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    launch_write<kDecided>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R);
+    if (small_p) launch_write_ranked<256>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
+    else launch_write_ranked<kMaxP>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
   }
   return hipGetLastError();
 }

@@ -117,7 +117,7 @@ def test_reduce_noalloc_rejects_what_exceeds_its_scratch():
                                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p]
-    assert sg.REDUCE_SCRATCH_BYTES == 16 << 20
+    assert sg.REDUCE_SCRATCH_BYTES == 32 << 20
     big_P, big_N = 1024, 1 << 27  # the run-start table alone is 4 * 1024 * 32769 bytes
     assert sg.sparse_reduce_workspace_bytes(big_P, big_N, 1000) > sg.REDUCE_SCRATCH_BYTES
     off = (ctypes.c_uint64 * (big_P + 1))(*([0] * (big_P + 1)))
