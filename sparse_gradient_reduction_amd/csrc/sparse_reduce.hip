@@ -33,6 +33,7 @@
 #include "sparcml.h"
 
 #include <algorithm>
+#include <cmath>
 
 namespace sparcml {
 namespace {
@@ -562,26 +563,37 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
 // expected sparse. The count pass left each segment's union bitmap; a word
 // table (ranks before each 32-index word, and the word) gives every pair its
 // rank r in the segment with one LDS read and a popcount, so the sums
-// accumulate directly in output order: acc[r] (fp64) and sidx[r] (the index)
-// hold the segment's part of the result, which is stored as it stands: no
+// accumulate directly in output order and are stored as they stand: no
 // clearing or compaction of a 4096-entry tile, and a quarter of its LDS,
-// which lets more workgroups share a compute unit. Ranks come in windows of
-// kRankCap; a segment with more union entries takes one pass over its pairs
-// per window. A dense result (the count crossed T) writes every index of the
-// segment: the sum at its rank, or 0 outside the union.
+// which lets more workgroups share a compute unit.
+//
+// The vector-memory address unit and the VALU bound this pass, so each
+// memory instruction moves 16 bytes per lane where it can: pairs are loaded
+// as aligned quads (QUAD: fp32 values, idx and val 16-byte aligned; else one
+// pair per lane), and results are stored as aligned quads: rank r of a
+// window whose output starts at position P0 sits in slot r + (P0 mod 4), so
+// that slot quads are output quads. Ranks come in windows of kRankCap; a
+// segment with more union entries takes one pass over its pairs per window.
+// A dense result (the count crossed T) writes every index of the segment:
+// the sum at its rank, or 0 outside the union. For valid input every pair's
+// bit is set in the bitmap the count pass built from the same pairs; input
+// that failed the checks gives unspecified sums, but every LDS slot touched
+// stays inside the window.
 constexpr int kRankThreads = 256;
 constexpr uint32_t kRankCap = 1536;
+constexpr uint32_t kRankSlots = kRankCap + 4;
 
-template <int MAXP, int BITS>
+template <int MAXP, int BITS, bool QUAD>
 __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* __restrict__ idx,
                                                                const float* __restrict__ val,
                                                                uint32_t* __restrict__ out_idx,
                                                                float* __restrict__ out_val, RDev R,
                                                                uint32_t lane_bits) {
+  static_assert(!QUAD || BITS == 0, "quad loads take fp32 values");
   constexpr int NT = kRankThreads;
-  constexpr int kB = 8;  // node rows per pass
-  __shared__ double acc[kRankCap];
-  __shared__ uint32_t sidx[kRankCap];
+  constexpr int kB = QUAD ? 2 : 8;  // node rows per pass
+  __shared__ __align__(16) double acc[kRankSlots];
+  __shared__ __align__(16) uint16_t sloc[kRankSlots];  // index within the segment
   __shared__ uint2 words[kWords];  // (ranks before the word, the word)
   __shared__ uint2 runs[MAXP];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
@@ -591,17 +603,16 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   const Slots sl = make_slots(lane_bits, NT);
   // every load of the prologue goes out before any wait: the bitmap (wave 0),
-  // the decision, count and offset (vector loads by the last thread, so that
-  // no scalar load sits in front of them), and the run table
+  // the decision, count and offset, and the run table
   uint2 wpair = make_uint2(0u, 0u);
   if (threadIdx.x < kWords / 2) wpair = reinterpret_cast<const uint2*>(R.bitmaps + s * kWords)[threadIdx.x];
   uint32_t h0 = 0, h1 = 0, h2 = 0;
-  if (threadIdx.x == NT - 1) {  // non-temporal loads stay vector loads
-    h0 = __builtin_nontemporal_load(&R.state->is_dense);
-    h1 = __builtin_nontemporal_load(&R.cnt[s]);
-    h2 = __builtin_nontemporal_load(&R.off[s]);
+  if (threadIdx.x == NT - 1) {
+    h0 = R.state->is_dense;
+    h1 = R.cnt[s];
+    h2 = R.off[s];
   }
-  for (uint32_t r = threadIdx.x; r < kRankCap; r += NT) acc[r] = 0.0;
+  for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
   store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
   if (threadIdx.x < kWave) {  // word table: wave 0, two words per lane
     const uint32_t c0 = (uint32_t)__popc(wpair.x), c1 = (uint32_t)__popc(wpair.y);
@@ -633,49 +644,80 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
   };
   const uint32_t windows = std::max<uint32_t>(1u, (seg_cnt + kRankCap - 1) / kRankCap);
   for (uint32_t w0 = 0, win = 0; win < windows; ++win, w0 += kRankCap) {
+    const uint32_t sh = (seg_off + w0) & 3u;  // slot of the window's first rank
+    const uint32_t base = w0 - sh;             // rank r sits in slot r - base
     if (win > 0) {  // the previous window is stored: clear for this one
       __syncthreads();
-      for (uint32_t r = threadIdx.x; r < kRankCap; r += NT) acc[r] = 0.0;
+      for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
       __syncthreads();
     }
     auto add = [&](uint32_t i, float v) {
-      const uint32_t local = i - seg_lo;
-      if (local < seg_len) {
-        const uint2 wd = words[local >> 5];
-        const uint32_t bit = 1u << (local & 31);
-        const uint32_t r = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - w0;
-        if ((wd.y & bit) && r < kRankCap) {
-          atomicAdd(&acc[r], (double)v);
-          sidx[r] = i;
-        }
+      const uint32_t local = i & (kSeg - 1u);
+      const uint2 wd = words[local >> 5];
+      const uint32_t x = wd.x + (uint32_t)__popc(wd.y & ((1u << (local & 31)) - 1u)) - base;
+      if (x - sh < kRankCap) {
+        atomicAdd(&acc[x], (double)v);
+        sloc[x] = (uint16_t)local;
       }
     };
     for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
       uint2 rn[kB];
-      uint32_t ii[kB];
-      float vv[kB];
 #pragma unroll
       for (int b = 0; b < kB; ++b) {
         const uint32_t p = p0 + b * sl.groups + sl.group;
         rn[b] = p < R.P ? runs[p] : make_uint2(0u, 0u);
       }
+      const uint32_t step = 1u << lane_bits;
+      if constexpr (QUAD) {
+        // node run [a, a + L) covers quads q0 .. q1 - 1; lane l takes quad q0 + l
+        uint4 ii[kB];
+        float4 vv[kB];
+        uint32_t q0[kB], q1[kB];
 #pragma unroll
-      for (int b = 0; b < kB; ++b) {
-        if (sl.lane < rn[b].y) {
-          const uint32_t j = rn[b].x + sl.lane;
-          ii[b] = idx[j];
-          vv[b] = value_at(p0 + b * sl.groups + sl.group, j, sl.lane);
+        for (int b = 0; b < kB; ++b) {
+          q0[b] = rn[b].x >> 2;
+          q1[b] = rn[b].y ? (rn[b].x + rn[b].y + 3u) >> 2 : q0[b];
+          if (q0[b] + sl.lane < q1[b]) {
+            ii[b] = reinterpret_cast<const uint4*>(idx)[q0[b] + sl.lane];
+            vv[b] = reinterpret_cast<const float4*>(val)[q0[b] + sl.lane];
+          }
         }
-      }
+        auto add4 = [&](uint32_t q, const uint2& r, const uint4& i4, const float4& v4) {
+          const uint32_t e = 4u * q - r.x;  // run position of the quad's first pair (may wrap)
+          if (e < r.y) add(i4.x, v4.x);
+          if (e + 1u < r.y) add(i4.y, v4.y);
+          if (e + 2u < r.y) add(i4.z, v4.z);
+          if (e + 3u < r.y) add(i4.w, v4.w);
+        };
 #pragma unroll
-      for (int b = 0; b < kB; ++b)
-        if (sl.lane < rn[b].y) add(ii[b], vv[b]);
-      const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
-      for (int b = 0; b < kB; ++b) {
-        const uint32_t p = p0 + b * sl.groups + sl.group;
-        for (uint32_t jr = sl.lane + step; jr < rn[b].y; jr += step) {
-          const uint32_t j = rn[b].x + jr;
-          add(idx[j], value_at(p, j, jr));
+        for (int b = 0; b < kB; ++b)
+          if (q0[b] + sl.lane < q1[b]) add4(q0[b] + sl.lane, rn[b], ii[b], vv[b]);
+        for (int b = 0; b < kB; ++b) {  // the rest of runs longer than the group's quads
+          if (__ballot(q1[b] - q0[b] > step) == 0ull) continue;
+          for (uint32_t q = q0[b] + sl.lane + step; q < q1[b]; q += step)
+            add4(q, rn[b], reinterpret_cast<const uint4*>(idx)[q], reinterpret_cast<const float4*>(val)[q]);
+        }
+      } else {
+        uint32_t ii[kB];
+        float vv[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+          if (sl.lane < rn[b].y) {
+            const uint32_t j = rn[b].x + sl.lane;
+            ii[b] = idx[j];
+            vv[b] = value_at(p0 + b * sl.groups + sl.group, j, sl.lane);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+          if (sl.lane < rn[b].y) add(ii[b], vv[b]);
+        for (int b = 0; b < kB; ++b) {  // the rest of runs longer than the group
+          if (__ballot(rn[b].y > step) == 0ull) continue;
+          const uint32_t p = p0 + b * sl.groups + sl.group;
+          for (uint32_t jr = sl.lane + step; jr < rn[b].y; jr += step) {
+            const uint32_t j = rn[b].x + jr;
+            add(idx[j], value_at(p, j, jr));
+          }
         }
       }
     }
@@ -690,22 +732,41 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
         for (int t = 0; t < 4; ++t) {
           const uint32_t local = 4 * q + t;
           const uint32_t bit = 1u << (local & 31);
-          const uint32_t r = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - w0;
-          o[t] = (wd.y & bit) && r < kRankCap ? (float)acc[r] : 0.0f;
-          if (!whole && local < seg_len) {
-            const bool mine = (wd.y & bit) ? r < kRankCap : win == 0u;
-            if (mine) out[local] = o[t];
-          }
+          const uint32_t x = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - base;
+          const bool in = (wd.y & bit) && x - sh < kRankCap;
+          o[t] = in ? (float)acc[x] : 0.0f;
+          if (!whole && local < seg_len && (in || (!(wd.y & bit) && win == 0u))) out[local] = o[t];
         }
         if (whole) reinterpret_cast<float4*>(out)[q] = make_float4(o[0], o[1], o[2], o[3]);
       }
     } else {
+      // slots [sh, sh + n) hold ranks w0 .. w0 + n - 1, at output positions
+      // pos0 + slot with pos0 = seg_off + w0 - sh a multiple of 4, so slot
+      // quads are output quads
       const uint32_t n = std::min(seg_cnt - w0, kRankCap);
-      for (uint32_t r = threadIdx.x; r < n; r += NT) {
-        const uint64_t pos = (uint64_t)seg_off + w0 + r;
-        if (pos < R.out_idx_cap) {
-          out_idx[pos] = sidx[r];
-          out_val[pos] = (float)acc[r];
+      const uint64_t pos0 = (uint64_t)seg_off + w0 - sh;  // a multiple of 4
+      for (uint32_t k = threadIdx.x; 4 * k < sh + n; k += NT) {
+        const double2 a01 = reinterpret_cast<const double2*>(acc)[2 * k];
+        const double2 a23 = reinterpret_cast<const double2*>(acc)[2 * k + 1];
+        const uint2 lp = reinterpret_cast<const uint2*>(sloc)[k];  // four 16-bit indices
+        const uint4 oi = make_uint4(seg_lo + (lp.x & 0xFFFFu), seg_lo + (lp.x >> 16), seg_lo + (lp.y & 0xFFFFu),
+                                    seg_lo + (lp.y >> 16));
+        const float4 ov = make_float4((float)a01.x, (float)a01.y, (float)a23.x, (float)a23.y);
+        const uint64_t pos = pos0 + 4ull * k;
+        if (4 * k >= sh && 4 * k + 4 <= sh + n && pos + 4 <= R.out_idx_cap) {
+          reinterpret_cast<uint4*>(out_idx)[pos >> 2] = oi;
+          reinterpret_cast<float4*>(out_val)[pos >> 2] = ov;
+        } else {  // a quad at either end of the window, shared with the neighbours' outputs
+          const uint32_t oiv[4] = {oi.x, oi.y, oi.z, oi.w};
+          const float ovv[4] = {ov.x, ov.y, ov.z, ov.w};
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const uint32_t x = 4 * k + t;
+            if (x >= sh && x < sh + n && pos + t < R.out_idx_cap) {
+              out_idx[pos + t] = oiv[t];
+              out_val[pos + t] = ovv[t];
+            }
+          }
         }
       }
     }
@@ -739,14 +800,18 @@ void launch_write(bool small_p, uint32_t bits, dim3 grid, hipStream_t stream, co
 }
 
 template <int MAXP>
-void launch_write_ranked(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                         uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
+void launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t stream, const uint32_t* idx,
+                         const float* val, uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb,
+                         uint32_t lbq) {
   const dim3 block(kRankThreads);
   switch (bits) {
-    case 0: hipLaunchKernelGGL((k_write_ranked<MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 2: hipLaunchKernelGGL((k_write_ranked<MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 4: hipLaunchKernelGGL((k_write_ranked<MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    default: hipLaunchKernelGGL((k_write_ranked<MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 0:
+      if (quad) hipLaunchKernelGGL((k_write_ranked<MAXP, 0, true>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lbq);
+      else hipLaunchKernelGGL((k_write_ranked<MAXP, 0, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb);
+      break;
+    case 2: hipLaunchKernelGGL((k_write_ranked<MAXP, 2, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 4: hipLaunchKernelGGL((k_write_ranked<MAXP, 4, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    default: hipLaunchKernelGGL((k_write_ranked<MAXP, 8, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
   }
 }
 
@@ -757,6 +822,17 @@ uint32_t lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
   const double mean = (double)total / ((double)P * (double)S);
   uint32_t lb = 4;
   while (lb < 7 && (double)(1u << lb) < 1.5 * mean) ++lb;
+  return lb;
+}
+
+// Lanes per node when each lane takes an aligned quad of pairs: the mean
+// number of quads a run meets (its length / 4, plus 3/4 for the unaligned
+// ends) with room for one standard deviation and more; 2 to 64.
+uint32_t quad_lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
+  const double mean = (double)total / ((double)P * (double)S);
+  const double quads = mean / 4.0 + 0.75 + std::sqrt(mean) / 4.0 + 1.0;
+  uint32_t lb = 1;
+  while (lb < 6 && (double)(1u << lb) < quads) ++lb;
   return lb;
 }
 
@@ -815,8 +891,11 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
     if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
     else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
     hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    if (small_p) launch_write_ranked<256>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
-    else launch_write_ranked<kMaxP>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
+    // 16-byte quads of pairs where both arrays allow them
+    const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
+    const uint32_t lbq = quad_lanes_log2(P, L.S, R.total);
+    if (small_p) launch_write_ranked<256>(R.bits, quad, segs, stream, idx, val, out_idx, out_val, R, lb, lbq);
+    else launch_write_ranked<kMaxP>(R.bits, quad, segs, stream, idx, val, out_idx, out_val, R, lb, lbq);
   }
   return hipGetLastError();
 }
