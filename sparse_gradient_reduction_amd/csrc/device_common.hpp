@@ -44,6 +44,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
+// The value of the lane below (0 in lane 0), by a DPP whole-wave shift right
+// by one lane: one VALU instruction, no LDS permute.
+__device__ __forceinline__ uint32_t from_lane_below(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x138, 0xF, 0xF, false);  // wave_shr:1
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave (all lanes active):
 // shifts by 1, 2, 4 and 8 lanes within each row of 16 (DPP row_shr, lanes
 // without a source add 0), then each row adds the totals of the rows below,

@@ -9,24 +9,26 @@
 //
 // One GPU holds all P contributions. The index space is cut into segments of
 // 4096 indices, the one-GPU analogue of the split phase's index-range owners;
-// a workgroup owns one segment, takes each node's sub-run of pairs falling in
-// it, and merges them by scatter-adding into an LDS-resident fp64 tile of the
-// segment with an occupancy bitmap beside it (ds_add_f64 makes the sums
-// independent of arrival order up to fp64 rounding; the result is rounded to
-// fp32 once). An ordered compaction of the bitmap then emits the segment's
-// part of the sorted sparse result, or the tile is written densely.
+// a workgroup owns one segment and takes each node's run of pairs falling in
+// it. Sums accumulate in fp64 in LDS (ds_add_f64: independent of arrival
+// order up to fp64 rounding) and are rounded to fp32 once.
 //
-//   setup    offsets into the workspace (passed inline, 256 nodes per launch),
-//            state cleared
 //   bounds   node-major streaming pass over the indices: where each node's
-//            run crosses a segment boundary; checks range and order
-//   count    (count-first) per segment: union size from the LDS bitmap
-//   decide   exclusive scan of segment counts, K, dense iff K >= T
-//   write    per segment: fp64 LDS accumulate, then dense tile or compacted
-//            sparse pairs (staged in LDS, stored coalesced) at the segment's
-//            offset
-// Dense-first (estimate >= T): write<dense> also counts; decide; a sparse
-// rewrite runs only if the exact K turned out below T.
+//            run crosses a segment boundary; checks range and order. Its
+//            first workgroup also stores
+//            the node offsets (passed inline) and clears the call's state
+//            and group totals.
+//   count    per segment: union bitmap in LDS, stored for the writer, and
+//            its popcount
+//   decide   exclusive scan of the segment counts, K, dense iff K >= T
+//   write    per segment: the sums, stored densely or as the segment's
+//            sorted part of the sparse result at its offset
+// The estimate of K picks the writer: a full 4096-entry tile when the result
+// is expected dense, slots in union-rank order otherwise; both write either
+// result. More than 256 nodes take setup launches for the offsets first.
+// (Per-group totals added up by atomics in the count pass, to let every
+// writer find its own offset without the scan, made the count pass more than
+// twice as slow: hundreds of workgroups adding to one word.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "qsgd_format.hpp"
@@ -53,12 +55,18 @@ struct State {
 
 struct Layout {
   uint64_t S;  // segments
-  size_t state, offs, qoffs, bounds, cnt, off, bitmaps, total;
+  size_t state, offs, qoffs, flagw, bounds, cnt, off, bitmaps, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Layout make_layout(uint32_t P, uint64_t N) {
+// Workgroups per node in the bounds pass: one per 4096 pairs of the longest
+// node, at most 4096.
+uint32_t bounds_blocks(uint64_t max_nnz) {
+  return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
+}
+
+Layout make_layout(uint32_t P, uint64_t N, uint64_t total_nnz) {
   Layout L{};
   L.S = (N + kSeg - 1) / kSeg;
   size_t o = 0;
@@ -70,6 +78,7 @@ Layout make_layout(uint32_t P, uint64_t N) {
   L.state = take(sizeof(State));
   L.offs = take(8ull * (P + 1));
   L.qoffs = take(16ull * (P + 1));  // code-byte and scale offsets per node (quantized input)
+  L.flagw = take(4ull * P * bounds_blocks(total_nnz));  // input-check bits of every bounds workgroup
   L.bounds = take(4ull * P * (L.S + 1));
   L.cnt = take(4ull * L.S);
   L.off = take(4ull * L.S);
@@ -88,6 +97,8 @@ struct RDev {
   uint64_t out_idx_cap;
   State* state;
   uint64_t* offs;
+  uint32_t* flagw;  // [P * bx]: input-check bits found by each bounds workgroup
+  uint64_t nflagw;
   uint32_t* bounds;
   uint32_t* cnt;
   uint32_t* off;
@@ -108,13 +119,18 @@ struct InlineOffsets {
   uint64_t v[kInlineOffsets];
 };
 
+// The state of the call starts at zero.
+__device__ __forceinline__ void clear_state(const RDev& R) {
+  R.state->flags = 0u;
+  R.state->is_dense = 0u;
+  R.state->K = 0ull;
+}
+
+// More than 256 nodes: offsets stored by launches of 256, the first of which
+// clears the state.
 __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in, int clear) {
   for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) R.offs[first + i] = in.v[i];
-  if (clear && threadIdx.x == 0) {
-    R.state->flags = 0u;
-    R.state->is_dense = 0u;
-    R.state->K = 0ull;
-  }
+  if (clear && threadIdx.x == 0) clear_state(R);
 }
 
 // Quantized input: code-byte and scale offsets of every node, exclusive
@@ -158,22 +174,47 @@ __global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
 // index >= s*4096 (s = S stands for N), written by the pair where the run
 // crosses into segment s. The table is node-major, so the entries one node
 // writes are consecutive words (a segment's workgroup later gathers its P
-// run starts, one word per node).
+// run starts, one word per node). Checks range and order: each workgroup
+// stores the bits it found in its own word, which the count pass folds into
+// the call's state (cleared here before the count pass runs).
 // Each lane loads four consecutive pairs as one 16-byte-aligned quad (quad q
 // holds elements 4q - shift .. 4q - shift + 3, shift placing the quads on
 // 16-byte boundaries of the index array); a quad's left neighbour comes from
 // the lane below through a cross-lane shift, and only lane 0 loads its own.
-__global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift) {
+// With up to 256 nodes the offsets come inline (`in`), and workgroup (0, 0)
+// stores them for the later passes, clears the state and,
+// for quantized input, lays out the code and scale offsets.
+__global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift,
+                                                     InlineOffsets in, int inline_offs) {
   constexpr int kQuads = 4;  // quads per thread and pass
   const uint32_t p = blockIdx.y;
+  if (inline_offs && blockIdx.x == 0 && blockIdx.y == 0) {
+    __shared__ uint64_t scr[kThreads / kWave + 1];
+    for (uint32_t i = threadIdx.x; i <= R.P; i += kThreads) R.offs[i] = in.v[i];
+    if (threadIdx.x == 0) clear_state(R);
+    if (R.bits) {  // code-byte and scale offsets: exclusive prefix sums over the nodes (P <= 256)
+      const uint32_t q = threadIdx.x;
+      const uint64_t nnz = q < R.P ? in.v[q + 1] - in.v[q] : 0ull;
+      uint64_t tc, ts;
+      const uint64_t c = block_exclusive_scan_u64<kThreads>((nnz * R.bits + 7) / 8, scr, tc);
+      const uint64_t sc = block_exclusive_scan_u64<kThreads>((nnz + R.bucket - 1) / R.bucket, scr, ts);
+      if (q < R.P) {
+        R.coffs[q] = c;
+        R.soffs[q] = sc;
+      }
+    }
+  }
   // positions fit in 32 bits (total < 2^32) and so do segment numbers
-  const uint32_t o0 = (uint32_t)R.offs[p], o1 = (uint32_t)R.offs[p + 1];
+  const uint32_t o0 = (uint32_t)(inline_offs ? in.v[p] : R.offs[p]);
+  const uint32_t o1 = (uint32_t)(inline_offs ? in.v[p + 1] : R.offs[p + 1]);
   const uint32_t S = (uint32_t)R.S, N = R.N;
   uint32_t* b = R.bounds + (uint64_t)p * (S + 1);
+  uint32_t* flag = R.flagw + (uint64_t)p * gridDim.x + blockIdx.x;
   uint32_t bad = 0u;
   if (o1 == o0) {  // an empty node starts every segment at its offset
     if (blockIdx.x == 0)
       for (uint32_t s = threadIdx.x; s <= S; s += kThreads) b[s] = o0;
+    if (threadIdx.x == 0) *flag = 0u;
     return;
   }
   const uint32_t q0 = (uint32_t)(((uint64_t)o0 + shift) >> 2);
@@ -200,8 +241,8 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const uint32_t e = e0 + t;
-            const bool in = (!first_quad || (uint32_t)t >= shift) && e < R.total;
-            v[u][t] = in ? idx[e] : 0u;
+            const bool inside = (!first_quad || (uint32_t)t >= shift) && e < R.total;
+            v[u][t] = inside ? idx[e] : 0u;
           }
         }
         if (lane0 && !first_quad && e0 > o0) w[u] = idx[e0 - 1];
@@ -225,11 +266,9 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
         const bool live = (!first_quad || (uint32_t)t >= shift) && e >= o0 && e < o1;
         if (live) {
           const uint32_t s_cur = i < N ? i >> kSegBits : S;
-          uint32_t s_first = 0u;  // first segment whose run starts here
-          if (e > o0) {
-            if (ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
-            s_first = (ip < N ? ip >> kSegBits : S) + 1u;
-          }
+          // first segment whose run starts here (none if this pair is below its predecessor)
+          const uint32_t s_first = e > o0 ? (ip < N ? ip >> kSegBits : S) + 1u : 0u;
+          if (e > o0 && ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
           if (i >= N) bad |= SPARCML_FLAG_INDEX_RANGE;
           for (uint32_t sx = s_first; sx <= s_cur; ++sx) b[sx] = e;
           if (e + 1u == o1)
@@ -239,7 +278,13 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
       }
     }
   }
-  if (bad) atomicOr(&R.state->flags, bad);
+  // every workgroup stores its bits, so no word needs clearing first
+  __shared__ uint32_t block_bad;
+  if (threadIdx.x == 0) block_bad = 0u;
+  __syncthreads();
+  if (bad) atomicOr(&block_bad, bad);
+  __syncthreads();
+  if (threadIdx.x == 0) *flag = block_bad;
 }
 
 // Per-node tables of a quantized segment, in LDS: node-relative position of
@@ -303,14 +348,16 @@ __device__ __forceinline__ Slots make_slots(uint32_t lane_bits, int NT) {
 }
 
 constexpr int kCountThreads = 128;
-constexpr int kWriteThreads = 512;
 constexpr int kWordWaves = kWords / kWave;  // 2
 static_assert(kWords % kWave == 0 && kWords <= kCountThreads, "bitmap words cover whole waves");
 
 // One workgroup per segment: short, independent workgroups kept more
 // segments in flight than long ones walking several segments (measured).
-// Counting needs only the bitmap's 128 words, held by the first two waves;
-// the others leave once the merge is done.
+// Builds the segment's union bitmap in LDS and stores it with its popcount,
+// and folds a share of the bounds pass's check words into the state. (The
+// checks themselves cost the count pass 14 us at 64 x 671088 pairs, the
+// bounds pass, which compares every pair with its predecessor anyway, about
+// 4 us.)
 template <int MAXP>
 __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R,
                                                          uint32_t lane_bits) {
@@ -345,14 +392,21 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
     for (int b = 0; b < kB; ++b)
       if (sl.lane < rn[b].y) mark(ii[b]);
     const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
-    for (int b = 0; b < kB; ++b)
+    for (int b = 0; b < kB; ++b) {
+      if (__ballot(rn[b].y > step) == 0ull) continue;
       for (uint32_t j = sl.lane + step; j < rn[b].y; j += step) mark(idx[rn[b].x + j]);
+    }
+  }
+  if (threadIdx.x == 0) {  // the bounds pass's check bits: words s, s + S, ... of them
+    uint32_t f = 0u;
+    for (uint64_t w = s; w < R.nflagw; w += R.S) f |= R.flagw[w];
+    if (f) atomicOr(&R.state->flags, f);
   }
   __syncthreads();
   const uint32_t wid = threadIdx.x / kWave;
   if (wid >= (uint32_t)kWordWaves) return;
   const uint32_t word = bits[threadIdx.x];
-  R.bitmaps[s * kWords + threadIdx.x] = word;  // the ranked writer places pairs by it
+  R.bitmaps[s * kWords + threadIdx.x] = word;  // the writers place pairs by it
   const uint32_t c = wave_sum((uint32_t)__popc(word));
   if (lane_id() == 0) scr[wid] = c;
   __syncthreads();  // only the word waves are left
@@ -363,7 +417,8 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   }
 }
 
-// Exclusive scan of the segment counts by one workgroup: each thread loads
+// Exclusive scan of the segment counts by one workgroup, into per-segment
+// offsets, K, the dense decision and the result record. Each thread loads
 // 32 consecutive counts at once (one round trip per 32768 segments, 16-byte
 // loads where the run is whole), scans them in registers, and the
 // per-thread totals are scanned across the block.
@@ -423,37 +478,58 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
   }
 }
 
-enum WriteMode { kDecided = 0, kDenseFirst = 1, kSparseOnly = 2 };
+// What a writer workgroup needs of segment s before merging: whether the
+// result is dense, the segment's union count and its output offset. The last
+// thread loads them (its wave has no run-table loads to hold back while it
+// waits); seg_head_finish reads them after the caller's barrier.
+template <int NT>
+__device__ __forceinline__ void seg_head_load(const RDev& R, uint64_t s, uint32_t* head) {
+  if (threadIdx.x == NT - 1) {
+    const uint32_t dense = R.state->is_dense, cnt = R.cnt[s], off = R.off[s];
+    head[0] = dense;
+    head[1] = cnt;
+    head[2] = off;
+  }
+}
 
-// BITS = 0: fp32 values; 2, 4, 8: values decoded from b-bit codes on load
-template <int MODE, int MAXP, int BITS>
-__global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restrict__ idx,
-                                                         const float* __restrict__ val,
-                                                         uint32_t* __restrict__ out_idx, float* __restrict__ out_val,
-                                                         RDev R, uint32_t lane_bits) {
+template <int NT>
+__device__ __forceinline__ uint3 seg_head_finish(const RDev&, uint64_t, const uint32_t* head) {
+  return make_uint3(head[0], head[1], head[2]);
+}
+
+constexpr int kWriteThreads = 512;
+
+// Writer for results expected dense: each segment's sums in a 4096-entry
+// fp64 LDS tile, written out as float4 when the result is dense; when it
+// turns out sparse, each thread stores the union entries of its 8 indices at
+// their ranks from the count pass's bitmap.
+template <int MAXP, int BITS>
+__global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __restrict__ idx,
+                                                              const float* __restrict__ val,
+                                                              uint32_t* __restrict__ out_idx,
+                                                              float* __restrict__ out_val, RDev R,
+                                                              uint32_t lane_bits) {
   constexpr int NT = kWriteThreads;
   constexpr int kB = 4;  // node rows per pass
   __shared__ double acc[kSeg];
-  __shared__ uint32_t bits[kWords];
   __shared__ uint2 runs[MAXP];
-  __shared__ uint32_t scr[NT / kWave + 3];
+  __shared__ uint32_t scr[3];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
-  // these loads and the run table's go out together: one round trip
-  const bool dense = MODE == kDenseFirst ? true : R.state->is_dense != 0u;
-  if (MODE == kSparseOnly && dense) return;  // the dense-first pass already wrote the result
-  const uint32_t seg_cnt = MODE == kDenseFirst ? 1u : R.cnt[s];
-  const uint32_t seg_off = MODE == kDenseFirst ? 0u : R.off[s];
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
+  seg_head_load<NT>(R, s, scr);
+  uint32_t word = 0u;
+  if (threadIdx.x < kWords) word = R.bitmaps[s * kWords + threadIdx.x];
   for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
-  if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
   const Slots sl = make_slots(lane_bits, NT);
   store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
   __syncthreads();
+  const uint3 hd = seg_head_finish<NT>(R, s, scr);
+  const bool dense = hd.x != 0u;
+  const uint32_t seg_cnt = hd.y, seg_off = hd.z;
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
-  // value of node p's pair at absolute position j, run-relative position jr
   auto value_at = [&](uint32_t p, uint32_t j, uint32_t jr) -> float {
     if constexpr (BITS == 0) {
       return val[j];
@@ -465,13 +541,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
       return F::value(code, F::step(R.scales[qruns.sb[p] + bucket_no]));
     }
   };
-  auto add = [&](uint32_t i, float v) {
-    const uint32_t local = i - seg_lo;
-    if (local < seg_len) {
-      atomicAdd(&acc[local], (double)v);
-      atomicOr(&bits[local >> 5], 1u << (local & 31));
-    }
-  };
+  auto add = [&](uint32_t i, float v) { atomicAdd(&acc[i & (kSeg - 1u)], (double)v); };
   for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
     uint2 rn[kB];
     uint32_t ii[kB];
@@ -494,6 +564,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
       if (sl.lane < rn[b].y) add(ii[b], vv[b]);
     const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
     for (int b = 0; b < kB; ++b) {
+      if (__ballot(rn[b].y > step) == 0ull) continue;
       const uint32_t p = p0 + b * sl.groups + sl.group;
       for (uint32_t jr = sl.lane + step; jr < rn[b].y; jr += step) {
         const uint32_t j = rn[b].x + jr;
@@ -501,8 +572,15 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
       }
     }
   }
+  __shared__ uint32_t wbits[kWords], wrank[kWords], wtot[kWordWaves];  // bitmap words, ranks before them
+  if (!dense && threadIdx.x < kWords) {
+    const uint32_t c = (uint32_t)__popc(word);
+    const uint32_t inc = wave_inclusive_scan(c);
+    wbits[threadIdx.x] = word;
+    wrank[threadIdx.x] = inc - c;
+    if (lane_id() == kWave - 1) wtot[threadIdx.x / kWave] = inc;
+  }
   __syncthreads();
-
   if (dense) {
     float* out = out_val + seg_lo;
     if (seg_len == kSeg) {
@@ -514,47 +592,25 @@ __global__ __launch_bounds__(kWriteThreads) void k_write(const uint32_t* __restr
     } else {
       for (uint32_t i = threadIdx.x; i < seg_len; i += NT) out[i] = (float)acc[i];
     }
-    if (MODE != kDenseFirst) return;
-  }
-  if (MODE == kDenseFirst) {  // union size, in the word waves
-    const uint32_t wid = threadIdx.x / kWave;
-    if (wid >= (uint32_t)kWordWaves) return;
-    const uint32_t c = wave_sum((uint32_t)__popc(bits[threadIdx.x]));
-    if (lane_id() == 0) scr[wid] = c;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t tot = 0;
-      for (int w = 0; w < kWordWaves; ++w) tot += scr[w];
-      R.cnt[s] = tot;
-    }
     return;
   }
-  // ordered compaction: each thread owns 8 consecutive indices, stages its
-  // selected pairs in LDS at their rank, then the block stores them coalesced
+  // each thread: indices 8t .. 8t + 7, byte (t mod 4) of word t / 4
   constexpr int kPerT = kSeg / NT;
-  static_assert(kPerT == 8, "one bitmap byte per thread");
-  double v[kPerT];
+  static_assert(kPerT == 8 && kWordWaves == 2, "one bitmap byte per thread");
+  const uint32_t wi = threadIdx.x / 4;
+  const uint32_t wd = wbits[wi];
+  const uint32_t sh = 8 * (threadIdx.x & 3);
+  const uint32_t byte = (wd >> sh) & 0xFFu;
+  uint32_t r = wrank[wi] + (wi >= (uint32_t)kWave ? wtot[0] : 0u) + (uint32_t)__popc(wd & ((1u << sh) - 1u));
 #pragma unroll
-  for (int r = 0; r < kPerT; ++r) v[r] = acc[kPerT * threadIdx.x + r];
-  const uint32_t byte = (bits[threadIdx.x / 4] >> (8 * (threadIdx.x & 3))) & 0xFFu;
-  uint32_t tot;
-  uint32_t q = block_exclusive_scan<NT>((uint32_t)__popc(byte), scr, tot);
-  float* sval = reinterpret_cast<float*>(acc);
-  uint32_t* sidx = reinterpret_cast<uint32_t*>(acc) + kSeg;
-#pragma unroll
-  for (int r = 0; r < kPerT; ++r) {
-    if ((byte >> r) & 1u) {
-      sval[q] = (float)v[r];
-      sidx[q] = seg_lo + kPerT * threadIdx.x + r;
-      ++q;
-    }
-  }
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < tot; i += NT) {
-    const uint64_t pos = (uint64_t)seg_off + i;
-    if (pos < R.out_idx_cap) {
-      out_idx[pos] = sidx[i];
-      out_val[pos] = sval[i];
+  for (int t = 0; t < kPerT; ++t) {
+    if ((byte >> t) & 1u) {
+      const uint64_t pos = (uint64_t)seg_off + r;
+      if (pos < R.out_idx_cap) {
+        out_idx[pos] = seg_lo + kPerT * threadIdx.x + t;
+        out_val[pos] = (float)acc[kPerT * threadIdx.x + t];
+      }
+      ++r;
     }
   }
 }
@@ -597,21 +653,16 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
   __shared__ uint2 words[kWords];  // (ranks before the word, the word)
   __shared__ uint2 runs[MAXP];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
-  __shared__ uint32_t head[3];     // is_dense, the segment's union count, its output offset
+  __shared__ uint32_t scr[3];
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
   const Slots sl = make_slots(lane_bits, NT);
   // every load of the prologue goes out before any wait: the bitmap (wave 0),
-  // the decision, count and offset, and the run table
+  // the counts and totals, and the run table
   uint2 wpair = make_uint2(0u, 0u);
   if (threadIdx.x < kWords / 2) wpair = reinterpret_cast<const uint2*>(R.bitmaps + s * kWords)[threadIdx.x];
-  uint32_t h0 = 0, h1 = 0, h2 = 0;
-  if (threadIdx.x == NT - 1) {
-    h0 = R.state->is_dense;
-    h1 = R.cnt[s];
-    h2 = R.off[s];
-  }
+  seg_head_load<NT>(R, s, scr);
   for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
   store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
   if (threadIdx.x < kWave) {  // word table: wave 0, two words per lane
@@ -620,15 +671,11 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
     words[2 * threadIdx.x] = make_uint2(inc - c0 - c1, wpair.x);
     words[2 * threadIdx.x + 1] = make_uint2(inc - c1, wpair.y);
   }
-  if (threadIdx.x == NT - 1) {
-    head[0] = h0;
-    head[1] = h1;
-    head[2] = h2;
-  }
   __syncthreads();
-  const bool dense = head[0] != 0u;
-  const uint32_t seg_cnt = head[1];
-  const uint32_t seg_off = head[2];
+  const uint3 hd = seg_head_finish<NT>(R, s, scr);
+  const bool dense = hd.x != 0u;
+  const uint32_t seg_cnt = hd.y;
+  const uint32_t seg_off = hd.z;
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
 
   auto value_at = [&](uint32_t p, uint32_t j, uint32_t jr) -> float {
@@ -775,28 +822,22 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
 
 }  // namespace
 
-size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t /*total_nnz*/) { return make_layout(P, N).total; }
+size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t total_nnz) {
+  return make_layout(P, N, total_nnz).total;
+}
 
 namespace {
 
-template <int MODE, int MAXP>
-void launch_write(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                  uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
+template <int MAXP>
+void launch_write_tile(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
+                       uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
   const dim3 block(kWriteThreads);
   switch (bits) {
-    case 0: hipLaunchKernelGGL((k_write<MODE, MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 2: hipLaunchKernelGGL((k_write<MODE, MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 4: hipLaunchKernelGGL((k_write<MODE, MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    default: hipLaunchKernelGGL((k_write<MODE, MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 0: hipLaunchKernelGGL((k_write_tile<MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 2: hipLaunchKernelGGL((k_write_tile<MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 4: hipLaunchKernelGGL((k_write_tile<MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    default: hipLaunchKernelGGL((k_write_tile<MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
   }
-}
-
-template <int MODE>
-void launch_write(bool small_p, uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                  uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
-  // run tables sized for up to 256 nodes keep the write workgroups small
-  if (small_p) launch_write<MODE, 256>(bits, grid, stream, idx, val, out_idx, out_val, R, lb);
-  else launch_write<MODE, kMaxP>(bits, grid, stream, idx, val, out_idx, out_val, R, lb);
 }
 
 template <int MAXP>
@@ -842,7 +883,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
                                 bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream) {
-  const Layout L = make_layout(P, N);
+  const Layout L = make_layout(P, N, h_offsets[P]);
   char* w = static_cast<char*>(ws);
   RDev R;
   R.P = P;
@@ -854,6 +895,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.out_idx_cap = out_idx_cap;
   R.state = reinterpret_cast<State*>(w + L.state);
   R.offs = reinterpret_cast<uint64_t*>(w + L.offs);
+  R.flagw = reinterpret_cast<uint32_t*>(w + L.flagw);
   R.bounds = reinterpret_cast<uint32_t*>(w + L.bounds);
   R.cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
   R.off = reinterpret_cast<uint32_t*>(w + L.off);
@@ -870,27 +912,34 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   uint64_t max_nnz = 0;
   for (uint32_t p = 0; p < P; ++p) max_nnz = std::max<uint64_t>(max_nnz, h_offsets[p + 1] - h_offsets[p]);
 
-  for (uint32_t first = 0; first < P + 1; first += kInlineOffsets) {
-    InlineOffsets in;
-    const uint32_t count = std::min<uint32_t>(kInlineOffsets, P + 1 - first);
-    for (uint32_t i = 0; i < count; ++i) in.v[i] = h_offsets[first + i];
-    hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, stream, R, first, count, in, first == 0 ? 1 : 0);
+  // offsets inline to the bounds pass for up to 256 nodes, else by setup launches
+  InlineOffsets in;
+  const bool inline_offs = P + 1 <= (uint32_t)kInlineOffsets;
+  if (inline_offs) {
+    for (uint32_t i = 0; i <= P; ++i) in.v[i] = h_offsets[i];
+  } else {
+    for (uint32_t first = 0; first < P + 1; first += kInlineOffsets) {
+      InlineOffsets part;
+      const uint32_t count = std::min<uint32_t>(kInlineOffsets, P + 1 - first);
+      for (uint32_t i = 0; i < count; ++i) part.v[i] = h_offsets[first + i];
+      hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, stream, R, first, count, part, first == 0 ? 1 : 0);
+    }
+    if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   }
-  if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
-  const uint32_t bx = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_nnz + 4095) / 4096, 4096));
+  const uint32_t bx = bounds_blocks(max_nnz);
+  R.nflagw = (uint64_t)bx * P;
   const uint32_t shift = (uint32_t)((reinterpret_cast<uintptr_t>(idx) >> 2) & 3u);
-  hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R, shift);
+  hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R, shift, in, inline_offs ? 1 : 0);
   const dim3 segs((uint32_t)L.S);
   const bool small_p = P <= 256;
   const uint32_t lb = lanes_log2(P, L.S, R.total);
-  if (dense_first) {
-    launch_write<kDenseFirst>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
-    hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-    launch_write<kSparseOnly>(small_p, R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
+  if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
+  else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
+  hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
+  if (dense_first) {  // the estimate expects a dense result: the full tile
+    if (small_p) launch_write_tile<256>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
+    else launch_write_tile<kMaxP>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
   } else {
-    if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
-    else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
-    hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
     // 16-byte quads of pairs where both arrays allow them
     const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
     const uint32_t lbq = quad_lanes_log2(P, L.S, R.total);
