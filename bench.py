@@ -27,7 +27,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4, help="0..4; 4 = wide-ResNet (2^27 x 64, q4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-nodes", type=int, default=8, help="nodes in the oracle's timed sample")
+    ap.add_argument("--cpu-nodes", type=int, default=16, help="nodes in the oracle's timed sample")
     ap.add_argument("--seed", type=int, default=987654321)
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the other workloads' timings (profiling runs: their kernels would mix into the averages)")
@@ -75,7 +75,8 @@ def med(xs):
 
 
 class HipEvents:
-    """Raw HIP events (the C ABI's profiling hook takes hipEvent_t)."""
+    """Raw HIP events: the measurement entry points (sparcml_bench_*) take
+    hipEvent_t handles and attach them to kernel dispatches."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
@@ -96,6 +97,22 @@ class HipEvents:
 
     def destroy(self, ev):
         self.hip.hipEventDestroy(ev)
+
+    def op_events(self, sg, kernel_pair: bool, op_stop: bool = True):
+        """A sparcml_bench_events with fresh events: the op's start (and stop),
+        and the dominant kernel's pair when asked for."""
+        new = lambda: self.create().value
+        return sg.BenchEvents(new(), new() if op_stop else None, new() if kernel_pair else None,
+                              new() if kernel_pair else None)
+
+    def span_ms(self, e):
+        """First kernel's start to last kernel's end of one op. Where the
+        dominant kernel is the op's last (the reduce's writer), its own stop
+        event closes the span."""
+        return self.elapsed_ms(ctypes.c_void_p(e.op_start), ctypes.c_void_p(e.op_stop or e.kernel_stop))
+
+    def kernel_ms(self, e):
+        return self.elapsed_ms(ctypes.c_void_p(e.kernel_start), ctypes.c_void_p(e.kernel_stop))
 
 
 def main():
@@ -144,30 +161,23 @@ def main():
         del src, dst
 
     ev = HipEvents()
-    step_events = [[ev.create() for _ in range(4)] for _ in range(steps)]
-    k1_events = [(ev.create(), ev.create()) for _ in range(steps)]
     lib = sg.lib()
+    # per timed step: events on the kernel dispatches of each op (Top-k: the
+    # op's span and k_stream's own pair; q4 and dq4: their one kernel; the
+    # reduce: its span, closed by the writer's own stop, and the writer's pair)
+    recs = [{"topk": ev.op_events(sg, True), "q4": ev.op_events(sg, False), "dq4": ev.op_events(sg, False),
+             "reduce": ev.op_events(sg, True, op_stop=False)} for _ in range(steps)]
 
-    def step(t, marks=None, k1=None):
-        stream = torch.cuda.current_stream(dev).cuda_stream
-        if marks:
-            ev.hip.hipEventRecord(marks[0], ctypes.c_void_p(stream))
-        if k1:
-            lib.sparcml_profile_next_topk(k1[0], k1[1])
-        sg.topk_ef(pool[t % 2], residual, k, out_idx=idx, out_val=val, workspace=ws_topk)
-        if marks:
-            ev.hip.hipEventRecord(marks[1], ctypes.c_void_p(stream))
+    def step(t, rec=None):
+        e = rec or {}
+        sg.topk_ef(pool[t % 2], residual, k, out_idx=idx, out_val=val, workspace=ws_topk, events=e.get("topk"))
         red_in = val
         if B:
-            sg.q4(val, B, args.seed, t, codes=codes, scales=scales)
-            sg.dq4(codes, scales, k, B, out=dval)
+            sg.q4(val, B, args.seed, t, codes=codes, scales=scales, events=e.get("q4"))
+            sg.dq4(codes, scales, k, B, out=dval, events=e.get("dq4"))
             red_in = dval
-        if marks:
-            ev.hip.hipEventRecord(marks[2], ctypes.c_void_p(stream))
         sg.sparse_reduce(offsets, idx.view(-1), red_in.view(-1), N, w.delta, out_idx=red_idx, out_val=red_val,
-                         result=red_res, workspace=ws_red)
-        if marks:
-            ev.hip.hipEventRecord(marks[3], ctypes.c_void_p(stream))
+                         result=red_res, workspace=ws_red, events=e.get("reduce"))
 
     for t in range(warmup):
         step(t)
@@ -176,37 +186,40 @@ def main():
 
     t0 = time.perf_counter()
     for t in range(steps):
-        step(warmup + t, marks=step_events[t], k1=k1_events[t])
+        step(warmup + t, recs[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     ms_step = 1000.0 * wall / steps
-    t_topk = sum(ev.elapsed_ms(m[0], m[1]) for m in step_events) / steps
-    t_q = sum(ev.elapsed_ms(m[1], m[2]) for m in step_events) / steps
-    t_red = sum(ev.elapsed_ms(m[2], m[3]) for m in step_events) / steps
-    t_gpu_step = sum(ev.elapsed_ms(m[0], m[3]) for m in step_events) / steps
-    t_k1 = sum(ev.elapsed_ms(a, b) for a, b in k1_events) / steps
+    mean = lambda xs: sum(xs) / len(xs)
+    topk_spans = [ev.span_ms(r["topk"]) for r in recs]
+    k1_list = sorted(ev.kernel_ms(r["topk"]) for r in recs)
+    red_spans = [ev.span_ms(r["reduce"]) for r in recs]
+    writer_list = sorted(ev.kernel_ms(r["reduce"]) for r in recs)
+    t_topk, t_red, t_k1 = mean(topk_spans), mean(red_spans), mean(k1_list)
+    t_q4 = mean([ev.span_ms(r["q4"]) for r in recs]) if B else 0.0
+    t_dq4 = mean([ev.span_ms(r["dq4"]) for r in recs]) if B else 0.0
+    # the GPU's own clock from the step's first dispatch to its last kernel's end
+    step_list = sorted(ev.elapsed_ms(ctypes.c_void_p(r["topk"].op_start), ctypes.c_void_p(r["reduce"].kernel_stop))
+                       for r in recs)
+    t_gpu_step = mean(step_list)
     K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()  # the timed steps' result
-    k1_list = sorted(ev.elapsed_ms(a, b) for a, b in k1_events)
-    step_list = sorted(ev.elapsed_ms(m[0], m[3]) for m in step_events)
 
     # ---- reduce alone, cold (LLC flushed by a 1 GiB write) and warm --------
     def time_reduce(cold, reps=10):
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None
-        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in e:
+        rr = [ev.op_events(sg, True, op_stop=False) for _ in range(reps)]
+        for e in rr:
             if cold:
                 flush.fill_(1.0)
-            a.record()
             sg.sparse_reduce(offsets, idx.view(-1), red_in_last.view(-1), N, w.delta, out_idx=red_idx,
-                             out_val=red_val, result=red_res, workspace=ws_red)
-            b.record()
+                             out_val=red_val, result=red_res, workspace=ws_red, events=e)
         torch.cuda.synchronize()
-        return sorted(a.elapsed_time(b) for a, b in e)
+        return sorted(ev.span_ms(e) for e in rr), sorted(ev.kernel_ms(e) for e in rr)
 
     red_in_last = dval if B else val
-    red_cold = time_reduce(True)
-    red_warm = time_reduce(False)
+    red_cold, red_cold_writer = time_reduce(True)
+    red_warm, red_warm_writer = time_reduce(False)
 
     def time_ops(fn, reps=10):
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -329,14 +342,15 @@ def main():
     t_copy = time_torch(lambda: scratch.copy_(residual))
     t_add = time_torch(lambda: torch.add(pool[0], residual, out=scratch))
     # the library's plain streaming add with the stream kernel's access pattern, timed like k_stream
-    ref_ev = [(ev.create(), ev.create()) for _ in range(5)]
+    ref_ev = [ev.op_events(sg, False) for _ in range(5)]
     stream_h = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    for a_ev, b_ev in [ref_ev[0]] + ref_ev:
-        st = lib.sparcml_reference_stream(P * N, ctypes.c_void_p(pool[0].data_ptr()),
-                                          ctypes.c_void_p(scratch.data_ptr()), a_ev, b_ev, stream_h)
+    for e in [ref_ev[0]] + ref_ev:
+        st = sg.bench_lib().sparcml_bench_reference_stream(P * N, ctypes.c_void_p(pool[0].data_ptr()),
+                                                           ctypes.c_void_p(scratch.data_ptr()), ctypes.byref(e),
+                                                           stream_h)
         assert st == 0, st
     torch.cuda.synchronize()
-    t_ref = min(ev.elapsed_ms(a_ev, b_ev) for a_ev, b_ev in ref_ev)
+    t_ref = min(ev.span_ms(e) for e in ref_ev)
     del scratch
 
     paths = sg.topk_ef_paths(ws_topk, P).cpu()
@@ -345,16 +359,22 @@ def main():
     # algorithmic bytes per step
     nb = (k + B - 1) // B if B else 0
     b_topk = 12 * P * N + 8 * P * k
-    b_q = (P * k * 4.5 + 4 * P * nb) * 2 if B else 0
+    b_q4 = P * k * 4.5 + 4 * P * nb if B else 0  # read values, write codes and scales
+    b_dq4 = b_q4                                 # read codes and scales, write values
     b_red_in = 8 * P * k
     b_red_out = 4 * N if is_dense else 8 * K
-    b_step = b_topk + b_q + b_red_in + b_red_out
+    b_step = b_topk + b_q4 + b_dq4 + b_red_in + b_red_out
     k1_bytes = 12 * P * N
     k1_gbs = k1_bytes / (t_k1 * 1e-3) / 1e9
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    frac = lambda nbytes, ms: round(gbs(nbytes, ms) / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": METRIC,
-        "value": round(b_step / (ms_step * 1e-3) / 1e9, 2),
+        "value": round(gbs(b_step, ms_step), 2),
+        "value_is": "whole-step algorithmic GB/s: the bytes one step's ops must move (Top-k EF, q4, dq4, reduce "
+                    "input and output) over the wall-clock time per step; the metric's own parts follow as "
+                    "reduce_*, topk_* and q4_*",
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": steps,
@@ -367,16 +387,34 @@ def main():
         "data": "synthetic (seeded gradients resident in HBM; no dataset)",
         "config": {"workload": w.name, "P": P, "N": N, "k": k, "delta": w.delta, "q4_bucket": B,
                    "ef_steps": "carried across all timed steps", "parallelism": "none (1 GPU)"},
-        "breakdown_ms": {"topk_ef": round(t_topk, 4), "q4_dq4": round(t_q, 4), "sparse_reduce": round(t_red, 4),
-                         "gpu_step": round(t_gpu_step, 4)},
-        "step_gpu_ms_median_min": [round(med(step_list), 4), round(step_list[0], 4)],
+        # the metric's parts, each from events on its ops' own kernel dispatches in the timed steps
+        "reduce_input_gb_per_s": round(gbs(b_red_in, t_red), 2),
+        "reduce_gb_per_s": round(gbs(b_red_in + b_red_out, t_red), 2),
+        "reduce_frac_hbm_peak": frac(b_red_in + b_red_out, t_red),
         "topk_gelem_per_s": round(P * N / (t_topk * 1e-3) / 1e9, 2),
-        "reduce_input_gb_per_s": round(b_red_in / (t_red * 1e-3) / 1e9, 2),
-        "reduce_frac_hbm_peak": round((b_red_in + b_red_out) / (t_red * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "step_frac_hbm_peak": round(b_step / (t_gpu_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "reduce_alone_ms": {"cold_median": round(med(red_cold), 4), "cold_min": round(red_cold[0], 4),
+        "topk_gb_per_s": round(gbs(b_topk, t_topk), 2),
+        "topk_frac_hbm_peak": frac(b_topk, t_topk),
+        "q4_gb_per_s": round(gbs(b_q4, t_q4), 2) if B else None,
+        "q4_frac_hbm_peak": frac(b_q4, t_q4) if B else None,
+        "dq4_gb_per_s": round(gbs(b_dq4, t_dq4), 2) if B else None,
+        "dq4_frac_hbm_peak": frac(b_dq4, t_dq4) if B else None,
+        "breakdown_ms": {"what": "mean over the timed steps of each op's span on the GPU clock: its first "
+                                 "kernel's start to its last kernel's end (events attached to the dispatches)",
+                         "topk_ef": round(t_topk, 4), "q4": round(t_q4, 4), "dq4": round(t_dq4, 4),
+                         "sparse_reduce": round(t_red, 4), "gpu_step": round(t_gpu_step, 4),
+                         "between_ops": round(t_gpu_step - t_topk - t_q4 - t_dq4 - t_red, 4),
+                         "k_stream": round(t_k1, 4), "reduce_writer": round(mean(writer_list), 4)},
+        "step_gpu_ms_median_min": [round(med(step_list), 4), round(step_list[0], 4)],
+        "step_frac_hbm_peak": frac(b_step, t_gpu_step),
+        "algorithmic_bytes": {"topk_ef": b_topk, "q4": b_q4, "dq4": b_dq4, "reduce_in": b_red_in,
+                              "reduce_out": b_red_out, "step": b_step},
+        "reduce_alone_ms": {"what": "the reduce of the last step's pairs repeated alone, its span from dispatch "
+                                    "events; cold = after a 1 GiB write that flushes the last-level cache",
+                            "cold_median": round(med(red_cold), 4), "cold_min": round(red_cold[0], 4),
                             "warm_median": round(med(red_warm), 4), "warm_min": round(red_warm[0], 4),
-                            "cold_input_gb_per_s": round(b_red_in / (med(red_cold) * 1e-3) / 1e9, 2)},
+                            "cold_writer_median": round(med(red_cold_writer), 4),
+                            "cold_input_gb_per_s": round(gbs(b_red_in, med(red_cold)), 2),
+                            "cold_frac_hbm_peak": frac(b_red_in + b_red_out, med(red_cold))},
         "reduce_result": {"nnz": K, "dense": is_dense},
         **extra,
         "topk_rescan_nodes": int((paths[0] == 1).sum()),
@@ -386,8 +424,9 @@ def main():
                      "avg_launch_ms": round(t_k1, 4), "median_min_launch_ms": [round(med(k1_list), 4),
                                                                               round(k1_list[0], 4)],
                      "algorithmic_bytes": k1_bytes},
-        "streaming_ceiling": {"what": "torch copy/add and the library's plain streaming add (the stream kernel's "
-                                      "access pattern, no candidates) on the same [P][N] fp32 arrays, best of 5",
+        "streaming_ceiling": {"what": "torch copy/add and the plain streaming add of libsparcml_bench.so (the "
+                                      "stream kernel's access pattern, no candidates) on the same [P][N] fp32 "
+                                      "arrays, best of 5",
                               "copy_gb_per_s": round(8 * P * N / (t_copy * 1e-3) / 1e9, 1),
                               "add_gb_per_s": round(12 * P * N / (t_add * 1e-3) / 1e9, 1),
                               "k_stream_over_add": round(t_add / t_k1, 4),
@@ -403,17 +442,20 @@ def main():
         if B:
             del codes, scales, dval
         torch.cuda.synchronize()
-        out["other_configs"] = other_configs(sg, W, dev, w.wid)
+        out["other_configs"] = other_configs(sg, W, dev, w.wid, ev)
     print(json.dumps(out), flush=True)
 
 
-def other_configs(sg, W, dev, skip_wid):
+def other_configs(sg, W, dev, skip_wid, ev):
     """The other workloads at their full sizes, outside the timed steps: the
-    median per-step time of Top-k EF and of the reduce of its pairs over the
+    median per-step span of Top-k EF and of the reduce of its pairs over the
     workload's error-feedback steps (from a zero residual), or of the reduce
-    alone for the already-sparse workload, each with its algorithmic bytes;
-    and the same step (or reduce) captured once as a HIP graph and replayed,
-    which removes the launch gaps that dominate the small workloads."""
+    alone for the already-sparse workload, each with its algorithmic bytes.
+    Spans come from events on the ops' own kernel dispatches; `cold` runs each
+    op after a 1 GiB write that flushes the last-level cache (the headline
+    figures), `warm` right after the previous op. Also the same step (or
+    reduce) captured once as a HIP graph and replayed, which removes the
+    launch gaps that dominate the small workloads."""
     import numpy as np
     import torch
 
@@ -434,15 +476,16 @@ def other_configs(sg, W, dev, skip_wid):
         with torch.cuda.graph(graph):
             fn()
         graph.replay()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for a, b in ev:
+        tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in tev:
             a.record()
             graph.replay()
             b.record()
         torch.cuda.synchronize()
         del graph
-        return med([a.elapsed_time(b) for a, b in ev])
+        return med([a.elapsed_time(b) for a, b in tev])
 
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     res = {}
     for wi in range(5):
         w = W.workload(wi)
@@ -459,18 +502,23 @@ def other_configs(sg, W, dev, skip_wid):
             rv = torch.empty(N, dtype=torch.float32, device=dev)
             rr = torch.zeros(16, dtype=torch.uint8, device=dev)
             wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, off[-1]), dtype=torch.uint8, device=dev)
-            run = lambda: sg.sparse_reduce(off, ii, vv, N, w.delta, out_idx=ri, out_val=rv, result=rr, workspace=wr)
+            run = lambda e=None: sg.sparse_reduce(off, ii, vv, N, w.delta, out_idx=ri, out_val=rv, result=rr,
+                                                  workspace=wr, events=e)
             run()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-            for a, b in ev:
-                a.record()
-                run()
-                b.record()
-            torch.cuda.synchronize()
-            t = med([a.elapsed_time(b) for a, b in ev])
+            spans = {}
+            for mode in ("cold", "warm"):
+                es = [ev.op_events(sg, True, op_stop=False) for _ in range(10)]
+                for e in es:
+                    if mode == "cold":
+                        flush.fill_(1.0)
+                    run(e)
+                torch.cuda.synchronize()
+                spans[mode] = med([ev.span_ms(e) for e in es])
+            t = spans["cold"]
             K, dense, flags = sg.ReduceOutput(rr, ri, rv, N).read()
             b_in, b_out = 8 * off[-1], (4 * N if dense else 8 * K)
-            res[w.name] = {"reduce_ms": round(t, 4), "pairs": off[-1], "nnz": K, "dense": dense,
+            res[w.name] = {"reduce_ms": round(t, 4), "reduce_warm_ms": round(spans["warm"], 4), "pairs": off[-1],
+                           "nnz": K, "dense": dense,
                            "reduce_input_gb_per_s": round(b_in / (t * 1e-3) / 1e9, 1),
                            "reduce_frac_hbm_peak": round((b_in + b_out) / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                            "reduce_graph_ms": round(graph_ms(run), 4)}
@@ -485,25 +533,30 @@ def other_configs(sg, W, dev, skip_wid):
         rv = torch.empty(N, dtype=torch.float32, device=dev)
         rr = torch.zeros(16, dtype=torch.uint8, device=dev)
         wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
-        t_topk, t_red, per_step = [], [], []
-        for rep in range(2):  # the first pass warms up; the second is timed
+        t_topk = {"cold": [], "warm": []}
+        t_red = {"cold": [], "warm": []}
+        per_step = []
+        for mode in ("warm-up", "warm", "cold"):  # each pass from a zero residual over the EF steps
             r.zero_()
             for t in range(w.steps):
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-                e[0].record()
-                sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws)
-                e[1].record()
+                et, er = ev.op_events(sg, True), ev.op_events(sg, True, op_stop=False)
+                if mode == "cold":
+                    flush.fill_(1.0)
+                sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws, events=et)
+                if mode == "cold":
+                    flush.fill_(1.0)
                 sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
-                                 workspace=wr)
-                e[2].record()
-                if rep == 1:
-                    torch.cuda.synchronize()
+                                 workspace=wr, events=er)
+                if mode == "warm-up":
+                    continue
+                torch.cuda.synchronize()
+                t_topk[mode].append(ev.span_ms(et))
+                t_red[mode].append(ev.span_ms(er))
+                if mode == "cold":
                     K, dense, flags = sg.ReduceOutput(rr, ri, rv, N).read()
-                    t_topk.append(e[0].elapsed_time(e[1]))
-                    t_red.append(e[1].elapsed_time(e[2]))
                     per_step.append({"nnz": K, "dense": dense})
         torch.cuda.synchronize()
-        tk, tr = med(t_topk), med(t_red)
+        tk, tr = med(t_topk["cold"]), med(t_red["cold"])
 
         def one_step():
             sg.topk_ef(grads[0], r, k, out_idx=idx, out_val=val, workspace=ws)
@@ -519,18 +572,19 @@ def other_configs(sg, W, dev, skip_wid):
         lv = torch.empty((P, int(lks.sum())), dtype=torch.float32, device=dev)
         layers_call = lambda: sg.topk_ef_layers(grads[0], r, lo, lks, out_idx=li, out_val=lv, workspace=wl)
         layers_call()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
-        for a, b in ev:
+        tev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for a, b in tev:
             a.record()
             layers_call()
             b.record()
         torch.cuda.synchronize()
-        t_layers = med([a.elapsed_time(b) for a, b in ev])
+        t_layers = med([a.elapsed_time(b) for a, b in tev])
         del wl, li, lv
         b_topk = 12 * P * N + 8 * P * k
         b_in = 8 * P * k
         b_out = [4 * N if s["dense"] else 8 * s["nnz"] for s in per_step]
         res[w.name] = {"steps": w.steps, "topk_ms": round(tk, 4), "reduce_ms": round(tr, 4),
+                       "topk_warm_ms": round(med(t_topk["warm"]), 4), "reduce_warm_ms": round(med(t_red["warm"]), 4),
                        "topk_gelem_per_s": round(P * N / (tk * 1e-3) / 1e9, 1),
                        "topk_frac_hbm_peak": round(b_topk / (tk * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                        "reduce_input_gb_per_s": round(b_in / (tr * 1e-3) / 1e9, 1),
@@ -540,7 +594,20 @@ def other_configs(sg, W, dev, skip_wid):
                        "per_step": per_step}
         del grads, r, ws, idx, val, ri, rv, rr, wr
         torch.cuda.synchronize()
+    del flush
     return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w, g_dev, args, sg):
@@ -570,7 +637,14 @@ def cpu_baseline(w, g_dev, args, sg):
     b = 12 * S * w.N + 8 * S * w.k + ((S * w.k * 4.5 + 4 * S * nb) * 2 if B else 0) + 8 * S * w.k + \
         (4 * w.N if dense else 8 * K)
     return {"value": round(b / (t3 - t0) / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{S} of {w.P} nodes, full N={w.N} each: Top-k EF, q4+dq4, reduce of their pairs",
+            "sample": f"{S} of {w.P} nodes, full N={w.N} each: Top-k EF, q4+dq4, and the reduce of these {S} "
+                      f"nodes' pairs only (K={K} of the sample, not of all {w.P} nodes)",
+            "threads_used": threads,
+            "thread_cap": f"the oracle runs one thread per node (OpenMP over nodes), so it uses at most the "
+                          f"{S} sampled nodes' worth of threads: min(OpenMP threads {oracle.max_threads()}, {S})",
+            "host_cores": len(os.sched_getaffinity(0)),
+            "cpu_count": os.cpu_count(),
+            "cpu_model": cpu_model(),
             "seconds": {"topk_ef": round(t1 - t0, 3), "q4_dq4": round(t2 - t1, 3), "reduce": round(t3 - t2, 3)},
             "topk_gelem_per_s": round(S * w.N / (t1 - t0) / 1e9, 4)}
 

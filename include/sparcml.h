@@ -22,7 +22,9 @@
  *   - Pointers marked "device" are HIP device allocations on the current
  *     device; pointers marked "host" are ordinary host memory.
  *   - The caller owns every buffer. The library allocates nothing and keeps
- *     no state between calls, apart from the optional profiling events below.
+ *     no state between calls (the allocation-free reduce's static scratch
+ *     aside). Measurement variants that attach caller-owned events to the
+ *     kernel dispatches are declared in sparcml_bench.h.
  *   - Calls are asynchronous on `stream` and stream-ordered, in the spirit of
  *     the non-blocking collectives of the paper (section 7, "Non-Blocking
  *     Operations"): results are valid once the stream has reached them.
@@ -375,28 +377,6 @@ sparcml_status sparcml_qsgd_dense_result(uint32_t bits, uint64_t N, uint32_t buc
 /* Uniform-model estimate of K used when no hint is given (Appendix B.1):
  * N * (1 - prod_p (1 - nnz_p / N)), capped by sum_p nnz_p. Host only. */
 double sparcml_estimate_nnz(uint32_t P, uint64_t N, const uint64_t* h_offsets);
-
-/* ------------------------------------------------------------------------
- * Profiling hook (measurement only). Attaches `start` and `stop` to the
- * dispatch of the streaming error-feedback kernel of the next
- * sparcml_topk_ef call made by the calling thread (hipExtLaunchKernel), so
- * that hipEventElapsedTime(start, stop) is that kernel's own duration; the
- * events are then forgotten. Pass NULL, NULL to cancel. The events belong to
- * the caller and must have been created on the current device.
- * ---------------------------------------------------------------------- */
-void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop);
-
-/* ------------------------------------------------------------------------
- * Attainable-bandwidth reference (measurement only, not part of the method):
- * r[i] += g[i] for i < n with exactly the stream kernel's access pattern
- * (one 1024-element tile per workgroup, non-temporal float4 loads and
- * stores). `start` / `stop` (may be NULL) are attached to the kernel's
- * dispatch, as for sparcml_profile_next_topk.
- *   g, r   device, n fp32 each, 16-byte aligned, not overlapping
- *   n      < 1024 * 2^24
- * ---------------------------------------------------------------------- */
-sparcml_status sparcml_reference_stream(uint64_t n, const float* g, float* r, hipEvent_t start,
-                                        hipEvent_t stop, hipStream_t stream);
 
 #ifdef __cplusplus
 }

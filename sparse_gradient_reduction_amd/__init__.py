@@ -18,6 +18,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparcml.so")
+BENCH_LIB_PATH = os.path.join(_PKG, "libsparcml_bench.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = 0, 1, 2, 3, 4
 REDUCE_SCRATCH_BYTES = 32 << 20  # SPARCML_REDUCE_SCRATCH_BYTES: static scratch of sparse_reduce_noalloc
@@ -78,10 +79,15 @@ def _load():
     L.sparcml_sparse_reduce_noalloc.restype = st
     L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
     L.sparcml_estimate_nnz.restype = f64
-    L.sparcml_reference_stream.argtypes = [u64, vp, vp, vp, vp, vp]
-    L.sparcml_reference_stream.restype = st
-    L.sparcml_profile_next_topk.argtypes = [vp, vp]
-    L.sparcml_profile_next_topk.restype = None
+    ev = ctypes.POINTER(BenchEvents)
+    L.sparcml_bench_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, ev, vp]
+    L.sparcml_bench_topk_ef.restype = st
+    L.sparcml_bench_qsgd.argtypes = [u32, u32, u64, u32, u64, u32, u32, vp, vp, vp, ev, vp]
+    L.sparcml_bench_qsgd.restype = st
+    L.sparcml_bench_dqsgd.argtypes = [u32, u32, u64, u32, vp, vp, vp, ev, vp]
+    L.sparcml_bench_dqsgd.restype = st
+    L.sparcml_bench_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
+    L.sparcml_bench_sparse_reduce.restype = st
     _lib = L
     return L
 
@@ -89,6 +95,31 @@ def _load():
 def lib():
     """The loaded ctypes handle of libsparcml.so."""
     return _load()
+
+
+class BenchEvents(ctypes.Structure):
+    """sparcml_bench_events: HIP events (raw handles, or None) that the
+    measurement entry points attach to kernel dispatches."""
+    _fields_ = [("op_start", ctypes.c_void_p), ("op_stop", ctypes.c_void_p),
+                ("kernel_start", ctypes.c_void_p), ("kernel_stop", ctypes.c_void_p)]
+
+
+_bench_lib = None
+
+
+def bench_lib():
+    """The loaded ctypes handle of libsparcml_bench.so (measurement only: the
+    bandwidth reference kernel)."""
+    global _bench_lib
+    if _bench_lib is None:
+        if not os.path.exists(BENCH_LIB_PATH):
+            raise RuntimeError(f"{BENCH_LIB_PATH} is not built; run `python -m sparse_gradient_reduction_amd.build`")
+        L = ctypes.CDLL(BENCH_LIB_PATH)
+        L.sparcml_bench_reference_stream.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.POINTER(BenchEvents), ctypes.c_void_p]
+        L.sparcml_bench_reference_stream.restype = ctypes.c_int
+        _bench_lib = L
+    return _bench_lib
 
 
 def _stream(device) -> int:
@@ -115,9 +146,11 @@ def topk_ef_workspace_bytes(P: int, N: int, k: int) -> int:
 
 
 def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optional[torch.Tensor] = None,
-            out_val: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+            out_val: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            events: Optional[BenchEvents] = None):
     """Error-feedback Top-k on [P, N] fp32 `grad`; `residual` is updated in place.
-    Returns (idx [P, k] int32 holding uint32 indices, val [P, k] float32)."""
+    Returns (idx [P, k] int32 holding uint32 indices, val [P, k] float32).
+    `events` (measurement only) routes the call through sparcml_bench_topk_ef."""
     _check_dev(grad, torch.float32, "grad")
     _check_dev(residual, torch.float32, "residual")
     if grad.dim() != 2 or grad.shape != residual.shape:
@@ -132,8 +165,13 @@ def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optiona
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     L = _load()
-    st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
-                           _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    if events is None:
+        st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
+                               _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    else:
+        st = L.sparcml_bench_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
+                                     _ptr(workspace), workspace.numel(), ctypes.byref(events),
+                                     ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_topk_ef")
     return out_idx, out_val
 
@@ -213,7 +251,7 @@ def topk_ef_paths(workspace: torch.Tensor, P: int) -> torch.Tensor:
 
 # ---------------------------------------------------------------------------
 def q4(val: torch.Tensor, bucket: int, seed: int, step: int, codes: Optional[torch.Tensor] = None,
-       scales: Optional[torch.Tensor] = None):
+       scales: Optional[torch.Tensor] = None, events: Optional[BenchEvents] = None):
     """[P, n] fp32 -> (codes [P, ceil(n/2)] uint8, scales [P, ceil(n/bucket)] fp32)."""
     _check_dev(val, torch.float32, "val")
     P, n = val.shape
@@ -222,20 +260,29 @@ def q4(val: torch.Tensor, bucket: int, seed: int, step: int, codes: Optional[tor
         codes = torch.empty((P, (n + 1) // 2), dtype=torch.uint8, device=dev)
     if scales is None:
         scales = torch.empty((P, (n + bucket - 1) // bucket), dtype=torch.float32, device=dev)
-    st = _load().sparcml_q4(P, n, bucket, seed & ((1 << 64) - 1), step, _ptr(val), _ptr(codes), _ptr(scales),
-                            ctypes.c_void_p(_stream(dev)))
+    if events is None:
+        st = _load().sparcml_q4(P, n, bucket, seed & ((1 << 64) - 1), step, _ptr(val), _ptr(codes), _ptr(scales),
+                                ctypes.c_void_p(_stream(dev)))
+    else:  # measurement: the same call with events on its kernel
+        st = _load().sparcml_bench_qsgd(4, P, n, bucket, seed & ((1 << 64) - 1), step, 0, _ptr(val), _ptr(codes),
+                                        _ptr(scales), ctypes.byref(events), ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_q4")
     return codes, scales
 
 
-def dq4(codes: torch.Tensor, scales: torch.Tensor, n: int, bucket: int, out: Optional[torch.Tensor] = None):
+def dq4(codes: torch.Tensor, scales: torch.Tensor, n: int, bucket: int, out: Optional[torch.Tensor] = None,
+        events: Optional[BenchEvents] = None):
     _check_dev(codes, torch.uint8, "codes")
     _check_dev(scales, torch.float32, "scales")
     P = codes.shape[0]
     if out is None:
         out = torch.empty((P, n), dtype=torch.float32, device=codes.device)
-    st = _load().sparcml_dq4(P, n, bucket, _ptr(codes), _ptr(scales), _ptr(out),
-                             ctypes.c_void_p(_stream(codes.device)))
+    if events is None:
+        st = _load().sparcml_dq4(P, n, bucket, _ptr(codes), _ptr(scales), _ptr(out),
+                                 ctypes.c_void_p(_stream(codes.device)))
+    else:  # measurement: the same call with events on its kernel
+        st = _load().sparcml_bench_dqsgd(4, P, n, bucket, _ptr(codes), _ptr(scales), _ptr(out), ctypes.byref(events),
+                                         ctypes.c_void_p(_stream(codes.device)))
     _raise(st, "sparcml_dq4")
     return out
 
@@ -377,9 +424,10 @@ def qsgd_dense_result(out: "ReduceOutput", bits: int, bucket: int, seed: int, st
 def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
                   expected_nnz_hint: int = 0, out_idx: Optional[torch.Tensor] = None,
                   out_val: Optional[torch.Tensor] = None, result: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None) -> ReduceOutput:
+                  workspace: Optional[torch.Tensor] = None, events: Optional[BenchEvents] = None) -> ReduceOutput:
     """Sum of P sparse contributions (node p owns pairs [offsets[p], offsets[p+1])).
-    idx: int32 tensor holding uint32 indices, val: float32 tensor."""
+    idx: int32 tensor holding uint32 indices, val: float32 tensor. `events`
+    (measurement only) routes the call through sparcml_bench_sparse_reduce."""
     _check_dev(idx, torch.int32, "idx")
     _check_dev(val, torch.float32, "val")
     P = len(offsets) - 1
@@ -387,9 +435,15 @@ def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, 
     dev = idx.device
     out_idx, out_val, result, workspace = _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result,
                                                           workspace)
-    st = _load().sparcml_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val), int(expected_nnz_hint),
-                                       _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
-                                       workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    if events is None:
+        st = _load().sparcml_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val), int(expected_nnz_hint),
+                                           _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
+                                           workspace.numel(), ctypes.c_void_p(_stream(dev)))
+    else:
+        st = _load().sparcml_bench_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val),
+                                                 int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val), _ptr(result),
+                                                 _ptr(workspace), workspace.numel(), ctypes.byref(events),
+                                                 ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_sparse_reduce")
     return ReduceOutput(result, out_idx, out_val, N)
 

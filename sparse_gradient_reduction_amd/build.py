@@ -1,4 +1,5 @@
-"""Build libsparcml.so (HIP kernels + C ABI) for gfx950, in-tree.
+"""Build libsparcml.so (HIP kernels + C ABI) and libsparcml_bench.so (the
+measurement-only bandwidth reference) for gfx950, in-tree.
 
     python -m sparse_gradient_reduction_amd.build
 """
@@ -12,10 +13,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsparcml.so")
+BENCH_LIB = os.path.join(PKG, "libsparcml_bench.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["api.hip", "topk_ef.hip", "topk_row.hip", "topk_bucketed.hip", "qsgd.hip", "sparse_reduce.hip",
-           "reference_stream.hip"]
+SOURCES = ["api.hip", "topk_ef.hip", "topk_row.hip", "topk_bucketed.hip", "qsgd.hip", "sparse_reduce.hip"]
+BENCH_SOURCES = ["reference_stream.hip"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -40,16 +42,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
+    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
+    os.replace(tmp, out)
+
+
 def build(jobs: int = 4) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     try:
         with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-            objs = list(ex.map(_compile, SOURCES))
+            objs = list(ex.map(_compile, SOURCES + BENCH_SOURCES))
     except subprocess.CalledProcessError as e:
         raise RuntimeError(f"hipcc failed:\n{e.stdout.decode(errors='replace')}") from e
-    tmp = LIB + ".tmp"
-    subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
-    os.replace(tmp, LIB)
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     return LIB
 
 

@@ -1,6 +1,8 @@
 // C ABI of the SparCML hot path: argument checks, workspace sizing, launch.
-// The declarations and their contracts are in include/sparcml.h.
+// The declarations and their contracts are in include/sparcml.h and, for the
+// measurement variants, include/sparcml_bench.h.
 #include "sparcml.h"
+#include "sparcml_bench.h"
 
 #include <algorithm>
 #include <atomic>
@@ -41,9 +43,6 @@ hipError_t scratch_of_current_device(void** out) {
   return hipSuccess;
 }
 
-thread_local hipEvent_t g_prof_start = nullptr;
-thread_local hipEvent_t g_prof_stop = nullptr;
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
@@ -76,29 +75,15 @@ const char* sparcml_status_string(sparcml_status status) {
   return "SPARCML: unknown status";
 }
 
-sparcml_status sparcml_reference_stream(uint64_t n, const float* g, float* r, hipEvent_t start, hipEvent_t stop,
-                                        hipStream_t stream) {
-  if (n >= (1ull << 42) || (n > 0 && (!g || !r || !aligned16(g) || !aligned16(r)))) return SPARCML_ERR_INVALID_ARG;
-  if ((n + 1023) / 1024 >= (1ull << 24)) return SPARCML_ERR_INVALID_ARG;  // one launch dimension
-  return from_hip(sparcml::reference_add_launch(n, g, r, stream, start, stop));
-}
-
-void sparcml_profile_next_topk(hipEvent_t start, hipEvent_t stop) {
-  g_prof_start = start;
-  g_prof_stop = stop;
-}
-
 // --------------------------------------------------------------------------
 size_t sparcml_topk_ef_workspace(uint32_t P, uint64_t N, uint64_t k) {
   if (P == 0 || N > kMaxTopkN || k > N || P > 65535u) return 0;
   return sparcml::topk_workspace_bytes(P, N, k);
 }
 
-sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                               uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
-  hipEvent_t ev0 = g_prof_start, ev1 = g_prof_stop;
-  g_prof_start = g_prof_stop = nullptr;
+static sparcml_status topk_common(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                  uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream,
+                                  const sparcml::OpEvents* ev) {
   if (P == 0 || P > 65535u || N > kMaxTopkN || k > N) return SPARCML_ERR_INVALID_ARG;
   if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
   // one 256-thread workgroup per 1024-element tile slot (a node's tiles start at
@@ -111,8 +96,14 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* 
   // short rows in a small call: one workgroup per node beats the candidate pipeline's kernel chain
   if (N <= SPARCML_TOPK_ROW_MAX && (uint64_t)P * N <= SPARCML_TOPK_ROW_TOTAL_MAX)
     return from_hip(sparcml::topk_row_launch(P, N, k, grad, residual, out_idx, out_val, static_cast<uint32_t*>(ws),
-                                             stream, ev0, ev1));
-  return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev0, ev1));
+                                             stream, ev));
+  return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev));
+}
+
+sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                               uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, ws, ws_bytes, stream, nullptr);
 }
 
 // --------------------------------------------------------------------------
@@ -188,21 +179,33 @@ static bool qsgd_args_ok(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket)
   return true;  // any number of buckets: the kernels loop over them
 }
 
-sparcml_status sparcml_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
-                            uint32_t node0, const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
+static sparcml_status qsgd_common(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed,
+                                  uint32_t step, uint32_t node0, const float* val, uint8_t* codes, float* scales,
+                                  hipStream_t stream, const sparcml::OpEvents* ev) {
   if (!qsgd_args_ok(bits, P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
   if ((uint64_t)node0 + P - 1 > 0xFFFFFFFFull) return SPARCML_ERR_INVALID_ARG;
   if (n == 0) return SPARCML_OK;
   if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
-  return from_hip(sparcml::qsgd_launch(bits, P, n, bucket, seed, step, node0, nullptr, val, codes, scales, stream));
+  return from_hip(
+      sparcml::qsgd_launch(bits, P, n, bucket, seed, step, node0, nullptr, val, codes, scales, stream, ev));
+}
+
+static sparcml_status dqsgd_common(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                                   const float* scales, float* val, hipStream_t stream, const sparcml::OpEvents* ev) {
+  if (!qsgd_args_ok(bits, P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
+  if (n == 0) return SPARCML_OK;
+  if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
+  return from_hip(sparcml::dqsgd_launch(bits, P, n, bucket, codes, scales, val, stream, ev));
+}
+
+sparcml_status sparcml_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
+                            uint32_t node0, const float* val, uint8_t* codes, float* scales, hipStream_t stream) {
+  return qsgd_common(bits, P, n, bucket, seed, step, node0, val, codes, scales, stream, nullptr);
 }
 
 sparcml_status sparcml_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
                              const float* scales, float* val, hipStream_t stream) {
-  if (!qsgd_args_ok(bits, P, n, bucket)) return SPARCML_ERR_INVALID_ARG;
-  if (n == 0) return SPARCML_OK;
-  if (!val || !codes || !scales || !aligned16(val)) return SPARCML_ERR_INVALID_ARG;
-  return from_hip(sparcml::dqsgd_launch(bits, P, n, bucket, codes, scales, val, stream));
+  return dqsgd_common(bits, P, n, bucket, codes, scales, val, stream, nullptr);
 }
 
 sparcml_status sparcml_q4(uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
@@ -248,7 +251,7 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
                                     const uint32_t* idx, const float* val, const sparcml::ReduceQuantized* quant,
                                     uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
                                     sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, const sparcml::OpEvents* ev = nullptr) {
   if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !std::isfinite(delta)) return SPARCML_ERR_INVALID_ARG;
   if (!h_offsets || !d_result || !out_val || !aligned16(out_val)) return SPARCML_ERR_INVALID_ARG;
   if (h_offsets[0] != 0) return SPARCML_ERR_INVALID_ARG;
@@ -265,7 +268,7 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
   const bool dense_first = est >= (double)T;
   return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, dense_first, out_idx, cap,
                                                 out_val, reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws,
-                                                stream));
+                                                stream, ev));
 }
 
 sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
@@ -299,6 +302,51 @@ sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32
   const sparcml::ReduceQuantized q{bits, bucket, codes, scales};
   return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, expected_nnz_hint, out_idx, out_val, d_result, ws,
                        ws_bytes, stream);
+}
+
+// --------------------------------------------------------------------------
+// Measurement entry points: the calls above with caller-owned events
+// attached to their kernel dispatches.
+static sparcml::OpEvents op_events(const sparcml_bench_events* ev) {
+  sparcml::OpEvents e;
+  if (ev) {
+    e.op_start = ev->op_start;
+    e.op_stop = ev->op_stop;
+    e.k_start = ev->kernel_start;
+    e.k_stop = ev->kernel_stop;
+  }
+  return e;
+}
+
+sparcml_status sparcml_bench_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                     uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
+                                     const sparcml_bench_events* ev, hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, ws, ws_bytes, stream, &e);
+}
+
+sparcml_status sparcml_bench_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed,
+                                  uint32_t step, uint32_t node0, const float* val, uint8_t* codes, float* scales,
+                                  const sparcml_bench_events* ev, hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return qsgd_common(bits, P, n, bucket, seed, step, node0, val, codes, scales, stream, &e);
+}
+
+sparcml_status sparcml_bench_dqsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
+                                   const float* scales, float* val, const sparcml_bench_events* ev,
+                                   hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return dqsgd_common(bits, P, n, bucket, codes, scales, val, stream, &e);
+}
+
+sparcml_status sparcml_bench_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                           const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
+                                           uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
+                                           void* ws, size_t ws_bytes, const sparcml_bench_events* ev,
+                                           hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
+                       ws_bytes, stream, &e);
 }
 
 }  // extern "C"

@@ -2,23 +2,55 @@
 // argument checks. Each returns hipSuccess or the first HIP error.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace sparcml {
 
+// Measurement only: events a sparcml_bench_* call attaches to kernel
+// dispatches (any may be null). op_start rides on the op's first kernel,
+// op_stop on its last; k_start / k_stop on the op's dominant kernel (the
+// error-feedback stream kernel of Top-k).
+struct OpEvents {
+  hipEvent_t op_start = nullptr;
+  hipEvent_t op_stop = nullptr;
+  hipEvent_t k_start = nullptr;
+  hipEvent_t k_stop = nullptr;
+};
+
+template <class T>
+struct same_type {
+  using type = T;
+};
+
+// Launches fn on `stream`; `start` / `stop`, when not null, are recorded as
+// the kernel itself starts and ends (hipExtLaunchKernel), so that their
+// elapsed time is that kernel's and nothing queued around it.
+template <typename... P>
+hipError_t launch_ev(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                     typename same_type<P>::type... a) {
+  if (start == nullptr && stop == nullptr) {
+    hipLaunchKernelGGL(fn, grid, block, 0, stream, a...);
+    return hipGetLastError();
+  }
+  void* args[] = {static_cast<void*>(&a)...};
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream, start,
+                                          stop, 0);
+  return e != hipSuccess ? e : hipGetLastError();
+}
+
 // ---- error-feedback Top-k -------------------------------------------------
 size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k);
 hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop);
+                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream, const OpEvents* ev);
 
 // ---- error-feedback Top-k of short rows: one workgroup per node; info holds
 // the [P] path words (2) and the [P] consistency words the workspace reports
 hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
                            uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,
-                           hipEvent_t ev_start, hipEvent_t ev_stop);
+                           const OpEvents* ev);
 
 // per-layer call whose layers all hold at most SPARCML_TOPK_ROW_MAX elements:
 // one workgroup per (node, layer) row. Uses the first
@@ -45,9 +77,9 @@ hipError_t topk_bucketed_launch(uint32_t P, uint64_t N, uint32_t bucket, uint32_
 // gate: null, or a device word that must be nonzero for the quantizer to run
 hipError_t qsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
                        uint32_t node0, const uint32_t* gate, const float* val, uint8_t* codes, float* scales,
-                       hipStream_t stream);
+                       hipStream_t stream, const OpEvents* ev = nullptr);
 hipError_t dqsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
-                        const float* scales, float* val, hipStream_t stream);
+                        const float* scales, float* val, hipStream_t stream, const OpEvents* ev = nullptr);
 
 // ---- sparse reduction --------------------------------------------------------
 struct ReduceResultDev {
@@ -68,10 +100,7 @@ struct ReduceQuantized {
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
                                 bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
-                                ReduceResultDev* d_result, void* ws, hipStream_t stream);
-
-// ---- measurement only: plain streaming add with the stream kernel's access pattern
-hipError_t reference_add_launch(uint64_t n, const float* g, float* r, hipStream_t stream, hipEvent_t ev_start,
-                                hipEvent_t ev_stop);
+                                ReduceResultDev* d_result, void* ws, hipStream_t stream,
+                                const OpEvents* ev = nullptr);
 
 }  // namespace sparcml

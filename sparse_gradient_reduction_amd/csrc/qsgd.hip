@@ -229,33 +229,33 @@ QArgs make_args(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t
 
 hipError_t qsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed, uint32_t step,
                        uint32_t node0, const uint32_t* gate, const float* val, uint8_t* codes, float* scales,
-                       hipStream_t stream) {
+                       hipStream_t stream, const OpEvents* ev) {
   const QArgs A = make_args(bits, P, n, bucket, seed, step, node0);
   if (n == 0) return hipSuccess;
   // a wave per bucket, up to the 2^32 work-items a grid dimension allows
   const dim3 grid((uint32_t)std::min<uint64_t>((A.nb + 3) / 4, 1u << 22), P);
+  const hipEvent_t e0 = ev ? ev->op_start : nullptr, e1 = ev ? ev->op_stop : nullptr;
   switch (bits) {
-    case 2: hipLaunchKernelGGL(k_qsgd<2>, grid, dim3(256), 0, stream, val, codes, scales, A, gate); break;
-    case 4: hipLaunchKernelGGL(k_qsgd<4>, grid, dim3(256), 0, stream, val, codes, scales, A, gate); break;
-    case 8: hipLaunchKernelGGL(k_qsgd<8>, grid, dim3(256), 0, stream, val, codes, scales, A, gate); break;
+    case 2: return launch_ev(k_qsgd<2>, grid, dim3(256), stream, e0, e1, val, codes, scales, A, gate);
+    case 4: return launch_ev(k_qsgd<4>, grid, dim3(256), stream, e0, e1, val, codes, scales, A, gate);
+    case 8: return launch_ev(k_qsgd<8>, grid, dim3(256), stream, e0, e1, val, codes, scales, A, gate);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t dqsgd_launch(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, const uint8_t* codes,
-                        const float* scales, float* val, hipStream_t stream) {
+                        const float* scales, float* val, hipStream_t stream, const OpEvents* ev) {
   const QArgs A = make_args(bits, P, n, bucket, 0, 0, 0);
   if (n == 0) return hipSuccess;
   const uint64_t lanes = (n + kPerLane - 1) / kPerLane;
   const dim3 grid((uint32_t)((lanes + 255) / 256), P);
+  const hipEvent_t e0 = ev ? ev->op_start : nullptr, e1 = ev ? ev->op_stop : nullptr;
   switch (bits) {
-    case 2: hipLaunchKernelGGL(k_dqsgd<2>, grid, dim3(256), 0, stream, codes, scales, val, A); break;
-    case 4: hipLaunchKernelGGL(k_dqsgd<4>, grid, dim3(256), 0, stream, codes, scales, val, A); break;
-    case 8: hipLaunchKernelGGL(k_dqsgd<8>, grid, dim3(256), 0, stream, codes, scales, val, A); break;
+    case 2: return launch_ev(k_dqsgd<2>, grid, dim3(256), stream, e0, e1, codes, scales, val, A);
+    case 4: return launch_ev(k_dqsgd<4>, grid, dim3(256), stream, e0, e1, codes, scales, val, A);
+    case 8: return launch_ev(k_dqsgd<8>, grid, dim3(256), stream, e0, e1, codes, scales, val, A);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace sparcml

@@ -6,10 +6,11 @@
 // store per thread. Its rate is the streaming bandwidth the hardware gives a
 // kernel of this shape; the stream kernel's rate divided by it is the cost of
 // the candidate compaction it adds.
+// Built into its own library, libsparcml_bench.so, apart from the method's.
+#include "sparcml_bench.h"
+
 #include "device_common.hpp"
 #include "kernels.hpp"
-
-#include <hip/hip_ext.h>
 
 namespace sparcml {
 namespace {
@@ -26,17 +27,15 @@ __global__ __launch_bounds__(256) void k_reference_add(const float* __restrict__
 }
 
 }  // namespace
-
-hipError_t reference_add_launch(uint64_t n, const float* g, float* r, hipStream_t stream, hipEvent_t ev_start,
-                                hipEvent_t ev_stop) {
-  if (n == 0) return hipSuccess;
-  const uint64_t blocks = (n + 1023) / 1024;
-  const float* ga = g;
-  float* ra = r;
-  uint64_t na = n;
-  void* args[] = {&ga, &ra, &na};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&k_reference_add), dim3((uint32_t)blocks), dim3(256), args, 0,
-                            stream, ev_start, ev_stop, 0);
-}
-
 }  // namespace sparcml
+
+extern "C" sparcml_status sparcml_bench_reference_stream(uint64_t n, const float* g, float* r,
+                                                         const sparcml_bench_events* ev, hipStream_t stream) {
+  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; };
+  if (n > (1ull << 34) - 1024 || (n > 0 && (!g || !r || misaligned(g) || misaligned(r)))) return SPARCML_ERR_INVALID_ARG;
+  if (n == 0) return SPARCML_OK;
+  const uint64_t blocks = (n + 1023) / 1024;  // < 2^24 workgroups of 256: one launch dimension
+  const hipError_t e = sparcml::launch_ev(sparcml::k_reference_add, dim3((uint32_t)blocks), dim3(256), stream,
+                                          ev ? ev->op_start : nullptr, ev ? ev->op_stop : nullptr, g, r, n);
+  return e == hipSuccess ? SPARCML_OK : SPARCML_ERR_HIP;
+}

@@ -829,30 +829,36 @@ size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t total_nnz) {
 namespace {
 
 template <int MAXP>
-void launch_write_tile(uint32_t bits, dim3 grid, hipStream_t stream, const uint32_t* idx, const float* val,
-                       uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb) {
+hipError_t launch_write_tile(uint32_t bits, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+                             const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val, const RDev& R,
+                             uint32_t lb) {
   const dim3 block(kWriteThreads);
   switch (bits) {
-    case 0: hipLaunchKernelGGL((k_write_tile<MAXP, 0>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 2: hipLaunchKernelGGL((k_write_tile<MAXP, 2>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 4: hipLaunchKernelGGL((k_write_tile<MAXP, 4>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    default: hipLaunchKernelGGL((k_write_tile<MAXP, 8>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+    case 0: return launch_ev(k_write_tile<MAXP, 0>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 2: return launch_ev(k_write_tile<MAXP, 2>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 4: return launch_ev(k_write_tile<MAXP, 4>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    default: return launch_ev(k_write_tile<MAXP, 8>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
   }
 }
 
 template <int MAXP>
-void launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t stream, const uint32_t* idx,
-                         const float* val, uint32_t* out_idx, float* out_val, const RDev& R, uint32_t lb,
-                         uint32_t lbq) {
+hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+                               const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val,
+                               const RDev& R, uint32_t lb, uint32_t lbq) {
   const dim3 block(kRankThreads);
   switch (bits) {
     case 0:
-      if (quad) hipLaunchKernelGGL((k_write_ranked<MAXP, 0, true>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lbq);
-      else hipLaunchKernelGGL((k_write_ranked<MAXP, 0, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb);
-      break;
-    case 2: hipLaunchKernelGGL((k_write_ranked<MAXP, 2, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    case 4: hipLaunchKernelGGL((k_write_ranked<MAXP, 4, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
-    default: hipLaunchKernelGGL((k_write_ranked<MAXP, 8, false>), grid, block, 0, stream, idx, val, out_idx, out_val, R, lb); break;
+      if (quad)
+        return launch_ev(k_write_ranked<MAXP, 0, true>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R,
+                         lbq);
+      return launch_ev(k_write_ranked<MAXP, 0, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R,
+                       lb);
+    case 2:
+      return launch_ev(k_write_ranked<MAXP, 2, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 4:
+      return launch_ev(k_write_ranked<MAXP, 4, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    default:
+      return launch_ev(k_write_ranked<MAXP, 8, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
   }
 }
 
@@ -882,8 +888,12 @@ uint32_t quad_lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
                                 bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
-                                ReduceResultDev* d_result, void* ws, hipStream_t stream) {
+                                ReduceResultDev* d_result, void* ws, hipStream_t stream, const OpEvents* ev) {
   const Layout L = make_layout(P, N, h_offsets[P]);
+  // measurement events: the op's span runs from its first dispatch to the
+  // writer's end; the kernel pair times the writer alone
+  const OpEvents none{};
+  const OpEvents& E = ev ? *ev : none;
   char* w = static_cast<char*>(ws);
   RDev R;
   R.P = P;
@@ -922,31 +932,44 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
       InlineOffsets part;
       const uint32_t count = std::min<uint32_t>(kInlineOffsets, P + 1 - first);
       for (uint32_t i = 0; i < count; ++i) part.v[i] = h_offsets[first + i];
-      hipLaunchKernelGGL(k_setup, dim3(1), dim3(256), 0, stream, R, first, count, part, first == 0 ? 1 : 0);
+      const hipError_t e = launch_ev(k_setup, dim3(1), dim3(256), stream, first == 0 ? E.op_start : nullptr, nullptr,
+                                     R, first, count, part, first == 0 ? 1 : 0);
+      if (e != hipSuccess) return e;
     }
     if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   }
   const uint32_t bx = bounds_blocks(max_nnz);
   R.nflagw = (uint64_t)bx * P;
   const uint32_t shift = (uint32_t)((reinterpret_cast<uintptr_t>(idx) >> 2) & 3u);
-  hipLaunchKernelGGL(k_bounds, dim3(bx, P), dim3(kThreads), 0, stream, idx, R, shift, in, inline_offs ? 1 : 0);
+  hipError_t e = launch_ev(k_bounds, dim3(bx, P), dim3(kThreads), stream, inline_offs ? E.op_start : nullptr, nullptr,
+                           idx, R, shift, in, inline_offs ? 1 : 0);
+  if (e != hipSuccess) return e;
   const dim3 segs((uint32_t)L.S);
   const bool small_p = P <= 256;
   const uint32_t lb = lanes_log2(P, L.S, R.total);
   if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
   else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
   hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the writer is the op's last kernel: it carries the kernel pair, or the
+  // op's stop alone
+  const hipEvent_t w0 = E.k_start;
+  const hipEvent_t w1 = E.k_stop ? E.k_stop : E.op_stop;
   if (dense_first) {  // the estimate expects a dense result: the full tile
-    if (small_p) launch_write_tile<256>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
-    else launch_write_tile<kMaxP>(R.bits, segs, stream, idx, val, out_idx, out_val, R, lb);
+    e = small_p ? launch_write_tile<256>(R.bits, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb)
+                : launch_write_tile<kMaxP>(R.bits, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb);
   } else {
     // 16-byte quads of pairs where both arrays allow them
     const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
     const uint32_t lbq = quad_lanes_log2(P, L.S, R.total);
-    if (small_p) launch_write_ranked<256>(R.bits, quad, segs, stream, idx, val, out_idx, out_val, R, lb, lbq);
-    else launch_write_ranked<kMaxP>(R.bits, quad, segs, stream, idx, val, out_idx, out_val, R, lb, lbq);
+    e = small_p ? launch_write_ranked<256>(R.bits, quad, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
+                : launch_write_ranked<kMaxP>(R.bits, quad, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
+                                             lbq);
   }
-  return hipGetLastError();
+  // with both pairs asked for, the op's stop follows the writer's at once
+  if (e == hipSuccess && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
+  return e;
 }
 
 }  // namespace sparcml

@@ -1207,8 +1207,14 @@ template <bool ROWS>
 hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t groups, uint64_t max_tiles,
                uint64_t max_cap, uint64_t passes, uint64_t big_rows, uint64_t mid_rows, bool any_k, const float* grad,
                float* residual,
-               uint32_t* out_idx, float* out_val, hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
+               uint32_t* out_idx, float* out_val, hipStream_t stream, const OpEvents* ev) {
   const uint32_t R = (uint32_t)nrows;
+  // measurement events (whole-vector call only): the op's span runs from the
+  // predictor's dispatch to the last kernel's, the stream kernel's own pair
+  // times it alone
+  const OpEvents none{};
+  const OpEvents& E = ev ? *ev : none;
+  hipError_t e = hipSuccess;
   if constexpr (ROWS) {
     if (mid_rows > 0)
       hipLaunchKernelGGL((k_predict<true, kSmallPredictThreads, 1>), dim3((uint32_t)mid_rows),
@@ -1217,25 +1223,25 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
       hipLaunchKernelGGL((k_predict<true, kLayerPredictThreads, 2>), dim3((uint32_t)big_rows),
                          dim3(kLayerPredictThreads), 0, stream, grad, residual, D);
   } else {
-    hipLaunchKernelGGL((k_predict<false, kPredictThreads, 0>), dim3(R), dim3(kPredictThreads), 0, stream, grad,
-                       residual, D);
+    const bool predict_last = stream_blocks == 0 && !any_k;
+    e = launch_ev(k_predict<false, kPredictThreads, 0>, dim3(R), dim3(kPredictThreads), stream, E.op_start,
+                  predict_last ? E.op_stop : nullptr, grad, residual, D);
   }
-  hipError_t e = hipSuccess;
-  if (stream_blocks > 0) {
-    if (ev_start || ev_stop) {
-      // profiling: the events ride on the kernel's own dispatch and time exactly it
-      const float* ga = grad;
-      float* ra = residual;
-      Dev da = D;
-      void* args[] = {&ga, &ra, &da};
-      e = hipExtLaunchKernel(reinterpret_cast<const void*>(&k_stream<ROWS>), dim3((uint32_t)stream_blocks),
-                             dim3(kStreamThreads), args, 0, stream, ev_start, ev_stop, 0);
+  if (e == hipSuccess && stream_blocks > 0) {
+    if (E.k_start || E.k_stop || (!any_k && E.op_stop)) {
+      // the stream kernel carries one start and one stop event: its own pair,
+      // or the op's stop when it is the op's last kernel and its pair is unused
+      const hipEvent_t s0 = E.k_start;
+      const hipEvent_t s1 = E.k_stop ? E.k_stop : (!any_k ? E.op_stop : nullptr);
+      e = launch_ev(k_stream<ROWS>, dim3((uint32_t)stream_blocks), dim3(kStreamThreads), stream, s0, s1, grad,
+                    residual, D);
+      if (e == hipSuccess && !any_k && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
     } else {
       hipLaunchKernelGGL(k_stream<ROWS>, dim3((uint32_t)stream_blocks), dim3(kStreamThreads), 0, stream, grad,
                          residual, D);
+      e = hipGetLastError();
     }
   }
-  if (e == hipSuccess) e = hipGetLastError();
   if (e != hipSuccess || !any_k) return e;
 
   // per-row block counts sized for the candidate list; the rescan path loops
@@ -1263,8 +1269,9 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
   hipLaunchKernelGGL((k_hist<2, ROWS>), gH, dim3(256), 0, stream, residual, D);
   hipLaunchKernelGGL(k_count<ROWS>, gC, dim3(kChunkThreads), 0, stream, residual, D);
   hipLaunchKernelGGL(k_scan<ROWS>, dim3(R), dim3(1024), 0, stream, D);
-  hipLaunchKernelGGL(k_emit<ROWS>, gC, dim3(kChunkThreads), 0, stream, residual, out_idx, out_val, D);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_ev(k_emit<ROWS>, gC, dim3(kChunkThreads), stream, nullptr, E.op_stop, residual, out_idx, out_val, D);
 }
 
 Dev make_dev(const Layout& L, char* w, uint32_t P) {
@@ -1303,8 +1310,7 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
 size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k) { return make_node_layout(P, N, k).total; }
 
 hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream,
-                          hipEvent_t ev_start, hipEvent_t ev_stop) {
+                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream, const OpEvents* ev) {
   const Layout L = make_node_layout(P, N, k);
   Dev D = make_dev(L, static_cast<char*>(ws), P);
   D.N = (uint32_t)N;
@@ -1317,7 +1323,7 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
     D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
   }
   return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, 0, k > 0, grad, residual, out_idx, out_val, stream,
-                    ev_start, ev_stop);
+                    ev);
 }
 
 size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {
@@ -1370,7 +1376,7 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
                      pass_row, D);
   return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.Q.mid,
                    lp.K > 0,
-                   grad, residual, out_idx, out_val, stream, nullptr, nullptr);
+                   grad, residual, out_idx, out_val, stream, nullptr);
 }
 
 }  // namespace sparcml

@@ -539,29 +539,16 @@ hipError_t topk_layer_rows_launch(uint32_t P, uint64_t N, uint32_t nl, const uin
 
 hipError_t topk_row_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
                            uint32_t* out_idx, float* out_val, uint32_t* info, hipStream_t stream,
-                           hipEvent_t ev_start, hipEvent_t ev_stop) {
-  if (ev_start || ev_stop) {  // profiling: the events ride on the kernel's own dispatch
-    const float* ga = grad;
-    float* ra = residual;
-    uint64_t n = N;
-    uint32_t kk = (uint32_t)k;
-    uint32_t* oi = out_idx;
-    float* ov = out_val;
-    uint32_t* in = info;
-    void* args[] = {&ga, &ra, &n, &kk, &oi, &ov, &in};
-    const void* fn = N <= kRowRegMax ? reinterpret_cast<const void*>(&k_topk_row<true>)
-                                     : reinterpret_cast<const void*>(&k_topk_row<false>);
-    const hipError_t e = hipExtLaunchKernel(fn, dim3(P), dim3(kRowThreads),
-                                            args, 0, stream, ev_start, ev_stop, 0);
-    return e != hipSuccess ? e : hipGetLastError();
-  }
+                           const OpEvents* ev) {
+  // one kernel, the op's first, last and dominant at once: it carries the
+  // op's pair when one is given, else the kernel pair
+  const hipEvent_t e0 = ev ? (ev->op_start ? ev->op_start : ev->k_start) : nullptr;
+  const hipEvent_t e1 = ev ? (ev->op_stop ? ev->op_stop : ev->k_stop) : nullptr;
   if (N <= kRowRegMax)
-    hipLaunchKernelGGL(k_topk_row<true>, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k,
-                       out_idx, out_val, info);
-  else
-    hipLaunchKernelGGL(k_topk_row<false>, dim3(P), dim3(kRowThreads), 0, stream, grad, residual, N, (uint32_t)k,
-                       out_idx, out_val, info);
-  return hipGetLastError();
+    return launch_ev(k_topk_row<true>, dim3(P), dim3(kRowThreads), stream, e0, e1, grad, residual, N, (uint32_t)k,
+                     out_idx, out_val, info);
+  return launch_ev(k_topk_row<false>, dim3(P), dim3(kRowThreads), stream, e0, e1, grad, residual, N, (uint32_t)k,
+                   out_idx, out_val, info);
 }
 
 }  // namespace sparcml

@@ -1,4 +1,4 @@
-/* A plain C99 client of include/sparcml.h, built and run by test_abi.py with
+/* A plain C99 client of include/sparcml.h and include/sparcml_bench.h, built and run by test_abi.py with
  * no GPU: it checks that the header compiles as C and that the library links
  * and answers the calls that need no device (status names, the host-side
  * estimate, and argument checks that return before any launch). Prints "ok"
@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "sparcml.h"
+#include "sparcml_bench.h"
 
 static int fails = 0;
 #define CHECK(c)                                              \
@@ -34,6 +35,11 @@ int main(void) {
   CHECK(sparcml_topk_ef_workspace(0, 1000, 10) == 0);
   CHECK(sparcml_topk_ef_workspace(4, 1000, 10) > 0);
   CHECK(sparcml_sparse_reduce_workspace(4, 1000, 400) > 0);
+
+  /* the measurement variants take the same checks before touching any event */
+  sparcml_bench_events ev = {NULL, NULL, NULL, NULL};
+  CHECK(sparcml_bench_topk_ef(0, 1000, 10, NULL, NULL, NULL, NULL, NULL, 0, &ev, NULL) == SPARCML_ERR_INVALID_ARG);
+  CHECK(sparcml_bench_qsgd(3, 1, 100, 512, 1, 0, 0, NULL, NULL, NULL, &ev, NULL) == SPARCML_ERR_INVALID_ARG);
 
   if (fails == 0) printf("ok\n");
   return fails == 0 ? 0 : 1;

@@ -1,6 +1,7 @@
-"""The C-ABI library on the host (no GPU needed): it loads, exports every
-function include/sparcml.h declares, and rejects bad arguments before
-launching anything."""
+"""The C-ABI libraries on the host (no GPU needed): they load, export every
+function include/sparcml.h and include/sparcml_bench.h declare, reject bad
+arguments before launching anything, and report a missing device as a HIP
+error without aborting."""
 import ctypes
 import math
 import os
@@ -12,6 +13,7 @@ import sparse_gradient_reduction_amd as sg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparcml.h")
+BENCH_HEADER = os.path.join(ROOT, "include", "sparcml_bench.h")
 
 if not os.path.exists(sg.LIB_PATH):
     pytest.skip("libsparcml.so not built", allow_module_level=True)
@@ -21,8 +23,8 @@ FAKE_ODD = ctypes.c_void_p(4100)   # not 16-byte aligned
 FAKE_WS_ODD = ctypes.c_void_p(4096 + 128)  # 16- but not 256-byte aligned
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sparcml_[a-z0-9_]+)\s*\(", text)))
 
@@ -38,6 +40,91 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(sg.LIB_PATH)
     for name in declared_functions():
         assert hasattr(L, name), name
+
+
+def test_measurement_entry_points_are_exported_apart():
+    """The measurement variants of the method's calls come from libsparcml.so;
+    the bandwidth reference kernel only from libsparcml_bench.so."""
+    names = declared_functions(BENCH_HEADER)
+    assert set(names) == {"sparcml_bench_topk_ef", "sparcml_bench_qsgd", "sparcml_bench_dqsgd",
+                          "sparcml_bench_sparse_reduce", "sparcml_bench_reference_stream"}
+    L = ctypes.CDLL(sg.LIB_PATH)
+    B = ctypes.CDLL(sg.BENCH_LIB_PATH)
+    for name in names:
+        if name == "sparcml_bench_reference_stream":
+            assert hasattr(B, name) and not hasattr(L, name)
+        else:
+            assert hasattr(L, name), name
+            # each is the call of the same name plus its events
+            assert name.replace("sparcml_bench_", "sparcml_") in declared_functions()
+    # no hidden profiling state: nothing else in the method's library is about measurement
+    assert not hasattr(L, "sparcml_profile_next_topk") and not hasattr(L, "sparcml_reference_stream")
+
+
+def test_measurement_entry_points_check_arguments_first():
+    L = sg.lib()
+    ev = sg.BenchEvents()
+    evp = ctypes.byref(ev)
+    ws = sg.topk_ef_workspace_bytes(4, 1000, 10)
+    assert L.sparcml_bench_topk_ef(0, 1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws, evp, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_bench_topk_ef(4, 1000, 10, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, ws, evp, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_bench_topk_ef(4, 1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None, None) == sg.ERR_WORKSPACE
+    assert L.sparcml_bench_qsgd(3, 1, 100, 512, 1, 0, 0, FAKE, FAKE, FAKE, evp, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_bench_dqsgd(4, 1, 100, 12, FAKE, FAKE, FAKE, evp, None) == sg.ERR_INVALID_ARG
+    off = (ctypes.c_uint64 * 3)(0, 100, 200)
+    wsr = sg.sparse_reduce_workspace_bytes(2, 1000, 200)
+    assert L.sparcml_bench_sparse_reduce(2, 1000, 0.5, off, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE_WS_ODD, wsr,
+                                         evp, None) == sg.ERR_WORKSPACE
+    assert L.sparcml_bench_sparse_reduce(0, 1000, 0.5, off, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, wsr,
+                                         evp, None) == sg.ERR_INVALID_ARG
+    B = sg.bench_lib()
+    assert B.sparcml_bench_reference_stream(1000, FAKE_ODD, FAKE, evp, None) == sg.ERR_INVALID_ARG
+    assert B.sparcml_bench_reference_stream((1 << 34) - 1023, FAKE, FAKE, evp, None) == sg.ERR_INVALID_ARG
+    assert B.sparcml_bench_reference_stream(0, None, None, None, None) == sg.OK
+
+
+_NO_DEVICE_CLIENT = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+import sparse_gradient_reduction_amd as sg
+L, B = sg.lib(), sg.bench_lib()
+F = ctypes.c_void_p(1 << 20)  # 16- and 256-byte aligned; never dereferenced on the host
+off = (ctypes.c_uint64 * 3)(0, 100, 200)
+wt = sg.topk_ef_workspace_bytes(2, 1 << 20, 1000)
+wr = sg.sparse_reduce_workspace_bytes(2, 1000, 200)
+ev = ctypes.byref(sg.BenchEvents())
+calls = {
+    "topk_ef": lambda: L.sparcml_topk_ef(2, 1 << 20, 1000, F, F, F, F, F, wt, None),
+    "topk_ef_rows": lambda: L.sparcml_topk_ef(2, 4096, 100, F, F, F, F, F, sg.topk_ef_workspace_bytes(2, 4096, 100),
+                                              None),
+    "q4": lambda: L.sparcml_q4(1, 1024, 512, 1, 0, F, F, F, None),
+    "dq4": lambda: L.sparcml_dq4(1, 1024, 512, F, F, F, None),
+    "sparse_reduce": lambda: L.sparcml_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, None),
+    "sparse_reduce_noalloc": lambda: L.sparcml_sparse_reduce_noalloc(2, 1000, 0.5, off, F, F, 0, F, F, F, None),
+    "bench_sparse_reduce": lambda: L.sparcml_bench_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, ev,
+                                                                 None),
+    "bench_reference_stream": lambda: B.sparcml_bench_reference_stream(4096, F, F, ev, None),
+}
+for name, call in calls.items():
+    print(name, call(), flush=True)
+print("done", flush=True)
+"""
+
+
+def test_launching_call_without_a_device_returns_hip_error():
+    """With no visible GPU, calls whose arguments pass every check reach their
+    first HIP call and return SPARCML_ERR_HIP; the process goes on and exits
+    normally (no abort, no exception out of the library)."""
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="")
+    out = subprocess.run([sys.executable, "-c", _NO_DEVICE_CLIENT, ROOT], env=env, capture_output=True, text=True,
+                         timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    lines = out.stdout.split()
+    assert lines[-1] == "done", out.stdout
+    got = dict(zip(lines[0:-1:2], lines[1:-1:2]))
+    assert len(got) == 8 and all(v == str(sg.ERR_HIP) for v in got.values()), got
 
 
 def test_status_strings():
