@@ -69,6 +69,21 @@ def measured_traffic(workload_name: str):
         return None
 
 
+class CacheFlush:
+    """Evicts the caches before a cold measurement by reading 1 GiB (four
+    times the last-level cache) and reducing it to one number: the caches end
+    up full of clean lines of this buffer, so the measured op neither hits its
+    inputs in cache nor pays for writing back dirty lines left by the flush."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.torch.sum(self.buf, out=self.out)
+
+
 def med(xs):
     n = len(xs)
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
@@ -205,13 +220,13 @@ def main():
     t_gpu_step = mean(step_list)
     K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()  # the timed steps' result
 
-    # ---- reduce alone, cold (LLC flushed by a 1 GiB write) and warm --------
+    # ---- reduce alone, cold (caches flushed by a 1 GiB read) and warm --------
     def time_reduce(cold, reps=10):
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold else None
+        flush = CacheFlush(torch, dev) if cold else None
         rr = [ev.op_events(sg, True, op_stop=False) for _ in range(reps)]
         for e in rr:
             if cold:
-                flush.fill_(1.0)
+                flush()
             sg.sparse_reduce(offsets, idx.view(-1), red_in_last.view(-1), N, w.delta, out_idx=red_idx,
                              out_val=red_val, result=red_res, workspace=ws_red, events=e)
         torch.cuda.synchronize()
@@ -409,7 +424,7 @@ def main():
         "algorithmic_bytes": {"topk_ef": b_topk, "q4": b_q4, "dq4": b_dq4, "reduce_in": b_red_in,
                               "reduce_out": b_red_out, "step": b_step},
         "reduce_alone_ms": {"what": "the reduce of the last step's pairs repeated alone, its span from dispatch "
-                                    "events; cold = after a 1 GiB write that flushes the last-level cache",
+                                    "events; cold = after a 1 GiB read that flushes the caches",
                             "cold_median": round(med(red_cold), 4), "cold_min": round(red_cold[0], 4),
                             "warm_median": round(med(red_warm), 4), "warm_min": round(red_warm[0], 4),
                             "cold_writer_median": round(med(red_cold_writer), 4),
@@ -452,7 +467,7 @@ def other_configs(sg, W, dev, skip_wid, ev):
     workload's error-feedback steps (from a zero residual), or of the reduce
     alone for the already-sparse workload, each with its algorithmic bytes.
     Spans come from events on the ops' own kernel dispatches; `cold` runs each
-    op after a 1 GiB write that flushes the last-level cache (the headline
+    op after a 1 GiB read that flushes the caches (the headline
     figures), `warm` right after the previous op. Also the same step (or
     reduce) captured once as a HIP graph and replayed, which removes the
     launch gaps that dominate the small workloads."""
@@ -485,7 +500,7 @@ def other_configs(sg, W, dev, skip_wid, ev):
         del graph
         return med([a.elapsed_time(b) for a, b in tev])
 
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    flush = CacheFlush(torch, dev)
     res = {}
     for wi in range(5):
         w = W.workload(wi)
@@ -510,7 +525,7 @@ def other_configs(sg, W, dev, skip_wid, ev):
                 es = [ev.op_events(sg, True, op_stop=False) for _ in range(10)]
                 for e in es:
                     if mode == "cold":
-                        flush.fill_(1.0)
+                        flush()
                     run(e)
                 torch.cuda.synchronize()
                 spans[mode] = med([ev.span_ms(e) for e in es])
@@ -541,10 +556,10 @@ def other_configs(sg, W, dev, skip_wid, ev):
             for t in range(w.steps):
                 et, er = ev.op_events(sg, True), ev.op_events(sg, True, op_stop=False)
                 if mode == "cold":
-                    flush.fill_(1.0)
+                    flush()
                 sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws, events=et)
                 if mode == "cold":
-                    flush.fill_(1.0)
+                    flush()
                 sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
                                  workspace=wr, events=er)
                 if mode == "warm-up":

@@ -259,23 +259,42 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
       const uint32_t e0 = 4u * (q0 + jq) - shift;
       const bool first_quad = q0 + jq == 0u && shift != 0u;
       uint32_t ip = lane0 ? w[u] : up;  // the element before the current one
+      // segments whose run starts in this quad: [lo, hi], each at the quad's
+      // first pair whose segment reaches it; the node's last pair also
+      // starts every later segment (at o1)
+      uint32_t sc[4];
+      bool lv[4];
+      uint32_t lo = 1u, hi = 0u, last_e = 0u, last_s = 0u;
+      bool any = false, ends = false;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t e = e0 + t;
         const uint32_t i = v[u][t];
-        const bool live = (!first_quad || (uint32_t)t >= shift) && e >= o0 && e < o1;
-        if (live) {
-          const uint32_t s_cur = i < N ? i >> kSegBits : S;
+        lv[t] = (!first_quad || (uint32_t)t >= shift) && e >= o0 && e < o1;
+        sc[t] = i < N ? i >> kSegBits : S;
+        if (lv[t]) {
           // first segment whose run starts here (none if this pair is below its predecessor)
           const uint32_t s_first = e > o0 ? (ip < N ? ip >> kSegBits : S) + 1u : 0u;
           if (e > o0 && ip >= i) bad |= SPARCML_FLAG_NOT_ASCENDING;
           if (i >= N) bad |= SPARCML_FLAG_INDEX_RANGE;
-          for (uint32_t sx = s_first; sx <= s_cur; ++sx) b[sx] = e;
-          if (e + 1u == o1)
-            for (uint32_t sx = s_cur + 1u; sx <= S; ++sx) b[sx] = o1;
+          if (!any) lo = s_first;
+          any = true;
+          hi = sc[t];
+          last_e = e;
+          last_s = sc[t];
+          ends |= e + 1u == o1;
         }
         ip = i;
       }
+      for (uint32_t sx = lo; sx <= hi; ++sx) {
+        uint32_t at = last_e;
+#pragma unroll
+        for (int t = 3; t >= 0; --t)
+          if (lv[t] && sc[t] >= sx) at = e0 + t;
+        b[sx] = at;
+      }
+      if (ends)
+        for (uint32_t sx = last_s + 1u; sx <= S; ++sx) b[sx] = o1;
     }
   }
   // every workgroup stores its bits, so no word needs clearing first
@@ -895,7 +914,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const OpEvents none{};
   const OpEvents& E = ev ? *ev : none;
   char* w = static_cast<char*>(ws);
-  RDev R;
+  RDev R{};
   R.P = P;
   R.N = (uint32_t)N;
   R.total = (uint32_t)h_offsets[P];
