@@ -75,13 +75,13 @@ class CacheFlush:
     up full of clean lines of this buffer, so the measured op neither hits its
     inputs in cache nor pays for writing back dirty lines left by the flush."""
 
-    def __init__(self, torch, dev):
+    def __init__(self, torch, dev, nbytes=1 << 30):
         self.torch = torch
-        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         self.out = torch.empty((), dtype=torch.float32, device=dev)
 
     def __call__(self):
-        self.torch.sum(self.buf, out=self.out)
+        self.torch.sum(self.buf, dim=0, out=self.out)
 
 
 def med(xs):

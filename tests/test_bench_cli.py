@@ -14,3 +14,14 @@ def test_bench_refuses_several_gpus():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_cache_flush_reads_its_buffer():
+    """The cold-run flush (a read of its whole buffer) runs as written: here on
+    the CPU with a small buffer."""
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    f = bench.CacheFlush(torch, torch.device("cpu"), nbytes=4096)
+    f()
+    assert float(f.out) == 1024.0
