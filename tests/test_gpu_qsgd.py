@@ -47,6 +47,41 @@ def test_qsgd_zero_buckets_and_extremes(dev, bits):
     _check_qsgd(v, bits, 512, seed=3, step=1, node0=0, dev=dev)
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_qsgd_ratio_edge_cases(dev, bits):
+    """Buckets whose ratios |v| / scale are hard for the quotient: tiny and
+    denormal values beside a normal scale, buckets of denormals only, scales
+    near the top of the range, values on and one ulp off every level
+    boundary, and random significands over wide exponent ranges."""
+    rng = np.random.default_rng(bits)
+    B = 512
+    rows = []
+    r = np.zeros(8 * B, np.float32)
+    r[0:B] = np.float32(1.0)
+    r[1:B:3] = np.float32(2.0 ** -120)  # ratios below 2^-100 take the division
+    r[2:B:3] = np.float32(1e-45)        # smallest denormal
+    r[B:2 * B] = (rng.standard_normal(B) * 1e-39).astype(np.float32)  # denormals only
+    r[2 * B:3 * B] = (rng.standard_normal(B) * 1e37).astype(np.float32)
+    r[2 * B] = np.float32(3.0e38)
+    s = (1 << (bits - 1)) - 1
+    sc = np.float32(0.7311)
+    lv = np.arange(B) % (s + 1)
+    on = (np.float64(sc) * lv / s).astype(np.float32)
+    r[3 * B:4 * B] = on
+    r[3 * B] = sc
+    r[4 * B:5 * B] = np.nextafter(on, np.float32(0))
+    r[4 * B] = sc
+    r[5 * B:6 * B] = np.nextafter(on, np.float32(1))
+    r[5 * B] = np.float32(1.0)
+    r[6 * B:8 * B] = (rng.standard_normal(2 * B) * np.exp2(rng.integers(-40, 40, 2 * B))).astype(np.float32)
+    rows.append(r)
+    rows.append(-r)
+    v = np.stack(rows)
+    print(f"qsgd ratio edges bits={bits}", flush=True)
+    for step in range(3):
+        _check_qsgd(v, bits, B, seed=0x5EED + step, step=step, node0=3, dev=dev)
+
+
 def test_q4_is_qsgd_4(dev):
     rng = np.random.default_rng(8)
     v = torch.from_numpy(rng.standard_normal((3, 2049)).astype(np.float32)).to(dev)
