@@ -145,6 +145,9 @@ def main():
 
     w = W.workload(args.workload)
     dev = torch.device("cuda:0")
+    if not w.has_topk:  # already-sparse contributions: the step is the reduce alone
+        reduce_only(args, w, sg, W, dev)
+        return
     P, N, k = w.P, w.N, w.k
     B = w.q4_bucket
     steps, warmup = args.steps, args.warmup
@@ -459,6 +462,64 @@ def main():
         torch.cuda.synchronize()
         out["other_configs"] = other_configs(sg, W, dev, w.wid, ev)
     print(json.dumps(out), flush=True)
+
+
+def reduce_only(args, w, sg, W, dev):
+    """The step of a workload whose contributions are already sparse (Zipf
+    feature indices): the sparse reduce alone over its seeded pairs, timed
+    like the Top-k step's reduce (events on its own kernel dispatches)."""
+    import numpy as np
+    import torch
+
+    P, N = w.P, w.N
+    o, i_np, v_np = W.zipf_sparse(w)
+    off = [int(x) for x in o]
+    idx = torch.from_numpy(i_np.view(np.int32)).to(dev)
+    val = torch.from_numpy(v_np).to(dev)
+    T = sg.dense_threshold(w.delta, N)
+    ri = torch.empty(max(1, min(N, T - 1)), dtype=torch.int32, device=dev)
+    rv = torch.empty(N, dtype=torch.float32, device=dev)
+    rr = torch.zeros(16, dtype=torch.uint8, device=dev)
+    wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, off[-1]), dtype=torch.uint8, device=dev)
+    ev = HipEvents()
+    run = lambda e=None: sg.sparse_reduce(off, idx, val, N, w.delta, out_idx=ri, out_val=rv, result=rr,
+                                          workspace=wr, events=e)
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    recs = [ev.op_events(sg, True, op_stop=False) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in recs:
+        run(e)
+    torch.cuda.synchronize()
+    ms_step = 1000.0 * (time.perf_counter() - t0) / args.steps
+    spans = sorted(ev.span_ms(e) for e in recs)
+    writer = sorted(ev.kernel_ms(e) for e in recs)
+    t_red = sum(spans) / len(spans)
+    K, dense, flags = sg.ReduceOutput(rr, ri, rv, N).read()
+    assert flags == 0
+    b_in, b_out = 8 * off[-1], (4 * N if dense else 8 * K)
+    gbs = lambda nbytes, t: nbytes / (t * 1e-3) / 1e9
+    t_w = sum(writer) / len(writer)
+    print(json.dumps({
+        "metric": METRIC, "value": round(gbs(b_in, ms_step), 2),
+        "value_is": "sparse-reduce input GB/s over the wall-clock time per step (the step is the reduce alone)",
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Zipf feature indices, N(0,1) values, resident in HBM)",
+        "config": {"workload": w.name, "P": P, "N": N, "pairs": off[-1], "delta": w.delta, "parallelism": "none (1 GPU)"},
+        "reduce_input_gb_per_s": round(gbs(b_in, t_red), 2),
+        "reduce_gb_per_s": round(gbs(b_in + b_out, t_red), 2),
+        "reduce_frac_hbm_peak": round(gbs(b_in + b_out, t_red) / HBM_PEAK_GBS, 4),
+        "breakdown_ms": {"what": "mean span of the reduce on the GPU clock (first kernel's start to the writer's "
+                                 "end) and of its writer alone", "sparse_reduce": round(t_red, 4),
+                         "reduce_writer": round(t_w, 4)},
+        "reduce_result": {"nnz": K, "dense": dense},
+        "roofline": {"kernel": "reduce writer", "bound": "hbm", "achieved": round(gbs(b_in + b_out, t_w), 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs(b_in + b_out, t_w) / HBM_PEAK_GBS, 4),
+                     "traffic": None, "avg_launch_ms": round(t_w, 4), "algorithmic_bytes": b_in + b_out},
+        "cpu_baseline": None,
+    }), flush=True)
 
 
 def other_configs(sg, W, dev, skip_wid, ev):

@@ -73,8 +73,10 @@ __device__ __forceinline__ uint32_t quantize_one(float v, float ratio, uint32_t 
 }
 
 // Smallest ratio the fp64 route below takes: its results lie in the normal
-// fp32 range, where the bound of its proof holds.
+// fp32 range, where the bound of its proof holds. A nonnegative fp32 ratio r
+// is in (0, kTinyRatio) iff bits(r) - 1 < kTinyBits - 1 as unsigned.
 constexpr float kTinyRatio = 0x1p-100f;
+constexpr uint32_t kTinyBits = 27u << 23;  // bits of 2^-100
 
 // ratio[i] = |v[i]| / scale, correctly rounded to fp32, for a bucket scale
 // (scale = max |v| over the bucket, so every ratio is in [0, 1]). The fp32
@@ -98,7 +100,7 @@ __device__ __forceinline__ void ratios(const float (&v)[K], float scale, float (
 #pragma unroll
   for (int i = 0; i < K; ++i) {
     ratio[i] = (float)((double)fabsf(v[i]) * rs);
-    tiny |= ratio[i] < kTinyRatio && v[i] != 0.0f;
+    tiny |= __float_as_uint(ratio[i]) - 1u < kTinyBits - 1u;
   }
   if (__builtin_expect(__ballot(tiny) != 0ull, 0)) {
 #pragma unroll

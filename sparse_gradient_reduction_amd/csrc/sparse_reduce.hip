@@ -655,7 +655,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
 // that failed the checks gives unspecified sums, but every LDS slot touched
 // stays inside the window.
 constexpr int kRankThreads = 256;
-constexpr uint32_t kRankCap = 1536;
+constexpr uint32_t kRankCap = 1280;
 constexpr uint32_t kRankSlots = kRankCap + 4;
 
 template <int MAXP, int BITS, bool QUAD>
