@@ -315,7 +315,7 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
  * SPARCML_ERR_SCRATCH_LIMIT, launching nothing, when
  * sparcml_sparse_reduce_workspace(P, N, h_offsets[P]) exceeds
  * SPARCML_REDUCE_SCRATCH_BYTES (32 MiB: for instance 64 nodes over an index
- * space of 2^27 take 25.2 MB).
+ * space of 2^27 take 26.5 MB).
  * Every call on one GPU uses the same scratch: calls that may overlap in time
  * on one GPU (different streams without ordering between them) race and
  * give unspecified results. Calls ordered on one stream are safe; each clears
