@@ -28,17 +28,24 @@ struct same_type {
 // Launches fn on `stream`; `start` / `stop`, when not null, are recorded as
 // the kernel itself starts and ends (hipExtLaunchKernel), so that their
 // elapsed time is that kernel's and nothing queued around it.
+// `lds` bytes of dynamic LDS.
 template <typename... P>
-hipError_t launch_ev(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
-                     typename same_type<P>::type... a) {
+hipError_t launch_ev_lds(void (*fn)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop, typename same_type<P>::type... a) {
   if (start == nullptr && stop == nullptr) {
-    hipLaunchKernelGGL(fn, grid, block, 0, stream, a...);
+    hipLaunchKernelGGL(fn, grid, block, lds, stream, a...);
     return hipGetLastError();
   }
   void* args[] = {static_cast<void*>(&a)...};
-  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, 0, stream, start,
+  const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, args, lds, stream, start,
                                           stop, 0);
   return e != hipSuccess ? e : hipGetLastError();
+}
+
+template <typename... P>
+hipError_t launch_ev(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                     typename same_type<P>::type... a) {
+  return launch_ev_lds(fn, grid, block, 0, stream, start, stop, a...);
 }
 
 // ---- error-feedback Top-k -------------------------------------------------

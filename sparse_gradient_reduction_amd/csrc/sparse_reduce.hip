@@ -9,26 +9,30 @@
 //
 // One GPU holds all P contributions. The index space is cut into segments of
 // 4096 indices, the one-GPU analogue of the split phase's index-range owners;
-// a workgroup owns one segment and takes each node's run of pairs falling in
-// it. Sums accumulate in fp64 in LDS (ds_add_f64: independent of arrival
-// order up to fp64 rounding) and are rounded to fp32 once.
+// a workgroup owns a group of consecutive segments and takes each node's run
+// of pairs falling in it. Sums accumulate in fp64 in LDS (ds_add_f64:
+// independent of arrival order up to fp64 rounding) and are rounded to fp32
+// once.
 //
 //   bounds   node-major streaming pass over the indices: where each node's
 //            run crosses a segment boundary; checks range and order. Its
-//            first workgroup also stores
-//            the node offsets (passed inline) and clears the call's state
-//            and group totals.
-//   count    per segment: union bitmap in LDS, stored for the writer, and
-//            its popcount
-//   decide   exclusive scan of the segment counts, K, dense iff K >= T
-//   write    per segment: the sums, stored densely or as the segment's
-//            sorted part of the sparse result at its offset
-// The estimate of K picks the writer: a full 4096-entry tile when the result
-// is expected dense, slots in union-rank order otherwise; both write either
-// result. More than 256 nodes take setup launches for the offsets first.
-// (Per-group totals added up by atomics in the count pass, to let every
-// writer find its own offset without the scan, made the count pass more than
-// twice as slow: hundreds of workgroups adding to one word.)
+//            first workgroup also stores the node offsets (passed inline) and
+//            clears the call's state.
+//   count    per count group of 2^glog segments: union bitmap in LDS, stored
+//            for the writer, and the union count of every writer group in it
+//   decide   exclusive scan of the writer-group counts, K, dense iff K >= T
+//   write    per writer group of 2^mlog segments: the sums, stored densely or
+//            as the group's sorted part of the sparse result at its offset
+// Groups of several segments serve inputs with few pairs per segment, where
+// one segment per workgroup leaves each workgroup too little to load. The
+// estimate of K picks the writer: a full 4096-entry tile per segment when the
+// result is expected dense, slots in union-rank order otherwise; both write
+// either result. More than 256 nodes take setup launches for the offsets
+// first. (Per-group totals added up by atomics in the count pass, to let
+// every writer find its own offset without the scan, made the count pass more
+// than twice as slow: hundreds of workgroups adding to one word. Finding each
+// node's run ends by searching its indices in the count pass, instead of the
+// bounds pass, cost more than the pass it saved: every probe is a cache line.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "qsgd_format.hpp"
@@ -43,10 +47,23 @@ namespace {
 constexpr int kSegBits = 12;
 constexpr uint32_t kSeg = 1u << kSegBits;  // 4096 indices per segment
 constexpr int kThreads = 256;              // bounds kernel
+constexpr int kWordBits = 7;
 constexpr int kWords = kSeg / 32;          // bitmap words per segment
+static_assert(kWords == 1 << kWordBits, "segment words");
 constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
-
+// Group sizes, measured on MI355X: count workgroups of up to 2048 pairs
+// whose node runs stay within about 200 pairs (its lanes take one pair of a
+// run each), and rank-order writers whose pairs stay within 1024 (the union
+// of a group may exceed its 1280 rank slots only by chance; the writer then
+// takes another pass). Both keep at least 512 workgroups.
+constexpr uint32_t kMaxCountLog2 = 4;   // at most 16 segments per count workgroup
+constexpr uint32_t kMaxWriterLog2 = 2;  // at most 4 segments per rank-order writer
+constexpr double kCountPairs = 2048.0;
+constexpr double kCountRun = 200.0;
+constexpr uint64_t kCountGroupsWanted = 512;
+constexpr double kWriterFill = 1024.0;
+constexpr uint64_t kWriterGroupsWanted = 512;
 struct State {
   uint32_t flags;
   uint32_t is_dense;
@@ -91,8 +108,11 @@ struct RDev {
   uint32_t P;
   uint32_t N;
   uint32_t total;  // pairs over all nodes
+  uint32_t glog;   // segments per count group: 2^glog
+  uint32_t mlog;   // segments per writer group: 2^mlog (mlog <= glog)
   uint32_t pad;
-  uint64_t S;
+  uint64_t S;      // segments
+  uint64_t W;      // writer groups
   uint64_t T;
   uint64_t out_idx_cap;
   State* state;
@@ -100,8 +120,8 @@ struct RDev {
   uint32_t* flagw;  // [P * bx]: input-check bits found by each bounds workgroup
   uint64_t nflagw;
   uint32_t* bounds;
-  uint32_t* cnt;
-  uint32_t* off;
+  uint32_t* cnt;      // [W] union count per writer group
+  uint32_t* off;      // [W] its offset in the sparse result
   uint32_t* bitmaps;  // [S][128]: bit i of segment s set iff s * 4096 + i is in the union
   ReduceResultDev* result;
   // quantized input only: node p's codes start at byte coffs[p], its
@@ -318,25 +338,26 @@ struct QRuns {
   uint32_t sb[MAXP];
 };
 
-// Run of node p in segment s: (absolute position of the node's first pair
-// in the segment, number of its pairs there). Run ends are clamped to the
+// Run of node p in segments [s0, s1): (absolute position of the node's
+// first pair there, number of its pairs there). Run ends are clamped to the
 // node's own pairs, which keeps every later load inside them even for input
 // whose order check failed.
-__device__ __forceinline__ uint2 node_run(const RDev& R, uint64_t s, uint32_t p) {
-  const uint32_t* b = R.bounds + p * (R.S + 1) + s;  // node-major run-start table
+__device__ __forceinline__ uint2 node_run(const RDev& R, uint64_t s0, uint64_t s1, uint32_t p) {
+  const uint32_t* b = R.bounds + p * (R.S + 1);  // node-major run-start table
   const uint32_t lo = (uint32_t)R.offs[p], hi = (uint32_t)R.offs[p + 1];
-  const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[0], lo), hi);
-  const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[1], lo), hi);
+  const uint32_t b0 = std::min<uint32_t>(std::max<uint32_t>(b[s0], lo), hi);
+  const uint32_t b1 = std::min<uint32_t>(std::max<uint32_t>(b[s1], lo), hi);
   return make_uint2(b0, b1 > b0 ? b1 - b0 : 0u);
 }
 
-// The run table of segment s in LDS (node p's run at runs[p]), and for
-// quantized input the node's code tables. All loads of a thread go out
+// The run table of segments [s0, s1) in LDS (node p's run at runs[p]), and
+// for quantized input the node's code tables. All loads of a thread go out
 // before it waits; the caller's barrier publishes the table.
 template <int NT, int MAXP>
-__device__ __forceinline__ void store_run_table(const RDev& R, uint64_t s, uint2* runs, QRuns<MAXP>* q) {
+__device__ __forceinline__ void store_run_table(const RDev& R, uint64_t s0, uint64_t s1, uint2* runs,
+                                                QRuns<MAXP>* q) {
   for (uint32_t p = threadIdx.x; p < R.P; p += NT) {
-    const uint2 rn = node_run(R, s, p);
+    const uint2 rn = node_run(R, s0, s1, p);
     runs[p] = rn;
     if (q != nullptr) {
       q->rel[p] = rn.x - (uint32_t)R.offs[p];
@@ -367,34 +388,40 @@ __device__ __forceinline__ Slots make_slots(uint32_t lane_bits, int NT) {
 }
 
 constexpr int kCountThreads = 128;
-constexpr int kWordWaves = kWords / kWave;  // 2
-static_assert(kWords % kWave == 0 && kWords <= kCountThreads, "bitmap words cover whole waves");
+constexpr uint32_t kMaxWritersPerCount = 1u << kMaxCountLog2;
 
-// One workgroup per segment: short, independent workgroups kept more
-// segments in flight than long ones walking several segments (measured).
-// Builds the segment's union bitmap in LDS and stores it with its popcount,
-// and folds a share of the bounds pass's check words into the state. (The
-// checks themselves cost the count pass 14 us at 64 x 671088 pairs, the
-// bounds pass, which compares every pair with its predecessor anyway, about
-// 4 us.)
+// One workgroup per count group g, segments [s0, s1) = [g 2^glog, ...):
+// short, independent workgroups kept more segments in flight than long ones
+// walking several groups (measured), and a group of several segments gives
+// each workgroup enough pairs where a segment holds few. Builds the group's
+// union bitmap in LDS, stores it with the union count of each writer group
+// in the group, and folds a share of the bounds pass's check words into the
+// state. (The checks themselves cost the count pass 14 us at 64 x 671088
+// pairs, the bounds pass, which compares every pair with its predecessor
+// anyway, about 4 us.)
 template <int MAXP>
 __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R,
                                                          uint32_t lane_bits) {
   constexpr int NT = kCountThreads;
   constexpr int kB = 16;  // node rows per pass: 16 index loads in flight per thread
-  __shared__ uint32_t bits[kWords];
+  static_assert(kWords % NT == 0 || NT % kWords == 0, "bitmap words cover whole waves");
   __shared__ uint2 runs[MAXP];
-  __shared__ uint32_t scr[NT / kWave];
-  const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
-  const uint32_t seg_lo = (uint32_t)(s << kSegBits);
-  const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
-  if (threadIdx.x < kWords) bits[threadIdx.x] = 0u;
+  __shared__ uint32_t wc[kMaxWritersPerCount];
+  extern __shared__ uint32_t bits[];  // [128 << glog]: the group's bitmap
+  const uint64_t g = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
+  const uint64_t s0 = g << R.glog;
+  const uint64_t s1 = std::min<uint64_t>(s0 + (1u << R.glog), R.S);
+  const uint32_t segs = (uint32_t)(s1 - s0);
+  const uint32_t glo = (uint32_t)(s0 << kSegBits);
+  const uint32_t glen = std::min<uint32_t>(segs << kSegBits, R.N - glo);
+  for (uint32_t i = threadIdx.x; i < segs * kWords; i += NT) bits[i] = 0u;
+  if (threadIdx.x < kMaxWritersPerCount) wc[threadIdx.x] = 0u;
   const Slots sl = make_slots(lane_bits, NT);
-  store_run_table<NT, MAXP>(R, s, runs, nullptr);
+  store_run_table<NT, MAXP>(R, s0, s1, runs, nullptr);
   __syncthreads();
   auto mark = [&](uint32_t i) {
-    const uint32_t local = i - seg_lo;
-    if (local < seg_len) atomicOr(&bits[local >> 5], 1u << (local & 31));
+    const uint32_t local = i - glo;
+    if (local < glen) atomicOr(&bits[local >> 5], 1u << (local & 31));
   };
   for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
     uint2 rn[kB];
@@ -416,38 +443,39 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
       for (uint32_t j = sl.lane + step; j < rn[b].y; j += step) mark(idx[rn[b].x + j]);
     }
   }
-  if (threadIdx.x == 0) {  // the bounds pass's check bits: words s, s + S, ... of them
+  if (threadIdx.x == 0) {  // the bounds pass's check bits: words g, g + groups, ... of them
     uint32_t f = 0u;
-    for (uint64_t w = s; w < R.nflagw; w += R.S) f |= R.flagw[w];
+    for (uint64_t w = g; w < R.nflagw; w += gridDim.x) f |= R.flagw[w];
     if (f) atomicOr(&R.state->flags, f);
   }
   __syncthreads();
-  const uint32_t wid = threadIdx.x / kWave;
-  if (wid >= (uint32_t)kWordWaves) return;
-  const uint32_t word = bits[threadIdx.x];
-  R.bitmaps[s * kWords + threadIdx.x] = word;  // the writers place pairs by it
-  const uint32_t c = wave_sum((uint32_t)__popc(word));
-  if (lane_id() == 0) scr[wid] = c;
-  __syncthreads();  // only the word waves are left
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0;
-    for (int w = 0; w < kWordWaves; ++w) tot += scr[w];
-    R.cnt[s] = tot;
+  // the bitmaps, whole waves at a time (the words come in multiples of 128),
+  // and the union count of every writer group
+  uint32_t* gb = R.bitmaps + s0 * kWords;
+  for (uint32_t k = threadIdx.x; k < segs * kWords; k += NT) {
+    const uint32_t word = bits[k];
+    gb[k] = word;
+    const uint32_t c = wave_sum((uint32_t)__popc(word));
+    if (lane_id() == 0u) atomicAdd(&wc[k >> (kWordBits + R.mlog)], c);
   }
+  __syncthreads();
+  const uint64_t wfirst = g << (R.glog - R.mlog);
+  const uint64_t wn = std::min<uint64_t>(1u << (R.glog - R.mlog), R.W - wfirst);
+  if (threadIdx.x < wn) R.cnt[wfirst + threadIdx.x] = wc[threadIdx.x];
 }
 
-// Exclusive scan of the segment counts by one workgroup, into per-segment
-// offsets, K, the dense decision and the result record. Each thread loads
-// 32 consecutive counts at once (one round trip per 32768 segments, 16-byte
-// loads where the run is whole), scans them in registers, and the
-// per-thread totals are scanned across the block.
+// Exclusive scan of the writer-group counts by one workgroup, into offsets,
+// K, the dense decision and the result record. Each thread loads 32
+// consecutive counts at once (one round trip per 32768 groups, 16-byte loads
+// where the run is whole), scans them in registers, and the per-thread totals
+// are scanned across the block.
 __global__ __launch_bounds__(1024) void k_decide(RDev R) {
   constexpr int kPer = 32;
   __shared__ uint32_t scr[1024 / kWave + 3];
   uint64_t carry = 0;
-  for (uint64_t s0 = 0; s0 < R.S; s0 += 1024 * kPer) {
+  for (uint64_t s0 = 0; s0 < R.W; s0 += 1024 * kPer) {
     const uint64_t first = s0 + (uint64_t)threadIdx.x * kPer;
-    const bool whole = first + kPer <= R.S;  // cnt and off are 256-byte aligned, first % 32 == 0
+    const bool whole = first + kPer <= R.W;  // cnt and off are 256-byte aligned, first % 32 == 0
     uint32_t c[kPer];
     if (whole) {
       const uint4* src = reinterpret_cast<const uint4*>(R.cnt + first);
@@ -461,7 +489,7 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kPer; ++u) c[u] = first + u < R.S ? R.cnt[first + u] : 0u;
+      for (int u = 0; u < kPer; ++u) c[u] = first + u < R.W ? R.cnt[first + u] : 0u;
     }
     uint32_t sum = 0;
 #pragma unroll
@@ -481,7 +509,7 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
     } else {
 #pragma unroll
       for (int u = 0; u < kPer; ++u)
-        if (first + u < R.S) R.off[first + u] = c[u];
+        if (first + u < R.W) R.off[first + u] = c[u];
     }
     carry += tot;
   }
@@ -497,32 +525,87 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
   }
 }
 
-// What a writer workgroup needs of segment s before merging: whether the
-// result is dense, the segment's union count and its output offset. The last
-// thread loads them (its wave has no run-table loads to hold back while it
-// waits); seg_head_finish reads them after the caller's barrier.
-template <int NT>
-__device__ __forceinline__ void seg_head_load(const RDev& R, uint64_t s, uint32_t* head) {
-  if (threadIdx.x == NT - 1) {
-    const uint32_t dense = R.state->is_dense, cnt = R.cnt[s], off = R.off[s];
-    head[0] = dense;
-    head[1] = cnt;
-    head[2] = off;
-  }
-}
+// What a writer workgroup needs of its group w before merging: whether the
+// result is dense, the group's union count and its output offset. After the
+// decide pass the last thread loads them (its wave has no run-table loads to
+// hold back while it waits). Without it (SCAN, for at most kScanMaxW groups,
+// where one more launch costs more than the scan), every workgroup adds up
+// the group counts itself: all of them for K, those before w for its offset;
+// the workgroup of group 0 stores the result record. load() goes out with the
+// other prologue loads; finish() follows the caller's barrier and is called
+// by every thread.
+constexpr uint64_t kScanMaxW = 2048;
 
-template <int NT>
-__device__ __forceinline__ uint3 seg_head_finish(const RDev&, uint64_t, const uint32_t* head) {
-  return make_uint3(head[0], head[1], head[2]);
-}
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+
+template <int NT, bool SCAN>
+struct WriterHead {
+  uint32_t before = 0u, all = 0u;
+
+  __device__ __forceinline__ void load(const RDev& R, uint64_t w, uint32_t* head) {
+    if constexpr (!SCAN) {
+      if (threadIdx.x == NT - 1) {
+        const uint32_t dense = R.state->is_dense, cnt = R.cnt[w], off = R.off[w];
+        head[0] = dense;
+        head[1] = cnt;
+        head[2] = off;
+      }
+    } else {
+      constexpr int kPer = (int)(kScanMaxW / NT);
+      static_assert(kPer % 4 == 0, "whole 16-byte loads");
+      const uint64_t first = (uint64_t)threadIdx.x * kPer;  // cnt is 256-byte aligned
+      uint32_t c[kPer];
+      if (first + kPer <= R.W) {
+#pragma unroll
+        for (int q = 0; q < kPer / 4; ++q) {
+          const uint4 x = reinterpret_cast<const uint4*>(R.cnt + first)[q];
+          c[4 * q] = x.x;
+          c[4 * q + 1] = x.y;
+          c[4 * q + 2] = x.z;
+          c[4 * q + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) c[u] = first + u < R.W ? R.cnt[first + u] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        all += c[u];
+        before += first + u < w ? c[u] : 0u;
+        if (first + u == w) head[1] = c[u];
+      }
+    }
+  }
+
+  // The values are the same in every thread; readfirstlane keeps them in
+  // scalar registers and the branches on them uniform.
+  __device__ __forceinline__ uint3 finish(const RDev& R, uint64_t w, const uint32_t* head, uint32_t* scratch) {
+    if constexpr (!SCAN) {
+      return make_uint3(uniform(head[0]), uniform(head[1]), uniform(head[2]));
+    } else {
+      uint32_t K, off;
+      block_sum2<NT>(all, before, scratch, K, off);
+      const uint32_t dense = K >= R.T ? 1u : 0u;
+      if (w == 0 && threadIdx.x == 0) {
+        ReduceResultDev res;
+        res.nnz = K;
+        res.is_dense = dense;
+        res.flags = R.state->flags;
+        *R.result = res;
+      }
+      return make_uint3(uniform(dense), uniform(head[1]), uniform(off));
+    }
+  }
+};
 
 constexpr int kWriteThreads = 512;
+constexpr int kWordWaves = kWords / kWave;  // 2
 
 // Writer for results expected dense: each segment's sums in a 4096-entry
 // fp64 LDS tile, written out as float4 when the result is dense; when it
 // turns out sparse, each thread stores the union entries of its 8 indices at
 // their ranks from the count pass's bitmap.
-template <int MAXP, int BITS>
+template <int MAXP, int BITS, bool SCAN>
 __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __restrict__ idx,
                                                               const float* __restrict__ val,
                                                               uint32_t* __restrict__ out_idx,
@@ -533,18 +616,20 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
   __shared__ double acc[kSeg];
   __shared__ uint2 runs[MAXP];
   __shared__ uint32_t scr[3];
+  __shared__ uint32_t hscr[SCAN ? 2 * NT / kWave : 1];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   const uint32_t seg_lo = (uint32_t)(s << kSegBits);
   const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
-  seg_head_load<NT>(R, s, scr);
+  WriterHead<NT, SCAN> hw;
+  hw.load(R, s, scr);
   uint32_t word = 0u;
   if (threadIdx.x < kWords) word = R.bitmaps[s * kWords + threadIdx.x];
   for (uint32_t i = threadIdx.x; i < kSeg; i += NT) acc[i] = 0.0;
   const Slots sl = make_slots(lane_bits, NT);
-  store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
+  store_run_table<NT, BITS ? MAXP : 1>(R, s, s + 1, runs, BITS ? &qruns : nullptr);
   __syncthreads();
-  const uint3 hd = seg_head_finish<NT>(R, s, scr);
+  const uint3 hd = hw.finish(R, s, scr, hscr);
   const bool dense = hd.x != 0u;
   const uint32_t seg_cnt = hd.y, seg_off = hd.z;
   if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
@@ -634,10 +719,12 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
   }
 }
 
-// Writer placing pairs by their rank in the segment's union, for results
-// expected sparse. The count pass left each segment's union bitmap; a word
-// table (ranks before each 32-index word, and the word) gives every pair its
-// rank r in the segment with one LDS read and a popcount, so the sums
+// Writer placing pairs by their rank in its group's union, for results
+// expected sparse; a group is 2^mlog consecutive segments (up to 4, where
+// the pairs per segment are few). The count pass left each segment's union
+// bitmap; a word table in LDS (ranks before each 32-index word, and the word)
+// gives every pair its rank r in the group with one LDS read and a popcount,
+// so the sums
 // accumulate directly in output order and are stored as they stand: no
 // clearing or compaction of a 4096-entry tile, and a quarter of its LDS,
 // which lets more workgroups share a compute unit.
@@ -648,8 +735,8 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
 // pair per lane), and results are stored as aligned quads: rank r of a
 // window whose output starts at position P0 sits in slot r + (P0 mod 4), so
 // that slot quads are output quads. Ranks come in windows of kRankCap; a
-// segment with more union entries takes one pass over its pairs per window.
-// A dense result (the count crossed T) writes every index of the segment:
+// group with more union entries takes one pass over its pairs per window.
+// A dense result (the count crossed T) writes every index of the group:
 // the sum at its rank, or 0 outside the union. For valid input every pair's
 // bit is set in the bitmap the count pass built from the same pairs; input
 // that failed the checks gives unspecified sums, but every LDS slot touched
@@ -658,7 +745,7 @@ constexpr int kRankThreads = 256;
 constexpr uint32_t kRankCap = 1280;
 constexpr uint32_t kRankSlots = kRankCap + 4;
 
-template <int MAXP, int BITS, bool QUAD>
+template <int MAXP, int BITS, bool QUAD, bool SCAN>
 __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* __restrict__ idx,
                                                                const float* __restrict__ val,
                                                                uint32_t* __restrict__ out_idx,
@@ -668,34 +755,51 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
   constexpr int NT = kRankThreads;
   constexpr int kB = QUAD ? 2 : 8;  // node rows per pass
   __shared__ __align__(16) double acc[kRankSlots];
-  __shared__ __align__(16) uint16_t sloc[kRankSlots];  // index within the segment
-  __shared__ uint2 words[kWords];  // (ranks before the word, the word)
+  __shared__ __align__(16) uint16_t sloc[kRankSlots];  // index within the group
   __shared__ uint2 runs[MAXP];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
   __shared__ uint32_t scr[3];
+  __shared__ uint32_t hscr[SCAN ? 2 * NT / kWave : 1];
+  __shared__ uint32_t sscr[NT / kWave + 1];
+  extern __shared__ uint2 words[];  // [128 << mlog]: (ranks before the word, the word)
   const uint64_t s = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
-  const uint32_t seg_lo = (uint32_t)(s << kSegBits);
-  const uint32_t seg_len = std::min<uint32_t>(kSeg, R.N - seg_lo);
+  const uint32_t mlog = R.mlog;
+  const uint32_t seg_lo = (uint32_t)(s << (kSegBits + mlog));
+  const uint32_t span = kSeg << mlog;
+  const uint32_t seg_len = std::min<uint32_t>(span, R.N - seg_lo);
   const Slots sl = make_slots(lane_bits, NT);
-  // every load of the prologue goes out before any wait: the bitmap (wave 0),
-  // the counts and totals, and the run table
-  uint2 wpair = make_uint2(0u, 0u);
-  if (threadIdx.x < kWords / 2) wpair = reinterpret_cast<const uint2*>(R.bitmaps + s * kWords)[threadIdx.x];
-  seg_head_load<NT>(R, s, scr);
+  // every load of the prologue goes out before any wait: the bitmaps (two
+  // words per thread), the counts and totals, and the run table
+  const uint32_t npairs = (kWords / 2) << mlog;
+  const uint32_t nvalid = (kWords / 2) * (uint32_t)std::min<uint64_t>(1u << mlog, R.S - (s << mlog));
+  uint2 wpair = make_uint2(0u, 0u);  // segments past the last (in the last group) hold nothing
+  if (threadIdx.x < nvalid) wpair = reinterpret_cast<const uint2*>(R.bitmaps + (s << mlog) * kWords)[threadIdx.x];
+  WriterHead<NT, SCAN> hw;
+  hw.load(R, s, scr);
   for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
-  store_run_table<NT, BITS ? MAXP : 1>(R, s, runs, BITS ? &qruns : nullptr);
-  if (threadIdx.x < kWave) {  // word table: wave 0, two words per lane
-    const uint32_t c0 = (uint32_t)__popc(wpair.x), c1 = (uint32_t)__popc(wpair.y);
-    const uint32_t inc = wave_inclusive_scan(c0 + c1);
-    words[2 * threadIdx.x] = make_uint2(inc - c0 - c1, wpair.x);
-    words[2 * threadIdx.x + 1] = make_uint2(inc - c1, wpair.y);
+  store_run_table<NT, BITS ? MAXP : 1>(R, s << mlog, std::min<uint64_t>((s + 1) << mlog, R.S), runs,
+                                       BITS ? &qruns : nullptr);
+  const uint32_t c0 = (uint32_t)__popc(wpair.x), c1 = (uint32_t)__popc(wpair.y);
+  if (mlog == 0u) {
+    if (threadIdx.x < kWave) {  // word table: wave 0
+      const uint32_t inc = wave_inclusive_scan(c0 + c1);
+      words[2 * threadIdx.x] = make_uint2(inc - c0 - c1, wpair.x);
+      words[2 * threadIdx.x + 1] = make_uint2(inc - c1, wpair.y);
+    }
+  } else {  // word table of several segments: a scan over the block
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<NT>(c0 + c1, sscr, tot);
+    if (threadIdx.x < npairs) {
+      words[2 * threadIdx.x] = make_uint2(ex, wpair.x);
+      words[2 * threadIdx.x + 1] = make_uint2(ex + c0, wpair.y);
+    }
   }
   __syncthreads();
-  const uint3 hd = seg_head_finish<NT>(R, s, scr);
+  const uint3 hd = hw.finish(R, s, scr, hscr);
   const bool dense = hd.x != 0u;
   const uint32_t seg_cnt = hd.y;
   const uint32_t seg_off = hd.z;
-  if (!dense && seg_cnt == 0u) return;  // nothing of this segment in a sparse result
+  if (!dense && seg_cnt == 0u) return;  // nothing of this group in a sparse result
 
   auto value_at = [&](uint32_t p, uint32_t j, uint32_t jr) -> float {
     if constexpr (BITS == 0) {
@@ -708,6 +812,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
       return F::value(code, F::step(R.scales[qruns.sb[p] + bucket_no]));
     }
   };
+  const uint32_t lmask = span - 1u;
   const uint32_t windows = std::max<uint32_t>(1u, (seg_cnt + kRankCap - 1) / kRankCap);
   for (uint32_t w0 = 0, win = 0; win < windows; ++win, w0 += kRankCap) {
     const uint32_t sh = (seg_off + w0) & 3u;  // slot of the window's first rank
@@ -718,7 +823,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
       __syncthreads();
     }
     auto add = [&](uint32_t i, float v) {
-      const uint32_t local = i & (kSeg - 1u);
+      const uint32_t local = i & lmask;
       const uint2 wd = words[local >> 5];
       const uint32_t x = wd.x + (uint32_t)__popc(wd.y & ((1u << (local & 31)) - 1u)) - base;
       if (x - sh < kRankCap) {
@@ -788,9 +893,9 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
       }
     }
     __syncthreads();
-    if (dense) {  // every index of the segment: its sum, or 0 outside the union
+    if (dense) {  // every index of the group: its sum, or 0 outside the union
       float* out = out_val + seg_lo;
-      const bool whole = windows == 1u && seg_len == kSeg;
+      const bool whole = windows == 1u && seg_len == span;
       for (uint32_t q = threadIdx.x; q < (seg_len + 3) / 4; q += NT) {
         const uint2 wd = words[q >> 3];
         float o[4];
@@ -847,45 +952,68 @@ size_t reduce_workspace_bytes(uint32_t P, uint64_t N, uint64_t total_nnz) {
 
 namespace {
 
-template <int MAXP>
+template <int MAXP, bool SCAN>
 hipError_t launch_write_tile(uint32_t bits, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
                              const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val, const RDev& R,
                              uint32_t lb) {
   const dim3 block(kWriteThreads);
   switch (bits) {
-    case 0: return launch_ev(k_write_tile<MAXP, 0>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
-    case 2: return launch_ev(k_write_tile<MAXP, 2>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
-    case 4: return launch_ev(k_write_tile<MAXP, 4>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
-    default: return launch_ev(k_write_tile<MAXP, 8>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 0:
+      return launch_ev(k_write_tile<MAXP, 0, SCAN>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 2:
+      return launch_ev(k_write_tile<MAXP, 2, SCAN>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    case 4:
+      return launch_ev(k_write_tile<MAXP, 4, SCAN>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+    default:
+      return launch_ev(k_write_tile<MAXP, 8, SCAN>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
   }
 }
 
-template <int MAXP>
+template <int MAXP, bool SCAN>
 hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
                                const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val,
                                const RDev& R, uint32_t lb, uint32_t lbq) {
   const dim3 block(kRankThreads);
+  const size_t lds = sizeof(uint2) * ((size_t)kWords << R.mlog);  // the word table
   switch (bits) {
     case 0:
       if (quad)
-        return launch_ev(k_write_ranked<MAXP, 0, true>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R,
-                         lbq);
-      return launch_ev(k_write_ranked<MAXP, 0, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R,
-                       lb);
+        return launch_ev_lds(k_write_ranked<MAXP, 0, true, SCAN>, grid, block, lds, stream, e0, e1, idx, val,
+                             out_idx, out_val, R, lbq);
+      return launch_ev_lds(k_write_ranked<MAXP, 0, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
+                           out_val, R, lb);
     case 2:
-      return launch_ev(k_write_ranked<MAXP, 2, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+      return launch_ev_lds(k_write_ranked<MAXP, 2, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
+                           out_val, R, lb);
     case 4:
-      return launch_ev(k_write_ranked<MAXP, 4, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+      return launch_ev_lds(k_write_ranked<MAXP, 4, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
+                           out_val, R, lb);
     default:
-      return launch_ev(k_write_ranked<MAXP, 8, false>, grid, block, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+      return launch_ev_lds(k_write_ranked<MAXP, 8, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
+                           out_val, R, lb);
   }
 }
 
-// Lanes per node in the count and write passes (as a power of two): about
-// 1.5 times the mean run length of a node in a segment, so that few runs
-// spill past their lanes while lanes stay mostly busy; 16 to 128.
-uint32_t lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
-  const double mean = (double)total / ((double)P * (double)S);
+// The writer for (tile or rank order) x (nodes up to 256 or 1024) x (its own
+// scan or the decide pass's).
+template <bool SCAN>
+hipError_t launch_writer(bool tile, bool small_p, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0,
+                         hipEvent_t e1, const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val,
+                         const RDev& R, uint32_t lb, uint32_t lbq) {
+  if (tile)
+    return small_p ? launch_write_tile<256, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb)
+                   : launch_write_tile<kMaxP, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+  return small_p ? launch_write_ranked<256, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R,
+                                                  lb, lbq)
+                 : launch_write_ranked<kMaxP, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R,
+                                                    lb, lbq);
+}
+
+// Lanes per node in the write passes (as a power of two): about 1.5 times
+// the mean run length of a node in a writer group, so that few runs spill
+// past their lanes while lanes stay mostly busy; 16 to 128.
+uint32_t lanes_log2(uint32_t P, uint64_t W, uint64_t total) {
+  const double mean = (double)total / ((double)P * (double)W);
   uint32_t lb = 4;
   while (lb < 7 && (double)(1u << lb) < 1.5 * mean) ++lb;
   return lb;
@@ -894,12 +1022,35 @@ uint32_t lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
 // Lanes per node when each lane takes an aligned quad of pairs: the mean
 // number of quads a run meets (its length / 4, plus 3/4 for the unaligned
 // ends) with room for one standard deviation and more; 2 to 64.
-uint32_t quad_lanes_log2(uint32_t P, uint64_t S, uint64_t total) {
-  const double mean = (double)total / ((double)P * (double)S);
+uint32_t quad_lanes_log2(uint32_t P, uint64_t W, uint64_t total) {
+  const double mean = (double)total / ((double)P * (double)W);
   const double quads = mean / 4.0 + 0.75 + std::sqrt(mean) / 4.0 + 1.0;
   uint32_t lb = 1;
   while (lb < 6 && (double)(1u << lb) < quads) ++lb;
   return lb;
+}
+
+// Segments per rank-order writer group (log2): as many as keep the group's
+// pairs, which bound its union, within kWriterFill and leave at least
+// kWriterGroupsWanted groups. The tile writer takes one segment.
+uint32_t writer_log2(uint64_t S, uint64_t total, bool tile) {
+  if (tile) return 0;
+  const double per_seg = (double)total / (double)S;
+  uint32_t m = 0;
+  while (m < kMaxWriterLog2 && (double)(2u << m) * per_seg <= kWriterFill && (S >> (m + 1)) >= kWriterGroupsWanted) ++m;
+  return m;
+}
+
+// Segments per count group (log2): a multiple of the writer group, doubled
+// while its pairs stay below kCountPairs, a node's mean run in the doubled
+// group within kCountRun, and at least kCountGroupsWanted groups remain.
+uint32_t count_log2(uint32_t P, uint64_t S, uint64_t total, uint32_t mlog) {
+  const double per_seg = (double)total / (double)S;
+  uint32_t g = mlog;
+  while (g < kMaxCountLog2 && (double)(1u << g) * per_seg < kCountPairs &&
+         (double)(2u << g) * per_seg / (double)P <= kCountRun && (S >> (g + 1)) >= kCountGroupsWanted)
+    ++g;
+  return g;
 }
 
 }  // namespace
@@ -918,8 +1069,11 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.P = P;
   R.N = (uint32_t)N;
   R.total = (uint32_t)h_offsets[P];
+  R.mlog = writer_log2(L.S, R.total, dense_first);
+  R.glog = count_log2(P, L.S, R.total, R.mlog);
   R.pad = 0;
   R.S = L.S;
+  R.W = (L.S + (1u << R.mlog) - 1) >> R.mlog;
   R.T = T;
   R.out_idx_cap = out_idx_cap;
   R.state = reinterpret_cast<State*>(w + L.state);
@@ -941,7 +1095,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   uint64_t max_nnz = 0;
   for (uint32_t p = 0; p < P; ++p) max_nnz = std::max<uint64_t>(max_nnz, h_offsets[p + 1] - h_offsets[p]);
 
-  // offsets inline to the bounds pass for up to 256 nodes, else by setup launches
+  // offsets inline to the bounds pass for up to 255 nodes, else by setup launches
   InlineOffsets in;
   const bool inline_offs = P + 1 <= (uint32_t)kInlineOffsets;
   if (inline_offs) {
@@ -963,29 +1117,31 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   hipError_t e = launch_ev(k_bounds, dim3(bx, P), dim3(kThreads), stream, inline_offs ? E.op_start : nullptr, nullptr,
                            idx, R, shift, in, inline_offs ? 1 : 0);
   if (e != hipSuccess) return e;
-  const dim3 segs((uint32_t)L.S);
   const bool small_p = P <= 256;
-  const uint32_t lb = lanes_log2(P, L.S, R.total);
-  if (small_p) hipLaunchKernelGGL((k_count<256>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
-  else hipLaunchKernelGGL((k_count<kMaxP>), segs, dim3(kCountThreads), 0, stream, idx, R, lb);
-  hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
+  const uint64_t groups = (L.S + (1u << R.glog) - 1) >> R.glog;  // count workgroups
+  const dim3 cgrid((uint32_t)groups);
+  const uint32_t lbc = lanes_log2(P, groups, R.total);
+  const size_t clds = sizeof(uint32_t) * ((size_t)kWords << R.glog);
+  if (small_p) hipLaunchKernelGGL((k_count<256>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  else hipLaunchKernelGGL((k_count<kMaxP>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  const bool scan_in_writer = R.W <= kScanMaxW;
+  if (!scan_in_writer) hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the writer is the op's last kernel: it carries the kernel pair, or the
   // op's stop alone
   const hipEvent_t w0 = E.k_start;
   const hipEvent_t w1 = E.k_stop ? E.k_stop : E.op_stop;
-  if (dense_first) {  // the estimate expects a dense result: the full tile
-    e = small_p ? launch_write_tile<256>(R.bits, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb)
-                : launch_write_tile<kMaxP>(R.bits, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb);
-  } else {
-    // 16-byte quads of pairs where both arrays allow them
-    const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
-    const uint32_t lbq = quad_lanes_log2(P, L.S, R.total);
-    e = small_p ? launch_write_ranked<256>(R.bits, quad, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
-                : launch_write_ranked<kMaxP>(R.bits, quad, segs, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
-                                             lbq);
-  }
+  const dim3 wgrid((uint32_t)R.W);
+  const uint32_t lb = lanes_log2(P, R.W, R.total);
+  // the estimate expecting a dense result takes the full tile; rank order
+  // loads 16-byte quads of pairs where both arrays allow them
+  const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
+  const uint32_t lbq = quad_lanes_log2(P, R.W, R.total);
+  e = scan_in_writer
+          ? launch_writer<true>(dense_first, small_p, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
+          : launch_writer<false>(dense_first, small_p, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
+                                 lbq);
   // with both pairs asked for, the op's stop follows the writer's at once
   if (e == hipSuccess && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
   return e;

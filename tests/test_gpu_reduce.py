@@ -234,3 +234,75 @@ def test_reduce_deterministic(dev):
     assert a[0] == b[0]
     assert torch.equal(a[3], b[3])
     assert torch.equal(a[4].view(torch.int32), b[4].view(torch.int32))
+
+
+def _sparse_sorted(rng, P, N, nnz):
+    """P nodes of nnz sorted distinct indices below N (drawn with repeats,
+    deduplicated, topped up), N(0,1) values."""
+    parts = []
+    for _ in range(P):
+        cand = np.unique(rng.integers(0, N, size=int(nnz * 1.05) + 8))
+        while cand.size < nnz:
+            cand = np.unique(np.concatenate([cand, rng.integers(0, N, size=nnz)]))
+        parts.append(np.sort(rng.choice(cand, size=nnz, replace=False)).astype(np.uint32))
+    off = np.arange(P + 1, dtype=np.uint64) * nnz
+    return off, np.concatenate(parts), rng.standard_normal(P * nnz).astype(np.float32)
+
+
+@pytest.mark.parametrize("P,N,nnz", [
+    (64, 1 << 24, 16384),   # 4096 segments of 256 pairs: writer groups of 4, count groups of 8; writers scan
+    (8, 1 << 26, 262144),   # 16384 segments of 128 pairs: 4096 writer groups, the decide pass scans
+    (3, 1 << 25, 700000),   # long runs of few nodes: writer groups of 2, count groups of 2
+])
+@pytest.mark.parametrize("delta", [0.3, 0.01])
+def test_multi_segment_groups(dev, P, N, nnz, delta):
+    """Few pairs per 4096-index segment: the count pass takes groups of
+    several segments and the rank-order writer groups of up to four, whose
+    union ranks span the group. Both results (delta = 0.01 is dense), each
+    written by both writers (hint 1: rank order, N: the tile)."""
+    rng = np.random.default_rng(P + nnz)
+    off, idx, val = _sparse_sorted(rng, P, N, nnz)
+    print(f"multi-segment P={P} N={N} nnz={nnz} delta={delta}", flush=True)
+    for hint in (1, N):
+        _check(off, idx, val, N, delta, dev, hint=hint)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_multi_segment_groups_quantized(dev, bits):
+    """The same grouping with 4- and 8-bit codes dequantized on load (pairs
+    one per lane), against the oracle on the dequantized values."""
+    rng = np.random.default_rng(60 + bits)
+    P, N, nnz, bucket = 64, 1 << 24, 16384, 512
+    off, idx, val = _sparse_sorted(rng, P, N, nnz)
+    codes, scales = oracle.qsgd(val.reshape(P, nnz), bits, bucket, 77, 2)
+    deq = oracle.dqsgd(codes, scales, nnz, bits, bucket).reshape(-1)
+    K, dense, oi, ov = oracle.reduce(off, idx, deq, N, 0.3)
+    out = sg.sparse_reduce_qsgd([int(x) for x in off], torch.from_numpy(idx.view(np.int32)).to(dev),
+                                torch.from_numpy(codes.reshape(-1)).to(dev),
+                                torch.from_numpy(scales.reshape(-1)).to(dev), bits, bucket, N, 0.3,
+                                expected_nnz_hint=1)
+    torch.cuda.synchronize()
+    gK, gdense, flags, gi, gv = out.host()
+    assert flags == 0 and gK == K and gdense == dense and not dense
+    np.testing.assert_array_equal(gi.numpy().astype(np.uint32), oi)
+    assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= reduce_tolerance(P, deq)
+
+
+def test_multi_segment_groups_unaligned(dev):
+    """Writer groups of four segments over pair arrays 8 bytes past a 16-byte
+    boundary (pairs one per lane in the writer, partial quads in the bounds
+    pass)."""
+    rng = np.random.default_rng(61)
+    P, N, nnz = 64, 1 << 24, 16384
+    off, idx, val = _sparse_sorted(rng, P, N, nnz)
+    K, dense, oi, ov = oracle.reduce(off, idx, val, N, 0.3)
+    n = idx.size
+    bi = torch.zeros(n + 8, dtype=torch.int32, device=dev)
+    bv = torch.zeros(n + 8, dtype=torch.float32, device=dev)
+    bi[2:2 + n] = torch.from_numpy(idx.view(np.int32)).to(dev)
+    bv[2:2 + n] = torch.from_numpy(val).to(dev)
+    gK, gdense, flags, gi, gv = sg.sparse_reduce([int(x) for x in off], bi[2:2 + n], bv[2:2 + n], N, 0.3,
+                                                 expected_nnz_hint=1).host()
+    assert flags == 0 and gK == K and gdense == dense and not dense
+    np.testing.assert_array_equal(gi.numpy().astype(np.uint32), oi)
+    assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= reduce_tolerance(P, val)
