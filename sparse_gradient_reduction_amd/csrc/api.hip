@@ -264,11 +264,14 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
   const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);
   if (cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
-  const double est = expected_nnz_hint ? (double)expected_nnz_hint : sparcml_estimate_nnz(P, N, h_offsets);
+  // the model's union estimate sizes the writer groups; a hint, where given,
+  // picks the writer in its place
+  const double model = sparcml_estimate_nnz(P, N, h_offsets);
+  const double est = expected_nnz_hint ? (double)expected_nnz_hint : model;
   const bool dense_first = est >= (double)T;
-  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, dense_first, out_idx, cap,
-                                                out_val, reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws,
-                                                stream, ev));
+  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, dense_first, model, out_idx,
+                                                cap, out_val, reinterpret_cast<sparcml::ReduceResultDev*>(d_result),
+                                                ws, stream, ev));
 }
 
 sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,

@@ -103,10 +103,12 @@ struct ReduceQuantized {
   const uint8_t* codes;
   const float* scales;
 };
-// val is used when quant is null, quant otherwise
+// val is used when quant is null, quant otherwise; union_est, the expected
+// union size, sizes the writer groups
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
-                                bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
+                                bool dense_first, double union_est, uint32_t* out_idx, uint64_t out_idx_cap,
+                                float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream,
                                 const OpEvents* ev = nullptr);
 

@@ -54,15 +54,16 @@ constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
 // Group sizes, measured on MI355X: count workgroups of up to 2048 pairs
 // whose node runs stay within about 200 pairs (its lanes take one pair of a
-// run each), and rank-order writers whose pairs stay within 1024 (the union
-// of a group may exceed its 1280 rank slots only by chance; the writer then
-// takes another pass). Both keep at least 512 workgroups.
+// run each), and rank-order writers of up to 4 segments whose expected union
+// fits the rank slots. Both keep at least 512 workgroups. The writer is bound
+// by the bytes its workgroups have in flight: five workgroups of two
+// 4096-index segments each (2560 rank slots) kept more in flight than eight
+// of one.
 constexpr uint32_t kMaxCountLog2 = 4;   // at most 16 segments per count workgroup
 constexpr uint32_t kMaxWriterLog2 = 2;  // at most 4 segments per rank-order writer
 constexpr double kCountPairs = 2048.0;
 constexpr double kCountRun = 200.0;
 constexpr uint64_t kCountGroupsWanted = 512;
-constexpr double kWriterFill = 1024.0;
 constexpr uint64_t kWriterGroupsWanted = 512;
 struct State {
   uint32_t flags;
@@ -720,16 +721,15 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
 }
 
 // Writer placing pairs by their rank in its group's union, for results
-// expected sparse; a group is 2^mlog consecutive segments (up to 4, where
-// the pairs per segment are few). The count pass left each segment's union
-// bitmap; a word table in LDS (ranks before each 32-index word, and the word)
-// gives every pair its rank r in the group with one LDS read and a popcount,
-// so the sums
-// accumulate directly in output order and are stored as they stand: no
-// clearing or compaction of a 4096-entry tile, and a quarter of its LDS,
-// which lets more workgroups share a compute unit.
+// expected sparse; a group is 2^mlog consecutive segments (up to 4, as many
+// as keep the group's pairs near the rank slots). The count pass left each
+// segment's union bitmap; a word table in LDS (ranks before each 32-index
+// word, and the word) gives every pair its rank r in the group with one LDS
+// read and a popcount, so the sums accumulate directly in output order and
+// are stored as they stand: no clearing or compaction of a dense tile, and
+// LDS for the union only.
 //
-// The vector-memory address unit and the VALU bound this pass, so each
+// The pass is bound by the bytes its workgroups have in flight, so each
 // memory instruction moves 16 bytes per lane where it can: pairs are loaded
 // as aligned quads (QUAD: fp32 values, idx and val 16-byte aligned; else one
 // pair per lane), and results are stored as aligned quads: rank r of a
@@ -742,7 +742,7 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
 // that failed the checks gives unspecified sums, but every LDS slot touched
 // stays inside the window.
 constexpr int kRankThreads = 256;
-constexpr uint32_t kRankCap = 1280;
+constexpr uint32_t kRankCap = 2560;
 constexpr uint32_t kRankSlots = kRankCap + 4;
 
 template <int MAXP, int BITS, bool QUAD, bool SCAN>
@@ -994,19 +994,21 @@ hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t 
   }
 }
 
-// The writer for (tile or rank order) x (nodes up to 256 or 1024) x (its own
-// scan or the decide pass's).
+// The writer for (tile or rank order) x (nodes up to 256 or 1024: the run
+// table's LDS) x (its own scan or the decide pass's).
 template <bool SCAN>
-hipError_t launch_writer(bool tile, bool small_p, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0,
-                         hipEvent_t e1, const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val,
-                         const RDev& R, uint32_t lb, uint32_t lbq) {
+hipError_t launch_writer(bool tile, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+                         const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val, const RDev& R,
+                         uint32_t lb, uint32_t lbq) {
   if (tile)
-    return small_p ? launch_write_tile<256, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb)
-                   : launch_write_tile<kMaxP, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
-  return small_p ? launch_write_ranked<256, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R,
-                                                  lb, lbq)
-                 : launch_write_ranked<kMaxP, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R,
-                                                    lb, lbq);
+    return R.P <= 256
+               ? launch_write_tile<256, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb)
+               : launch_write_tile<kMaxP, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
+  return R.P <= 256
+             ? launch_write_ranked<256, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
+                                              lbq)
+             : launch_write_ranked<kMaxP, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
+                                                lbq);
 }
 
 // Lanes per node in the write passes (as a power of two): about 1.5 times
@@ -1031,13 +1033,19 @@ uint32_t quad_lanes_log2(uint32_t P, uint64_t W, uint64_t total) {
 }
 
 // Segments per rank-order writer group (log2): as many as keep the group's
-// pairs, which bound its union, within kWriterFill and leave at least
-// kWriterGroupsWanted groups. The tile writer takes one segment.
-uint32_t writer_log2(uint64_t S, uint64_t total, bool tile) {
+// expected union u (from the estimate) with room for 4 sqrt(u) + 16 more
+// within the rank slots, and leave at least kWriterGroupsWanted groups. A
+// union past the slots costs one more pass over the group's pairs. The tile
+// writer takes one segment.
+uint32_t writer_log2(uint64_t S, double union_est, bool tile) {
   if (tile) return 0;
-  const double per_seg = (double)total / (double)S;
+  const double per_seg = union_est / (double)S;
+  auto fits = [&](uint32_t m) {
+    const double u = (double)(1u << m) * per_seg;
+    return u + 4.0 * std::sqrt(u) + 16.0 <= (double)kRankCap;
+  };
   uint32_t m = 0;
-  while (m < kMaxWriterLog2 && (double)(2u << m) * per_seg <= kWriterFill && (S >> (m + 1)) >= kWriterGroupsWanted) ++m;
+  while (m < kMaxWriterLog2 && fits(m + 1) && (S >> (m + 1)) >= kWriterGroupsWanted) ++m;
   return m;
 }
 
@@ -1057,7 +1065,8 @@ uint32_t count_log2(uint32_t P, uint64_t S, uint64_t total, uint32_t mlog) {
 
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
-                                bool dense_first, uint32_t* out_idx, uint64_t out_idx_cap, float* out_val,
+                                bool dense_first, double union_est, uint32_t* out_idx, uint64_t out_idx_cap,
+                                float* out_val,
                                 ReduceResultDev* d_result, void* ws, hipStream_t stream, const OpEvents* ev) {
   const Layout L = make_layout(P, N, h_offsets[P]);
   // measurement events: the op's span runs from its first dispatch to the
@@ -1069,7 +1078,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.P = P;
   R.N = (uint32_t)N;
   R.total = (uint32_t)h_offsets[P];
-  R.mlog = writer_log2(L.S, R.total, dense_first);
+  R.mlog = writer_log2(L.S, union_est, dense_first);
   R.glog = count_log2(P, L.S, R.total, R.mlog);
   R.pad = 0;
   R.S = L.S;
@@ -1139,9 +1148,8 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
   const uint32_t lbq = quad_lanes_log2(P, R.W, R.total);
   e = scan_in_writer
-          ? launch_writer<true>(dense_first, small_p, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
-          : launch_writer<false>(dense_first, small_p, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
-                                 lbq);
+          ? launch_writer<true>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
+          : launch_writer<false>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq);
   // with both pairs asked for, the op's stop follows the writer's at once
   if (e == hipSuccess && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
   return e;

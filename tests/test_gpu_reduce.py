@@ -252,7 +252,7 @@ def _sparse_sorted(rng, P, N, nnz):
 @pytest.mark.parametrize("P,N,nnz", [
     (64, 1 << 24, 16384),   # 4096 segments of 256 pairs: writer groups of 4, count groups of 8; writers scan
     (8, 1 << 26, 262144),   # 16384 segments of 128 pairs: 4096 writer groups, the decide pass scans
-    (3, 1 << 25, 700000),   # long runs of few nodes: writer groups of 2, count groups of 2
+    (3, 1 << 25, 700000),   # long runs of few nodes (about 340 pairs per group): groups of 4 for both
 ])
 @pytest.mark.parametrize("delta", [0.3, 0.01])
 def test_multi_segment_groups(dev, P, N, nnz, delta):
