@@ -280,6 +280,28 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
       const uint32_t e0 = 4u * (q0 + jq) - shift;
       const bool first_quad = q0 + jq == 0u && shift != 0u;
       uint32_t ip = lane0 ? w[u] : up;  // the element before the current one
+      if (!first_quad && e0 >= o0 && e0 + 4u <= o1) {
+        // a quad inside the node's pairs (all but its two ends): segments
+        // (s_{t-1}, s_t] start at element t, s_{-1} the predecessor's segment
+        // (or below 0 for the node's first element); the node's last element
+        // also starts every later segment (at o1)
+        const uint32_t i0 = v[u][0], i1 = v[u][1], i2 = v[u][2], i3 = v[u][3];
+        const bool has_prev = e0 > o0;
+        if ((has_prev && ip >= i0) || i0 >= i1 || i1 >= i2 || i2 >= i3) bad |= SPARCML_FLAG_NOT_ASCENDING;
+        if (std::max(std::max(i0, i1), std::max(i2, i3)) >= N) bad |= SPARCML_FLAG_INDEX_RANGE;
+        auto seg = [&](uint32_t i) { return i < N ? i >> kSegBits : S; };
+        const uint32_t s0 = seg(i0), s1 = seg(i1), s2 = seg(i2), s3 = seg(i3);
+        const uint32_t from = has_prev ? seg(ip) + 1u : 0u;
+        if (from <= s3 || from <= s0) {
+          for (uint32_t sx = from; sx <= s0; ++sx) b[sx] = e0;
+          for (uint32_t sx = std::max(s0 + 1u, from); sx <= s1; ++sx) b[sx] = e0 + 1u;
+          for (uint32_t sx = std::max(s1 + 1u, from); sx <= s2; ++sx) b[sx] = e0 + 2u;
+          for (uint32_t sx = std::max(s2 + 1u, from); sx <= s3; ++sx) b[sx] = e0 + 3u;
+        }
+        if (e0 + 4u == o1)
+          for (uint32_t sx = s3 + 1u; sx <= S; ++sx) b[sx] = o1;
+        continue;
+      }
       // segments whose run starts in this quad: [lo, hi], each at the quad's
       // first pair whose segment reaches it; the node's last pair also
       // starts every later segment (at o1)
@@ -399,12 +421,15 @@ constexpr uint32_t kMaxWritersPerCount = 1u << kMaxCountLog2;
 // in the group, and folds a share of the bounds pass's check words into the
 // state. (The checks themselves cost the count pass 14 us at 64 x 671088
 // pairs, the bounds pass, which compares every pair with its predecessor
-// anyway, about 4 us.)
-template <int MAXP>
+// anyway, about 4 us.) The pass is bound by its VALU work per index, so
+// where the index array is 16-byte aligned (QUAD) each lane loads an
+// aligned quad of indices: node run [a, a + L) meets quads a / 4 ..
+// (a + L + 3) / 4 - 1, lane l of the node's group takes quad a / 4 + l.
+template <int MAXP, bool QUAD>
 __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R,
                                                          uint32_t lane_bits) {
   constexpr int NT = kCountThreads;
-  constexpr int kB = 16;  // node rows per pass: 16 index loads in flight per thread
+  constexpr int kB = QUAD ? 4 : 16;  // node rows per pass: 64 bytes of index loads in flight per thread
   static_assert(kWords % NT == 0 || NT % kWords == 0, "bitmap words cover whole waves");
   __shared__ uint2 runs[MAXP];
   __shared__ uint32_t wc[kMaxWritersPerCount];
@@ -424,24 +449,50 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
     const uint32_t local = i - glo;
     if (local < glen) atomicOr(&bits[local >> 5], 1u << (local & 31));
   };
+  const uint32_t step = 1u << lane_bits;  // lanes per node
   for (uint32_t p0 = 0; p0 < R.P; p0 += sl.groups * kB) {
     uint2 rn[kB];
-    uint32_t ii[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const uint32_t p = p0 + b * sl.groups + sl.group;
       rn[b] = p < R.P ? runs[p] : make_uint2(0u, 0u);
     }
+    if constexpr (QUAD) {
+      const uint4* idx4 = reinterpret_cast<const uint4*>(idx);
+      uint32_t q0[kB], q1[kB];
+      uint4 ii[kB];
 #pragma unroll
-    for (int b = 0; b < kB; ++b)
-      if (sl.lane < rn[b].y) ii[b] = idx[rn[b].x + sl.lane];
+      for (int b = 0; b < kB; ++b) {
+        q0[b] = rn[b].x >> 2;
+        q1[b] = rn[b].y ? (rn[b].x + rn[b].y + 3u) >> 2 : q0[b];
+        if (q0[b] + sl.lane < q1[b]) ii[b] = idx4[q0[b] + sl.lane];
+      }
+      auto mark4 = [&](uint32_t q, const uint2& r, const uint4& i4) {
+        const uint32_t e = 4u * q - r.x;  // run position of the quad's first index (may wrap)
+        if (e < r.y) mark(i4.x);
+        if (e + 1u < r.y) mark(i4.y);
+        if (e + 2u < r.y) mark(i4.z);
+        if (e + 3u < r.y) mark(i4.w);
+      };
 #pragma unroll
-    for (int b = 0; b < kB; ++b)
-      if (sl.lane < rn[b].y) mark(ii[b]);
-    const uint32_t step = 1u << lane_bits;  // the rest of runs longer than the group
-    for (int b = 0; b < kB; ++b) {
-      if (__ballot(rn[b].y > step) == 0ull) continue;
-      for (uint32_t j = sl.lane + step; j < rn[b].y; j += step) mark(idx[rn[b].x + j]);
+      for (int b = 0; b < kB; ++b)
+        if (q0[b] + sl.lane < q1[b]) mark4(q0[b] + sl.lane, rn[b], ii[b]);
+      for (int b = 0; b < kB; ++b) {  // the rest of runs longer than the group's quads
+        if (__ballot(q1[b] - q0[b] > step) == 0ull) continue;
+        for (uint32_t q = q0[b] + sl.lane + step; q < q1[b]; q += step) mark4(q, rn[b], idx4[q]);
+      }
+    } else {
+      uint32_t ii[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (sl.lane < rn[b].y) ii[b] = idx[rn[b].x + sl.lane];
+#pragma unroll
+      for (int b = 0; b < kB; ++b)
+        if (sl.lane < rn[b].y) mark(ii[b]);
+      for (int b = 0; b < kB; ++b) {  // the rest of runs longer than the group
+        if (__ballot(rn[b].y > step) == 0ull) continue;
+        for (uint32_t j = sl.lane + step; j < rn[b].y; j += step) mark(idx[rn[b].x + j]);
+      }
     }
   }
   if (threadIdx.x == 0) {  // the bounds pass's check bits: words g, g + groups, ... of them
@@ -1131,8 +1182,15 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const dim3 cgrid((uint32_t)groups);
   const uint32_t lbc = lanes_log2(P, groups, R.total);
   const size_t clds = sizeof(uint32_t) * ((size_t)kWords << R.glog);
-  if (small_p) hipLaunchKernelGGL((k_count<256>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
-  else hipLaunchKernelGGL((k_count<kMaxP>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  const bool idx_quads = (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;  // the count pass loads aligned quads
+  const uint32_t lbcq = std::min<uint32_t>(quad_lanes_log2(P, groups, R.total), 7u);
+  if (small_p) {
+    if (idx_quads) hipLaunchKernelGGL((k_count<256, true>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbcq);
+    else hipLaunchKernelGGL((k_count<256, false>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  } else {
+    if (idx_quads) hipLaunchKernelGGL((k_count<kMaxP, true>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbcq);
+    else hipLaunchKernelGGL((k_count<kMaxP, false>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  }
   const bool scan_in_writer = R.W <= kScanMaxW;
   if (!scan_in_writer) hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
   e = hipGetLastError();
