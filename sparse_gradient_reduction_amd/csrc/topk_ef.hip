@@ -468,11 +468,15 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
     const uint64_t base = R.base;
     const uint32_t nsamp = R.schunks * kSampleChunk;  // <= NT * kPredictKeys
     const bool whole = R.n <= nsamp;
+    // chunk c starts at c * stride, stride = (n - 64) / (chunks - 1) rounded
+    // down: the last chunk ends at most chunks - 1 elements short of the row's
+    // end (the sample only guides the thresholds)
+    const uint64_t stride = whole ? 0ull : (uint64_t)(R.n - kSampleChunk) / (R.schunks - 1);
     auto sample_key = [&](uint32_t i) -> uint32_t {  // 0xFFFFFFFF marks "no sample"
       if (whole) return i < R.n ? mag_key(g[base + i] + r[base + i]) : 0xFFFFFFFFu;
       if (i >= nsamp) return 0xFFFFFFFFu;
       const uint32_t c = i / kSampleChunk, o = i % kSampleChunk;
-      const uint64_t start = (uint64_t)c * (R.n - kSampleChunk) / (R.schunks - 1);
+      const uint64_t start = (uint64_t)c * stride;
       return mag_key(g[base + start + o] + r[base + start + o]);
     };
     uint32_t keys[kPredictKeys];

@@ -253,13 +253,16 @@ def _sparse_sorted(rng, P, N, nnz):
     (64, 1 << 24, 16384),   # 4096 segments of 256 pairs: writer groups of 4, count groups of 8; writers scan
     (8, 1 << 26, 262144),   # 16384 segments of 128 pairs: 4096 writer groups, the decide pass scans
     (3, 1 << 25, 700000),   # long runs of few nodes (about 340 pairs per group): groups of 4 for both
+    (300, 1 << 24, 3000),   # more than 256 nodes (run tables for 1024) in writer groups of 4
+    (5, 1 << 26, 300),      # very sparse: consecutive indices of a node about 54 segments apart
 ])
 @pytest.mark.parametrize("delta", [0.3, 0.01])
 def test_multi_segment_groups(dev, P, N, nnz, delta):
     """Few pairs per 4096-index segment: the count pass takes groups of
     several segments and the rank-order writer groups of up to four, whose
-    union ranks span the group. Both results (delta = 0.01 is dense), each
-    written by both writers (hint 1: rank order, N: the tile)."""
+    union ranks span the group. Both thresholds (at delta = 0.01 the result
+    is dense but for the very sparse case), each result written by both
+    writers (hint 1: rank order, N: the tile)."""
     rng = np.random.default_rng(P + nnz)
     off, idx, val = _sparse_sorted(rng, P, N, nnz)
     print(f"multi-segment P={P} N={N} nnz={nnz} delta={delta}", flush=True)

@@ -97,8 +97,8 @@ def test_topk_sample_underestimate_takes_rescan_path(dev):
     P, N, k = 2, 1 << 20, 60000
     rng = np.random.default_rng(9)
     g = (rng.standard_normal((P, N)) * 1e-3).astype(np.float32)
-    for c in range(1024):  # the 1024 sampled chunks of 64 elements
-        s = c * (N - 64) // 1023
+    for c in range(1024):  # the 1024 sampled chunks of 64 elements, c * ((N - 64) // 1023) on
+        s = c * ((N - 64) // 1023)
         g[:, s:s + 64] = (10.0 + rng.random((P, 64))).astype(np.float32)
     r = np.zeros_like(g)
     _check(g, r, k, dev, expect_path=1)
