@@ -21,13 +21,15 @@
 //   count    per count group of 2^glog segments: union bitmap in LDS, stored
 //            for the writer, and the union count of every writer group in it
 //   decide   exclusive scan of the writer-group counts, K, dense iff K >= T
+//            (not launched for at most 2048 writer groups: every writer adds
+//            up the counts itself)
 //   write    per writer group of 2^mlog segments: the sums, stored densely or
 //            as the group's sorted part of the sparse result at its offset
 // Groups of several segments serve inputs with few pairs per segment, where
 // one segment per workgroup leaves each workgroup too little to load. The
 // estimate of K picks the writer: a full 4096-entry tile per segment when the
 // result is expected dense, slots in union-rank order otherwise; both write
-// either result. More than 256 nodes take setup launches for the offsets
+// either result. More than 255 nodes take setup launches for the offsets
 // first. (Per-group totals added up by atomics in the count pass, to let
 // every writer find its own offset without the scan, made the count pass more
 // than twice as slow: hundreds of workgroups adding to one word. Finding each
@@ -70,8 +72,8 @@ static_assert(kWords == 1 << kWordBits, "segment words");
 constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
 // Group sizes, measured on MI355X: count workgroups of up to 2048 pairs
-// whose node runs stay within about 200 pairs (its lanes take one pair of a
-// run each), and rank-order writers of up to 4 segments whose expected union
+// whose node runs stay within about 200 pairs (its lanes take one pair, or
+// one quad, of a run each), and rank-order writers of up to 4 segments whose expected union
 // fits the rank slots. Both keep at least 512 workgroups. The writer is bound
 // by the bytes its workgroups have in flight: five workgroups of two
 // 4096-index segments each (2560 rank slots) kept more in flight than eight
