@@ -83,6 +83,12 @@ constexpr int kSmallSample = kSmallPredictThreads * kPredictKeys;  // 16384
 constexpr int kLayerPredictThreads = 512;
 constexpr int kLayerSampleChunks = kLayerPredictThreads * kPredictKeys / kSampleChunk;  // 512
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
+// Whole-node call: the gather also counts the second digit of the keys whose
+// first digit is one of kSpecBins bins around the prediction `mid`'s; when
+// T*'s first digit is among them, that count is the second radix level and
+// its pass over the candidates is skipped (the per-layer call, with many
+// rows, keeps the pass rather than 12 KB more workspace per row).
+constexpr uint32_t kSpecBins = 3;
 constexpr int kGroup = 512;                              // tiles per gather group
 constexpr int kChunkThreads = 256;
 constexpr int kChunkIt = 16;
@@ -197,7 +203,7 @@ struct Layout {
   uint64_t MT;    // whole-node call: tiles per node (slots)
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
-  size_t info, err, state, h0, h1, h2, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
+  size_t info, err, state, h0, h1, h2, h1s, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
       cout, rows, tile_row, group_row, pass_row, big_rows, mid_rows, loff, lk, lkoff, total;
 };
 
@@ -218,6 +224,7 @@ Layout make_layout(const Plan& Q, uint64_t nlayers) {
   L.h0 = take(4ull * R * kH0);
   L.h1 = take(4ull * R * kH1);
   L.h2 = take(4ull * R * kH2);
+  L.h1s = take(Q.layers ? 0 : 4ull * R * kSpecBins * kH1);
   L.sub = take(128ull * R * kSub);  // one counter per 128-byte line
   L.cand = take(8ull * Q.cand);
   L.oidx = take(4ull * Q.cand);
@@ -316,6 +323,7 @@ struct Dev {
   uint32_t* h0;
   uint32_t* h1;
   uint32_t* h2;
+  uint32_t* h1s;  // [rows][kSpecBins][kH1]: second-digit counts of the gather's speculated bins
   uint32_t* sub;
   uint64_t* cand;  // unordered runs: index << 32 | value bits
   uint32_t* oidx;
@@ -404,14 +412,23 @@ __device__ __forceinline__ uint64_t source_len(const Dev& D, const Row& R, uint3
 // ---------------------------------------------------------------------------
 // predict: reset the node's state and choose the two key thresholds.
 // ---------------------------------------------------------------------------
+// First of the kSpecBins first-digit bins the gather counts the second digit
+// of: the bin of `mid` and its two neighbours.
+__device__ __forceinline__ uint32_t spec_first_bin(uint32_t mid) {
+  const uint32_t b = mid >> 20;
+  return b > 0u ? b - 1u : 0u;
+}
+
 // Clears a row's histograms, the reservation counters its stream uses, and
 // (with its thresholds) its state and flags.
-template <int NT>
+template <int NT, bool ROWS = false>
 __device__ __forceinline__ void reset_row(const Dev& D, uint32_t p, const Row& R) {
   const uint32_t tid = threadIdx.x;
   for (uint32_t i = tid; i < kH0; i += NT) D.h0[(size_t)p * kH0 + i] = 0u;
   for (uint32_t i = tid; i < kH1; i += NT) D.h1[(size_t)p * kH1 + i] = 0u;
   for (uint32_t i = tid; i < kH2; i += NT) D.h2[(size_t)p * kH2 + i] = 0u;
+  if constexpr (!ROWS)
+    for (uint32_t i = tid; i < kSpecBins * kH1; i += NT) D.h1s[(size_t)p * kSpecBins * kH1 + i] = 0u;
   for (uint32_t i = tid; i < R.nsub; i += NT) D.sub[((size_t)p * kSub + i) * 32] = 0u;  // the counters in use
 }
 __device__ __forceinline__ void set_state(const Dev& D, uint32_t p, uint32_t lo, uint32_t mid) {
@@ -709,6 +726,7 @@ template <bool ROWS>
 __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
   constexpr int kU = 8;
   __shared__ uint32_t h[kH0];
+  __shared__ uint32_t hs[ROWS ? 1 : kSpecBins * kH1];
   __shared__ uint32_t s_excl[kGroup + 1];
   __shared__ uint32_t s_toff[kGroup];
   __shared__ uint32_t scr[kGroup / kWave + 3];
@@ -719,6 +737,9 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
   const uint32_t nt = row_tiles(R);
   if (gidx * kGroup >= nt) return;
   for (uint32_t i = threadIdx.x; i < kH0; i += kGroup) h[i] = 0u;
+  if constexpr (!ROWS)
+    for (uint32_t i = threadIdx.x; i < kSpecBins * kH1; i += kGroup) hs[i] = 0u;
+  const uint32_t slo = spec_first_bin(D.state[p].mid);
   const uint64_t t = gidx * kGroup + threadIdx.x;
   const uint64_t meta = t < nt ? D.tmeta[R.tile0 + t] : 0ull;
   const uint32_t cnt = (uint32_t)(meta >> 32);
@@ -752,18 +773,28 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
     for (int u = 0; u < kU; ++u) {
       const bool valid = src[u] != 0xFFFFFFFFu;
       const float v = __uint_as_float((uint32_t)c[u]);
+      const uint32_t key = mag_key(v);
       if (valid) {
         const uint32_t i = i0 + u * kGroup;
         D.oval[out + i] = v;
         D.oidx[out + i] = (uint32_t)(c[u] >> 32);
+        if constexpr (!ROWS) {
+          const uint32_t sb = (key >> 20) - slo;
+          if (sb < kSpecBins) atomicAdd(&hs[sb * kH1 + ((key >> 10) & 1023u)], 1u);
+        }
       }
-      wave_hist_add_capped<2>(h, mag_key(v) >> 20, valid);
+      wave_hist_add_capped<2>(h, key >> 20, valid);
     }
   }
   __syncthreads();
   uint32_t* gh = D.h0 + (size_t)p * kH0;
   for (uint32_t i = threadIdx.x; i < kH0; i += kGroup)
     if (h[i]) atomicAdd(&gh[i], h[i]);
+  if constexpr (!ROWS) {
+    uint32_t* gs = D.h1s + (size_t)p * kSpecBins * kH1;
+    for (uint32_t i = threadIdx.x; i < kSpecBins * kH1; i += kGroup)
+      if (hs[i]) atomicAdd(&gs[i], hs[i]);
+  }
 }
 
 // Digits chosen so far, recomputed from the global histograms of the levels
@@ -839,6 +870,17 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
   load(bx * 256 * kU + threadIdx.x, key);  // in flight while the digits are decided
   uint32_t prefix, krem;
   bins.decide(R.k, LEVEL, scr, prefix, krem);
+  if (LEVEL == 1 && !ROWS && !rescan) {
+    const uint32_t sb = prefix - spec_first_bin(D.state[p].mid);
+    if (sb < kSpecBins) {  // the gather counted this level already
+      if (bx == 0) {
+        const uint32_t* src = D.h1s + (size_t)p * kSpecBins * kH1 + (size_t)sb * kH1;
+        uint32_t* dst = D.h1 + (size_t)p * kH1;
+        for (uint32_t i = threadIdx.x; i < kH1; i += 256) dst[i] = src[i];
+      }
+      return;
+    }
+  }
   __syncthreads();
   for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
     uint32_t nkey[kU];
@@ -1194,7 +1236,7 @@ __global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* ti
   const uint32_t p = blockIdx.x;
   const Row R = rows[p];
   // every row reset here; the rows that need no sample get their thresholds
-  reset_row<256>(D, p, R);
+  reset_row<256, true>(D, p, R);
   uint32_t lo, mid;
   if (threadIdx.x == 0 && fixed_thresholds(R, true, lo, mid)) set_state(D, p, lo, mid);
   const uint32_t nt = row_tiles(R);
@@ -1293,6 +1335,7 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
   D.h0 = reinterpret_cast<uint32_t*>(w + L.h0);
   D.h1 = reinterpret_cast<uint32_t*>(w + L.h1);
   D.h2 = reinterpret_cast<uint32_t*>(w + L.h2);
+  D.h1s = reinterpret_cast<uint32_t*>(w + L.h1s);
   D.sub = reinterpret_cast<uint32_t*>(w + L.sub);
   D.cand = reinterpret_cast<uint64_t*>(w + L.cand);
   D.oidx = reinterpret_cast<uint32_t*>(w + L.oidx);
