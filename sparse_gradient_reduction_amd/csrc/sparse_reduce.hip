@@ -73,17 +73,19 @@ constexpr uint32_t kMaxP = 1024;
 constexpr int kInlineOffsets = 256;
 // Group sizes, measured on MI355X: count workgroups of up to 2048 pairs
 // whose node runs stay within about 200 pairs (its lanes take one pair, or
-// one quad, of a run each), and rank-order writers of up to 4 segments whose expected union
-// fits the rank slots. Both keep at least 512 workgroups. The writer is bound
-// by the bytes its workgroups have in flight: five workgroups of two
-// 4096-index segments each (2560 rank slots) kept more in flight than eight
-// of one.
+// one quad, of a run each), and rank-order writers of up to 4 segments whose
+// expected union fits the rank slots. Both keep at least 512 workgroups. The
+// writer is bound by the bytes its workgroups have in flight: five
+// workgroups of two 4096-index segments each (2560 rank slots) kept more in
+// flight than eight of one, and more than four of two with 3072 slots or
+// three of four with 5120.
 constexpr uint32_t kMaxCountLog2 = 4;   // at most 16 segments per count workgroup
 constexpr uint32_t kMaxWriterLog2 = 2;  // at most 4 segments per rank-order writer
 constexpr double kCountPairs = 2048.0;
 constexpr double kCountRun = 200.0;
 constexpr uint64_t kCountGroupsWanted = 512;
 constexpr uint64_t kWriterGroupsWanted = 512;
+
 struct State {
   uint32_t flags;
   uint32_t is_dense;
@@ -166,7 +168,7 @@ __device__ __forceinline__ void clear_state(const RDev& R) {
   R.state->K = 0ull;
 }
 
-// More than 256 nodes: offsets stored by launches of 256, the first of which
+// More than 255 nodes: offsets stored by launches of 256, the first of which
 // clears the state.
 __global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in, int clear) {
   for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) R.offs[first + i] = in.v[i];
@@ -213,17 +215,18 @@ __global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
 // Node-major pass: start[p][s] = absolute index of node p's first pair with
 // index >= s*4096 (s = S stands for N), written by the pair where the run
 // crosses into segment s. The table is node-major, so the entries one node
-// writes are consecutive words (a segment's workgroup later gathers its P
-// run starts, one word per node). Checks range and order: each workgroup
+// writes are consecutive words (a group's workgroup later gathers two words
+// per node, at the group's first segment and the next group's). Checks range
+// and order: each workgroup
 // stores the bits it found in its own word, which the count pass folds into
 // the call's state (cleared here before the count pass runs).
 // Each lane loads four consecutive pairs as one 16-byte-aligned quad (quad q
 // holds elements 4q - shift .. 4q - shift + 3, shift placing the quads on
 // 16-byte boundaries of the index array); a quad's left neighbour comes from
 // the lane below through a cross-lane shift, and only lane 0 loads its own.
-// With up to 256 nodes the offsets come inline (`in`), and workgroup (0, 0)
-// stores them for the later passes, clears the state and,
-// for quantized input, lays out the code and scale offsets.
+// With up to 255 nodes the offsets come inline (`in`), and workgroup (0, 0)
+// stores them for the later passes, clears the state and, for quantized
+// input, lays out the code and scale offsets.
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift,
                                                      InlineOffsets in, int inline_offs) {
   constexpr int kQuads = 4;  // quads per thread and pass
