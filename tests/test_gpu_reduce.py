@@ -255,6 +255,8 @@ def _sparse_sorted(rng, P, N, nnz):
     (3, 1 << 25, 700000),   # long runs of few nodes (about 340 pairs per group): groups of 4 for both
     (300, 1 << 24, 3000),   # more than 256 nodes (run tables for 1024) in writer groups of 4
     (5, 1 << 26, 300),      # very sparse: consecutive indices of a node about 54 segments apart
+    (64, (1 << 24) + 5 * 4096 + 7, 16384),  # ragged ends: last writer group 2 of 4 segments, last count
+                                            # group 6 of 8, last segment 7 indices
 ])
 @pytest.mark.parametrize("delta", [0.3, 0.01])
 def test_multi_segment_groups(dev, P, N, nnz, delta):
