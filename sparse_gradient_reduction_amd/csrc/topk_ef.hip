@@ -27,9 +27,9 @@
 //   gscan    per node: group offsets, candidate count, and the path: the
 //            candidate list when every tile was stored and it holds >= k
 //            candidates, else an exact rescan of the whole node.
-//   restore  rescan path only: zeroed candidates go back into residual.
 //   gather   candidate runs copied into index order; LDS histogram of key
-//            bits 30..20 (first radix level) on the way.
+//            bits 30..20 (first radix level) on the way. On the rescan path
+//            it puts the zeroed candidates back into residual instead.
 //   hist     further radix levels of T* (bits 19..10, 9..0) over the ordered
 //            candidates, or all three levels over the residual on the rescan
 //            path; each level's digit is picked from the previous histogram.
@@ -692,38 +692,16 @@ __global__ __launch_bounds__(1024) void k_gscan(Dev D) {
 }
 
 // ---------------------------------------------------------------------------
-// restore: rescan path only - zeroed candidates go back into residual.
-// ---------------------------------------------------------------------------
-template <bool ROWS>
-__global__ __launch_bounds__(256) void k_restore(float* __restrict__ r, Dev D) {
-  const uint32_t p = blockIdx.y;
-  if (D.state[p].mode == 0u) return;
-  const Row R = row_of<ROWS>(D, p);
-  const uint32_t mid = D.state[p].mid;
-  const uint32_t nt = row_tiles(R);
-  const uint64_t pN = R.base;
-  for (uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x; t < nt; t += (uint64_t)gridDim.x * 256) {
-    const uint64_t meta = D.tmeta[R.tile0 + t];
-    const uint32_t off = (uint32_t)meta;
-    const uint32_t cnt = (uint32_t)(meta >> 32);
-    if (off == kNotStored) continue;
-    for (uint32_t j = 0; j < cnt; ++j) {
-      const uint64_t c = D.cand[R.cand + off + j];
-      const float v = __uint_as_float((uint32_t)c);
-      if (mag_key(v) >= mid) r[pN + (uint32_t)(c >> 32)] = v;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // gather: candidate runs into index order, first radix level on the way.
 // A block owns kGroup consecutive tiles, whose runs land contiguously in the
 // ordered list; each thread walks output positions and finds its tile by a
 // binary search over the block's prefix of run lengths in LDS, so loads and
-// stores stay spread over the whole block.
+// stores stay spread over the whole block. On the rescan path it restores
+// instead: thread t puts the zeroed candidates of the group's tile t back
+// into residual (one launch less than a kernel of its own).
 // ---------------------------------------------------------------------------
 template <bool ROWS>
-__global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
+__global__ __launch_bounds__(kGroup) void k_gather(float* __restrict__ r, Dev D) {
   constexpr int kU = 8;
   __shared__ uint32_t h[kH0];
   __shared__ uint32_t hs[ROWS ? 1 : kSpecBins * kH1];
@@ -731,11 +709,23 @@ __global__ __launch_bounds__(kGroup) void k_gather(Dev D) {
   __shared__ uint32_t s_toff[kGroup];
   __shared__ uint32_t scr[kGroup / kWave + 3];
   const uint32_t p = ROWS ? D.group_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid over groups
-  if (D.state[p].mode != 0u) return;
   const Row R = row_of<ROWS>(D, p);
   const uint64_t gidx = ROWS ? blockIdx.x - R.group0 : blockIdx.x;
   const uint32_t nt = row_tiles(R);
   if (gidx * kGroup >= nt) return;
+  if (D.state[p].mode != 0u) {  // rescan path
+    const uint64_t t = gidx * kGroup + threadIdx.x;
+    const uint64_t meta = t < nt ? D.tmeta[R.tile0 + t] : ((uint64_t)0 << 32 | kNotStored);
+    const uint32_t off = (uint32_t)meta, cnt = (uint32_t)(meta >> 32);
+    if (off == kNotStored) return;
+    const uint32_t mid = D.state[p].mid;
+    for (uint32_t j = 0; j < cnt; ++j) {
+      const uint64_t c = D.cand[R.cand + off + j];
+      const float v = __uint_as_float((uint32_t)c);
+      if (mag_key(v) >= mid) r[R.base + (uint32_t)(c >> 32)] = v;
+    }
+    return;
+  }
   for (uint32_t i = threadIdx.x; i < kH0; i += kGroup) h[i] = 0u;
   if constexpr (!ROWS)
     for (uint32_t i = threadIdx.x; i < kSpecBins * kH1; i += kGroup) hs[i] = 0u;
@@ -1290,12 +1280,9 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
   }
   if (e != hipSuccess || !any_k) return e;
 
-  // per-row block counts sized for the candidate list; the rescan path loops
-  // over more work with the same grids
-  const uint64_t per_row = std::max<uint64_t>(1, 8192 / nrows);
-  const uint32_t tile_blocks = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_tiles + 255) / 256, per_row));
   // select / count / emit passes: enough blocks to fill the chip once, each
-  // looping over several chunks, so the per-block digit decisions are amortised
+  // looping over several chunks, so the per-block digit decisions are
+  // amortised; the rescan path loops over more work with the same grids
   const uint64_t pass_row = std::max<uint64_t>(1, 2048 / nrows);
   const uint32_t hist_blocks =
       (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>((max_cap + 16383) / 16384, pass_row));
@@ -1308,8 +1295,7 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
   if (ROWS && groups > 0) hipLaunchKernelGGL(k_tsum<ROWS>, gG, dim3(256), 0, stream, D);
   if (!ROWS) hipLaunchKernelGGL(k_tsum<ROWS>, gG, dim3(256), 0, stream, D);
   hipLaunchKernelGGL(k_gscan<ROWS>, dim3(R), dim3(1024), 0, stream, D);
-  hipLaunchKernelGGL(k_restore<ROWS>, dim3(tile_blocks, R), dim3(256), 0, stream, residual, D);
-  if (!ROWS || groups > 0) hipLaunchKernelGGL(k_gather<ROWS>, gG, dim3(kGroup), 0, stream, D);
+  if (!ROWS || groups > 0) hipLaunchKernelGGL(k_gather<ROWS>, gG, dim3(kGroup), 0, stream, residual, D);
   hipLaunchKernelGGL((k_hist<0, ROWS>), gH, dim3(256), 0, stream, residual, D);
   hipLaunchKernelGGL((k_hist<1, ROWS>), gH, dim3(256), 0, stream, residual, D);
   hipLaunchKernelGGL((k_hist<2, ROWS>), gH, dim3(256), 0, stream, residual, D);
