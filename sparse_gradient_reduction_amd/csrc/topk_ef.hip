@@ -489,16 +489,25 @@ __global__ __launch_bounds__(NT) void k_predict(const float* __restrict__ g,
     // down: the last chunk ends at most chunks - 1 elements short of the row's
     // end (the sample only guides the thresholds)
     const uint64_t stride = whole ? 0ull : (uint64_t)(R.n - kSampleChunk) / (R.schunks - 1);
-    auto sample_key = [&](uint32_t i) -> uint32_t {  // 0xFFFFFFFF marks "no sample"
-      if (whole) return i < R.n ? mag_key(g[base + i] + r[base + i]) : 0xFFFFFFFFu;
-      if (i >= nsamp) return 0xFFFFFFFFu;
-      const uint32_t c = i / kSampleChunk, o = i % kSampleChunk;
-      const uint64_t start = (uint64_t)c * stride;
-      return mag_key(g[base + start + o] + r[base + start + o]);
+    const uint32_t nvalid = whole ? R.n : nsamp;
+    // Sample i's element; positions past the sample read element 0 and are
+    // masked afterwards. No branch around the loads, so all of a thread's
+    // loads are in flight together (a branch per sample made each wait for
+    // the previous one).
+    auto sample_pos = [&](uint32_t i) -> uint64_t {
+      const uint64_t pos = whole ? (uint64_t)i : (uint64_t)(i / kSampleChunk) * stride + i % kSampleChunk;
+      return i < nvalid ? pos : 0ull;
     };
+    const float* gb = g + base;
+    const float* rb = r + base;
     uint32_t keys[kPredictKeys];
 #pragma unroll
-    for (int j = 0; j < kPredictKeys; ++j) keys[j] = sample_key(j * NT + tid);
+    for (int j = 0; j < kPredictKeys; ++j) {
+      const uint32_t i = j * NT + tid;
+      const uint64_t pos = sample_pos(i);
+      const uint32_t key = mag_key(gb[pos] + rb[pos]);
+      keys[j] = i < nvalid ? key : 0xFFFFFFFFu;  // 0xFFFFFFFF marks "no sample"
+    }
 #pragma unroll
     for (int j = 0; j < kPredictKeys; ++j)
       if (keys[j] != 0xFFFFFFFFu) atomicAdd(&h1[keys[j] >> 19], 1u);
