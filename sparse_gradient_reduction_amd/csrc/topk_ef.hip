@@ -852,21 +852,22 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
   const uint64_t n = source_len(D, R, p, rescan);
   const float* src = rescan ? r + R.base : D.oval + R.cand;
   const uint64_t stride = nbx * 256 * kU;
-  // keys of the pass starting at i0 (0xFFFFFFFF past the end, where the
-  // load rereads the last element: no branch around the loads)
+  // values of the pass starting at i0; positions past the end reread the
+  // last element and are masked where the values are used, a pass later.
+  // (Masking them here let the compiler put each load under its own branch
+  // and wait for it there, one load in flight at a time.)
   const uint64_t last = n ? n - 1 : 0;
-  auto load = [&](uint64_t i0, uint32_t (&key)[kU]) {
+  auto load = [&](uint64_t i0, float (&x)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const uint64_t i = i0 + (uint64_t)u * 256;
-      const float x = src[i < n ? i : last];
-      key[u] = i < n ? mag_key(x) : 0xFFFFFFFFu;
+      x[u] = src[i < n ? i : last];
     }
   };
   DigitBins<256> bins;
   bins.load(D, p, LEVEL);
-  uint32_t key[kU];
-  load(bx * 256 * kU + threadIdx.x, key);  // in flight while the digits are decided
+  float x[kU];
+  load(bx * 256 * kU + threadIdx.x, x);  // in flight while the digits are decided
   uint32_t prefix, krem;
   bins.decide(R.k, LEVEL, scr, prefix, krem);
   if (LEVEL == 1 && !ROWS && !rescan) {
@@ -882,11 +883,11 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
   }
   __syncthreads();
   for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
-    uint32_t nkey[kU];
-    load(i0 + stride, nkey);  // the block's next pass, in flight during this one
+    float nx[kU];
+    load(i0 + stride, nx);  // the block's next pass, in flight during this one
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const uint32_t kk = key[u];
+      const uint32_t kk = i0 + (uint64_t)u * 256 < n ? mag_key(x[u]) : 0xFFFFFFFFu;
       bool hit;
       uint32_t bin;
       if (LEVEL == 0) {
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
       }
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) key[u] = nkey[u];
+    for (int u = 0; u < kU; ++u) x[u] = nx[u];
   }
   __syncthreads();
   uint32_t* gh = (LEVEL == 0 ? D.h0 : (LEVEL == 1 ? D.h1 : D.h2)) + (size_t)p * NB;
