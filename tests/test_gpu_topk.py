@@ -104,6 +104,19 @@ def test_topk_sample_underestimate_takes_rescan_path(dev):
     _check(g, r, k, dev, expect_path=1)
 
 
+def test_topk_skewed_quarter(dev):
+    """One quarter of each node at 1000 times the scale of the rest: every
+    selected element lies in it, the sample's estimate comes from the chunks
+    that fall in it, and the result is exact on the candidate path."""
+    P, N = 2, 1 << 22
+    k = N // 200
+    rng = np.random.default_rng(22)
+    g = rng.standard_normal((P, N)).astype(np.float32)
+    g[:, :N // 4] *= 1000.0
+    r = (rng.standard_normal((P, N)) * 1e-2).astype(np.float32)
+    _check(g, r, k, dev, expect_path=0)
+
+
 def test_topk_normal_data_takes_candidate_path(dev):
     rng = np.random.default_rng(10)
     P, N = 4, 1 << 20
