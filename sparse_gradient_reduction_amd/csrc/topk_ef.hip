@@ -750,27 +750,28 @@ __global__ __launch_bounds__(kGroup) void k_gather(float* __restrict__ r, Dev D)
   const size_t nbase = R.cand;
   const size_t out = nbase + D.gbase[R.group0 + gidx];
   for (uint32_t i0 = threadIdx.x; i0 < tot; i0 += kGroup * kU) {
+    // Positions past the group's candidates search for (and load) its last
+    // one, and only the stores are masked: with the search and the load under
+    // the position's condition, the per-layer build kept them as branches and
+    // waited for every store to complete before the next.
     uint32_t src[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const uint32_t i = i0 + u * kGroup;
-      src[u] = 0xFFFFFFFFu;
-      if (i < tot) {
-        // the last tile whose run starts at or before i (a fixed number of
-        // branch-free steps, so the kU searches interleave)
-        uint32_t lo = 0;
+      const uint32_t i = std::min(i0 + u * kGroup, tot - 1u);
+      // the last tile whose run starts at or before i (a fixed number of
+      // branch-free steps, so the kU searches interleave)
+      uint32_t lo = 0;
 #pragma unroll
-        for (uint32_t step = kGroup / 2; step > 0; step >>= 1)
-          lo = s_excl[lo + step] <= i ? lo + step : lo;
-        src[u] = s_toff[lo] + (i - s_excl[lo]);
-      }
+      for (uint32_t step = kGroup / 2; step > 0; step >>= 1)
+        lo = s_excl[lo + step] <= i ? lo + step : lo;
+      src[u] = s_toff[lo] + (i - s_excl[lo]);
     }
     uint64_t c[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) c[u] = src[u] != 0xFFFFFFFFu ? D.cand[nbase + src[u]] : 0ull;
+    for (int u = 0; u < kU; ++u) c[u] = D.cand[nbase + src[u]];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const bool valid = src[u] != 0xFFFFFFFFu;
+      const bool valid = i0 + u * kGroup < tot;
       const float v = __uint_as_float((uint32_t)c[u]);
       const uint32_t key = mag_key(v);
       if (valid) {
