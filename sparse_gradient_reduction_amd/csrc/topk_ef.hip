@@ -1231,6 +1231,100 @@ __global__ __launch_bounds__(1024) void k_rows_plan(Row* rows, uint32_t* big_row
   }
 }
 
+// The same table where every node's layer l starts at the same tile phase
+// (N a multiple of kTileAlign) and there are at most 1024 layers: all nodes'
+// rows then have one node's sizes, so a single scan over the layers gives
+// each layer's offsets inside a node and the node's totals, and row
+// p * nl + l is p times the totals plus layer l's offsets (k_rows_plan's
+// scans over every row took 102 us for 64 nodes of 160 layers).
+__global__ __launch_bounds__(1024) void k_rows_plan_nodes(Row* rows, uint32_t* big_rows, uint32_t* mid_rows,
+                                                          const uint64_t* loff, const uint64_t* lk,
+                                                          const uint64_t* lkoff, uint32_t P, uint64_t N, uint32_t nl,
+                                                          uint64_t K) {
+  __shared__ uint64_t scr[1024 / kWave + 1];
+  __shared__ uint64_t s_cand[1024];
+  __shared__ uint32_t s_tile[1024], s_group[1024], s_chunk[1024], s_pass[1024], s_big[1024], s_mid[1024];
+  __shared__ uint32_t s_capS[1024], s_rslo[1024], s_rsmid[1024], s_misc[1024];
+  __shared__ uint64_t s_tot[7];
+  const uint32_t l = threadIdx.x;
+  const bool in = l < nl;
+  uint64_t n = 0, k = 0, xoff = 0;
+  if (in) {
+    xoff = loff[l];
+    n = loff[l + 1] - xoff;
+    k = lk[l];
+  }
+  const RowSize z = row_size(xoff, n, k, true);  // node p's layer: base p * N + xoff, the same phase
+  const bool big = in && big_predict(n, k, z.schunks);
+  const bool sampled = in && layer_sampled(n, k) && !big;
+  uint64_t t;
+  const uint64_t cand = block_exclusive_scan_u64<1024>(in ? (uint64_t)z.nsub * z.capS : 0, scr, t);
+  if (l == 0) s_tot[0] = t;
+  const uint64_t tile = block_exclusive_scan_u64<1024>(in ? z.nt : 0, scr, t);
+  if (l == 0) s_tot[1] = t;
+  const uint64_t group = block_exclusive_scan_u64<1024>(in ? z.groups : 0, scr, t);
+  if (l == 0) s_tot[2] = t;
+  const uint64_t chunk = block_exclusive_scan_u64<1024>(in ? z.chunks : 0, scr, t);
+  if (l == 0) s_tot[3] = t;
+  const uint64_t pass = block_exclusive_scan_u64<1024>(in ? z.npass : 0, scr, t);
+  if (l == 0) s_tot[4] = t;
+  const uint64_t nbig = block_exclusive_scan_u64<1024>(big ? 1 : 0, scr, t);
+  if (l == 0) s_tot[5] = t;
+  const uint64_t nmid = block_exclusive_scan_u64<1024>(sampled ? 1 : 0, scr, t);
+  if (l == 0) s_tot[6] = t;
+  s_cand[l] = cand;
+  // within a node these fit 32 bits: tiles, groups, chunks and blocks are
+  // at most a node's elements over 1024, 262144, 4096 and 8192
+  s_tile[l] = (uint32_t)tile;
+  s_group[l] = (uint32_t)group;
+  s_chunk[l] = (uint32_t)chunk;
+  s_pass[l] = (uint32_t)pass;
+  s_big[l] = (uint32_t)nbig;
+  s_mid[l] = (uint32_t)nmid;
+  const uint64_t S = (uint64_t)z.schunks * kSampleChunk;
+  if (n <= S) {
+    s_rslo[l] = s_rsmid[l] = (uint32_t)k;
+  } else {
+    const double qs = (double)k / (double)n * (double)S;
+    s_rslo[l] = (uint32_t)fmin(ceil(qs + 4.0 * sqrt(qs) + 16.0), (double)S);
+    s_rsmid[l] = (uint32_t)fmin(fmax(1.0, ceil(qs)), (double)S);
+  }
+  s_capS[l] = (uint32_t)z.capS;
+  // counter regions (<= 256), log2 of tiles per counter (<= 4), the two row
+  // lists, sample chunks (<= 512) and blocks per pass (<= 64)
+  s_misc[l] = z.nsub | z.tps_log << 9 | (big ? 1u : 0u) << 12 | (sampled ? 1u : 0u) << 13 | z.schunks << 14 |
+              z.npass << 24;
+  __syncthreads();
+  const uint64_t nrows = (uint64_t)P * nl;
+  for (uint64_t ri = threadIdx.x; ri < nrows; ri += 1024) {
+    const uint64_t p = ri / nl;
+    const uint32_t ll = (uint32_t)(ri % nl);
+    const uint32_t misc = s_misc[ll];
+    const uint64_t xo = loff[ll];
+    Row R{};
+    R.base = p * N + xo;
+    R.cand = p * s_tot[0] + s_cand[ll];
+    R.tile0 = p * s_tot[1] + s_tile[ll];
+    R.group0 = p * s_tot[2] + s_group[ll];
+    R.chunk0 = p * s_tot[3] + s_chunk[ll];
+    R.out0 = p * K + lkoff[ll];
+    R.n = (uint32_t)(loff[ll + 1] - xo);
+    R.k = (uint32_t)lk[ll];
+    R.capS = s_capS[ll];
+    R.nsub = misc & 511u;
+    R.tps_log = (misc >> 9) & 7u;
+    R.rs_lo = s_rslo[ll];
+    R.rs_mid = s_rsmid[ll];
+    R.idx_off = (uint32_t)xo;
+    R.schunks = (misc >> 14) & 1023u;
+    R.pass0 = (uint32_t)(p * s_tot[4] + s_pass[ll]);
+    R.npass = misc >> 24;
+    rows[ri] = R;
+    if ((misc >> 12) & 1u) big_rows[p * s_tot[5] + s_big[ll]] = (uint32_t)ri;
+    if ((misc >> 13) & 1u) mid_rows[p * s_tot[6] + s_mid[ll]] = (uint32_t)ri;
+  }
+}
+
 // block-to-row tables of the per-layer grids; each row reset for the call
 __global__ __launch_bounds__(256) void k_tile_rows(const Row* rows, uint32_t* tile_row, uint32_t* group_row,
                                                    uint32_t* pass_row, Dev D) {
@@ -1414,8 +1508,12 @@ hipError_t topk_layers_launch(uint32_t P, uint64_t N, uint32_t nl, const uint64_
     in.off[count] = off[first + count];
     hipLaunchKernelGGL(k_layers_in, dim3(1), dim3(128), 0, stream, loff, lk, lkoff, first, count, in);
   }
-  hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, mid_rows, loff, lk, lkoff, P, N, nl,
-                     lp.K);
+  if (N % kTileAlign == 0 && nl <= 1024)
+    hipLaunchKernelGGL(k_rows_plan_nodes, dim3(1), dim3(1024), 0, stream, rows, big_rows, mid_rows, loff, lk, lkoff,
+                       P, N, nl, lp.K);
+  else
+    hipLaunchKernelGGL(k_rows_plan, dim3(1), dim3(1024), 0, stream, rows, big_rows, mid_rows, loff, lk, lkoff, P, N,
+                       nl, lp.K);
   hipLaunchKernelGGL(k_tile_rows, dim3((uint32_t)lp.Q.rows), dim3(256), 0, stream, rows, tile_row, group_row,
                      pass_row, D);
   return run<true>(D, lp.Q.rows, lp.Q.tiles, lp.Q.groups, lp.max_tiles, lp.max_cap, lp.Q.passes, lp.Q.big, lp.Q.mid,
