@@ -20,6 +20,8 @@ Parity status per function (what pins it is in each C function's header):
             rocRAND's Philox stream; the exact code stream is fixed by the
             reading documented in oracle.cpp
   reduce    pinned (np.bincount / np.unique, overlap extremes, switch at T)
+  run_table pinned (brute-force count per node and range, end entries, every
+            pair inside its range)
 """
 import ctypes
 import os
@@ -58,6 +60,8 @@ def lib():
         L.oracle_dqsgd.argtypes = [u32, u32, u64, u32, vp, vp, vp]
         L.oracle_dqsgd.restype = None
         L.oracle_reduce.argtypes = [u32, u64, f64, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_run_table.argtypes = [u32, u64, u32, vp, vp, vp]
+        L.oracle_run_table.restype = ctypes.c_int
         L.oracle_reduce.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = ctypes.c_int
@@ -199,3 +203,21 @@ def reduce(offsets, idx, val, N, delta):
     if dense[0]:
         return K, True, np.zeros(0, np.uint32), out_val[:N].copy()
     return K, False, out_idx[:K].copy(), out_val[:K].copy()
+
+
+SEGMENT = 4096  # indices per range of a run table
+
+
+def run_table(offsets, idx, N, seg=SEGMENT):
+    """Run table of sorted sparse contributions: [P, S+1] uint32 with
+    runs[p, s] = offsets[p] + (node p's pairs with index < s * seg),
+    S = ceil(N / seg)."""
+    off = _c(offsets, np.uint64)
+    ii = _c(idx, np.uint32)
+    P = off.shape[0] - 1
+    S = (N + seg - 1) // seg
+    runs = np.zeros((P, S + 1), np.uint32)
+    rc = lib().oracle_run_table(P, N, seg, _ptr(off), _ptr(ii), _ptr(runs))
+    if rc != 0:
+        raise ValueError("oracle_run_table: an index is >= N")
+    return runs

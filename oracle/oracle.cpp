@@ -373,4 +373,39 @@ int oracle_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* offsets,
   return 0;
 }
 
+// ---------------------------------------------------------------------------
+// Run table of sorted sparse contributions ([SparCML] §5.3.2: the split phase
+// gives each owner one range of indices, and each node hands it the part of
+// its sorted pairs that falls in that range).
+//
+// The index space is cut into S = ceil(N / seg) ranges of seg indices. For
+// node p (pairs [offsets[p], offsets[p+1])) and s = 0..S:
+//   runs[p][s] = offsets[p] + #{ pairs of node p with index < s * seg }
+// written out as a count per range and a running sum over the ranges, so
+// that for ascending indices it is the position of the node's first pair
+// with index >= s * seg (the node's end for s = S). Returns -1 for an index
+// >= N.
+// Pinned by: a brute-force count over every (node, s) on small inputs,
+// runs[p][0] = offsets[p], runs[p][S] = offsets[p+1], and every pair between
+// runs[p][s] and runs[p][s+1] lying in range s.
+// ---------------------------------------------------------------------------
+int oracle_run_table(uint32_t P, uint64_t N, uint32_t seg, const uint64_t* offsets, const uint32_t* idx,
+                     uint32_t* runs) {
+  const uint64_t S = (N + seg - 1) / seg;
+  std::vector<uint64_t> cnt(S + 1);
+  for (uint64_t p = 0; p < P; ++p) {
+    std::fill(cnt.begin(), cnt.end(), 0);
+    for (uint64_t e = offsets[p]; e < offsets[p + 1]; ++e) {
+      if ((uint64_t)idx[e] >= N) return -1;
+      cnt[idx[e] / seg] += 1;  // pairs in range idx / seg
+    }
+    uint64_t below = offsets[p];  // offsets[p] + pairs in ranges before s
+    for (uint64_t s = 0; s <= S; ++s) {
+      runs[p * (S + 1) + s] = (uint32_t)below;
+      below += cnt[s];
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"
