@@ -169,6 +169,8 @@ def main():
     red_val = torch.empty(N, dtype=torch.float32, device=dev)
     red_res = torch.zeros(16, dtype=torch.uint8, device=dev)
     ws_red = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
+    # the run table of the Top-k output, written by its emit pass and read by the reduce
+    runs = torch.empty(sg.run_table_shape(P, N), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     print("[bench] inputs resident", file=sys.stderr, flush=True)
     if args.copy_calibration:
@@ -188,14 +190,15 @@ def main():
 
     def step(t, rec=None):
         e = rec or {}
-        sg.topk_ef(pool[t % 2], residual, k, out_idx=idx, out_val=val, workspace=ws_topk, events=e.get("topk"))
+        sg.topk_ef(pool[t % 2], residual, k, out_idx=idx, out_val=val, workspace=ws_topk, events=e.get("topk"),
+                   runs=runs)
         red_in = val
         if B:
             sg.q4(val, B, args.seed, t, codes=codes, scales=scales, events=e.get("q4"))
             sg.dq4(codes, scales, k, B, out=dval, events=e.get("dq4"))
             red_in = dval
         sg.sparse_reduce(offsets, idx.view(-1), red_in.view(-1), N, w.delta, out_idx=red_idx, out_val=red_val,
-                         result=red_res, workspace=ws_red, events=e.get("reduce"))
+                         result=red_res, workspace=ws_red, events=e.get("reduce"), runs=runs)
 
     for t in range(warmup):
         step(t)
@@ -224,20 +227,22 @@ def main():
     K, is_dense, flags = sg.ReduceOutput(red_res, red_idx, red_val, N).read()  # the timed steps' result
 
     # ---- reduce alone, cold (caches flushed by a 1 GiB read) and warm --------
-    def time_reduce(cold, reps=10):
+    def time_reduce(cold, reps=10, table=True):
         flush = CacheFlush(torch, dev) if cold else None
         rr = [ev.op_events(sg, True, op_stop=False) for _ in range(reps)]
         for e in rr:
             if cold:
                 flush()
             sg.sparse_reduce(offsets, idx.view(-1), red_in_last.view(-1), N, w.delta, out_idx=red_idx,
-                             out_val=red_val, result=red_res, workspace=ws_red, events=e)
+                             out_val=red_val, result=red_res, workspace=ws_red, events=e,
+                             runs=runs if table else None)
         torch.cuda.synchronize()
         return sorted(ev.span_ms(e) for e in rr), sorted(ev.kernel_ms(e) for e in rr)
 
     red_in_last = dval if B else val
     red_cold, red_cold_writer = time_reduce(True)
     red_warm, red_warm_writer = time_reduce(False)
+    red_own_cold, _ = time_reduce(True, table=False)  # the reduce finding the runs itself (bounds pass)
 
     def time_ops(fn, reps=10):
         e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -427,12 +432,16 @@ def main():
         "algorithmic_bytes": {"topk_ef": b_topk, "q4": b_q4, "dq4": b_dq4, "reduce_in": b_red_in,
                               "reduce_out": b_red_out, "step": b_step},
         "reduce_alone_ms": {"what": "the reduce of the last step's pairs repeated alone, its span from dispatch "
-                                    "events; cold = after a 1 GiB read that flushes the caches",
+                                    "events, with the Top-k's run table as in the step; cold = after a 1 GiB "
+                                    "read that flushes the caches; own_runs = without the table (the reduce's "
+                                    "own pass over the indices finds the runs)",
                             "cold_median": round(med(red_cold), 4), "cold_min": round(red_cold[0], 4),
                             "warm_median": round(med(red_warm), 4), "warm_min": round(red_warm[0], 4),
                             "cold_writer_median": round(med(red_cold_writer), 4),
                             "cold_input_gb_per_s": round(gbs(b_red_in, med(red_cold)), 2),
-                            "cold_frac_hbm_peak": frac(b_red_in + b_red_out, med(red_cold))},
+                            "cold_frac_hbm_peak": frac(b_red_in + b_red_out, med(red_cold)),
+                            "own_runs_cold_median": round(med(red_own_cold), 4),
+                            "own_runs_cold_frac_hbm_peak": frac(b_red_in + b_red_out, med(red_own_cold))},
         "reduce_result": {"nnz": K, "dense": is_dense},
         **extra,
         "topk_rescan_nodes": int((paths[0] == 1).sum()),
@@ -456,7 +465,7 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, pool[0], args, sg)
     if not args.no_other_configs:
-        del pool, residual, ws_topk, idx, val, red_idx, red_val, ws_red
+        del pool, residual, ws_topk, idx, val, red_idx, red_val, ws_red, runs
         if B:
             del codes, scales, dval
         torch.cuda.synchronize()
@@ -609,6 +618,7 @@ def other_configs(sg, W, dev, skip_wid, ev):
         rv = torch.empty(N, dtype=torch.float32, device=dev)
         rr = torch.zeros(16, dtype=torch.uint8, device=dev)
         wr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
+        runs = torch.empty(sg.run_table_shape(P, N), dtype=torch.int32, device=dev)  # Top-k -> reduce
         t_topk = {"cold": [], "warm": []}
         t_red = {"cold": [], "warm": []}
         per_step = []
@@ -618,11 +628,11 @@ def other_configs(sg, W, dev, skip_wid, ev):
                 et, er = ev.op_events(sg, True), ev.op_events(sg, True, op_stop=False)
                 if mode == "cold":
                     flush()
-                sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws, events=et)
+                sg.topk_ef(grads[t], r, k, out_idx=idx, out_val=val, workspace=ws, events=et, runs=runs)
                 if mode == "cold":
                     flush()
                 sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
-                                 workspace=wr, events=er)
+                                 workspace=wr, events=er, runs=runs)
                 if mode == "warm-up":
                     continue
                 torch.cuda.synchronize()
@@ -635,9 +645,9 @@ def other_configs(sg, W, dev, skip_wid, ev):
         tk, tr = med(t_topk["cold"]), med(t_red["cold"])
 
         def one_step():
-            sg.topk_ef(grads[0], r, k, out_idx=idx, out_val=val, workspace=ws)
+            sg.topk_ef(grads[0], r, k, out_idx=idx, out_val=val, workspace=ws, runs=runs)
             sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=rr,
-                             workspace=wr)
+                             workspace=wr, runs=runs)
 
         t_graph = graph_ms(one_step)  # the residual keeps accumulating: EF steps on the first gradient
         # the same rows as 20 layers (sizes log-uniform), the same fraction kept per layer
@@ -668,7 +678,7 @@ def other_configs(sg, W, dev, skip_wid, ev):
                        "step_graph_ms": round(t_graph, 4),
                        "topk_20_layers_ms": round(t_layers, 4),
                        "per_step": per_step}
-        del grads, r, ws, idx, val, ri, rv, rr, wr
+        del grads, r, ws, idx, val, ri, rv, rr, wr, runs
         torch.cuda.synchronize()
     del flush
     return res

@@ -113,6 +113,35 @@ sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Run tables (paper section 5.3.2: the split phase gives each owner one
+ * range of indices and every node sends it the part of its sorted pairs
+ * that falls there).
+ *
+ * The reduction cuts the index space into segments of SPARCML_SEGMENT
+ * indices. For sparse contributions laid out as in sparcml_sparse_reduce
+ * (node p's pairs at positions [h_offsets[p], h_offsets[p+1]), indices
+ * ascending), the run table is the [P][S+1] uint32 array, S =
+ * ceil(N / SPARCML_SEGMENT), with
+ *   runs[p*(S+1) + s] = position of node p's first pair whose index is
+ *                       >= s * SPARCML_SEGMENT, or h_offsets[p+1] if none
+ * so node p's pairs in segment s are positions [runs[p][s], runs[p][s+1]),
+ * runs[p][0] = h_offsets[p] and runs[p][S] = h_offsets[p+1].
+ * ---------------------------------------------------------------------- */
+#define SPARCML_SEGMENT 4096u
+
+/* sparcml_topk_ef that also writes the run table of its output (node p's k
+ * pairs at positions p*k .. p*k + k - 1, index space N), so that the sparse
+ * reduction of these pairs needs no pass of its own to find the runs
+ * (sparcml_sparse_reduce_runs). The emit pass, which walks every node's
+ * candidates in index order, writes the entries as it places the pairs.
+ *   runs   device, [P][ceil(N/SPARCML_SEGMENT) + 1] uint32, written
+ * Every other argument, the result and the errors are sparcml_topk_ef's;
+ * SPARCML_ERR_INVALID_ARG also for a NULL runs or P * k >= 2^32 - 15. */
+sparcml_status sparcml_topk_ef_runs(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                    uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Per-layer error-feedback Top-k (paper section 8.4: the ResNet50 runs
  * sparsify layer by layer; sections 2.2 and 4 as for sparcml_topk_ef).
  *
@@ -291,6 +320,8 @@ typedef struct sparcml_reduce_result {
 
 #define SPARCML_FLAG_INDEX_RANGE 1u    /* an index >= N */
 #define SPARCML_FLAG_NOT_ASCENDING 2u  /* a node's indices not strictly ascending */
+#define SPARCML_FLAG_RUN_TABLE 4u      /* a caller's run table that does not fit the pairs
+                                          (sparcml_sparse_reduce_runs) */
 
 size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nnz);
 
@@ -301,6 +332,27 @@ sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta,
                                      uint32_t* out_idx, float* out_val,
                                      sparcml_reduce_result* d_result,
                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse reduction with the caller's run table (see "Run tables" above),
+ * for pairs whose producer already knows where each node's sorted pairs
+ * cross the segments (sparcml_topk_ef_runs writes it for its output): the
+ * operation, result, workspace and errors of sparcml_sparse_reduce, without
+ * its pass over the indices that finds the runs and checks range and order.
+ *   runs   device, [P][ceil(N/SPARCML_SEGMENT) + 1] uint32, read only
+ * Instead, the table is checked against the pairs as they are read: entries
+ * outside a node's pairs or out of order, a first or last entry other than
+ * the node's offsets, or a pair whose index lies outside the segment its run
+ * places it in set SPARCML_FLAG_RUN_TABLE in d_result->flags (an index >= N
+ * sets SPARCML_FLAG_INDEX_RANGE). A table that passes covers every pair
+ * once, in its segment. Order within a segment is not checked: a repeated
+ * index within one node then counts once in K and adds all its values.
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                          const uint32_t* idx, const float* val, const uint32_t* runs,
+                                          uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                          sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Allocation-free sparse reduction, for callers that cannot allocate device

@@ -50,6 +50,11 @@ sparcml_status sparcml_bench_topk_ef(uint32_t P, uint64_t N, uint64_t k, const f
                                      uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
                                      const sparcml_bench_events* ev, hipStream_t stream);
 
+/* sparcml_topk_ef_runs, with the events of sparcml_bench_topk_ef. */
+sparcml_status sparcml_bench_topk_ef_runs(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                          uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws,
+                                          size_t ws_bytes, const sparcml_bench_events* ev, hipStream_t stream);
+
 /* One kernel each: it carries the op's pair (or the kernel pair). */
 sparcml_status sparcml_bench_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed,
                                   uint32_t step, uint32_t node0, const float* val, uint8_t* codes, float* scales,
@@ -65,6 +70,14 @@ sparcml_status sparcml_bench_sparse_reduce(uint32_t P, uint64_t N, double delta,
                                            uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
                                            void* ws, size_t ws_bytes, const sparcml_bench_events* ev,
                                            hipStream_t stream);
+
+/* sparcml_sparse_reduce_runs, with the events of sparcml_bench_sparse_reduce
+ * (the op's first kernel is then the count pass). */
+sparcml_status sparcml_bench_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                const uint32_t* idx, const float* val, const uint32_t* runs,
+                                                uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                                sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                const sparcml_bench_events* ev, hipStream_t stream);
 
 /* Attainable-bandwidth reference, in libsparcml_bench.so: r[i] += g[i] for
  * i < n with exactly the access pattern of the error-feedback stream kernel

@@ -51,6 +51,8 @@ def _load():
     L.sparcml_topk_ef_workspace.restype = sz
     L.sparcml_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, vp]
     L.sparcml_topk_ef.restype = st
+    L.sparcml_topk_ef_runs.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sparcml_topk_ef_runs.restype = st
     L.sparcml_topk_ef_layers_workspace.argtypes = [u32, u64, u32, vp, vp]
     L.sparcml_topk_ef_layers_workspace.restype = sz
     L.sparcml_topk_ef_layers.argtypes = [u32, u64, u32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -75,6 +77,8 @@ def _load():
     L.sparcml_sparse_reduce_workspace.restype = sz
     L.sparcml_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
     L.sparcml_sparse_reduce.restype = st
+    L.sparcml_sparse_reduce_runs.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
+    L.sparcml_sparse_reduce_runs.restype = st
     L.sparcml_sparse_reduce_noalloc.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp]
     L.sparcml_sparse_reduce_noalloc.restype = st
     L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
@@ -82,12 +86,16 @@ def _load():
     ev = ctypes.POINTER(BenchEvents)
     L.sparcml_bench_topk_ef.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, sz, ev, vp]
     L.sparcml_bench_topk_ef.restype = st
+    L.sparcml_bench_topk_ef_runs.argtypes = [u32, u64, u64, vp, vp, vp, vp, vp, vp, sz, ev, vp]
+    L.sparcml_bench_topk_ef_runs.restype = st
     L.sparcml_bench_qsgd.argtypes = [u32, u32, u64, u32, u64, u32, u32, vp, vp, vp, ev, vp]
     L.sparcml_bench_qsgd.restype = st
     L.sparcml_bench_dqsgd.argtypes = [u32, u32, u64, u32, vp, vp, vp, ev, vp]
     L.sparcml_bench_dqsgd.restype = st
     L.sparcml_bench_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
     L.sparcml_bench_sparse_reduce.restype = st
+    L.sparcml_bench_sparse_reduce_runs.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
+    L.sparcml_bench_sparse_reduce_runs.restype = st
     _lib = L
     return L
 
@@ -145,12 +153,22 @@ def topk_ef_workspace_bytes(P: int, N: int, k: int) -> int:
     return int(_load().sparcml_topk_ef_workspace(P, N, k))
 
 
+SEGMENT = 4096  # indices per segment of a run table (SPARCML_SEGMENT)
+
+
+def run_table_shape(P: int, N: int):
+    """Shape of the run table of P sorted contributions over N indices."""
+    return (P, (N + SEGMENT - 1) // SEGMENT + 1)
+
+
 def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optional[torch.Tensor] = None,
             out_val: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-            events: Optional[BenchEvents] = None):
+            events: Optional[BenchEvents] = None, runs: Optional[torch.Tensor] = None):
     """Error-feedback Top-k on [P, N] fp32 `grad`; `residual` is updated in place.
     Returns (idx [P, k] int32 holding uint32 indices, val [P, k] float32).
-    `events` (measurement only) routes the call through sparcml_bench_topk_ef."""
+    `runs` (int32 tensor of run_table_shape(P, N)) routes the call through
+    sparcml_topk_ef_runs, which also writes the run table of the output.
+    `events` (measurement only) routes the call through sparcml_bench_topk_ef(_runs)."""
     _check_dev(grad, torch.float32, "grad")
     _check_dev(residual, torch.float32, "residual")
     if grad.dim() != 2 or grad.shape != residual.shape:
@@ -165,13 +183,26 @@ def topk_ef(grad: torch.Tensor, residual: torch.Tensor, k: int, out_idx: Optiona
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     L = _load()
+    s = ctypes.c_void_p(_stream(dev))
+    if runs is not None:
+        _check_dev(runs, torch.int32, "runs")
+        if tuple(runs.shape) != run_table_shape(P, N) or not runs.is_contiguous():
+            raise ValueError(f"runs must be a contiguous {run_table_shape(P, N)} tensor")
+        if events is None:
+            st = L.sparcml_topk_ef_runs(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
+                                        _ptr(runs), _ptr(workspace), workspace.numel(), s)
+        else:
+            st = L.sparcml_bench_topk_ef_runs(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
+                                              _ptr(runs), _ptr(workspace), workspace.numel(), ctypes.byref(events),
+                                              s)
+        _raise(st, "sparcml_topk_ef_runs")
+        return out_idx, out_val
     if events is None:
         st = L.sparcml_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
-                               _ptr(workspace), workspace.numel(), ctypes.c_void_p(_stream(dev)))
+                               _ptr(workspace), workspace.numel(), s)
     else:
         st = L.sparcml_bench_topk_ef(P, N, k, _ptr(grad), _ptr(residual), _ptr(out_idx), _ptr(out_val),
-                                     _ptr(workspace), workspace.numel(), ctypes.byref(events),
-                                     ctypes.c_void_p(_stream(dev)))
+                                     _ptr(workspace), workspace.numel(), ctypes.byref(events), s)
     _raise(st, "sparcml_topk_ef")
     return out_idx, out_val
 
@@ -424,10 +455,13 @@ def qsgd_dense_result(out: "ReduceOutput", bits: int, bucket: int, seed: int, st
 def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,
                   expected_nnz_hint: int = 0, out_idx: Optional[torch.Tensor] = None,
                   out_val: Optional[torch.Tensor] = None, result: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, events: Optional[BenchEvents] = None) -> ReduceOutput:
+                  workspace: Optional[torch.Tensor] = None, events: Optional[BenchEvents] = None,
+                  runs: Optional[torch.Tensor] = None) -> ReduceOutput:
     """Sum of P sparse contributions (node p owns pairs [offsets[p], offsets[p+1])).
-    idx: int32 tensor holding uint32 indices, val: float32 tensor. `events`
-    (measurement only) routes the call through sparcml_bench_sparse_reduce."""
+    idx: int32 tensor holding uint32 indices, val: float32 tensor. `runs`, the
+    run table of these pairs (int32, run_table_shape(P, N), as topk_ef(runs=...)
+    writes it), routes the call through sparcml_sparse_reduce_runs. `events`
+    (measurement only) routes the call through sparcml_bench_sparse_reduce(_runs)."""
     _check_dev(idx, torch.int32, "idx")
     _check_dev(val, torch.float32, "val")
     P = len(offsets) - 1
@@ -435,6 +469,22 @@ def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, 
     dev = idx.device
     out_idx, out_val, result, workspace = _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result,
                                                           workspace)
+    if runs is not None:
+        _check_dev(runs, torch.int32, "runs")
+        if tuple(runs.shape) != run_table_shape(P, N) or not runs.is_contiguous():
+            raise ValueError(f"runs must be a contiguous {run_table_shape(P, N)} tensor")
+        s = ctypes.c_void_p(_stream(dev))
+        if events is None:
+            st = _load().sparcml_sparse_reduce_runs(P, N, float(delta), off, _ptr(idx), _ptr(val), _ptr(runs),
+                                                    int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
+                                                    _ptr(result), _ptr(workspace), workspace.numel(), s)
+        else:
+            st = _load().sparcml_bench_sparse_reduce_runs(P, N, float(delta), off, _ptr(idx), _ptr(val), _ptr(runs),
+                                                          int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
+                                                          _ptr(result), _ptr(workspace), workspace.numel(),
+                                                          ctypes.byref(events), s)
+        _raise(st, "sparcml_sparse_reduce_runs")
+        return ReduceOutput(result, out_idx, out_val, N)
     if events is None:
         st = _load().sparcml_sparse_reduce(P, N, float(delta), off, _ptr(idx), _ptr(val), int(expected_nnz_hint),
                                            _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),

@@ -81,10 +81,12 @@ size_t sparcml_topk_ef_workspace(uint32_t P, uint64_t N, uint64_t k) {
   return sparcml::topk_workspace_bytes(P, N, k);
 }
 
+// runs: null, or the run table of the output to write (sparcml_topk_ef_runs)
 static sparcml_status topk_common(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                                  uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream,
-                                  const sparcml::OpEvents* ev) {
+                                  uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws, size_t ws_bytes,
+                                  hipStream_t stream, const sparcml::OpEvents* ev) {
   if (P == 0 || P > 65535u || N > kMaxTopkN || k > N) return SPARCML_ERR_INVALID_ARG;
+  if (runs && (uint64_t)P * k > kMaxN - 15) return SPARCML_ERR_INVALID_ARG;  // table positions are uint32
   if ((uint64_t)P * N >= (1ull << 40)) return SPARCML_ERR_INVALID_ARG;
   // one 256-thread workgroup per 1024-element tile slot (a node's tiles start at
   // the 128-byte line of its first element), in one grid dimension of < 2^32 work-items
@@ -94,16 +96,27 @@ static sparcml_status topk_common(uint32_t P, uint64_t N, uint64_t k, const floa
   if (k > 0 && (!out_idx || !out_val)) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::topk_workspace_bytes(P, N, k)) return SPARCML_ERR_WORKSPACE;
   // short rows in a small call: one workgroup per node beats the candidate pipeline's kernel chain
-  if (N <= SPARCML_TOPK_ROW_MAX && (uint64_t)P * N <= SPARCML_TOPK_ROW_TOTAL_MAX)
-    return from_hip(sparcml::topk_row_launch(P, N, k, grad, residual, out_idx, out_val, static_cast<uint32_t*>(ws),
-                                             stream, ev));
-  return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, ws, stream, ev));
+  if (N <= SPARCML_TOPK_ROW_MAX && (uint64_t)P * N <= SPARCML_TOPK_ROW_TOTAL_MAX) {
+    hipError_t e =
+        sparcml::topk_row_launch(P, N, k, grad, residual, out_idx, out_val, static_cast<uint32_t*>(ws), stream, ev);
+    // the row kernel has no emit pass: the table comes from its output
+    if (e == hipSuccess && runs) e = sparcml::topk_runs_of_output_launch(P, N, k, out_idx, runs, stream);
+    return from_hip(e);
+  }
+  return from_hip(sparcml::topk_ef_launch(P, N, k, grad, residual, out_idx, out_val, runs, ws, stream, ev));
 }
 
 sparcml_status sparcml_topk_ef(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
                                uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
-  return topk_common(P, N, k, grad, residual, out_idx, out_val, ws, ws_bytes, stream, nullptr);
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, nullptr, ws, ws_bytes, stream, nullptr);
+}
+
+sparcml_status sparcml_topk_ef_runs(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                    uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, runs, ws, ws_bytes, stream, nullptr);
 }
 
 // --------------------------------------------------------------------------
@@ -247,10 +260,11 @@ size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nn
   return sparcml::reduce_workspace_bytes(P, N, total_nnz);
 }
 
+// runs: null, or the caller's run table (fp32 values only)
 static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
                                     const uint32_t* idx, const float* val, const sparcml::ReduceQuantized* quant,
-                                    uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
-                                    sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                    const uint32_t* runs, uint64_t expected_nnz_hint, uint32_t* out_idx,
+                                    float* out_val, sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
                                     hipStream_t stream, const sparcml::OpEvents* ev = nullptr) {
   if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !std::isfinite(delta)) return SPARCML_ERR_INVALID_ARG;
   if (!h_offsets || !d_result || !out_val || !aligned16(out_val)) return SPARCML_ERR_INVALID_ARG;
@@ -269,17 +283,28 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
   const double model = sparcml_estimate_nnz(P, N, h_offsets);
   const double est = expected_nnz_hint ? (double)expected_nnz_hint : model;
   const bool dense_first = est >= (double)T;
-  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, dense_first, model, out_idx,
-                                                cap, out_val, reinterpret_cast<sparcml::ReduceResultDev*>(d_result),
-                                                ws, stream, ev));
+  return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, runs, dense_first, model,
+                                                out_idx, cap, out_val,
+                                                reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws, stream,
+                                                ev));
 }
 
 sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
                                      const uint32_t* idx, const float* val, uint64_t expected_nnz_hint,
                                      uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
                                      void* ws, size_t ws_bytes, hipStream_t stream) {
-  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
                        ws_bytes, stream);
+}
+
+sparcml_status sparcml_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                          const uint32_t* idx, const float* val, const uint32_t* runs,
+                                          uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                          sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream);
 }
 
 sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
@@ -292,7 +317,7 @@ sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delt
     return SPARCML_ERR_SCRATCH_LIMIT;
   void* ws = nullptr;
   if (scratch_of_current_device(&ws) != hipSuccess) return SPARCML_ERR_HIP;
-  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
                        SPARCML_REDUCE_SCRATCH_BYTES, stream);
 }
 
@@ -303,7 +328,7 @@ sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32
                                           size_t ws_bytes, hipStream_t stream) {
   if (!qsgd_args_ok(bits, 1, 0, bucket)) return SPARCML_ERR_INVALID_ARG;
   const sparcml::ReduceQuantized q{bits, bucket, codes, scales};
-  return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, expected_nnz_hint, out_idx, out_val, d_result, ws,
+  return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
                        ws_bytes, stream);
 }
 
@@ -325,7 +350,15 @@ sparcml_status sparcml_bench_topk_ef(uint32_t P, uint64_t N, uint64_t k, const f
                                      uint32_t* out_idx, float* out_val, void* ws, size_t ws_bytes,
                                      const sparcml_bench_events* ev, hipStream_t stream) {
   const sparcml::OpEvents e = op_events(ev);
-  return topk_common(P, N, k, grad, residual, out_idx, out_val, ws, ws_bytes, stream, &e);
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, nullptr, ws, ws_bytes, stream, &e);
+}
+
+sparcml_status sparcml_bench_topk_ef_runs(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
+                                          uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws,
+                                          size_t ws_bytes, const sparcml_bench_events* ev, hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  const sparcml::OpEvents e = op_events(ev);
+  return topk_common(P, N, k, grad, residual, out_idx, out_val, runs, ws, ws_bytes, stream, &e);
 }
 
 sparcml_status sparcml_bench_qsgd(uint32_t bits, uint32_t P, uint64_t n, uint32_t bucket, uint64_t seed,
@@ -348,8 +381,19 @@ sparcml_status sparcml_bench_sparse_reduce(uint32_t P, uint64_t N, double delta,
                                            void* ws, size_t ws_bytes, const sparcml_bench_events* ev,
                                            hipStream_t stream) {
   const sparcml::OpEvents e = op_events(ev);
-  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
-                       ws_bytes, stream, &e);
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, nullptr, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream, &e);
+}
+
+sparcml_status sparcml_bench_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                const uint32_t* idx, const float* val, const uint32_t* runs,
+                                                uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                                sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                const sparcml_bench_events* ev, hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  const sparcml::OpEvents e = op_events(ev);
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream, &e);
 }
 
 }  // extern "C"

@@ -50,8 +50,14 @@ hipError_t launch_ev(void (*fn)(P...), dim3 grid, dim3 block, hipStream_t stream
 
 // ---- error-feedback Top-k -------------------------------------------------
 size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k);
+// runs: null, or the [P][ceil(N / SPARCML_SEGMENT) + 1] run table of the
+// output, written by the emit pass
 hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream, const OpEvents* ev);
+                          uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws, hipStream_t stream,
+                          const OpEvents* ev);
+// the run table of a finished [P][k] output (P * k < 2^32)
+hipError_t topk_runs_of_output_launch(uint32_t P, uint64_t N, uint64_t k, const uint32_t* out_idx, uint32_t* runs,
+                                      hipStream_t stream);
 
 // ---- error-feedback Top-k of short rows: one workgroup per node; info holds
 // the [P] path words (2) and the [P] consistency words the workspace reports
@@ -103,13 +109,13 @@ struct ReduceQuantized {
   const uint8_t* codes;
   const float* scales;
 };
-// val is used when quant is null, quant otherwise; union_est, the expected
-// union size, sizes the writer groups
+// val is used when quant is null, quant otherwise; runs, when not null, is
+// the caller's run table (fp32 values only) and replaces the bounds pass;
+// union_est, the expected union size, sizes the writer groups
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
-                                bool dense_first, double union_est, uint32_t* out_idx, uint64_t out_idx_cap,
-                                float* out_val,
-                                ReduceResultDev* d_result, void* ws, hipStream_t stream,
-                                const OpEvents* ev = nullptr);
+                                const uint32_t* runs, bool dense_first, double union_est, uint32_t* out_idx,
+                                uint64_t out_idx_cap, float* out_val, ReduceResultDev* d_result, void* ws,
+                                hipStream_t stream, const OpEvents* ev = nullptr);
 
 }  // namespace sparcml

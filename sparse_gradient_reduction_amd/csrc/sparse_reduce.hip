@@ -16,13 +16,15 @@
 //
 //   bounds   node-major streaming pass over the indices: where each node's
 //            run crosses a segment boundary; checks range and order. Its
-//            first workgroup also stores the node offsets (passed inline) and
-//            clears the call's state.
+//            first workgroup also stores the node offsets (passed inline).
+//            Not launched when the caller gives that run table (the
+//            whole-vector Top-k writes it for its own output as it emits).
 //   count    per count group of 2^glog segments: union bitmap in LDS, stored
 //            for the writer, and the union count of every writer group in it
-//   decide   exclusive scan of the writer-group counts, K, dense iff K >= T
-//            (not launched for at most 2048 writer groups: every writer adds
-//            up the counts itself)
+//            with the group's input-check bits in the word's top bits
+//   decide   exclusive scan of the writer-group counts, K, dense iff K >= T,
+//            the check bits of all groups (not launched for at most 2048
+//            writer groups: every writer adds up the counts itself)
 //   write    per writer group of 2^mlog segments: the sums, stored densely or
 //            as the group's sorted part of the sparse result at its offset
 // Groups of several segments serve inputs with few pairs per segment, where
@@ -42,6 +44,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 namespace sparcml {
 namespace {
@@ -69,7 +72,12 @@ constexpr int kThreads = 256;              // bounds kernel
 constexpr int kWordBits = 7;
 constexpr int kWords = kSeg / 32;          // bitmap words per segment
 static_assert(kWords == 1 << kWordBits, "segment words");
+static_assert(kSeg == SPARCML_SEGMENT, "run tables of the C ABI use this segment");
 constexpr uint32_t kMaxP = 1024;
+// A writer group's count word: the union count (at most 4 segments of 4096)
+// below bit kCountBits, the input-check bits of its count group above.
+constexpr int kCountBits = 24;
+constexpr uint32_t kCountMask = (1u << kCountBits) - 1u;
 constexpr int kInlineOffsets = 256;
 // Group sizes, measured on MI355X: count workgroups of up to 2048 pairs
 // whose node runs stay within about 200 pairs (its lanes take one pair, or
@@ -86,9 +94,11 @@ constexpr double kCountRun = 200.0;
 constexpr uint64_t kCountGroupsWanted = 512;
 constexpr uint64_t kWriterGroupsWanted = 512;
 
+// Written by the decide pass for the writers; nothing accumulates into it,
+// so it needs no clearing.
 struct State {
-  uint32_t flags;
   uint32_t is_dense;
+  uint32_t pad;
   uint64_t K;
 };
 
@@ -141,8 +151,8 @@ struct RDev {
   uint64_t* offs;
   uint32_t* flagw;  // [P * bx]: input-check bits found by each bounds workgroup
   uint64_t nflagw;
-  uint32_t* bounds;
-  uint32_t* cnt;      // [W] union count per writer group
+  uint32_t* bounds;   // [P][S+1] run starts: the bounds pass's, or the caller's table
+  uint32_t* cnt;      // [W] union count per writer group, with its count group's check bits above kCountBits
   uint32_t* off;      // [W] its offset in the sparse result
   uint32_t* bitmaps;  // [S][128]: bit i of segment s set iff s * 4096 + i is in the union
   ReduceResultDev* result;
@@ -161,18 +171,9 @@ struct InlineOffsets {
   uint64_t v[kInlineOffsets];
 };
 
-// The state of the call starts at zero.
-__device__ __forceinline__ void clear_state(const RDev& R) {
-  R.state->flags = 0u;
-  R.state->is_dense = 0u;
-  R.state->K = 0ull;
-}
-
-// More than 255 nodes: offsets stored by launches of 256, the first of which
-// clears the state.
-__global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in, int clear) {
+// More than 255 nodes: offsets stored by launches of 256.
+__global__ void k_setup(RDev R, uint32_t first, uint32_t count, InlineOffsets in) {
   for (uint32_t i = threadIdx.x; i < count; i += blockDim.x) R.offs[first + i] = in.v[i];
-  if (clear && threadIdx.x == 0) clear_state(R);
 }
 
 // Quantized input: code-byte and scale offsets of every node, exclusive
@@ -219,14 +220,14 @@ __global__ __launch_bounds__(1024) void k_qoffsets(RDev R) {
 // per node, at the group's first segment and the next group's). Checks range
 // and order: each workgroup
 // stores the bits it found in its own word, which the count pass folds into
-// the call's state (cleared here before the count pass runs).
+// its groups' check words.
 // Each lane loads four consecutive pairs as one 16-byte-aligned quad (quad q
 // holds elements 4q - shift .. 4q - shift + 3, shift placing the quads on
 // 16-byte boundaries of the index array); a quad's left neighbour comes from
 // the lane below through a cross-lane shift, and only lane 0 loads its own.
 // With up to 255 nodes the offsets come inline (`in`), and workgroup (0, 0)
-// stores them for the later passes, clears the state and, for quantized
-// input, lays out the code and scale offsets.
+// stores them for the later passes and, for quantized input, lays out the
+// code and scale offsets.
 __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict__ idx, RDev R, uint32_t shift,
                                                      InlineOffsets in, int inline_offs) {
   constexpr int kQuads = 4;  // quads per thread and pass
@@ -234,7 +235,6 @@ __global__ __launch_bounds__(kThreads) void k_bounds(const uint32_t* __restrict_
   if (inline_offs && blockIdx.x == 0 && blockIdx.y == 0) {
     __shared__ uint64_t scr[kThreads / kWave + 1];
     for (uint32_t i = threadIdx.x; i <= R.P; i += kThreads) R.offs[i] = in.v[i];
-    if (threadIdx.x == 0) clear_state(R);
     if (R.bits) {  // code-byte and scale offsets: exclusive prefix sums over the nodes (P <= 256)
       const uint32_t q = threadIdx.x;
       const uint64_t nnz = q < R.P ? in.v[q + 1] - in.v[q] : 0ull;
@@ -447,14 +447,28 @@ constexpr uint32_t kMaxWritersPerCount = 1u << kMaxCountLog2;
 // where the index array is 16-byte aligned (QUAD) each lane loads an
 // aligned quad of indices: node run [a, a + L) meets quads a / 4 ..
 // (a + L + 3) / 4 - 1, lane l of the node's group takes quad a / 4 + l.
-template <int MAXP, bool QUAD>
+//
+// RUNS: the run table is the caller's (no bounds pass ran). The offsets then
+// come inline (`in`, up to 255 nodes; workgroup 0 stores them for the
+// writer) or from the setup launches, and the pass checks the table as it
+// reads it: each node's entries at the group's two edges lie within the
+// node's pairs and in order, the first segment's entry is the node's first
+// pair and the last segment's the node's end, and every pair of a run lies
+// in the run's segments. A table that passes these checks covers every pair
+// exactly once, in its own segment.
+struct NoOffsets {};
+
+template <int MAXP, bool QUAD, bool RUNS>
 __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restrict__ idx, RDev R,
-                                                         uint32_t lane_bits) {
+                                                         uint32_t lane_bits,
+                                                         std::conditional_t<RUNS, InlineOffsets, NoOffsets> in,
+                                                         int inline_offs) {
   constexpr int NT = kCountThreads;
   constexpr int kB = QUAD ? 4 : 16;  // node rows per pass: 64 bytes of index loads in flight per thread
   static_assert(kWords % NT == 0 || NT % kWords == 0, "bitmap words cover whole waves");
   __shared__ uint2 runs[MAXP];
   __shared__ uint32_t wc[kMaxWritersPerCount];
+  __shared__ uint32_t s_bad;
   extern __shared__ uint32_t bits[];  // [128 << glog]: the group's bitmap
   const uint64_t g = xcd_contiguous(blockIdx.x, gridDim.x);  // neighbours share run-edge lines
   const uint64_t s0 = g << R.glog;
@@ -464,12 +478,30 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   const uint32_t glen = std::min<uint32_t>(segs << kSegBits, R.N - glo);
   for (uint32_t i = threadIdx.x; i < segs * kWords; i += NT) bits[i] = 0u;
   if (threadIdx.x < kMaxWritersPerCount) wc[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) s_bad = 0u;
   const Slots sl = make_slots(lane_bits, NT);
-  store_run_table<NT, MAXP>(R, s0, s1, runs, nullptr);
+  uint32_t bad = 0u;
+  if constexpr (RUNS) {
+    auto off_at = [&](uint32_t p) -> uint32_t { return (uint32_t)(inline_offs ? in.v[p] : R.offs[p]); };
+    if (inline_offs && blockIdx.x == 0)
+      for (uint32_t i = threadIdx.x; i <= R.P; i += NT) R.offs[i] = in.v[i];
+    for (uint32_t p = threadIdx.x; p < R.P; p += NT) {
+      const uint32_t lo = off_at(p), hi = off_at(p + 1);
+      const uint32_t* b = R.bounds + p * (R.S + 1);
+      const uint32_t a0 = b[s0], a1 = b[s1];
+      if (a0 < lo || a1 > hi || a1 < a0 || (s0 == 0u && a0 != lo) || (s1 == R.S && a1 != hi))
+        bad |= SPARCML_FLAG_RUN_TABLE;
+      const uint32_t b0 = std::min(std::max(a0, lo), hi), b1 = std::min(std::max(a1, lo), hi);
+      runs[p] = make_uint2(b0, b1 > b0 ? b1 - b0 : 0u);
+    }
+  } else {
+    store_run_table<NT, MAXP>(R, s0, s1, runs, nullptr);
+  }
   __syncthreads();
   auto mark = [&](uint32_t i) {
     const uint32_t local = i - glo;
     if (local < glen) atomicOr(&bits[local >> 5], 1u << (local & 31));
+    else if (RUNS) bad |= i >= R.N ? SPARCML_FLAG_INDEX_RANGE : SPARCML_FLAG_RUN_TABLE;
   };
   const uint32_t step = 1u << lane_bits;  // lanes per node
   // Every lane loads, whether its position is in a run or not, from a
@@ -521,11 +553,11 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
       }
     }
   }
-  if (threadIdx.x == 0) {  // the bounds pass's check bits: words g, g + groups, ... of them
-    uint32_t f = 0u;
-    for (uint64_t w = g; w < R.nflagw; w += gridDim.x) f |= R.flagw[w];
-    if (f) atomicOr(&R.state->flags, f);
-  }
+  // the group's check bits: its own, and the bounds pass's words g,
+  // g + groups, ... (none when the run table is the caller's)
+  if (threadIdx.x == 0)
+    for (uint64_t w = g; w < R.nflagw; w += gridDim.x) bad |= R.flagw[w];
+  if (bad) atomicOr(&s_bad, bad);
   __syncthreads();
   // the bitmaps, whole waves at a time (the words come in multiples of 128),
   // and the union count of every writer group
@@ -539,7 +571,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   __syncthreads();
   const uint64_t wfirst = g << (R.glog - R.mlog);
   const uint64_t wn = std::min<uint64_t>(1u << (R.glog - R.mlog), R.W - wfirst);
-  if (threadIdx.x < wn) R.cnt[wfirst + threadIdx.x] = wc[threadIdx.x];
+  if (threadIdx.x < wn) R.cnt[wfirst + threadIdx.x] = wc[threadIdx.x] | (s_bad << kCountBits);
 }
 
 // Exclusive scan of the writer-group counts by one workgroup, into offsets,
@@ -550,6 +582,9 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
 __global__ __launch_bounds__(1024) void k_decide(RDev R) {
   constexpr int kPer = 32;
   __shared__ uint32_t scr[1024 / kWave + 3];
+  __shared__ uint32_t s_flags;
+  if (threadIdx.x == 0) s_flags = 0u;
+  uint32_t f = 0u;  // the count groups' check bits, from the count words' top bits
   uint64_t carry = 0;
   for (uint64_t s0 = 0; s0 < R.W; s0 += 1024 * kPer) {
     const uint64_t first = s0 + (uint64_t)threadIdx.x * kPer;
@@ -571,7 +606,11 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
     }
     uint32_t sum = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) sum += c[u];
+    for (int u = 0; u < kPer; ++u) {
+      f |= c[u] >> kCountBits;
+      c[u] &= kCountMask;
+      sum += c[u];
+    }
     uint32_t tot;
     uint32_t run = (uint32_t)carry + block_exclusive_scan<1024>(sum, scr, tot);
 #pragma unroll
@@ -591,6 +630,8 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
     }
     carry += tot;
   }
+  if (f) atomicOr(&s_flags, f);
+  __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t dense = carry >= R.T ? 1u : 0u;
     R.state->K = carry;
@@ -598,7 +639,7 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
     ReduceResultDev res;
     res.nnz = carry;
     res.is_dense = dense;
-    res.flags = R.state->flags;
+    res.flags = s_flags;
     *R.result = res;
   }
 }
@@ -618,12 +659,12 @@ __device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__bui
 
 template <int NT, bool SCAN>
 struct WriterHead {
-  uint32_t before = 0u, all = 0u;
+  uint32_t before = 0u, all = 0u, flags = 0u;
 
   __device__ __forceinline__ void load(const RDev& R, uint64_t w, uint32_t* head) {
     if constexpr (!SCAN) {
       if (threadIdx.x == NT - 1) {
-        const uint32_t dense = R.state->is_dense, cnt = R.cnt[w], off = R.off[w];
+        const uint32_t dense = R.state->is_dense, cnt = R.cnt[w] & kCountMask, off = R.off[w];
         head[0] = dense;
         head[1] = cnt;
         head[2] = off;
@@ -648,6 +689,8 @@ struct WriterHead {
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
+        flags |= c[u] >> kCountBits;  // the result record's check bits (group 0 stores them)
+        c[u] &= kCountMask;
         all += c[u];
         before += first + u < w ? c[u] : 0u;
         if (first + u == w) head[1] = c[u];
@@ -664,12 +707,19 @@ struct WriterHead {
       uint32_t K, off;
       block_sum2<NT>(all, before, scratch, K, off);
       const uint32_t dense = K >= R.T ? 1u : 0u;
-      if (w == 0 && threadIdx.x == 0) {
-        ReduceResultDev res;
-        res.nnz = K;
-        res.is_dense = dense;
-        res.flags = R.state->flags;
-        *R.result = res;
+      if (w == 0) {  // uniform over the block
+        __shared__ uint32_t s_flags;
+        if (threadIdx.x == 0) s_flags = 0u;
+        __syncthreads();
+        if (flags) atomicOr(&s_flags, flags);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+          ReduceResultDev res;
+          res.nnz = K;
+          res.is_dense = dense;
+          res.flags = s_flags;
+          *R.result = res;
+        }
       }
       return make_uint3(uniform(dense), uniform(head[1]), uniform(off));
     }
@@ -1154,9 +1204,9 @@ uint32_t count_log2(uint32_t P, uint64_t S, uint64_t total, uint32_t mlog) {
 
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
-                                bool dense_first, double union_est, uint32_t* out_idx, uint64_t out_idx_cap,
-                                float* out_val,
-                                ReduceResultDev* d_result, void* ws, hipStream_t stream, const OpEvents* ev) {
+                                const uint32_t* runs, bool dense_first, double union_est, uint32_t* out_idx,
+                                uint64_t out_idx_cap, float* out_val, ReduceResultDev* d_result, void* ws,
+                                hipStream_t stream, const OpEvents* ev) {
   const Layout L = make_layout(P, N, h_offsets[P]);
   // measurement events: the op's span runs from its first dispatch to the
   // writer's end; the kernel pair times the writer alone
@@ -1177,7 +1227,8 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.state = reinterpret_cast<State*>(w + L.state);
   R.offs = reinterpret_cast<uint64_t*>(w + L.offs);
   R.flagw = reinterpret_cast<uint32_t*>(w + L.flagw);
-  R.bounds = reinterpret_cast<uint32_t*>(w + L.bounds);
+  // the caller's run table is only read (by the count pass and the writer)
+  R.bounds = runs ? const_cast<uint32_t*>(runs) : reinterpret_cast<uint32_t*>(w + L.bounds);
   R.cnt = reinterpret_cast<uint32_t*>(w + L.cnt);
   R.off = reinterpret_cast<uint32_t*>(w + L.off);
   R.bitmaps = reinterpret_cast<uint32_t*>(w + L.bitmaps);
@@ -1204,17 +1255,20 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
       const uint32_t count = std::min<uint32_t>(kInlineOffsets, P + 1 - first);
       for (uint32_t i = 0; i < count; ++i) part.v[i] = h_offsets[first + i];
       const hipError_t e = launch_ev(k_setup, dim3(1), dim3(256), stream, first == 0 ? E.op_start : nullptr, nullptr,
-                                     R, first, count, part, first == 0 ? 1 : 0);
+                                     R, first, count, part);
       if (e != hipSuccess) return e;
     }
     if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   }
-  const uint32_t bx = bounds_blocks(max_nnz);
-  R.nflagw = (uint64_t)bx * P;
-  const uint32_t shift = (uint32_t)((reinterpret_cast<uintptr_t>(idx) >> 2) & 3u);
-  hipError_t e = launch_ev(k_bounds, dim3(bx, P), dim3(kThreads), stream, inline_offs ? E.op_start : nullptr, nullptr,
-                           idx, R, shift, in, inline_offs ? 1 : 0);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (runs == nullptr) {
+    const uint32_t bx = bounds_blocks(max_nnz);
+    R.nflagw = (uint64_t)bx * P;
+    const uint32_t shift = (uint32_t)((reinterpret_cast<uintptr_t>(idx) >> 2) & 3u);
+    e = launch_ev(k_bounds, dim3(bx, P), dim3(kThreads), stream, inline_offs ? E.op_start : nullptr, nullptr, idx, R,
+                  shift, in, inline_offs ? 1 : 0);
+    if (e != hipSuccess) return e;
+  }
   const bool small_p = P <= 256;
   const uint64_t groups = (L.S + (1u << R.glog) - 1) >> R.glog;  // count workgroups
   const dim3 cgrid((uint32_t)groups);
@@ -1222,12 +1276,31 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const size_t clds = sizeof(uint32_t) * ((size_t)kWords << R.glog);
   const bool idx_quads = (reinterpret_cast<uintptr_t>(idx) & 15u) == 0;  // the count pass loads aligned quads
   const uint32_t lbcq = std::min<uint32_t>(quad_lanes_log2(P, groups, R.total), 7u);
-  if (small_p) {
-    if (idx_quads) hipLaunchKernelGGL((k_count<256, true>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbcq);
-    else hipLaunchKernelGGL((k_count<256, false>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+  const uint32_t lbk = idx_quads ? lbcq : lbc;
+  const dim3 cblock(kCountThreads);
+  if (runs != nullptr) {
+    // no bounds pass: the count pass is the op's first kernel (after any setup launches)
+    const hipEvent_t c0 = inline_offs ? E.op_start : nullptr;
+    const int io = inline_offs ? 1 : 0;
+    if (small_p)
+      e = idx_quads ? launch_ev_lds(k_count<256, true, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in, io)
+                    : launch_ev_lds(k_count<256, false, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in,
+                                    io);
+    else
+      e = idx_quads
+              ? launch_ev_lds(k_count<kMaxP, true, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in, io)
+              : launch_ev_lds(k_count<kMaxP, false, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in,
+                              io);
+    if (e != hipSuccess) return e;
   } else {
-    if (idx_quads) hipLaunchKernelGGL((k_count<kMaxP, true>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbcq);
-    else hipLaunchKernelGGL((k_count<kMaxP, false>), cgrid, dim3(kCountThreads), clds, stream, idx, R, lbc);
+    const NoOffsets none_in{};
+    if (small_p) {
+      if (idx_quads) hipLaunchKernelGGL((k_count<256, true, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
+      else hipLaunchKernelGGL((k_count<256, false, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
+    } else {
+      if (idx_quads) hipLaunchKernelGGL((k_count<kMaxP, true, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
+      else hipLaunchKernelGGL((k_count<kMaxP, false, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
+    }
   }
   const bool scan_in_writer = R.W <= kScanMaxW;
   if (!scan_in_writer) hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);

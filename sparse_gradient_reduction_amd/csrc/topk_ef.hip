@@ -50,6 +50,7 @@
 // decides how much the candidate work costs.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "sparcml.h"
 
 #include <hip/hip_ext.h>
 
@@ -93,8 +94,14 @@ constexpr int kGroup = 512;                              // tiles per gather gro
 constexpr int kChunkThreads = 256;
 constexpr int kChunkIt = 16;
 constexpr int kChunk = kChunkThreads * kChunkIt;          // 4096 candidates per chunk
+// The emit pass that also writes the run table holds 8 candidates of a chunk
+// per thread (512 threads) instead of 16: the table's extra live values then
+// leave room for more waves per SIMD.
+constexpr int kEmitRunsIt = 8;
 constexpr uint32_t kNotStored = 0xFFFFFFFFu;
-constexpr uint32_t kSmallLayer = 16384;  // per-layer call: rows this small skip the sampled prediction
+constexpr uint32_t kSmallLayer = 16384;
+constexpr int kSegmentBits = 12;  // run tables: segments of 4096 indices
+static_assert((1u << kSegmentBits) == SPARCML_SEGMENT, "run table segment");  // per-layer call: rows this small skip the sampled prediction
 
 struct NodeState {
   uint32_t lo;      // candidate threshold on the key
@@ -341,6 +348,8 @@ struct Dev {
   const uint32_t* pass_row;   // per-layer call: row of every select / count / emit block
   const uint32_t* big_rows;   // per-layer call: the rows with big_predict, in row order
   const uint32_t* mid_rows;   // per-layer call: the other sampled rows, in row order
+  uint32_t* runs;             // whole-node call: run table of the output, [P][S+1], or null
+  uint32_t S;                 // segments of SPARCML_SEGMENT indices: ceil(N / SPARCML_SEGMENT)
 };
 
 // Geometry of one selection row. For the [P][N] call it follows from (P, N,
@@ -1012,16 +1021,39 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
 
 // ---------------------------------------------------------------------------
 // emit: selected pairs in index order; residual finished.
+//
+// RUNS (whole-node call): the run table of the output as well, the one the
+// sparse reduce would otherwise build with a pass over the indices:
+// runs[p][s] = position of node p's first output pair with index >= s * 4096
+// (positions count from the start of the [P][k] output; runs[p][S] is the
+// node's end). Candidates are in index order and a superset of the output,
+// so entry s is the output position of the first candidate with index >=
+// s * 4096, which is the number of selected candidates before it: candidate
+// j (index e_j) writes the entries s with e_{j-1} < s * 4096 <= e_j, and the
+// node's last candidate also the entries past it (the node's end). The
+// predecessor's index comes from the lane below (a DPP shift); a wave's
+// lane 0 takes it from the last lane of the wave before, through LDS, and the
+// chunk's first candidate from memory.
 // ---------------------------------------------------------------------------
-template <bool ROWS>
-__global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, uint32_t* __restrict__ out_idx,
+template <bool ROWS, bool RUNS, int IT>
+__global__ __launch_bounds__(kChunk / IT) void k_emit(float* __restrict__ r, uint32_t* __restrict__ out_idx,
                                                         float* __restrict__ out_val, Dev D) {
-  constexpr int NW = kChunkThreads / kWave;
-  __shared__ uint32_t s_eq[kChunkIt * NW];
-  __shared__ uint32_t s_sel[kChunkIt * NW];
+  static_assert(!(ROWS && RUNS), "run tables of whole-node calls only");
+  constexpr int NT = kChunk / IT;  // threads: IT candidates of each chunk per thread
+  constexpr int NW = NT / kWave;
+  __shared__ uint32_t s_eq[IT * NW];
+  __shared__ uint32_t s_sel[IT * NW];
+  __shared__ uint32_t s_last[RUNS ? IT * NW : 1];  // index of each (it, wave)'s last candidate
   const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid
   const Row R = row_of<ROWS>(D, p);
-  if (R.k == 0) return;
+  uint32_t* tab = RUNS ? D.runs + (uint64_t)p * (D.S + 1) : nullptr;
+  if (R.k == 0) {  // nothing selected: every run of the node is empty
+    if constexpr (RUNS)
+      for (uint64_t s = (uint64_t)blockIdx.x * NT + threadIdx.x; s <= D.S;
+           s += (uint64_t)gridDim.x * NT)
+        tab[s] = (uint32_t)R.out0;
+    return;
+  }
   const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
   const uint64_t nbx = ROWS ? R.npass : gridDim.x;
   const bool rescan = D.state[p].mode != 0u;
@@ -1038,45 +1070,49 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
   const uint32_t* isrc = D.oidx + R.cand;
   uint32_t* oi = out_idx + R.out0;
   float* ov = out_val + R.out0;
-  // chunk c's values and row-local indices; positions past the end reread
-  // the last element (no branch around the loads) and are masked where used
+  // chunk c's values and row-local indices (RUNS: and the index of the
+  // candidate before the chunk); positions past the end reread the last
+  // element (no branch around the loads) and are masked where used
   const uint64_t last = n ? n - 1 : 0;
-  auto load = [&](uint64_t c, float (&v)[kChunkIt], uint32_t (&e)[kChunkIt]) {
+  auto load = [&](uint64_t c, float (&v)[IT], uint32_t (&e)[IT], uint32_t& pc) {
+    const uint64_t c0 = c * kChunk;
     if (rescan) {  // the source is the row itself: the position is the index
 #pragma unroll
-      for (int it = 0; it < kChunkIt; ++it) {
-        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+      for (int it = 0; it < IT; ++it) {
+        const uint64_t j = c0 + (uint64_t)it * NT + threadIdx.x;
         v[it] = vsrc[j < n ? j : last];
         e[it] = (uint32_t)j;
       }
+      pc = (uint32_t)c0 - 1u;
     } else {
 #pragma unroll
-      for (int it = 0; it < kChunkIt; ++it) {
-        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+      for (int it = 0; it < IT; ++it) {
+        const uint64_t j = c0 + (uint64_t)it * NT + threadIdx.x;
         const uint64_t jj = j < n ? j : last;
         v[it] = vsrc[jj];
         e[it] = isrc[jj];
       }
+      if constexpr (RUNS) pc = isrc[std::min(c0 ? c0 - 1 : 0, last)];  // the same word for every lane
     }
   };
-  float v[kChunkIt];
-  uint32_t e[kChunkIt];
-  load(bx, v, e);
+  float v[IT];
+  uint32_t e[IT], pc = 0u;
+  load(bx, v, e, pc);
   for (uint64_t c = bx; c < nchunks; c += nbx) {
     const uint32_t eq_base = D.ceqoff[R.chunk0 + c];
     const uint32_t out_base = D.cout[R.chunk0 + c];
     const uint32_t teq = D.ceq[R.chunk0 + c];
-    float nv[kChunkIt];
-    uint32_t ne[kChunkIt];
-    load(c + nbx, nv, ne);  // the block's next chunk, in flight during this one
+    float nv[IT];
+    uint32_t ne[IT], npc = 0u;
+    load(c + nbx, nv, ne, npc);  // the block's next chunk, in flight during this one
     // per (it, wave): ranks of equal keys, needed only where some key of the
     // chunk equals T* with tie quota left (usually one chunk of the row)
-    uint32_t eq_pre[kChunkIt];
+    uint32_t eq_pre[IT];
     uint32_t eq_bits = 0;
     if (teq != 0u && eq_base < m) {
 #pragma unroll
-      for (int it = 0; it < kChunkIt; ++it) {
-        const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+      for (int it = 0; it < IT; ++it) {
+        const uint64_t j = c * kChunk + (uint64_t)it * NT + threadIdx.x;
         const bool is_eq = j < n && mag_key(v[it]) == T;
         const uint64_t em = ballot(is_eq);
         eq_bits |= (is_eq ? 1u : 0u) << it;
@@ -1084,7 +1120,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
         if (lane == 0) s_eq[it * NW + wid] = popc64(em);
       }
       __syncthreads();
-      static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
+      static_assert(IT * NW == kWave, "one wave scans the per-(it, wave) counts");
       if (threadIdx.x < kWave) {
         const uint32_t x = s_eq[threadIdx.x];
         s_eq[threadIdx.x] = wave_inclusive_scan(x) - x;
@@ -1093,10 +1129,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
     }
     // then ranks of the selected elements
     uint32_t sel_bits = 0;
-    uint32_t sel_pre[kChunkIt];
+    uint32_t sel_pre[IT];
 #pragma unroll
-    for (int it = 0; it < kChunkIt; ++it) {
-      const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+    for (int it = 0; it < IT; ++it) {
+      const uint64_t j = c * kChunk + (uint64_t)it * NT + threadIdx.x;
       const uint32_t key = mag_key(v[it]);
       const bool is_eq = (eq_bits >> it) & 1u;  // set only on the tie path above
       const bool sel = j < n && (key > T || (is_eq && eq_base + s_eq[it * NW + wid] + eq_pre[it] < m));
@@ -1104,17 +1140,18 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
       const uint64_t sm = ballot(sel);
       sel_pre[it] = lanes_below(sm);
       if (lane == 0) s_sel[it * NW + wid] = popc64(sm);
+      if (RUNS && lane == kWave - 1) s_last[it * NW + wid] = e[it];
     }
     __syncthreads();
-    static_assert(kChunkIt * NW == kWave, "one wave scans the per-(it, wave) counts");
+    static_assert(IT * NW == kWave, "one wave scans the per-(it, wave) counts");
     if (threadIdx.x < kWave) {
       const uint32_t x = s_sel[threadIdx.x];
       s_sel[threadIdx.x] = wave_inclusive_scan(x) - x;
     }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < kChunkIt; ++it) {
-      const uint64_t j = c * kChunk + (uint64_t)it * kChunkThreads + threadIdx.x;
+    for (int it = 0; it < IT; ++it) {
+      const uint64_t j = c * kChunk + (uint64_t)it * NT + threadIdx.x;
       if (j >= n) continue;
       const bool high = mag_key(v[it]) >= mid;  // written as +0 by the stream kernel
       if ((sel_bits >> it) & 1u) {
@@ -1128,11 +1165,33 @@ __global__ __launch_bounds__(kChunkThreads) void k_emit(float* __restrict__ r, u
         r[pN + e[it]] = v[it];  // zeroed on the guess but not selected: restore
       }
     }
+    if constexpr (RUNS) {
 #pragma unroll
-    for (int it = 0; it < kChunkIt; ++it) {
+      for (int it = 0; it < IT; ++it) {
+        const uint64_t j = c * kChunk + (uint64_t)it * NT + threadIdx.x;
+        // the predecessor's index: the lane below, or for lane 0 the last
+        // candidate of the (it, wave) before, or the one before the chunk
+        const uint32_t flat = it * NW + wid;
+        const uint32_t below = flat ? s_last[flat - 1] : pc;
+        const uint32_t prev = (uint32_t)__builtin_amdgcn_update_dpp((int)below, (int)e[it], 0x138, 0xF, 0xF, false);
+        if (j >= n) continue;  // lanes past the end come after every active lane of the wave
+        const uint32_t s_hi = e[it] >> kSegmentBits;
+        const uint32_t s_lo = j ? (prev >> kSegmentBits) + 1u : 0u;
+        if (s_lo <= s_hi || j == n - 1) {
+          // selected candidates before this one (its output position if selected)
+          const uint32_t at = (uint32_t)R.out0 + std::min(out_base + s_sel[flat] + sel_pre[it], K);
+          for (uint32_t s = s_lo; s <= s_hi; ++s) tab[s] = at;
+          if (j == n - 1)
+            for (uint32_t s = s_hi + 1u; s <= D.S; ++s) tab[s] = (uint32_t)R.out0 + K;
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
       v[it] = nv[it];
       e[it] = ne[it];
     }
+    pc = npc;
     __syncthreads();  // s_eq / s_sel are reused by the next chunk
   }
 }
@@ -1408,7 +1467,33 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
   hipLaunchKernelGGL(k_scan<ROWS>, dim3(R), dim3(1024), 0, stream, D);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_ev(k_emit<ROWS>, gC, dim3(kChunkThreads), stream, nullptr, E.op_stop, residual, out_idx, out_val, D);
+  if (!ROWS && D.runs != nullptr)
+    return launch_ev(k_emit<false, true, kEmitRunsIt>, gC, dim3(kChunk / kEmitRunsIt), stream, nullptr, E.op_stop,
+                     residual, out_idx, out_val, D);
+  return launch_ev(k_emit<ROWS, false, kChunkIt>, gC, dim3(kChunkThreads), stream, nullptr, E.op_stop, residual,
+                   out_idx, out_val, D);
+}
+
+// Run table of a finished [P][k] output, by the emit pass's rule applied to
+// the output pairs themselves (pair j writes the entries s with
+// idx[j-1] < s * 4096 <= idx[j]): for calls where no emit pass runs (rows
+// selected by one workgroup each, and k == 0, where every run is empty).
+__global__ __launch_bounds__(256) void k_runs_of_output(const uint32_t* __restrict__ out_idx, uint32_t* runs,
+                                                        uint32_t k, uint32_t S) {
+  const uint32_t p = blockIdx.y;
+  uint32_t* tab = runs + (uint64_t)p * (S + 1);
+  const uint32_t base = p * k;  // the host checks P * k < 2^32
+  const uint32_t stride = gridDim.x * 256;
+  if (k == 0) {
+    for (uint32_t s = blockIdx.x * 256 + threadIdx.x; s <= S; s += stride) tab[s] = base;
+    return;
+  }
+  for (uint32_t j = blockIdx.x * 256 + threadIdx.x; j < k; j += stride) {
+    const uint32_t s_hi = out_idx[base + j] >> kSegmentBits;
+    for (uint32_t s = j ? (out_idx[base + j - 1] >> kSegmentBits) + 1u : 0u; s <= s_hi; ++s) tab[s] = base + j;
+    if (j == k - 1)
+      for (uint32_t s = s_hi + 1u; s <= S; ++s) tab[s] = base + k;
+  }
 }
 
 Dev make_dev(const Layout& L, char* w, uint32_t P) {
@@ -1447,12 +1532,24 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
 
 size_t topk_workspace_bytes(uint32_t P, uint64_t N, uint64_t k) { return make_node_layout(P, N, k).total; }
 
+hipError_t topk_runs_of_output_launch(uint32_t P, uint64_t N, uint64_t k, const uint32_t* out_idx, uint32_t* runs,
+                                      hipStream_t stream) {
+  const uint32_t S = (uint32_t)((N + SPARCML_SEGMENT - 1) / SPARCML_SEGMENT);
+  const uint64_t work = std::max<uint64_t>(k, (uint64_t)S + 1);
+  const uint32_t bx = (uint32_t)std::min<uint64_t>((work + 255) / 256, 64);
+  hipLaunchKernelGGL(k_runs_of_output, dim3(bx, P), dim3(256), 0, stream, out_idx, runs, (uint32_t)k, S);
+  return hipGetLastError();
+}
+
 hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad, float* residual,
-                          uint32_t* out_idx, float* out_val, void* ws, hipStream_t stream, const OpEvents* ev) {
+                          uint32_t* out_idx, float* out_val, uint32_t* runs, void* ws, hipStream_t stream,
+                          const OpEvents* ev) {
   const Layout L = make_node_layout(P, N, k);
   Dev D = make_dev(L, static_cast<char*>(ws), P);
   D.N = (uint32_t)N;
   D.k = (uint32_t)k;
+  D.runs = k > 0 ? runs : nullptr;
+  D.S = (uint32_t)((N + SPARCML_SEGMENT - 1) / SPARCML_SEGMENT);
   if (N <= (uint64_t)kSample) {
     D.rs_lo = D.rs_mid = (uint32_t)k;
   } else {
@@ -1460,8 +1557,11 @@ hipError_t topk_ef_launch(uint32_t P, uint64_t N, uint64_t k, const float* grad,
     D.rs_lo = (uint32_t)std::min<double>(std::ceil(qs + 4.0 * std::sqrt(qs) + 16.0), (double)kSample);
     D.rs_mid = (uint32_t)std::min<double>(std::max<double>(1.0, std::ceil(qs)), (double)kSample);
   }
-  return run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, 0, k > 0, grad, residual, out_idx, out_val, stream,
-                    ev);
+  const hipError_t e =
+      run<false>(D, P, L.MT * P, L.MG, L.MT, L.cap, 0, 0, 0, k > 0, grad, residual, out_idx, out_val, stream, ev);
+  // with k == 0 no emit pass runs: every run is empty
+  if (e == hipSuccess && runs != nullptr && k == 0) return topk_runs_of_output_launch(P, N, 0, out_idx, runs, stream);
+  return e;
 }
 
 size_t topk_layers_workspace_bytes(uint32_t P, uint64_t N, uint32_t nl, const uint64_t* off, const uint64_t* k) {

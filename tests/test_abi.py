@@ -46,8 +46,9 @@ def test_measurement_entry_points_are_exported_apart():
     """The measurement variants of the method's calls come from libsparcml.so;
     the bandwidth reference kernel only from libsparcml_bench.so."""
     names = declared_functions(BENCH_HEADER)
-    assert set(names) == {"sparcml_bench_topk_ef", "sparcml_bench_qsgd", "sparcml_bench_dqsgd",
-                          "sparcml_bench_sparse_reduce", "sparcml_bench_reference_stream"}
+    assert set(names) == {"sparcml_bench_topk_ef", "sparcml_bench_topk_ef_runs", "sparcml_bench_qsgd",
+                          "sparcml_bench_dqsgd", "sparcml_bench_sparse_reduce", "sparcml_bench_sparse_reduce_runs",
+                          "sparcml_bench_reference_stream"}
     L = ctypes.CDLL(sg.LIB_PATH)
     B = ctypes.CDLL(sg.BENCH_LIB_PATH)
     for name in names:
@@ -77,6 +78,10 @@ def test_measurement_entry_points_check_arguments_first():
                                          evp, None) == sg.ERR_WORKSPACE
     assert L.sparcml_bench_sparse_reduce(0, 1000, 0.5, off, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, wsr,
                                          evp, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_bench_topk_ef_runs(4, 1000, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, evp,
+                                        None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_bench_sparse_reduce_runs(2, 1000, 0.5, off, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, wsr,
+                                              evp, None) == sg.ERR_INVALID_ARG
     B = sg.bench_lib()
     assert B.sparcml_bench_reference_stream(1000, FAKE_ODD, FAKE, evp, None) == sg.ERR_INVALID_ARG
     assert B.sparcml_bench_reference_stream((1 << 34) - 1023, FAKE, FAKE, evp, None) == sg.ERR_INVALID_ARG
@@ -97,10 +102,12 @@ calls = {
     "topk_ef": lambda: L.sparcml_topk_ef(2, 1 << 20, 1000, F, F, F, F, F, wt, None),
     "topk_ef_rows": lambda: L.sparcml_topk_ef(2, 4096, 100, F, F, F, F, F, sg.topk_ef_workspace_bytes(2, 4096, 100),
                                               None),
+    "topk_ef_runs": lambda: L.sparcml_topk_ef_runs(2, 1 << 20, 1000, F, F, F, F, F, F, wt, None),
     "q4": lambda: L.sparcml_q4(1, 1024, 512, 1, 0, F, F, F, None),
     "dq4": lambda: L.sparcml_dq4(1, 1024, 512, F, F, F, None),
     "sparse_reduce": lambda: L.sparcml_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, None),
     "sparse_reduce_noalloc": lambda: L.sparcml_sparse_reduce_noalloc(2, 1000, 0.5, off, F, F, 0, F, F, F, None),
+    "sparse_reduce_runs": lambda: L.sparcml_sparse_reduce_runs(2, 1000, 0.5, off, F, F, F, 0, F, F, F, F, wr, None),
     "bench_sparse_reduce": lambda: L.sparcml_bench_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, ev,
                                                                  None),
     "bench_reference_stream": lambda: B.sparcml_bench_reference_stream(4096, F, F, ev, None),
@@ -124,7 +131,7 @@ def test_launching_call_without_a_device_returns_hip_error():
     lines = out.stdout.split()
     assert lines[-1] == "done", out.stdout
     got = dict(zip(lines[0:-1:2], lines[1:-1:2]))
-    assert len(got) == 8 and all(v == str(sg.ERR_HIP) for v in got.values()), got
+    assert len(got) == 10 and all(v == str(sg.ERR_HIP) for v in got.values()), got
 
 
 def test_status_strings():
@@ -155,6 +162,28 @@ def test_topk_argument_checks():
     assert call(4, 1000, 10, wb=ws - 1) == sg.ERR_WORKSPACE
     assert sg.topk_ef_workspace_bytes(0, 10, 1) == 0
     assert sg.topk_ef_workspace_bytes(2, 10, 11) == 0
+
+
+def test_run_table_call_argument_checks():
+    """The run-table variants reject a missing table, and Top-k outputs whose
+    positions would not fit the table's 32-bit words, before anything else."""
+    L = sg.lib()
+    ws = sg.topk_ef_workspace_bytes(4, 1000, 10)
+    assert L.sparcml_topk_ef_runs(4, 1000, 10, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, None) == sg.ERR_INVALID_ARG
+    # P * k >= 2^32 - 15: 65535 nodes of 65537 pairs
+    assert L.sparcml_topk_ef_runs(65535, 65537, 65537, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                  None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_topk_ef_runs(4, 1000, 10, FAKE, FAKE, FAKE, FAKE, FAKE, None, ws, None) == sg.ERR_WORKSPACE
+    off = (ctypes.c_uint64 * 3)(0, 5, 9)
+    wr = sg.sparse_reduce_workspace_bytes(2, 100, 9)
+    f64 = ctypes.c_double
+    assert L.sparcml_sparse_reduce_runs(2, 100, f64(0.25), off, FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, wr,
+                                        None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_runs(0, 100, f64(0.25), off, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, wr,
+                                        None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_runs(2, 100, f64(0.25), off, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, wr,
+                                        None) == sg.ERR_WORKSPACE
+    assert sg.run_table_shape(3, 4096 * 5 + 1) == (3, 7)
 
 
 def test_q4_argument_checks():

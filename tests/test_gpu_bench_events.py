@@ -86,6 +86,39 @@ def test_bench_reduce_matches_plain_call(P, N, k, delta):
         assert 0.0 < writer <= span + 1e-3, (writer, span)
 
 
+@pytest.mark.parametrize("P,N,k,delta", [(8, 1 << 20, 5243, 0.3), (4, 4096, 41, 0.3), (300, 70001, 30, 0.5)])
+def test_bench_run_table_calls_match_plain_calls(P, N, k, delta):
+    """sparcml_bench_topk_ef_runs and sparcml_bench_sparse_reduce_runs give
+    the results of the plain calls (the table included), and their spans
+    contain their dominant kernels; with the table the reduce's first kernel
+    is the count pass (or, past 255 nodes, the setup launches)."""
+    dev = torch.device("cuda:0")
+    g = torch.from_numpy(np.random.default_rng(P + N).standard_normal((P, N), dtype=np.float32)).to(dev)
+    ra, rb = torch.zeros_like(g), torch.zeros_like(g)
+    ta = torch.empty(sg.run_table_shape(P, N), dtype=torch.int32, device=dev)
+    tb = torch.empty_like(ta)
+    ia, va = sg.topk_ef(g, ra, k, runs=ta)
+    et = _events()
+    ib, vb = sg.topk_ef(g, rb, k, runs=tb, events=et)
+    torch.cuda.synchronize()
+    assert_bits_equal(ia.cpu().numpy(), ib.cpu().numpy(), "idx")
+    assert_bits_equal(va.cpu().numpy(), vb.cpu().numpy(), "val")
+    assert_bits_equal(ta.cpu().numpy(), tb.cpu().numpy(), "run table")
+    assert _ms(et.op_start, et.op_stop) > 0.0
+    off = [p * k for p in range(P + 1)]
+    a = sg.sparse_reduce(off, ia.view(-1), va.view(-1), N, delta, runs=ta)
+    e = _events(op_stop=False)
+    b = sg.sparse_reduce(off, ib.view(-1), vb.view(-1), N, delta, runs=tb, events=e)
+    torch.cuda.synchronize()
+    Ka, da, fa, xa, ya = a.host()
+    Kb, db, fb, xb, yb = b.host()
+    assert (Ka, da, fa) == (Kb, db, fb) and fa == 0
+    assert np.array_equal(xa.numpy(), xb.numpy())
+    assert_bits_equal(ya.numpy(), yb.numpy(), "reduce values")
+    writer = _ms(e.kernel_start, e.kernel_stop)
+    assert 0.0 < writer <= _ms(e.op_start, e.kernel_stop) + 1e-3
+
+
 def test_bench_q4_dq4_and_reference_stream():
     dev = torch.device("cuda:0")
     P, n, B = 4, 100003, 512

@@ -2,7 +2,8 @@
 stream argument): the library launches kernels only, with no allocation,
 copy, fill or host synchronisation, so one step records as a graph. Each of
 several replays, with eager work and synchronisation between them, must
-equal the eager step bit for bit."""
+equal the eager step bit for bit. The step runs with and without the run
+table that the Top-k writes for the reduce."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +15,8 @@ from tests.gpu_util import assert_bits_equal
 pytestmark = pytest.mark.gpu
 
 
-def test_step_replays_in_a_graph(dev):
+@pytest.mark.parametrize("table", [False, True])
+def test_step_replays_in_a_graph(dev, table):
     w = W.workload(4, N=500009, P=8)
     P, N, k, B = w.P, w.N, w.k, w.q4_bucket
     g = W.gradients(w, 0, device=dev)
@@ -32,13 +34,14 @@ def test_step_replays_in_a_graph(dev):
     rv = torch.empty(N, dtype=torch.float32, device=dev)
     res = torch.zeros(16, dtype=torch.uint8, device=dev)
     wsr = torch.empty(sg.sparse_reduce_workspace_bytes(P, N, P * k), dtype=torch.uint8, device=dev)
+    tab = torch.zeros(sg.run_table_shape(P, N), dtype=torch.int32, device=dev) if table else None
 
     def step():
-        sg.topk_ef(g, r, k, out_idx=idx, out_val=val, workspace=ws)
+        sg.topk_ef(g, r, k, out_idx=idx, out_val=val, workspace=ws, runs=tab)
         sg.q4(val, B, 5, 1, codes=codes, scales=scales)
         sg.dq4(codes, scales, k, B, out=deq)
         sg.sparse_reduce(off, idx.view(-1), deq.view(-1), N, w.delta, out_idx=ri, out_val=rv, result=res,
-                         workspace=wsr)
+                         workspace=wsr, runs=tab)
 
     def outputs():
         K, dense, flags = sg.ReduceOutput(res, ri, rv, N).read()
@@ -66,6 +69,8 @@ def test_step_replays_in_a_graph(dev):
         idx.zero_()
         rv.zero_()
         res.zero_()
+        if table:
+            tab.zero_()
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()

@@ -219,9 +219,11 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
     """The wide-ResNet-sized call as the bench makes it: P = 64 nodes of
     N = 2^27, k = 0.5% (671 088), two error-feedback steps with the residual
     carried on the device. Nodes 0 and 63 bit for bit against the oracle's
-    own residual chain, with the 4-bit codes of their sent values; on all 64
-    nodes the exact EF identity, strictly ascending indices and no unselected
-    magnitude above a selected one."""
+    own residual chain, with the 4-bit codes of their sent values and the run
+    table rows of their output (sparcml_topk_ef_runs); on all 64 nodes the
+    exact EF identity, strictly ascending indices and no unselected magnitude
+    above a selected one. The reduce of the last step's pairs with that table
+    equals the reduce that finds the runs itself, bit for bit."""
     w = W.workload(4)
     P, N, k, B = w.P, w.N, w.k, w.q4_bucket
     seed = 987654321
@@ -229,13 +231,14 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
     ws = torch.empty(sg.topk_ef_workspace_bytes(P, N, k), dtype=torch.uint8, device=dev)
     idx = torch.empty((P, k), dtype=torch.int32, device=dev)
     val = torch.empty((P, k), dtype=torch.float32, device=dev)
+    runs = torch.empty(sg.run_table_shape(P, N), dtype=torch.int32, device=dev)
     sample = (0, P - 1)
     r_o = {p: np.zeros((1, N), np.float32) for p in sample}
     for step in range(2):
         print(f"wide-ResNet Top-k step {step}", flush=True)
         g = W.gradients(w, step, device=dev)
         r_old = r.clone()
-        sg.topk_ef(g, r, k, out_idx=idx, out_val=val, workspace=ws)
+        sg.topk_ef(g, r, k, out_idx=idx, out_val=val, workspace=ws, runs=runs)
         codes, scales = sg.q4(val, B, seed, step)
         torch.cuda.synchronize()
         paths = sg.topk_ef_paths(ws, P).cpu().numpy()
@@ -246,6 +249,9 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
             assert_bits_equal(idx[p:p + 1].cpu().numpy().view(np.uint32), oi, f"idx node {p} step {step}")
             assert_bits_equal(val[p:p + 1].cpu().numpy(), ov, f"val node {p} step {step}")
             assert_bits_equal(r[p:p + 1].cpu().numpy(), orr, f"residual node {p} step {step}")
+            # node p's table row: the oracle's table of its own k pairs, positions counted from p * k
+            o_runs = oracle.run_table(np.array([0, k], np.uint64), oi.reshape(-1), N) + np.uint32(p * k)
+            assert_bits_equal(runs[p:p + 1].cpu().numpy().view(np.uint32), o_runs, f"run table node {p} step {step}")
             oc, osc = oracle.qsgd(ov, 4, B, seed, step, node0=p)
             assert_bits_equal(codes[p:p + 1].cpu().numpy(), oc, f"q4 codes node {p} step {step}")
             assert_bits_equal(scales[p:p + 1].cpu().numpy(), osc, f"q4 scales node {p} step {step}")
@@ -265,3 +271,12 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
             del il, a, recon
         del g, r_old, codes, scales
         torch.cuda.empty_cache()
+    off = [p * k for p in range(P + 1)]
+    plain = sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta)
+    with_runs = sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, runs=runs)
+    K, dense, flags = plain.read()
+    assert (K, dense, flags) == with_runs.read() and flags == 0
+    n = N if dense else K
+    assert torch.equal(plain.out_val[:n].view(torch.int32), with_runs.out_val[:n].view(torch.int32))
+    if not dense:
+        assert torch.equal(plain.out_idx[:K], with_runs.out_idx[:K])
