@@ -405,6 +405,18 @@ sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32
                                           sparcml_reduce_result* d_result, void* ws,
                                           size_t ws_bytes, hipStream_t stream);
 
+/* sparcml_sparse_reduce_qsgd with the caller's run table: the quantized
+ * contributions of sparcml_sparse_reduce_qsgd, the table and its checks of
+ * sparcml_sparse_reduce_runs. Where idx is 16-byte aligned and codes 4-byte
+ * aligned, the rank-order writer loads the pairs four at a time and decodes
+ * their codes from two aligned words. */
+sparcml_status sparcml_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N,
+                                               double delta, const uint64_t* h_offsets, const uint32_t* idx,
+                                               const uint8_t* codes, const float* scales, const uint32_t* runs,
+                                               uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                               sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                               hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Quantization of a dense reduction result, decided on the device (paper
  * section 4: the sum may be quantized once it has turned dense; section 6:

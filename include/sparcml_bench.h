@@ -79,6 +79,16 @@ sparcml_status sparcml_bench_sparse_reduce_runs(uint32_t P, uint64_t N, double d
                                                 sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
                                                 const sparcml_bench_events* ev, hipStream_t stream);
 
+/* sparcml_sparse_reduce_qsgd_runs, with the events of
+ * sparcml_bench_sparse_reduce_runs. */
+sparcml_status sparcml_bench_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N,
+                                                     double delta, const uint64_t* h_offsets, const uint32_t* idx,
+                                                     const uint8_t* codes, const float* scales,
+                                                     const uint32_t* runs, uint64_t expected_nnz_hint,
+                                                     uint32_t* out_idx, float* out_val,
+                                                     sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                     const sparcml_bench_events* ev, hipStream_t stream);
+
 /* Attainable-bandwidth reference, in libsparcml_bench.so: r[i] += g[i] for
  * i < n with exactly the access pattern of the error-feedback stream kernel
  * (one 1024-element tile per 256-thread workgroup, one non-temporal float4

@@ -73,6 +73,9 @@ def _load():
     L.sparcml_qsgd_dense_result.restype = st
     L.sparcml_sparse_reduce_qsgd.argtypes = [u32, u32, u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
     L.sparcml_sparse_reduce_qsgd.restype = st
+    L.sparcml_sparse_reduce_qsgd_runs.argtypes = [u32, u32, u32, u64, f64, vp, vp, vp, vp, vp, u64, vp, vp, vp, vp,
+                                                  sz, vp]
+    L.sparcml_sparse_reduce_qsgd_runs.restype = st
     L.sparcml_sparse_reduce_workspace.argtypes = [u32, u64, u64]
     L.sparcml_sparse_reduce_workspace.restype = sz
     L.sparcml_sparse_reduce.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
@@ -96,6 +99,9 @@ def _load():
     L.sparcml_bench_sparse_reduce.restype = st
     L.sparcml_bench_sparse_reduce_runs.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
     L.sparcml_bench_sparse_reduce_runs.restype = st
+    L.sparcml_bench_sparse_reduce_qsgd_runs.argtypes = [u32, u32, u32, u64, f64, vp, vp, vp, vp, vp, u64, vp, vp, vp,
+                                                        vp, sz, ev, vp]
+    L.sparcml_bench_sparse_reduce_qsgd_runs.restype = st
     _lib = L
     return L
 
@@ -411,11 +417,14 @@ def sparse_reduce_qsgd(offsets: Sequence[int], idx: torch.Tensor, codes: torch.T
                        bits: int, bucket: int, N: int, delta: float, expected_nnz_hint: int = 0,
                        out_idx: Optional[torch.Tensor] = None, out_val: Optional[torch.Tensor] = None,
                        result: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None) -> "ReduceOutput":
+                       workspace: Optional[torch.Tensor] = None, runs: Optional[torch.Tensor] = None,
+                       events: Optional[BenchEvents] = None) -> "ReduceOutput":
     """sparse_reduce with node p's values given as b-bit codes: node p's code
     row starts at byte sum_{q<p} ceil(nnz_q*bits/8), its scales at
     sum_{q<p} ceil(nnz_q/bucket) (the layout qsgd writes when every node has
-    the same count)."""
+    the same count). `runs` (the run table, as for sparse_reduce) routes the
+    call through sparcml_sparse_reduce_qsgd_runs, and with `events`
+    (measurement only) through sparcml_bench_sparse_reduce_qsgd_runs."""
     _check_dev(idx, torch.int32, "idx")
     _check_dev(codes, torch.uint8, "codes")
     _check_dev(scales, torch.float32, "scales")
@@ -424,6 +433,26 @@ def sparse_reduce_qsgd(offsets: Sequence[int], idx: torch.Tensor, codes: torch.T
     dev = idx.device
     out_idx, out_val, result, workspace = _reduce_outputs(offsets, N, delta, dev, out_idx, out_val, result,
                                                           workspace)
+    if runs is not None:
+        _check_dev(runs, torch.int32, "runs")
+        if tuple(runs.shape) != run_table_shape(P, N):
+            raise ValueError(f"runs must be a contiguous {run_table_shape(P, N)} tensor")
+        s = ctypes.c_void_p(_stream(dev))
+        if events is None:
+            st = _load().sparcml_sparse_reduce_qsgd_runs(bits, bucket, P, N, float(delta), off, _ptr(idx), _ptr(codes),
+                                                         _ptr(scales), _ptr(runs), int(expected_nnz_hint),
+                                                         _ptr(out_idx), _ptr(out_val), _ptr(result), _ptr(workspace),
+                                                         workspace.numel(), s)
+        else:
+            st = _load().sparcml_bench_sparse_reduce_qsgd_runs(bits, bucket, P, N, float(delta), off, _ptr(idx),
+                                                               _ptr(codes), _ptr(scales), _ptr(runs),
+                                                               int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
+                                                               _ptr(result), _ptr(workspace), workspace.numel(),
+                                                               ctypes.byref(events), s)
+        _raise(st, "sparcml_sparse_reduce_qsgd_runs")
+        return ReduceOutput(result, out_idx, out_val, N)
+    if events is not None:
+        raise ValueError("events need the run table (sparcml_bench_sparse_reduce_qsgd_runs)")
     st = _load().sparcml_sparse_reduce_qsgd(bits, bucket, P, N, float(delta), off, _ptr(idx), _ptr(codes),
                                             _ptr(scales), int(expected_nnz_hint), _ptr(out_idx), _ptr(out_val),
                                             _ptr(result), _ptr(workspace), workspace.numel(),

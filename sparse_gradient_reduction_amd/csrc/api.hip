@@ -260,7 +260,7 @@ size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nn
   return sparcml::reduce_workspace_bytes(P, N, total_nnz);
 }
 
-// runs: null, or the caller's run table (fp32 values only)
+// runs: null, or the caller's run table
 static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
                                     const uint32_t* idx, const float* val, const sparcml::ReduceQuantized* quant,
                                     const uint32_t* runs, uint64_t expected_nnz_hint, uint32_t* out_idx,
@@ -321,15 +321,36 @@ sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delt
                        SPARCML_REDUCE_SCRATCH_BYTES, stream);
 }
 
+static sparcml_status reduce_qsgd_common(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N, double delta,
+                                         const uint64_t* h_offsets, const uint32_t* idx, const uint8_t* codes,
+                                         const float* scales, const uint32_t* runs, uint64_t expected_nnz_hint,
+                                         uint32_t* out_idx, float* out_val, sparcml_reduce_result* d_result,
+                                         void* ws, size_t ws_bytes, hipStream_t stream,
+                                         const sparcml::OpEvents* ev = nullptr) {
+  if (!qsgd_args_ok(bits, 1, 0, bucket)) return SPARCML_ERR_INVALID_ARG;
+  const sparcml::ReduceQuantized q{bits, bucket, codes, scales};
+  return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, runs, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream, ev);
+}
+
 sparcml_status sparcml_sparse_reduce_qsgd(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N, double delta,
                                           const uint64_t* h_offsets, const uint32_t* idx, const uint8_t* codes,
                                           const float* scales, uint64_t expected_nnz_hint, uint32_t* out_idx,
                                           float* out_val, sparcml_reduce_result* d_result, void* ws,
                                           size_t ws_bytes, hipStream_t stream) {
-  if (!qsgd_args_ok(bits, 1, 0, bucket)) return SPARCML_ERR_INVALID_ARG;
-  const sparcml::ReduceQuantized q{bits, bucket, codes, scales};
-  return reduce_common(P, N, delta, h_offsets, idx, nullptr, &q, nullptr, expected_nnz_hint, out_idx, out_val, d_result, ws,
-                       ws_bytes, stream);
+  return reduce_qsgd_common(bits, bucket, P, N, delta, h_offsets, idx, codes, scales, nullptr, expected_nnz_hint,
+                            out_idx, out_val, d_result, ws, ws_bytes, stream);
+}
+
+sparcml_status sparcml_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N,
+                                               double delta, const uint64_t* h_offsets, const uint32_t* idx,
+                                               const uint8_t* codes, const float* scales, const uint32_t* runs,
+                                               uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                               sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                               hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  return reduce_qsgd_common(bits, bucket, P, N, delta, h_offsets, idx, codes, scales, runs, expected_nnz_hint,
+                            out_idx, out_val, d_result, ws, ws_bytes, stream);
 }
 
 // --------------------------------------------------------------------------
@@ -394,6 +415,19 @@ sparcml_status sparcml_bench_sparse_reduce_runs(uint32_t P, uint64_t N, double d
   const sparcml::OpEvents e = op_events(ev);
   return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
                        d_result, ws, ws_bytes, stream, &e);
+}
+
+sparcml_status sparcml_bench_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t bucket, uint32_t P, uint64_t N,
+                                                     double delta, const uint64_t* h_offsets, const uint32_t* idx,
+                                                     const uint8_t* codes, const float* scales,
+                                                     const uint32_t* runs, uint64_t expected_nnz_hint,
+                                                     uint32_t* out_idx, float* out_val,
+                                                     sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                     const sparcml_bench_events* ev, hipStream_t stream) {
+  if (!runs) return SPARCML_ERR_INVALID_ARG;
+  const sparcml::OpEvents e = op_events(ev);
+  return reduce_qsgd_common(bits, bucket, P, N, delta, h_offsets, idx, codes, scales, runs, expected_nnz_hint,
+                            out_idx, out_val, d_result, ws, ws_bytes, stream, &e);
 }
 
 }  // extern "C"

@@ -110,7 +110,7 @@ struct ReduceQuantized {
   const float* scales;
 };
 // val is used when quant is null, quant otherwise; runs, when not null, is
-// the caller's run table (fp32 values only) and replaces the bounds pass;
+// the caller's run table and replaces the bounds pass;
 // union_est, the expected union size, sizes the writer groups
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,

@@ -383,6 +383,58 @@ struct QRuns {
   uint32_t sb[MAXP];
 };
 
+// Values of one aligned quad of pairs decoded from b-bit codes, for the rank
+// writer's quad loads of quantized input (codes 4-byte aligned). The quad's
+// elements inside its node's run, t0 .. t0 + nv - 1, have consecutive
+// node-relative positions rel .. rel + nv - 1, so their codes are one span of
+// at most 32 bits: two aligned words hold it (the same word when it fits in
+// one; each holds a code of the node, so neither lies past the array's last
+// word). Their buckets are at most two, each with its scale. A quad with no
+// element in the run loads the arrays' first word and scale. The decode is
+// the op sequence of the pair-by-pair loader, so the sums are the same.
+template <int BITS>
+struct QuadCodes {
+  uint32_t lo, hi, bit, t0, split;  // split: the first t of the second bucket (4: one bucket)
+  float s_lo, s_hi;
+
+  // quad q of node p's run r (absolute start, length), whose first pair is
+  // at node-relative position rel_run; cb, sb: the node's code byte and
+  // scale offsets
+  __device__ __forceinline__ void load(const RDev& R, uint32_t q, uint2 r, uint32_t rel_run, uint32_t cb,
+                                       uint32_t sb) {
+    const uint32_t e = 4u * q - r.x;                 // run position of the quad's first pair (may wrap)
+    const uint32_t lead = e > 0xFFFFFFFCu ? 0u - e : 0u;  // pairs before the run's start
+    const bool any = lead < 4u && e + lead < r.y;
+    const uint32_t nv = any ? std::min(4u - lead, r.y - (e + lead)) : 1u;
+    const uint32_t rel = any ? rel_run + e + lead : 0u;
+    const uint64_t b0 = any ? (uint64_t)cb * 8u + (uint64_t)rel * BITS : 0u;
+    const uint64_t b1 = b0 + nv * BITS - 1u;
+    const uint32_t* cw = reinterpret_cast<const uint32_t*>(R.codes);
+    lo = cw[b0 >> 5];
+    hi = cw[b1 >> 5];
+    bit = (uint32_t)(b0 & 31u);
+    t0 = lead;
+    auto bucket = [&](uint32_t x) { return R.bucket_recip ? (uint32_t)__umul64hi((uint64_t)x, R.bucket_recip) : x; };
+    const uint32_t k0 = bucket(rel), k1 = bucket(rel + nv - 1u);
+    s_lo = R.scales[any ? sb + k0 : 0u];
+    s_hi = R.scales[any ? sb + k1 : 0u];
+    split = k1 != k0 ? lead + (k1 * R.bucket - rel) : 4u;
+  }
+
+  __device__ __forceinline__ float4 values() const {
+    using F = Qsgd<BITS>;
+    const uint64_t win = ((((uint64_t)hi) << 32) | lo) >> bit;
+    const float st_lo = F::step(s_lo), st_hi = F::step(s_hi);
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t code = t >= (int)t0 ? (uint32_t)(win >> ((t - t0) * BITS)) & F::kMask : 0u;
+      v[t] = F::value(code, (uint32_t)t < split ? st_lo : st_hi);
+    }
+    return make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
 // Run of node p in segments [s0, s1): (absolute position of the node's
 // first pair there, number of its pairs there). Run ends are clamped to the
 // node's own pairs, which keeps every later load inside them even for input
@@ -433,6 +485,7 @@ __device__ __forceinline__ Slots make_slots(uint32_t lane_bits, int NT) {
 }
 
 constexpr int kCountThreads = 128;
+static_assert(2 * kCountThreads >= kInlineOffsets, "two nodes' code offsets per count thread");
 constexpr uint32_t kMaxWritersPerCount = 1u << kMaxCountLog2;
 
 // One workgroup per count group g, segments [s0, s1) = [g 2^glog, ...):
@@ -483,8 +536,27 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const uint32_t* __restr
   uint32_t bad = 0u;
   if constexpr (RUNS) {
     auto off_at = [&](uint32_t p) -> uint32_t { return (uint32_t)(inline_offs ? in.v[p] : R.offs[p]); };
-    if (inline_offs && blockIdx.x == 0)
+    if (inline_offs && blockIdx.x == 0) {
       for (uint32_t i = threadIdx.x; i <= R.P; i += NT) R.offs[i] = in.v[i];
+      if (R.bits) {  // quantized input: the code-byte and scale offsets, two nodes per thread (P <= 255)
+        __shared__ uint64_t qscr[NT / kWave + 1];
+        const uint32_t pa = 2u * threadIdx.x, pb = pa + 1u;
+        auto nnz = [&](uint32_t q) -> uint64_t { return q < R.P ? in.v[q + 1] - in.v[q] : 0ull; };
+        const uint64_t ca = (nnz(pa) * R.bits + 7) / 8, cb = (nnz(pb) * R.bits + 7) / 8;
+        const uint64_t sa = (nnz(pa) + R.bucket - 1) / R.bucket, sb = (nnz(pb) + R.bucket - 1) / R.bucket;
+        uint64_t tc, ts;
+        const uint64_t xc = block_exclusive_scan_u64<NT>(ca + cb, qscr, tc);
+        const uint64_t xs = block_exclusive_scan_u64<NT>(sa + sb, qscr, ts);
+        if (pa < R.P) {
+          R.coffs[pa] = xc;
+          R.soffs[pa] = xs;
+        }
+        if (pb < R.P) {
+          R.coffs[pb] = xc + ca;
+          R.soffs[pb] = xs + sa;
+        }
+      }
+    }
     for (uint32_t p = threadIdx.x; p < R.P; p += NT) {
       const uint32_t lo = off_at(p), hi = off_at(p + 1);
       const uint32_t* b = R.bounds + p * (R.S + 1);
@@ -880,7 +952,6 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
                                                                uint32_t* __restrict__ out_idx,
                                                                float* __restrict__ out_val, RDev R,
                                                                uint32_t lane_bits) {
-  static_assert(!QUAD || BITS == 0, "quad loads take fp32 values");
   constexpr int NT = kRankThreads;
   constexpr int kB = QUAD ? 2 : 8;  // node rows per pass
   __shared__ __align__(16) double acc[kRankSlots];
@@ -979,14 +1050,35 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
         // node run [a, a + L) covers quads q0 .. q1 - 1; lane l takes quad q0 + l
         uint4 ii[kB];
         float4 vv[kB];
+        [[maybe_unused]] QuadCodes<BITS ? BITS : 4> qc[kB];
         uint32_t q0[kB], q1[kB];
+        // the quad's values: loaded, or decoded from the node's codes
+        auto quad_values = [&](uint32_t q, uint32_t b, uint2 r) -> float4 {
+          if constexpr (BITS == 0) {
+            return reinterpret_cast<const float4*>(val)[q];
+          } else {
+            const uint32_t p = p0 + b * sl.groups + sl.group;
+            QuadCodes<BITS> c;
+            c.load(R, q, r, qruns.rel[p], qruns.cb[p], qruns.sb[p]);
+            return c.values();
+          }
+        };
 #pragma unroll
         for (int b = 0; b < kB; ++b) {
           q0[b] = rn[b].x >> 2;
           q1[b] = rn[b].y ? (rn[b].x + rn[b].y + 3u) >> 2 : q0[b];
           const uint32_t q = std::min(q0[b] + sl.lane, qlast);
           ii[b] = ld_idx4_nt(idx + 4u * q);
-          vv[b] = reinterpret_cast<const float4*>(val)[q];
+          if constexpr (BITS == 0) {
+            vv[b] = reinterpret_cast<const float4*>(val)[q];
+          } else {
+            const uint32_t p = std::min(p0 + b * sl.groups + sl.group, R.P - 1u);
+            qc[b].load(R, q, rn[b], qruns.rel[p], qruns.cb[p], qruns.sb[p]);
+          }
+        }
+        if constexpr (BITS != 0) {
+#pragma unroll
+          for (int b = 0; b < kB; ++b) vv[b] = qc[b].values();
         }
         auto add4 = [&](uint32_t q, const uint2& r, const uint4& i4, const float4& v4) {
           const uint32_t e = 4u * q - r.x;  // run position of the quad's first pair (may wrap)
@@ -1001,7 +1093,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
         for (int b = 0; b < kB; ++b) {  // the rest of runs longer than the group's quads
           if (__ballot(q1[b] - q0[b] > step) == 0ull) continue;
           for (uint32_t q = q0[b] + sl.lane + step; q < q1[b]; q += step)
-            add4(q, rn[b], ld_idx4_nt(idx + 4u * q), reinterpret_cast<const float4*>(val)[q]);
+            add4(q, rn[b], ld_idx4_nt(idx + 4u * q), quad_values(q, b, rn[b]));
         }
       } else {
         uint32_t ii[kB];
@@ -1114,22 +1206,17 @@ hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t 
                                const RDev& R, uint32_t lb, uint32_t lbq) {
   const dim3 block(kRankThreads);
   const size_t lds = sizeof(uint2) * ((size_t)kWords << R.mlog);  // the word table
+  auto go = [&](auto kq, auto kp) {
+    return launch_ev_lds(k_write_ranked<MAXP, decltype(kq)::value, decltype(kp)::value, SCAN>, grid, block, lds,
+                         stream, e0, e1, idx, val, out_idx, out_val, R, decltype(kp)::value ? lbq : lb);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
   switch (bits) {
-    case 0:
-      if (quad)
-        return launch_ev_lds(k_write_ranked<MAXP, 0, true, SCAN>, grid, block, lds, stream, e0, e1, idx, val,
-                             out_idx, out_val, R, lbq);
-      return launch_ev_lds(k_write_ranked<MAXP, 0, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
-                           out_val, R, lb);
-    case 2:
-      return launch_ev_lds(k_write_ranked<MAXP, 2, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
-                           out_val, R, lb);
-    case 4:
-      return launch_ev_lds(k_write_ranked<MAXP, 4, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
-                           out_val, R, lb);
-    default:
-      return launch_ev_lds(k_write_ranked<MAXP, 8, false, SCAN>, grid, block, lds, stream, e0, e1, idx, val, out_idx,
-                           out_val, R, lb);
+    case 0: return quad ? go(std::integral_constant<int, 0>{}, T{}) : go(std::integral_constant<int, 0>{}, F{});
+    case 2: return quad ? go(std::integral_constant<int, 2>{}, T{}) : go(std::integral_constant<int, 2>{}, F{});
+    case 4: return quad ? go(std::integral_constant<int, 4>{}, T{}) : go(std::integral_constant<int, 4>{}, F{});
+    default: return quad ? go(std::integral_constant<int, 8>{}, T{}) : go(std::integral_constant<int, 8>{}, F{});
   }
 }
 
@@ -1314,7 +1401,10 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const uint32_t lb = lanes_log2(P, R.W, R.total);
   // the estimate expecting a dense result takes the full tile; rank order
   // loads 16-byte quads of pairs where both arrays allow them
-  const bool quad = R.bits == 0 && ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0;
+  // (quantized input: 16-byte index quads and 4-byte code words)
+  const bool quad = R.bits == 0
+                        ? ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0
+                        : (reinterpret_cast<uintptr_t>(idx) & 15u) == 0 && (reinterpret_cast<uintptr_t>(R.codes) & 3u) == 0;
   const uint32_t lbq = quad_lanes_log2(P, R.W, R.total);
   e = scan_in_writer
           ? launch_writer<true>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)

@@ -48,7 +48,7 @@ def test_measurement_entry_points_are_exported_apart():
     names = declared_functions(BENCH_HEADER)
     assert set(names) == {"sparcml_bench_topk_ef", "sparcml_bench_topk_ef_runs", "sparcml_bench_qsgd",
                           "sparcml_bench_dqsgd", "sparcml_bench_sparse_reduce", "sparcml_bench_sparse_reduce_runs",
-                          "sparcml_bench_reference_stream"}
+                          "sparcml_bench_sparse_reduce_qsgd_runs", "sparcml_bench_reference_stream"}
     L = ctypes.CDLL(sg.LIB_PATH)
     B = ctypes.CDLL(sg.BENCH_LIB_PATH)
     for name in names:
@@ -108,6 +108,8 @@ calls = {
     "sparse_reduce": lambda: L.sparcml_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, None),
     "sparse_reduce_noalloc": lambda: L.sparcml_sparse_reduce_noalloc(2, 1000, 0.5, off, F, F, 0, F, F, F, None),
     "sparse_reduce_runs": lambda: L.sparcml_sparse_reduce_runs(2, 1000, 0.5, off, F, F, F, 0, F, F, F, F, wr, None),
+    "sparse_reduce_qsgd_runs": lambda: L.sparcml_sparse_reduce_qsgd_runs(4, 512, 2, 1000, 0.5, off, F, F, F, F, 0, F, F,
+                                                                         F, F, wr, None),
     "bench_sparse_reduce": lambda: L.sparcml_bench_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, ev,
                                                                  None),
     "bench_reference_stream": lambda: B.sparcml_bench_reference_stream(4096, F, F, ev, None),
@@ -131,7 +133,7 @@ def test_launching_call_without_a_device_returns_hip_error():
     lines = out.stdout.split()
     assert lines[-1] == "done", out.stdout
     got = dict(zip(lines[0:-1:2], lines[1:-1:2]))
-    assert len(got) == 10 and all(v == str(sg.ERR_HIP) for v in got.values()), got
+    assert len(got) == 11 and all(v == str(sg.ERR_HIP) for v in got.values()), got
 
 
 def test_status_strings():
@@ -183,6 +185,13 @@ def test_run_table_call_argument_checks():
                                         None) == sg.ERR_INVALID_ARG
     assert L.sparcml_sparse_reduce_runs(2, 100, f64(0.25), off, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, wr,
                                         None) == sg.ERR_WORKSPACE
+    assert L.sparcml_sparse_reduce_qsgd_runs(4, 512, 2, 100, f64(0.25), off, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE,
+                                             FAKE, FAKE, wr, None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_qsgd_runs(3, 512, 2, 100, f64(0.25), off, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE,
+                                             FAKE, FAKE, wr, None) == sg.ERR_INVALID_ARG
+    ev = ctypes.byref(sg.BenchEvents())
+    assert L.sparcml_bench_sparse_reduce_qsgd_runs(4, 512, 2, 100, f64(0.25), off, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                                   FAKE, FAKE, FAKE, wr, ev, None) == sg.ERR_INVALID_ARG
     assert sg.run_table_shape(3, 4096 * 5 + 1) == (3, 7)
 
 

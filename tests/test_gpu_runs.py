@@ -184,3 +184,51 @@ def test_reduce_runs_tables_that_do_not_fit_set_flag(dev):
     # the right table afterwards: clean
     a, b = _reduce_pair(off, idx, val, good, N, 0.25, dev, 1)
     assert a[2] == 0 and b[2] == 0 and a[0] == b[0] == 6
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("P,N,nnz,bucket,delta", [
+    (3, 8191, 501, 8, 0.25), (8, 30000, 9000, 64, 0.25), (16, 100003, 2003, 512, 0.05), (300, 20000, 77, 16, 0.3),
+])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_reduce_qsgd_runs_equals_plain_and_oracle(dev, bits, P, N, nnz, bucket, delta, shift):
+    """Quantized contributions with the run table: the same result as
+    sparcml_sparse_reduce_qsgd (bit for bit) and the oracle's reduce of the
+    dequantized values. shift = 1 places the indices 4 bytes and the codes 1
+    byte past an aligned start (pair-by-pair loads instead of quads)."""
+    rng = np.random.default_rng(P * 17 + N + nnz + bits)
+    parts, cparts, sparts, dparts = [], [], [], []
+    for p in range(P):
+        n = int(rng.integers(0, nnz + 1))
+        ids = np.sort(rng.choice(N, size=min(n, N), replace=False)).astype(np.uint32)
+        vals = rng.standard_normal((1, ids.size)).astype(np.float32)
+        c, s = oracle.qsgd(vals, bits, bucket, 7, 3, node0=p)
+        parts.append(ids)
+        cparts.append(c[0])
+        sparts.append(s[0])
+        dparts.append(oracle.dqsgd(c, s, ids.size, bits, bucket)[0])
+    off = np.zeros(P + 1, np.uint64)
+    off[1:] = np.cumsum([a.size for a in parts])
+    idx, codes = np.concatenate(parts), np.concatenate(cparts).astype(np.uint8)
+    scales, deq = np.concatenate(sparts).astype(np.float32), np.concatenate(dparts).astype(np.float32)
+    runs = oracle.run_table(off, idx, N)
+    bi = torch.zeros(idx.size + 8, dtype=torch.int32, device=dev)
+    bc = torch.zeros(codes.size + 8, dtype=torch.uint8, device=dev)
+    bi[shift:shift + idx.size] = torch.from_numpy(idx.view(np.int32)).to(dev)
+    bc[shift:shift + codes.size] = torch.from_numpy(codes).to(dev)
+    it, ct = bi[shift:shift + idx.size], bc[shift:shift + codes.size]
+    st = torch.from_numpy(scales).to(dev)
+    rt = torch.from_numpy(runs.view(np.int32)).to(dev)
+    o = [int(x) for x in off]
+    K, dense, oi, ov = oracle.reduce(off, idx, deq, N, delta)
+    print(f"reduce_qsgd runs bits={bits} P={P} N={N} shift={shift}", flush=True)
+    for hint in (0, 1, N):
+        a = sg.sparse_reduce_qsgd(o, it, ct, st, bits, bucket, N, delta, expected_nnz_hint=hint).host()
+        b = sg.sparse_reduce_qsgd(o, it, ct, st, bits, bucket, N, delta, expected_nnz_hint=hint, runs=rt).host()
+        assert a[2] == 0 and b[2] == 0 and (a[0], a[1]) == (K, dense) == (b[0], b[1])
+        assert torch.equal(a[3], b[3])
+        assert_bits_equal(b[4].numpy(), a[4].numpy(), "quantized sums with and without the table")
+        if not dense:
+            np.testing.assert_array_equal(b[3].numpy().astype(np.uint32), oi)
+        err = np.max(np.abs(b[4].numpy().astype(np.float64) - ov)) if ov.size else 0.0
+        assert err <= reduce_tolerance(P, deq), err
