@@ -94,10 +94,11 @@ constexpr int kGroup = 512;                              // tiles per gather gro
 constexpr int kChunkThreads = 256;
 constexpr int kChunkIt = 16;
 constexpr int kChunk = kChunkThreads * kChunkIt;          // 4096 candidates per chunk
-// The emit pass that also writes the run table holds 8 candidates of a chunk
-// per thread (512 threads) instead of 16: the table's extra live values then
-// leave room for more waves per SIMD.
-constexpr int kEmitRunsIt = 8;
+// The emit pass holds 8 candidates of a chunk per thread (512 threads): with
+// 16 (256 threads) it needed 107 VGPRs (4 waves per SIMD), and 161 when it
+// also writes the run table (3 waves); with 8, 92 (5 waves), and the table
+// then costs nothing measurable.
+constexpr int kEmitIt = 8;
 constexpr uint32_t kNotStored = 0xFFFFFFFFu;
 constexpr uint32_t kSmallLayer = 16384;
 constexpr int kSegmentBits = 12;  // run tables: segments of 4096 indices
@@ -1468,9 +1469,9 @@ hipError_t run(const Dev& D, uint64_t nrows, uint64_t stream_blocks, uint64_t gr
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (!ROWS && D.runs != nullptr)
-    return launch_ev(k_emit<false, true, kEmitRunsIt>, gC, dim3(kChunk / kEmitRunsIt), stream, nullptr, E.op_stop,
-                     residual, out_idx, out_val, D);
-  return launch_ev(k_emit<ROWS, false, kChunkIt>, gC, dim3(kChunkThreads), stream, nullptr, E.op_stop, residual,
+    return launch_ev(k_emit<false, true, kEmitIt>, gC, dim3(kChunk / kEmitIt), stream, nullptr, E.op_stop, residual,
+                     out_idx, out_val, D);
+  return launch_ev(k_emit<ROWS, false, kEmitIt>, gC, dim3(kChunk / kEmitIt), stream, nullptr, E.op_stop, residual,
                    out_idx, out_val, D);
 }
 
