@@ -90,6 +90,12 @@ constexpr int kInlineOffsets = 256;
 constexpr uint32_t kMaxCountLog2 = 4;   // at most 16 segments per count workgroup
 constexpr uint32_t kMaxWriterLog2 = 2;  // at most 4 segments per rank-order writer
 constexpr double kCountPairs = 2048.0;
+// With the caller's run table no bounds pass has just read the indices into
+// the memory-side cache, and the count pass reads them from HBM: groups of
+// up to 6000 pairs (four segments at the wide-ResNet size) then keep more
+// bytes in flight (measured: 194 us for the reduce with one segment per
+// group, 189 with two, 185 with four, 198-201 with eight).
+constexpr double kCountPairsRuns = 6000.0;
 constexpr double kCountRun = 200.0;
 constexpr uint64_t kCountGroupsWanted = 512;
 constexpr uint64_t kWriterGroupsWanted = 512;
@@ -1276,12 +1282,13 @@ uint32_t writer_log2(uint64_t S, double union_est, bool tile) {
 }
 
 // Segments per count group (log2): a multiple of the writer group, doubled
-// while its pairs stay below kCountPairs, a node's mean run in the doubled
+// while its pairs stay below `pairs` (kCountPairs, or kCountPairsRuns with
+// the caller's run table), a node's mean run in the doubled
 // group within kCountRun, and at least kCountGroupsWanted groups remain.
-uint32_t count_log2(uint32_t P, uint64_t S, uint64_t total, uint32_t mlog) {
+uint32_t count_log2(uint32_t P, uint64_t S, uint64_t total, uint32_t mlog, double pairs) {
   const double per_seg = (double)total / (double)S;
   uint32_t g = mlog;
-  while (g < kMaxCountLog2 && (double)(1u << g) * per_seg < kCountPairs &&
+  while (g < kMaxCountLog2 && (double)(1u << g) * per_seg < pairs &&
          (double)(2u << g) * per_seg / (double)P <= kCountRun && (S >> (g + 1)) >= kCountGroupsWanted)
     ++g;
   return g;
@@ -1305,7 +1312,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   R.N = (uint32_t)N;
   R.total = (uint32_t)h_offsets[P];
   R.mlog = writer_log2(L.S, union_est, dense_first);
-  R.glog = count_log2(P, L.S, R.total, R.mlog);
+  R.glog = count_log2(P, L.S, R.total, R.mlog, runs ? kCountPairsRuns : kCountPairs);
   R.pad = 0;
   R.S = L.S;
   R.W = (L.S + (1u << R.mlog) - 1) >> R.mlog;
