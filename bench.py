@@ -127,6 +127,10 @@ class HipEvents:
         return self.elapsed_ms(ctypes.c_void_p(e.op_start), ctypes.c_void_p(e.op_stop or e.kernel_stop))
 
     def kernel_ms(self, e):
+        """The dominant kernel's own duration; without a kernel pair (an op
+        that is one kernel, which then carries the op's pair), the op's span."""
+        if not e.kernel_start:
+            return self.span_ms(e)
         return self.elapsed_ms(ctypes.c_void_p(e.kernel_start), ctypes.c_void_p(e.kernel_stop))
 
 
@@ -185,7 +189,9 @@ def main():
     # per timed step: events on the kernel dispatches of each op (Top-k: the
     # op's span and k_stream's own pair; q4 and dq4: their one kernel; the
     # reduce: its span, closed by the writer's own stop, and the writer's pair)
-    recs = [{"topk": ev.op_events(sg, True), "q4": ev.op_events(sg, False), "dq4": ev.op_events(sg, False),
+    # (rows short enough for one workgroup each: Top-k is that one kernel, which carries the op's pair)
+    row_path = N <= sg.TOPK_ROW_MAX and P * N <= sg.TOPK_ROW_TOTAL_MAX
+    recs = [{"topk": ev.op_events(sg, not row_path), "q4": ev.op_events(sg, False), "dq4": ev.op_events(sg, False),
              "reduce": ev.op_events(sg, True, op_stop=False)} for _ in range(steps)]
 
     def step(t, rec=None):
@@ -445,7 +451,8 @@ def main():
         "reduce_result": {"nnz": K, "dense": is_dense},
         **extra,
         "topk_rescan_nodes": int((paths[0] == 1).sum()),
-        "roofline": {"kernel": "k_stream (error-feedback accumulate + candidate compaction)",
+        "roofline": {"kernel": ("k_topk_row (one workgroup per node: accumulate, select, emit)" if row_path else
+                               "k_stream (error-feedback accumulate + candidate compaction)"),
                      "bound": "hbm", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k1_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name),
                      "avg_launch_ms": round(t_k1, 4), "median_min_launch_ms": [round(med(k1_list), 4),
