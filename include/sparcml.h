@@ -355,6 +355,35 @@ sparcml_status sparcml_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, 
                                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Sparse reduction in two phases: the union phase reads only the indices
+ * (their run starts, the union bitmaps and counts, K and the dense decision:
+ * paper Appendix B and section 5.3), the sums phase adds the values into the
+ * result. A training step knows its indices before its values are final
+ * (they may still be quantized and dequantized), so it can run the union
+ * phase right after the Top-k, while the Top-k's output is still in the
+ * GPU's memory-side cache, and the sums once the values are ready.
+ *
+ * sparcml_sparse_reduce_union followed, on the same stream, by
+ * sparcml_sparse_reduce_sums with the same P, N, delta, h_offsets (the same
+ * values), idx, runs, expected_nnz_hint, d_result and ws, the indices, the
+ * table and the workspace left unchanged in between, gives exactly the
+ * result of sparcml_sparse_reduce (runs == NULL) or
+ * sparcml_sparse_reduce_runs (runs given). d_result is complete after the
+ * sums phase. Arguments and errors are those of sparcml_sparse_reduce(_runs);
+ * the union phase takes no values or outputs. Other work may run on the
+ * stream between the two calls.
+ * ---------------------------------------------------------------------- */
+sparcml_status sparcml_sparse_reduce_union(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                           const uint32_t* idx, const uint32_t* runs, uint64_t expected_nnz_hint,
+                                           sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+sparcml_status sparcml_sparse_reduce_sums(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                          const uint32_t* idx, const float* val, const uint32_t* runs,
+                                          uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                          sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Allocation-free sparse reduction, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc).

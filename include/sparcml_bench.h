@@ -89,6 +89,20 @@ sparcml_status sparcml_bench_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t buc
                                                      sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
                                                      const sparcml_bench_events* ev, hipStream_t stream);
 
+/* The two phases of the reduction: the union phase's span runs from its
+ * first kernel to its last (the decide pass, or the count pass); the sums
+ * phase is the writer alone, which carries the op's pair when given, else
+ * the kernel pair. */
+sparcml_status sparcml_bench_sparse_reduce_union(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                 const uint32_t* idx, const uint32_t* runs, uint64_t expected_nnz_hint,
+                                                 sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                 const sparcml_bench_events* ev, hipStream_t stream);
+sparcml_status sparcml_bench_sparse_reduce_sums(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                const uint32_t* idx, const float* val, const uint32_t* runs,
+                                                uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                                sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                const sparcml_bench_events* ev, hipStream_t stream);
+
 /* Attainable-bandwidth reference, in libsparcml_bench.so: r[i] += g[i] for
  * i < n with exactly the access pattern of the error-feedback stream kernel
  * (one 1024-element tile per 256-thread workgroup, one non-temporal float4

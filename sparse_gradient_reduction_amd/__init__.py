@@ -82,6 +82,10 @@ def _load():
     L.sparcml_sparse_reduce.restype = st
     L.sparcml_sparse_reduce_runs.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
     L.sparcml_sparse_reduce_runs.restype = st
+    L.sparcml_sparse_reduce_union.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, sz, vp]
+    L.sparcml_sparse_reduce_union.restype = st
+    L.sparcml_sparse_reduce_sums.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, vp]
+    L.sparcml_sparse_reduce_sums.restype = st
     L.sparcml_sparse_reduce_noalloc.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, vp, vp]
     L.sparcml_sparse_reduce_noalloc.restype = st
     L.sparcml_estimate_nnz.argtypes = [u32, u64, vp]
@@ -99,6 +103,10 @@ def _load():
     L.sparcml_bench_sparse_reduce.restype = st
     L.sparcml_bench_sparse_reduce_runs.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
     L.sparcml_bench_sparse_reduce_runs.restype = st
+    L.sparcml_bench_sparse_reduce_union.argtypes = [u32, u64, f64, vp, vp, vp, u64, vp, vp, sz, ev, vp]
+    L.sparcml_bench_sparse_reduce_union.restype = st
+    L.sparcml_bench_sparse_reduce_sums.argtypes = [u32, u64, f64, vp, vp, vp, vp, u64, vp, vp, vp, vp, sz, ev, vp]
+    L.sparcml_bench_sparse_reduce_sums.restype = st
     L.sparcml_bench_sparse_reduce_qsgd_runs.argtypes = [u32, u32, u32, u64, f64, vp, vp, vp, vp, vp, u64, vp, vp, vp,
                                                         vp, sz, ev, vp]
     L.sparcml_bench_sparse_reduce_qsgd_runs.restype = st
@@ -525,6 +533,71 @@ def sparse_reduce(offsets: Sequence[int], idx: torch.Tensor, val: torch.Tensor, 
                                                  ctypes.c_void_p(_stream(dev)))
     _raise(st, "sparcml_sparse_reduce")
     return ReduceOutput(result, out_idx, out_val, N)
+
+
+class ReduceUnion:
+    """What sparse_reduce_union prepared for sparse_reduce_sums: the call's
+    arguments and the device buffers (workspace, result record) it filled."""
+
+    def __init__(self, offsets, off, idx, N, delta, runs, hint, result, workspace):
+        self.offsets, self.off, self.idx, self.N, self.delta = offsets, off, idx, N, delta
+        self.runs, self.hint, self.result, self.workspace = runs, hint, result, workspace
+
+
+def _check_runs(runs, P, N):
+    _check_dev(runs, torch.int32, "runs")
+    if tuple(runs.shape) != run_table_shape(P, N):
+        raise ValueError(f"runs must be a contiguous {run_table_shape(P, N)} tensor")
+
+
+def sparse_reduce_union(offsets: Sequence[int], idx: torch.Tensor, N: int, delta: float,
+                        runs: Optional[torch.Tensor] = None, expected_nnz_hint: int = 0,
+                        result: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        events: Optional[BenchEvents] = None) -> ReduceUnion:
+    """The union phase of the sparse reduce (indices only): run starts, union
+    bitmaps and counts, K and the dense decision. sparse_reduce_sums then
+    adds the values; together they give sparse_reduce's result."""
+    _check_dev(idx, torch.int32, "idx")
+    P = len(offsets) - 1
+    off = (ctypes.c_uint64 * (P + 1))(*[int(x) for x in offsets])
+    dev = idx.device
+    if runs is not None:
+        _check_runs(runs, P, N)
+    if result is None:
+        result = torch.zeros(16, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        need = sparse_reduce_workspace_bytes(P, N, int(offsets[-1]))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    s = ctypes.c_void_p(_stream(dev))
+    args = (P, N, float(delta), off, _ptr(idx), _ptr(runs), int(expected_nnz_hint), _ptr(result), _ptr(workspace),
+            workspace.numel())
+    if events is None:
+        st = _load().sparcml_sparse_reduce_union(*args, s)
+    else:
+        st = _load().sparcml_bench_sparse_reduce_union(*args, ctypes.byref(events), s)
+    _raise(st, "sparcml_sparse_reduce_union")
+    return ReduceUnion(offsets, off, idx, N, delta, runs, int(expected_nnz_hint), result, workspace)
+
+
+def sparse_reduce_sums(u: ReduceUnion, val: torch.Tensor, out_idx: Optional[torch.Tensor] = None,
+                       out_val: Optional[torch.Tensor] = None,
+                       events: Optional[BenchEvents] = None) -> ReduceOutput:
+    """The sums phase after sparse_reduce_union (same stream, the indices,
+    table and workspace unchanged in between)."""
+    _check_dev(val, torch.float32, "val")
+    P = len(u.offsets) - 1
+    dev = val.device
+    out_idx, out_val, result, workspace = _reduce_outputs(u.offsets, u.N, u.delta, dev, out_idx, out_val, u.result,
+                                                          u.workspace)
+    s = ctypes.c_void_p(_stream(dev))
+    args = (P, u.N, float(u.delta), u.off, _ptr(u.idx), _ptr(val), _ptr(u.runs), u.hint, _ptr(out_idx),
+            _ptr(out_val), _ptr(result), _ptr(workspace), workspace.numel())
+    if events is None:
+        st = _load().sparcml_sparse_reduce_sums(*args, s)
+    else:
+        st = _load().sparcml_bench_sparse_reduce_sums(*args, ctypes.byref(events), s)
+    _raise(st, "sparcml_sparse_reduce_sums")
+    return ReduceOutput(result, out_idx, out_val, u.N)
 
 
 def sparse_reduce_noalloc(offsets, idx: torch.Tensor, val: torch.Tensor, N: int, delta: float,

@@ -260,23 +260,27 @@ size_t sparcml_sparse_reduce_workspace(uint32_t P, uint64_t N, uint64_t total_nn
   return sparcml::reduce_workspace_bytes(P, N, total_nnz);
 }
 
-// runs: null, or the caller's run table
+// runs: null, or the caller's run table; phase: both phases, or one of them
+// (the union phase needs neither values nor outputs)
 static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
                                     const uint32_t* idx, const float* val, const sparcml::ReduceQuantized* quant,
                                     const uint32_t* runs, uint64_t expected_nnz_hint, uint32_t* out_idx,
                                     float* out_val, sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
-                                    hipStream_t stream, const sparcml::OpEvents* ev = nullptr) {
+                                    hipStream_t stream, const sparcml::OpEvents* ev = nullptr,
+                                    int phase = sparcml::kReduceBoth) {
+  const bool sums = (phase & sparcml::kReduceSums) != 0;
   if (P == 0 || P > 1024u || N == 0 || N > kMaxN || !std::isfinite(delta)) return SPARCML_ERR_INVALID_ARG;
-  if (!h_offsets || !d_result || !out_val || !aligned16(out_val)) return SPARCML_ERR_INVALID_ARG;
+  if (!h_offsets || !d_result || (sums && (!out_val || !aligned16(out_val)))) return SPARCML_ERR_INVALID_ARG;
   if (h_offsets[0] != 0) return SPARCML_ERR_INVALID_ARG;
   for (uint32_t p = 0; p < P; ++p)
     if (h_offsets[p + 1] < h_offsets[p]) return SPARCML_ERR_INVALID_ARG;
   const uint64_t total = h_offsets[P];
   if (total > kMaxN - 15) return SPARCML_ERR_INVALID_ARG;  // positions and quad ends fit in 32 bits
-  if (total > 0 && (!idx || (quant ? (!quant->codes || !quant->scales) : !val))) return SPARCML_ERR_INVALID_ARG;
+  if (total > 0 && (!idx || (sums && (quant ? (!quant->codes || !quant->scales) : !val))))
+    return SPARCML_ERR_INVALID_ARG;
   const uint64_t T = dense_threshold(delta, N);
   const uint64_t cap = T == 0 ? 0 : (T - 1 < N ? T - 1 : N);
-  if (cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
+  if (sums && cap > 0 && !out_idx) return SPARCML_ERR_INVALID_ARG;
   if (!ws || !aligned256(ws) || ws_bytes < sparcml::reduce_workspace_bytes(P, N, total)) return SPARCML_ERR_WORKSPACE;
   // the model's union estimate sizes the writer groups; a hint, where given,
   // picks the writer in its place
@@ -286,7 +290,7 @@ static sparcml_status reduce_common(uint32_t P, uint64_t N, double delta, const 
   return from_hip(sparcml::sparse_reduce_launch(P, N, T, h_offsets, idx, val, quant, runs, dense_first, model,
                                                 out_idx, cap, out_val,
                                                 reinterpret_cast<sparcml::ReduceResultDev*>(d_result), ws, stream,
-                                                ev));
+                                                ev, phase));
 }
 
 sparcml_status sparcml_sparse_reduce(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
@@ -305,6 +309,23 @@ sparcml_status sparcml_sparse_reduce_runs(uint32_t P, uint64_t N, double delta, 
   if (!runs) return SPARCML_ERR_INVALID_ARG;
   return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
                        d_result, ws, ws_bytes, stream);
+}
+
+sparcml_status sparcml_sparse_reduce_union(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                           const uint32_t* idx, const uint32_t* runs, uint64_t expected_nnz_hint,
+                                           sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  return reduce_common(P, N, delta, h_offsets, idx, nullptr, nullptr, runs, expected_nnz_hint, nullptr, nullptr,
+                       d_result, ws, ws_bytes, stream, nullptr, sparcml::kReduceUnion);
+}
+
+sparcml_status sparcml_sparse_reduce_sums(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                          const uint32_t* idx, const float* val, const uint32_t* runs,
+                                          uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                          sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                          hipStream_t stream) {
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream, nullptr, sparcml::kReduceSums);
 }
 
 sparcml_status sparcml_sparse_reduce_noalloc(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
@@ -428,6 +449,25 @@ sparcml_status sparcml_bench_sparse_reduce_qsgd_runs(uint32_t bits, uint32_t buc
   const sparcml::OpEvents e = op_events(ev);
   return reduce_qsgd_common(bits, bucket, P, N, delta, h_offsets, idx, codes, scales, runs, expected_nnz_hint,
                             out_idx, out_val, d_result, ws, ws_bytes, stream, &e);
+}
+
+sparcml_status sparcml_bench_sparse_reduce_union(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                 const uint32_t* idx, const uint32_t* runs, uint64_t expected_nnz_hint,
+                                                 sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                 const sparcml_bench_events* ev, hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return reduce_common(P, N, delta, h_offsets, idx, nullptr, nullptr, runs, expected_nnz_hint, nullptr, nullptr,
+                       d_result, ws, ws_bytes, stream, &e, sparcml::kReduceUnion);
+}
+
+sparcml_status sparcml_bench_sparse_reduce_sums(uint32_t P, uint64_t N, double delta, const uint64_t* h_offsets,
+                                                const uint32_t* idx, const float* val, const uint32_t* runs,
+                                                uint64_t expected_nnz_hint, uint32_t* out_idx, float* out_val,
+                                                sparcml_reduce_result* d_result, void* ws, size_t ws_bytes,
+                                                const sparcml_bench_events* ev, hipStream_t stream) {
+  const sparcml::OpEvents e = op_events(ev);
+  return reduce_common(P, N, delta, h_offsets, idx, val, nullptr, runs, expected_nnz_hint, out_idx, out_val,
+                       d_result, ws, ws_bytes, stream, &e, sparcml::kReduceSums);
 }
 
 }  // extern "C"

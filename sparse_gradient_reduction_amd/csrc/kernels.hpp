@@ -112,10 +112,15 @@ struct ReduceQuantized {
 // val is used when quant is null, quant otherwise; runs, when not null, is
 // the caller's run table and replaces the bounds pass;
 // union_est, the expected union size, sizes the writer groups
+// The reduce in one call, or its two phases: the union phase (run starts,
+// union count, decision; reads only the indices) and the sums phase (the
+// writer), which needs the workspace as the union phase left it and the same
+// arguments.
+enum ReducePhase { kReduceUnion = 1, kReduceSums = 2, kReduceBoth = 3 };
 hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64_t* h_offsets,
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
                                 const uint32_t* runs, bool dense_first, double union_est, uint32_t* out_idx,
                                 uint64_t out_idx_cap, float* out_val, ReduceResultDev* d_result, void* ws,
-                                hipStream_t stream, const OpEvents* ev = nullptr);
+                                hipStream_t stream, const OpEvents* ev = nullptr, int phase = kReduceBoth);
 
 }  // namespace sparcml

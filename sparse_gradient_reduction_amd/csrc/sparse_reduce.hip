@@ -1300,10 +1300,13 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
                                 const uint32_t* idx, const float* val, const ReduceQuantized* quant,
                                 const uint32_t* runs, bool dense_first, double union_est, uint32_t* out_idx,
                                 uint64_t out_idx_cap, float* out_val, ReduceResultDev* d_result, void* ws,
-                                hipStream_t stream, const OpEvents* ev) {
+                                hipStream_t stream, const OpEvents* ev, int phase) {
   const Layout L = make_layout(P, N, h_offsets[P]);
   // measurement events: the op's span runs from its first dispatch to the
-  // writer's end; the kernel pair times the writer alone
+  // writer's end; the kernel pair times the writer alone. A union phase's
+  // span ends at its last kernel; the sums phase is the writer alone, which
+  // then carries the op's pair (or else the kernel pair).
+  const bool do_union = (phase & kReduceUnion) != 0, do_sums = (phase & kReduceSums) != 0;
   const OpEvents none{};
   const OpEvents& E = ev ? *ev : none;
   char* w = static_cast<char*>(ws);
@@ -1341,6 +1344,9 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   // offsets inline to the bounds pass for up to 255 nodes, else by setup launches
   InlineOffsets in;
   const bool inline_offs = P + 1 <= (uint32_t)kInlineOffsets;
+  const bool scan_in_writer = R.W <= kScanMaxW;
+  hipError_t e = hipSuccess;
+  if (do_union) {
   if (inline_offs) {
     for (uint32_t i = 0; i <= P; ++i) in.v[i] = h_offsets[i];
   } else {
@@ -1354,7 +1360,6 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
     }
     if (R.bits) hipLaunchKernelGGL(k_qoffsets, dim3(1), dim3(1024), 0, stream, R);
   }
-  hipError_t e = hipSuccess;
   if (runs == nullptr) {
     const uint32_t bx = bounds_blocks(max_nnz);
     R.nflagw = (uint64_t)bx * P;
@@ -1372,38 +1377,43 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
   const uint32_t lbcq = std::min<uint32_t>(quad_lanes_log2(P, groups, R.total), 7u);
   const uint32_t lbk = idx_quads ? lbcq : lbc;
   const dim3 cblock(kCountThreads);
+  // a union phase ends with the decide pass or, without one, the count pass
+  const hipEvent_t c1 = !do_sums && scan_in_writer ? E.op_stop : nullptr;
   if (runs != nullptr) {
     // no bounds pass: the count pass is the op's first kernel (after any setup launches)
     const hipEvent_t c0 = inline_offs ? E.op_start : nullptr;
     const int io = inline_offs ? 1 : 0;
     if (small_p)
-      e = idx_quads ? launch_ev_lds(k_count<256, true, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in, io)
-                    : launch_ev_lds(k_count<256, false, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in,
-                                    io);
+      e = idx_quads ? launch_ev_lds(k_count<256, true, true>, cgrid, cblock, clds, stream, c0, c1, idx, R, lbk, in, io)
+                    : launch_ev_lds(k_count<256, false, true>, cgrid, cblock, clds, stream, c0, c1, idx, R, lbk, in, io);
     else
       e = idx_quads
-              ? launch_ev_lds(k_count<kMaxP, true, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in, io)
-              : launch_ev_lds(k_count<kMaxP, false, true>, cgrid, cblock, clds, stream, c0, nullptr, idx, R, lbk, in,
-                              io);
-    if (e != hipSuccess) return e;
+              ? launch_ev_lds(k_count<kMaxP, true, true>, cgrid, cblock, clds, stream, c0, c1, idx, R, lbk, in, io)
+              : launch_ev_lds(k_count<kMaxP, false, true>, cgrid, cblock, clds, stream, c0, c1, idx, R, lbk, in, io);
   } else {
-    const NoOffsets none_in{};
-    if (small_p) {
-      if (idx_quads) hipLaunchKernelGGL((k_count<256, true, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
-      else hipLaunchKernelGGL((k_count<256, false, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
-    } else {
-      if (idx_quads) hipLaunchKernelGGL((k_count<kMaxP, true, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
-      else hipLaunchKernelGGL((k_count<kMaxP, false, false>), cgrid, cblock, clds, stream, idx, R, lbk, none_in, 0);
-    }
+    const NoOffsets no{};
+    if (small_p)
+      e = idx_quads ? launch_ev_lds(k_count<256, true, false>, cgrid, cblock, clds, stream, nullptr, c1, idx, R, lbk, no, 0)
+                    : launch_ev_lds(k_count<256, false, false>, cgrid, cblock, clds, stream, nullptr, c1, idx, R, lbk, no,
+                                    0);
+    else
+      e = idx_quads
+              ? launch_ev_lds(k_count<kMaxP, true, false>, cgrid, cblock, clds, stream, nullptr, c1, idx, R, lbk, no, 0)
+              : launch_ev_lds(k_count<kMaxP, false, false>, cgrid, cblock, clds, stream, nullptr, c1, idx, R, lbk, no,
+                              0);
   }
-  const bool scan_in_writer = R.W <= kScanMaxW;
-  if (!scan_in_writer) hipLaunchKernelGGL(k_decide, dim3(1), dim3(1024), 0, stream, R);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (!scan_in_writer) {
+    e = launch_ev(k_decide, dim3(1), dim3(1024), stream, nullptr, do_sums ? nullptr : E.op_stop, R);
+    if (e != hipSuccess) return e;
+  }
+  }  // do_union
+  if (!do_sums) return hipSuccess;
   // the writer is the op's last kernel: it carries the kernel pair, or the
-  // op's stop alone
-  const hipEvent_t w0 = E.k_start;
-  const hipEvent_t w1 = E.k_stop ? E.k_stop : E.op_stop;
+  // op's stop alone (a sums phase: the op's pair, or else the kernel pair)
+  const bool alone = !do_union;
+  const hipEvent_t w0 = alone && E.op_start ? E.op_start : E.k_start;
+  const hipEvent_t w1 = alone && E.op_start ? E.op_stop : (E.k_stop ? E.k_stop : E.op_stop);
   const dim3 wgrid((uint32_t)R.W);
   const uint32_t lb = lanes_log2(P, R.W, R.total);
   // the estimate expecting a dense result takes the full tile; rank order
@@ -1417,7 +1427,7 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
           ? launch_writer<true>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
           : launch_writer<false>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq);
   // with both pairs asked for, the op's stop follows the writer's at once
-  if (e == hipSuccess && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
+  if (e == hipSuccess && !(alone && E.op_start) && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
   return e;
 }
 

@@ -48,7 +48,8 @@ def test_measurement_entry_points_are_exported_apart():
     names = declared_functions(BENCH_HEADER)
     assert set(names) == {"sparcml_bench_topk_ef", "sparcml_bench_topk_ef_runs", "sparcml_bench_qsgd",
                           "sparcml_bench_dqsgd", "sparcml_bench_sparse_reduce", "sparcml_bench_sparse_reduce_runs",
-                          "sparcml_bench_sparse_reduce_qsgd_runs", "sparcml_bench_reference_stream"}
+                          "sparcml_bench_sparse_reduce_qsgd_runs", "sparcml_bench_sparse_reduce_union",
+                          "sparcml_bench_sparse_reduce_sums", "sparcml_bench_reference_stream"}
     L = ctypes.CDLL(sg.LIB_PATH)
     B = ctypes.CDLL(sg.BENCH_LIB_PATH)
     for name in names:
@@ -108,6 +109,8 @@ calls = {
     "sparse_reduce": lambda: L.sparcml_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, None),
     "sparse_reduce_noalloc": lambda: L.sparcml_sparse_reduce_noalloc(2, 1000, 0.5, off, F, F, 0, F, F, F, None),
     "sparse_reduce_runs": lambda: L.sparcml_sparse_reduce_runs(2, 1000, 0.5, off, F, F, F, 0, F, F, F, F, wr, None),
+    "sparse_reduce_union": lambda: L.sparcml_sparse_reduce_union(2, 1000, 0.5, off, F, None, 0, F, F, wr, None),
+    "sparse_reduce_sums": lambda: L.sparcml_sparse_reduce_sums(2, 1000, 0.5, off, F, F, None, 0, F, F, F, F, wr, None),
     "sparse_reduce_qsgd_runs": lambda: L.sparcml_sparse_reduce_qsgd_runs(4, 512, 2, 1000, 0.5, off, F, F, F, F, 0, F, F,
                                                                          F, F, wr, None),
     "bench_sparse_reduce": lambda: L.sparcml_bench_sparse_reduce(2, 1000, 0.5, off, F, F, 0, F, F, F, F, wr, ev,
@@ -133,7 +136,7 @@ def test_launching_call_without_a_device_returns_hip_error():
     lines = out.stdout.split()
     assert lines[-1] == "done", out.stdout
     got = dict(zip(lines[0:-1:2], lines[1:-1:2]))
-    assert len(got) == 11 and all(v == str(sg.ERR_HIP) for v in got.values()), got
+    assert len(got) == 13 and all(v == str(sg.ERR_HIP) for v in got.values()), got
 
 
 def test_status_strings():
@@ -193,6 +196,26 @@ def test_run_table_call_argument_checks():
     assert L.sparcml_bench_sparse_reduce_qsgd_runs(4, 512, 2, 100, f64(0.25), off, FAKE, FAKE, FAKE, None, 0, FAKE,
                                                    FAKE, FAKE, FAKE, wr, ev, None) == sg.ERR_INVALID_ARG
     assert sg.run_table_shape(3, 4096 * 5 + 1) == (3, 7)
+
+
+def test_reduce_phase_argument_checks():
+    """The union phase takes no values or outputs; the sums phase checks them."""
+    L = sg.lib()
+    off = (ctypes.c_uint64 * 3)(0, 5, 9)
+    wr = sg.sparse_reduce_workspace_bytes(2, 100, 9)
+    f64 = ctypes.c_double
+    assert L.sparcml_sparse_reduce_union(0, 100, f64(0.25), off, FAKE, None, 0, FAKE, FAKE, wr,
+                                         None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_union(2, 100, f64(0.25), off, None, None, 0, FAKE, FAKE, wr,
+                                         None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_union(2, 100, f64(0.25), off, FAKE, None, 0, None, FAKE, wr,
+                                         None) == sg.ERR_INVALID_ARG
+    assert L.sparcml_sparse_reduce_union(2, 100, f64(0.25), off, FAKE, None, 0, FAKE, None, wr,
+                                         None) == sg.ERR_WORKSPACE
+    assert L.sparcml_sparse_reduce_sums(2, 100, f64(0.25), off, FAKE, None, None, 0, FAKE, FAKE, FAKE, FAKE, wr,
+                                        None) == sg.ERR_INVALID_ARG  # no values
+    assert L.sparcml_sparse_reduce_sums(2, 100, f64(0.25), off, FAKE, FAKE, None, 0, FAKE, FAKE_ODD, FAKE, FAKE, wr,
+                                        None) == sg.ERR_INVALID_ARG  # unaligned out_val
 
 
 def test_q4_argument_checks():

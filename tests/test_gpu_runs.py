@@ -232,3 +232,39 @@ def test_reduce_qsgd_runs_equals_plain_and_oracle(dev, bits, P, N, nnz, bucket, 
             np.testing.assert_array_equal(b[3].numpy().astype(np.uint32), oi)
         err = np.max(np.abs(b[4].numpy().astype(np.float64) - ov)) if ov.size else 0.0
         assert err <= reduce_tolerance(P, deq), err
+
+
+@pytest.mark.parametrize("P,N,nnz,delta", [
+    (3, 8193, 2000, 0.3), (16, 100003, 2000, 0.05), (300, 20000, 60, 0.3), (8, 1 << 24, 3000, 0.25),
+    (64, 1 << 20, 3000, 0.3),
+])
+@pytest.mark.parametrize("table", [False, True])
+@pytest.mark.parametrize("hint", [0, 1, "dense"])
+def test_reduce_in_two_phases_equals_one_call(dev, P, N, nnz, delta, table, hint):
+    """sparcml_sparse_reduce_union, other work on the stream, then
+    sparcml_sparse_reduce_sums: the one-call result bit for bit (with the
+    decide pass where there are more than 2048 writer groups, N = 2^24, and
+    writers that add up the counts themselves otherwise), and the oracle's."""
+    rng = np.random.default_rng(P * 7 + N + nnz)
+    off, idx, val = _sorted_nodes(rng, P, N, nnz)
+    runs = oracle.run_table(off, idx, N)
+    it = torch.from_numpy(idx.view(np.int32)).to(dev)
+    vt = torch.from_numpy(val).to(dev)
+    rt = torch.from_numpy(runs.view(np.int32)).to(dev) if table else None
+    o = [int(x) for x in off]
+    h = N if hint == "dense" else hint
+    print(f"two phases P={P} N={N} table={table} hint={hint}", flush=True)
+    one = sg.sparse_reduce(o, it, vt, N, delta, expected_nnz_hint=h, runs=rt).host()
+    u = sg.sparse_reduce_union(o, it, N, delta, runs=rt, expected_nnz_hint=h)
+    junk = torch.randn(1 << 20, device=dev)  # unrelated work between the phases
+    junk.mul_(2.0).sum().item()
+    two = sg.sparse_reduce_sums(u, vt).host()
+    assert one[:3] == two[:3] and one[2] == 0
+    assert torch.equal(one[3], two[3])
+    assert_bits_equal(two[4].numpy(), one[4].numpy(), "two phases")
+    K, dense, oi, ov = oracle.reduce(off, idx, val, N, delta)
+    assert (two[0], two[1]) == (K, dense)
+    if not dense:
+        np.testing.assert_array_equal(two[3].numpy().astype(np.uint32), oi)
+    err = np.max(np.abs(two[4].numpy().astype(np.float64) - ov)) if ov.size else 0.0
+    assert err <= reduce_tolerance(P, val), err

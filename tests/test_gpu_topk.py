@@ -222,8 +222,9 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
     own residual chain, with the 4-bit codes of their sent values and the run
     table rows of their output (sparcml_topk_ef_runs); on all 64 nodes the
     exact EF identity, strictly ascending indices and no unselected magnitude
-    above a selected one. The reduce of the last step's pairs with that table
-    equals the reduce that finds the runs itself, bit for bit."""
+    above a selected one. The reduce of the last step's pairs with that table,
+    in one call and in two phases, equals the reduce that finds the runs
+    itself, bit for bit."""
     w = W.workload(4)
     P, N, k, B = w.P, w.N, w.k, w.q4_bucket
     seed = 987654321
@@ -273,10 +274,16 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
         torch.cuda.empty_cache()
     off = [p * k for p in range(P + 1)]
     plain = sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta)
-    with_runs = sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, runs=runs)
     K, dense, flags = plain.read()
-    assert (K, dense, flags) == with_runs.read() and flags == 0
+    assert flags == 0
     n = N if dense else K
-    assert torch.equal(plain.out_val[:n].view(torch.int32), with_runs.out_val[:n].view(torch.int32))
-    if not dense:
-        assert torch.equal(plain.out_idx[:K], with_runs.out_idx[:K])
+    with_runs = sg.sparse_reduce(off, idx.view(-1), val.view(-1), N, w.delta, runs=runs)
+    # and in two phases with the table, the union before other work on the stream
+    u = sg.sparse_reduce_union(off, idx.view(-1), N, w.delta, runs=runs)
+    sg.q4(val, B, seed, 5)
+    phased = sg.sparse_reduce_sums(u, val.view(-1))
+    for other in (with_runs, phased):
+        assert (K, dense, flags) == other.read()
+        assert torch.equal(plain.out_val[:n].view(torch.int32), other.out_val[:n].view(torch.int32))
+        if not dense:
+            assert torch.equal(plain.out_idx[:K], other.out_idx[:K])
