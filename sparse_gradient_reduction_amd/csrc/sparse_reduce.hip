@@ -23,7 +23,7 @@
 //            for the writer, and the union count of every writer group in it
 //            with the group's input-check bits in the word's top bits
 //   decide   exclusive scan of the writer-group counts, K, dense iff K >= T,
-//            the check bits of all groups (not launched for at most 2048
+//            the check bits of all groups (not launched for at most 4096
 //            writer groups: every writer adds up the counts itself)
 //   write    per writer group of 2^mlog segments: the sums, stored densely or
 //            as the group's sorted part of the sparse result at its offset
@@ -731,7 +731,7 @@ __global__ __launch_bounds__(1024) void k_decide(RDev R) {
 // the workgroup of group 0 stores the result record. load() goes out with the
 // other prologue loads; finish() follows the caller's barrier and is called
 // by every thread.
-constexpr uint64_t kScanMaxW = 2048;
+constexpr uint64_t kScanMaxW = 4096;  // LSTM-sized reduce, 4096 writer groups: 41.3 -> 39.3 us cold
 
 __device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
 

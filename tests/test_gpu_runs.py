@@ -236,15 +236,16 @@ def test_reduce_qsgd_runs_equals_plain_and_oracle(dev, bits, P, N, nnz, bucket, 
 
 @pytest.mark.parametrize("P,N,nnz,delta", [
     (3, 8193, 2000, 0.3), (16, 100003, 2000, 0.05), (300, 20000, 60, 0.3), (8, 1 << 24, 3000, 0.25),
-    (64, 1 << 20, 3000, 0.3),
+    (8, 1 << 25, 3000, 0.25), (64, 1 << 20, 3000, 0.3),
 ])
 @pytest.mark.parametrize("table", [False, True])
 @pytest.mark.parametrize("hint", [0, 1, "dense"])
 def test_reduce_in_two_phases_equals_one_call(dev, P, N, nnz, delta, table, hint):
     """sparcml_sparse_reduce_union, other work on the stream, then
     sparcml_sparse_reduce_sums: the one-call result bit for bit (with the
-    decide pass where there are more than 2048 writer groups, N = 2^24, and
-    writers that add up the counts themselves otherwise), and the oracle's."""
+    decide pass where there are more than 4096 writer groups, N = 2^25, and
+    writers that add up the counts themselves otherwise, 4096 of them at
+    N = 2^24), and the oracle's."""
     rng = np.random.default_rng(P * 7 + N + nnz)
     off, idx, val = _sorted_nodes(rng, P, N, nnz)
     runs = oracle.run_table(off, idx, N)
