@@ -950,9 +950,14 @@ __global__ __launch_bounds__(kWriteThreads) void k_write_tile(const uint32_t* __
 // stays inside the window.
 constexpr int kRankThreads = 256;
 constexpr uint32_t kRankCap = 2560;
-constexpr uint32_t kRankSlots = kRankCap + 4;
+// Groups whose expected union leaves room within kRankCapSmall take a writer
+// with that many slots: less LDS, more workgroups per compute unit
+// (LSTM-sized reduce, 4 segments per group: 39.5 -> 37.2 us cold; with the
+// small cap for every call the wide-ResNet reduce, then one segment per
+// group, took 234 us instead of 184).
+constexpr uint32_t kRankCapSmall = 1536;
 
-template <int MAXP, int BITS, bool QUAD, bool SCAN>
+template <int MAXP, int BITS, bool QUAD, bool SCAN, uint32_t CAP>
 __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* __restrict__ idx,
                                                                const float* __restrict__ val,
                                                                uint32_t* __restrict__ out_idx,
@@ -960,8 +965,8 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
                                                                uint32_t lane_bits) {
   constexpr int NT = kRankThreads;
   constexpr int kB = QUAD ? 2 : 8;  // node rows per pass
-  __shared__ __align__(16) double acc[kRankSlots];
-  __shared__ __align__(16) uint16_t sloc[kRankSlots];  // index within the group
+  __shared__ __align__(16) double acc[(CAP + 4)];
+  __shared__ __align__(16) uint16_t sloc[(CAP + 4)];  // index within the group
   __shared__ uint2 runs[MAXP];
   __shared__ QRuns<BITS ? MAXP : 1> qruns;
   __shared__ uint32_t scr[3];
@@ -982,7 +987,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
   if (threadIdx.x < nvalid) wpair = reinterpret_cast<const uint2*>(R.bitmaps + (s << mlog) * kWords)[threadIdx.x];
   WriterHead<NT, SCAN> hw;
   hw.load(R, s, scr);
-  for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
+  for (uint32_t r = threadIdx.x; r < (CAP + 4); r += NT) acc[r] = 0.0;
   store_run_table<NT, BITS ? MAXP : 1>(R, s << mlog, std::min<uint64_t>((s + 1) << mlog, R.S), runs,
                                        BITS ? &qruns : nullptr);
   const uint32_t c0 = (uint32_t)__popc(wpair.x), c1 = (uint32_t)__popc(wpair.y);
@@ -1019,20 +1024,20 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
     }
   };
   const uint32_t lmask = span - 1u;
-  const uint32_t windows = std::max<uint32_t>(1u, (seg_cnt + kRankCap - 1) / kRankCap);
-  for (uint32_t w0 = 0, win = 0; win < windows; ++win, w0 += kRankCap) {
+  const uint32_t windows = std::max<uint32_t>(1u, (seg_cnt + CAP - 1) / CAP);
+  for (uint32_t w0 = 0, win = 0; win < windows; ++win, w0 += CAP) {
     const uint32_t sh = (seg_off + w0) & 3u;  // slot of the window's first rank
     const uint32_t base = w0 - sh;             // rank r sits in slot r - base
     if (win > 0) {  // the previous window is stored: clear for this one
       __syncthreads();
-      for (uint32_t r = threadIdx.x; r < kRankSlots; r += NT) acc[r] = 0.0;
+      for (uint32_t r = threadIdx.x; r < (CAP + 4); r += NT) acc[r] = 0.0;
       __syncthreads();
     }
     auto add = [&](uint32_t i, float v) {
       const uint32_t local = i & lmask;
       const uint2 wd = words[local >> 5];
       const uint32_t x = wd.x + (uint32_t)__popc(wd.y & ((1u << (local & 31)) - 1u)) - base;
-      if (x - sh < kRankCap) {
+      if (x - sh < CAP) {
         atomicAdd(&acc[x], (double)v);
         sloc[x] = (uint16_t)local;
       }
@@ -1141,7 +1146,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
           const uint32_t local = 4 * q + t;
           const uint32_t bit = 1u << (local & 31);
           const uint32_t x = wd.x + (uint32_t)__popc(wd.y & (bit - 1u)) - base;
-          const bool in = (wd.y & bit) && x - sh < kRankCap;
+          const bool in = (wd.y & bit) && x - sh < CAP;
           o[t] = in ? (float)acc[x] : 0.0f;
           if (!whole && local < seg_len && (in || (!(wd.y & bit) && win == 0u))) out[local] = o[t];
         }
@@ -1151,7 +1156,7 @@ __global__ __launch_bounds__(kRankThreads) void k_write_ranked(const uint32_t* _
       // slots [sh, sh + n) hold ranks w0 .. w0 + n - 1, at output positions
       // pos0 + slot with pos0 = seg_off + w0 - sh a multiple of 4, so slot
       // quads are output quads
-      const uint32_t n = std::min(seg_cnt - w0, kRankCap);
+      const uint32_t n = std::min(seg_cnt - w0, CAP);
       const uint64_t pos0 = (uint64_t)seg_off + w0 - sh;  // a multiple of 4
       for (uint32_t k = threadIdx.x; 4 * k < sh + n; k += NT) {
         const double2 a01 = reinterpret_cast<const double2*>(acc)[2 * k];
@@ -1207,14 +1212,19 @@ hipError_t launch_write_tile(uint32_t bits, dim3 grid, hipStream_t stream, hipEv
 }
 
 template <int MAXP, bool SCAN>
-hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+hipError_t launch_write_ranked(uint32_t bits, bool quad, bool small_cap, dim3 grid, hipStream_t stream, hipEvent_t e0,
+                               hipEvent_t e1,
                                const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val,
                                const RDev& R, uint32_t lb, uint32_t lbq) {
   const dim3 block(kRankThreads);
   const size_t lds = sizeof(uint2) * ((size_t)kWords << R.mlog);  // the word table
   auto go = [&](auto kq, auto kp) {
-    return launch_ev_lds(k_write_ranked<MAXP, decltype(kq)::value, decltype(kp)::value, SCAN>, grid, block, lds,
-                         stream, e0, e1, idx, val, out_idx, out_val, R, decltype(kp)::value ? lbq : lb);
+    constexpr int B = decltype(kq)::value;
+    constexpr bool Q = decltype(kp)::value;
+    return small_cap ? launch_ev_lds(k_write_ranked<MAXP, B, Q, SCAN, kRankCapSmall>, grid, block, lds, stream, e0,
+                                     e1, idx, val, out_idx, out_val, R, Q ? lbq : lb)
+                     : launch_ev_lds(k_write_ranked<MAXP, B, Q, SCAN, kRankCap>, grid, block, lds, stream, e0, e1, idx,
+                                     val, out_idx, out_val, R, Q ? lbq : lb);
   };
   using T = std::true_type;
   using F = std::false_type;
@@ -1229,7 +1239,8 @@ hipError_t launch_write_ranked(uint32_t bits, bool quad, dim3 grid, hipStream_t 
 // The writer for (tile or rank order) x (nodes up to 256 or 1024: the run
 // table's LDS) x (its own scan or the decide pass's).
 template <bool SCAN>
-hipError_t launch_writer(bool tile, bool quad, dim3 grid, hipStream_t stream, hipEvent_t e0, hipEvent_t e1,
+hipError_t launch_writer(bool tile, bool quad, bool small_cap, dim3 grid, hipStream_t stream, hipEvent_t e0,
+                         hipEvent_t e1,
                          const uint32_t* idx, const float* val, uint32_t* out_idx, float* out_val, const RDev& R,
                          uint32_t lb, uint32_t lbq) {
   if (tile)
@@ -1237,9 +1248,9 @@ hipError_t launch_writer(bool tile, bool quad, dim3 grid, hipStream_t stream, hi
                ? launch_write_tile<256, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb)
                : launch_write_tile<kMaxP, SCAN>(R.bits, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb);
   return R.P <= 256
-             ? launch_write_ranked<256, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
+             ? launch_write_ranked<256, SCAN>(R.bits, quad, small_cap, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
                                               lbq)
-             : launch_write_ranked<kMaxP, SCAN>(R.bits, quad, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
+             : launch_write_ranked<kMaxP, SCAN>(R.bits, quad, small_cap, grid, stream, e0, e1, idx, val, out_idx, out_val, R, lb,
                                                 lbq);
 }
 
@@ -1279,6 +1290,13 @@ uint32_t writer_log2(uint64_t S, double union_est, bool tile) {
   uint32_t m = 0;
   while (m < kMaxWriterLog2 && fits(m + 1) && (S >> (m + 1)) >= kWriterGroupsWanted) ++m;
   return m;
+}
+
+// Whether groups of 2^mlog segments fit the writer with kRankCapSmall slots
+// by the same margin.
+bool writer_small_cap(uint64_t S, double union_est, uint32_t mlog) {
+  const double u = (double)(1u << mlog) * union_est / (double)S;
+  return u + 4.0 * std::sqrt(u) + 16.0 <= (double)kRankCapSmall;
 }
 
 // Segments per count group (log2): a multiple of the writer group, doubled
@@ -1423,9 +1441,12 @@ hipError_t sparse_reduce_launch(uint32_t P, uint64_t N, uint64_t T, const uint64
                         ? ((reinterpret_cast<uintptr_t>(idx) | reinterpret_cast<uintptr_t>(val)) & 15u) == 0
                         : (reinterpret_cast<uintptr_t>(idx) & 15u) == 0 && (reinterpret_cast<uintptr_t>(R.codes) & 3u) == 0;
   const uint32_t lbq = quad_lanes_log2(P, R.W, R.total);
+  const bool small_cap = !dense_first && writer_small_cap(L.S, union_est, R.mlog);
   e = scan_in_writer
-          ? launch_writer<true>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq)
-          : launch_writer<false>(dense_first, quad, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb, lbq);
+          ? launch_writer<true>(dense_first, quad, small_cap, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
+                                lbq)
+          : launch_writer<false>(dense_first, quad, small_cap, wgrid, stream, w0, w1, idx, val, out_idx, out_val, R, lb,
+                                 lbq);
   // with both pairs asked for, the op's stop follows the writer's at once
   if (e == hipSuccess && !(alone && E.op_start) && E.k_stop && E.op_stop) e = hipEventRecord(E.op_stop, stream);
   return e;

@@ -311,3 +311,21 @@ def test_multi_segment_groups_unaligned(dev):
     assert flags == 0 and gK == K and gdense == dense and not dense
     np.testing.assert_array_equal(gi.numpy().astype(np.uint32), oi)
     assert np.max(np.abs(gv.numpy().astype(np.float64) - ov)) <= reduce_tolerance(P, val)
+
+
+@pytest.mark.parametrize("hint", [0, 1])
+def test_clustered_indices_take_several_rank_windows(dev, hint):
+    """Indices crowded into the first few segments while the uniform estimate
+    expects about 64 per segment: the rank writer sized by the estimate (the
+    smaller slot count) meets unions of about 4000 per segment and takes
+    several windows over the group's pairs."""
+    rng = np.random.default_rng(77 + hint)
+    P, N = 8, 1 << 22
+    parts, vals = [], []
+    for _ in range(P):
+        ids = np.sort(rng.choice(4 * 4096, size=8192, replace=False)).astype(np.uint32)
+        parts.append(ids)
+        vals.append(rng.standard_normal(ids.size).astype(np.float32))
+    off = np.arange(P + 1, dtype=np.uint64) * 8192
+    K, dense = _check(off, np.concatenate(parts), np.concatenate(vals), N, 0.25, dev, hint=hint)
+    assert not dense and K > 3 * 4096
