@@ -1157,9 +1157,10 @@ __global__ __launch_bounds__(kChunk / IT) void k_emit(float* __restrict__ r, uin
       const bool high = mag_key(v[it]) >= mid;  // written as +0 by the stream kernel
       if ((sel_bits >> it) & 1u) {
         const uint32_t pos = out_base + s_sel[it * NW + wid] + sel_pre[it];
-        if (pos < K) {
-          oi[pos] = e[it] + R.idx_off;
-          ov[pos] = v[it];
+        if (pos < K) {  // non-temporal: the reduce reads them from HBM anyway, and dirty lines
+                        // left in the memory-side cache would be written back during its first pass
+          __builtin_nontemporal_store(e[it] + R.idx_off, &oi[pos]);
+          __builtin_nontemporal_store(v[it], &ov[pos]);
         }
         if (rescan || !high) r[pN + e[it]] = 0.0f;
       } else if (!rescan && high) {
