@@ -84,6 +84,7 @@ constexpr int kSmallSample = kSmallPredictThreads * kPredictKeys;  // 16384
 constexpr int kLayerPredictThreads = 512;
 constexpr int kLayerSampleChunks = kLayerPredictThreads * kPredictKeys / kSampleChunk;  // 512
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
+constexpr int kDigCap = 16;  // last-digit slots per chunk for the keys that share T*'s upper 21 bits
 // Whole-node call: the gather also counts the second digit of the keys whose
 // first digit is one of kSpecBins bins around the prediction `mid`'s; when
 // T*'s first digit is among them, that count is the second radix level and
@@ -112,7 +113,7 @@ struct NodeState {
   uint32_t mode;    // 0 candidates, 1 exact rescan
   uint32_t T;       // k-th largest key
   uint32_t m;       // how many elements with key == T are selected
-  uint32_t pad;
+  uint32_t ovf;     // some chunk holds more keys of T*'s 21-bit prefix than its digit slots
 };
 
 // Sizes of one row's slices of the workspace arrays (integer formulas shared
@@ -212,7 +213,7 @@ struct Layout {
   uint64_t MG;    // whole-node call: tile groups per node
   uint64_t MC;    // whole-node call: chunks per node (slots, rescan worst case)
   size_t info, err, state, h0, h1, h2, h1s, sub, cand, oidx, oval, tmeta, gsum, gbase, cgt, ceq, ceqoff,
-      cout, rows, tile_row, group_row, pass_row, big_rows, mid_rows, loff, lk, lkoff, total;
+      cout, cdig, rows, tile_row, group_row, pass_row, big_rows, mid_rows, loff, lk, lkoff, total;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -244,6 +245,7 @@ Layout make_layout(const Plan& Q, uint64_t nlayers) {
   L.ceq = take(4ull * Q.chunks);
   L.ceqoff = take(4ull * Q.chunks);
   L.cout = take(4ull * Q.chunks);
+  L.cdig = take(2ull * kDigCap * Q.chunks);
   if (Q.layers) {
     L.rows = take(kRowBytes * R);
     L.tile_row = take(4ull * Q.tiles);
@@ -343,6 +345,7 @@ struct Dev {
   uint32_t* ceq;
   uint32_t* ceqoff;
   uint32_t* cout;
+  uint16_t* cdig;  // [chunk][kDigCap]: last digits of the chunk's keys with T*'s upper 21 bits
   const struct Row* rows;     // per-layer call: row table
   const uint32_t* tile_row;   // per-layer call: row of every stream workgroup
   const uint32_t* group_row;  // per-layer call: row of every tile group
@@ -844,13 +847,24 @@ struct DigitBins {
 // ---------------------------------------------------------------------------
 // hist: one radix level of T*. Level 0 runs only on the rescan path (the
 // gather kernel builds it for the candidate path).
+//
+// The last level also tallies each chunk of kChunk source elements against
+// T*'s upper 21 bits, which it knows: cgt[c] = keys above them, ceq[c] = keys
+// sharing them, and the last digits of the first kDigCap of those in
+// cdig[c]. Once the level's histogram gives the last digit, the scan turns
+// these into the chunk's counts above and equal to T*, so no pass over the
+// keys is needed for them; a chunk with more such keys than slots (ties)
+// sets the row's ovf and the count pass counts that row's chunks itself.
 // ---------------------------------------------------------------------------
 template <int LEVEL, bool ROWS>
 __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D) {
   constexpr int NB = LEVEL == 0 ? kH0 : (LEVEL == 1 ? kH1 : kH2);
   constexpr int kU = 16;
+  static_assert(256 * kU == kChunk, "a pass of the block is one chunk");
   __shared__ uint32_t h[NB];
   __shared__ uint32_t scr[256 / kWave + 3];
+  __shared__ uint32_t s_sum[2 * 256 / kWave];
+  __shared__ uint32_t s_eq;  // keys of the chunk sharing T*'s upper bits (last level)
   // per-layer call: a 1D grid, each row owning npass consecutive blocks
   const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;
   const bool rescan = D.state[p].mode != 0u;
@@ -892,10 +906,15 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
       return;
     }
   }
+  if (LEVEL == 2 && threadIdx.x == 0) s_eq = 0u;
   __syncthreads();
-  for (uint64_t i0 = bx * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
+  // passes are whole chunks, block-uniform (the last level's tallies take
+  // barriers): pass base c0 = chunk c's first element
+  for (uint64_t c0 = bx * 256 * kU; c0 < n; c0 += stride) {
+    const uint64_t i0 = c0 + threadIdx.x;
     float nx[kU];
     load(i0 + stride, nx);  // the block's next pass, in flight during this one
+    uint32_t above = 0u;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const uint32_t kk = i0 + (uint64_t)u * 256 < n ? mag_key(x[u]) : 0xFFFFFFFFu;
@@ -910,6 +929,7 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
       } else {
         hit = kk != 0xFFFFFFFFu && (kk >> 10) == prefix;
         bin = kk & 1023u;
+        above += (kk != 0xFFFFFFFFu && (kk >> 10) > prefix) ? 1u : 0u;
       }
       // level 0 keys crowd into a few bins: aggregate per wave; the lower
       // digits spread out, where plain LDS atomics are cheaper
@@ -917,7 +937,24 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
         wave_hist_add_capped<2>(h, bin, hit);
       } else if (hit) {
         atomicAdd(&h[bin], 1u);
+        if (LEVEL == 2) {
+          const uint32_t slot = atomicAdd(&s_eq, 1u);
+          if (slot < (uint32_t)kDigCap)
+            D.cdig[(R.chunk0 + c0 / kChunk) * kDigCap + slot] = (uint16_t)bin;
+        }
       }
+    }
+    if constexpr (LEVEL == 2) {
+      uint32_t tot_above, unused;
+      block_sum2<256>(above, 0u, s_sum, tot_above, unused);  // its barriers also order the s_eq adds
+      if (threadIdx.x == 0) {
+        const uint32_t eq = s_eq;
+        D.cgt[R.chunk0 + c0 / kChunk] = tot_above;
+        D.ceq[R.chunk0 + c0 / kChunk] = eq;
+        if (eq > (uint32_t)kDigCap) atomicOr(&D.state[p].ovf, 1u);
+        s_eq = 0u;
+      }
+      __syncthreads();  // the reset before the next pass's adds
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) x[u] = nx[u];
@@ -929,13 +966,17 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
 }
 
 // ---------------------------------------------------------------------------
-// count: per chunk of the source, elements above and equal to T*.
+// count: per chunk of the source, elements above and equal to T*, for rows
+// whose chunks the last histogram pass could not tally (ovf: a chunk with
+// more keys of T*'s upper 21 bits than its digit slots, as with many ties).
+// Other rows leave at once.
 // ---------------------------------------------------------------------------
 template <bool ROWS>
 __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict__ r, Dev D) {
   __shared__ uint32_t scr[kChunkThreads / kWave + 3];
   __shared__ uint32_t s_sum[2 * (kChunkThreads / kWave)];
   const uint32_t p = ROWS ? D.pass_row[blockIdx.x] : blockIdx.y;  // per-layer call: 1D grid
+  if (D.state[p].ovf == 0u) return;
   const Row R = row_of<ROWS>(D, p);
   if (R.k == 0) return;
   const uint64_t bx = ROWS ? blockIdx.x - R.pass0 : blockIdx.x;
@@ -960,10 +1001,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
   load(bx, v);  // in flight while the digits are decided
   uint32_t T, m;
   bins.decide(R.k, 3, scr, T, m);
-  if (bx == 0 && threadIdx.x == 0) {
-    D.state[p].T = T;
-    D.state[p].m = m;
-  }
   for (uint64_t c = bx; c < nchunks; c += nbx) {
     float nv[kChunkIt];
     load(c + nbx, nv);  // the block's next chunk, in flight during this one
@@ -987,7 +1024,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// scan: tie quota in index order, then each chunk's output offset.
+// scan: T* and its tie quota m from the three radix levels, each chunk's
+// counts above and equal to T* (finished from the last histogram pass's
+// tallies with T*'s last digit, or the count pass's where the row
+// overflowed its digit slots), then the tie quota in index order and each
+// chunk's output offset.
 // ---------------------------------------------------------------------------
 template <bool ROWS>
 __global__ __launch_bounds__(1024) void k_scan(Dev D) {
@@ -995,7 +1036,16 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
   const uint32_t p = blockIdx.x;
   const Row R = row_of<ROWS>(D, p);
   if (R.k == 0) return;
-  const uint32_t m = D.state[p].m;
+  DigitBins<1024> bins;
+  bins.load(D, p, 3);
+  uint32_t T, m;
+  bins.decide(R.k, 3, scr, T, m);
+  if (threadIdx.x == 0) {
+    D.state[p].T = T;
+    D.state[p].m = m;
+  }
+  const uint32_t d3 = T & 1023u;
+  const bool tallied = D.state[p].ovf == 0u;
   const bool rescan = D.state[p].mode != 0u;
   const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
@@ -1003,8 +1053,25 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
   for (uint64_t c0 = 0; c0 < nchunks; c0 += 1024) {
     const uint64_t c = c0 + threadIdx.x;
     const bool in = c < nchunks;
-    const uint32_t gt = in ? D.cgt[R.chunk0 + c] : 0u;
-    const uint32_t eq = in ? D.ceq[R.chunk0 + c] : 0u;
+    uint32_t gt = in ? D.cgt[R.chunk0 + c] : 0u;
+    uint32_t eq = in ? D.ceq[R.chunk0 + c] : 0u;
+    if (in && tallied) {  // keys of T*'s upper bits: above T* by their last digit, or equal
+      static_assert(kDigCap == 16, "two 16-byte loads of digits per chunk");
+      const uint4* dg = reinterpret_cast<const uint4*>(D.cdig + (R.chunk0 + c) * kDigCap);
+      const uint4 a = dg[0], b = dg[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t g2 = 0u, e2 = 0u;
+#pragma unroll
+      for (int i = 0; i < kDigCap; ++i) {
+        const uint32_t dgt = (w[i / 2] >> (16 * (i % 2))) & 0xFFFFu;
+        const bool valid = (uint32_t)i < eq;
+        g2 += (valid && dgt > d3) ? 1u : 0u;
+        e2 += (valid && dgt == d3) ? 1u : 0u;
+      }
+      gt += g2;
+      eq = e2;
+      D.ceq[R.chunk0 + c] = eq;  // the emit's tie test reads the final count
+    }
     uint32_t tot;
     const uint32_t eq_off = eq_carry + block_exclusive_scan<1024>(eq, scr, tot);
     eq_carry += tot;
@@ -1525,6 +1592,7 @@ Dev make_dev(const Layout& L, char* w, uint32_t P) {
   D.ceq = reinterpret_cast<uint32_t*>(w + L.ceq);
   D.ceqoff = reinterpret_cast<uint32_t*>(w + L.ceqoff);
   D.cout = reinterpret_cast<uint32_t*>(w + L.cout);
+  D.cdig = reinterpret_cast<uint16_t*>(w + L.cdig);
   D.rows = nullptr;
   D.tile_row = nullptr;
   return D;

@@ -287,3 +287,17 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
         assert torch.equal(plain.out_val[:n].view(torch.int32), other.out_val[:n].view(torch.int32))
         if not dense:
             assert torch.equal(plain.out_idx[:K], other.out_idx[:K])
+
+
+@pytest.mark.parametrize("scale", [64.0, 1 << 16])
+def test_topk_ties_around_the_threshold_on_the_candidate_path(dev, scale):
+    """Values on a grid of 1/scale: at 1/64 every chunk of candidates holds
+    far more keys sharing T*'s upper 21 bits than the 16 last-digit slots
+    the last histogram pass keeps (the count pass then counts the row's
+    chunks), at 2^-16 only a few (the scan finishes the counts from the
+    slots). Both against the oracle, on the candidate path."""
+    rng = np.random.default_rng(int(scale))
+    P, N, k = 3, 1 << 20, 10486
+    g = (np.round(rng.standard_normal((P, N)) * scale) / scale).astype(np.float32)
+    r = np.zeros_like(g)
+    _check(g, r, k, dev)
