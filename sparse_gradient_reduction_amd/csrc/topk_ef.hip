@@ -84,7 +84,8 @@ constexpr int kSmallSample = kSmallPredictThreads * kPredictKeys;  // 16384
 constexpr int kLayerPredictThreads = 512;
 constexpr int kLayerSampleChunks = kLayerPredictThreads * kPredictKeys / kSampleChunk;  // 512
 constexpr int kH0 = 2048, kH1 = 1024, kH2 = 1024;         // radix digits: 11 + 10 + 10 bits
-constexpr int kDigCap = 16;  // last-digit slots per chunk for the keys that share T*'s upper 21 bits
+constexpr int kDigCap = 32;  // last-digit slots per chunk for the keys that share T*'s upper 21 bits
+constexpr uint32_t kEqCounted = 1u << 31;  // ceq word: the count pass counted this chunk (past its digit slots)
 // Whole-node call: the gather also counts the second digit of the keys whose
 // first digit is one of kSpecBins bins around the prediction `mid`'s; when
 // T*'s first digit is among them, that count is the second radix level and
@@ -853,8 +854,9 @@ struct DigitBins {
 // sharing them, and the last digits of the first kDigCap of those in
 // cdig[c]. Once the level's histogram gives the last digit, the scan turns
 // these into the chunk's counts above and equal to T*, so no pass over the
-// keys is needed for them; a chunk with more such keys than slots (ties)
-// sets the row's ovf and the count pass counts that row's chunks itself.
+// keys is needed for them; a chunk with more such keys than slots (ties, or
+// the crowding of error-feedback residuals just under T*) sets the row's
+// ovf, and the count pass counts that chunk's keys itself.
 // ---------------------------------------------------------------------------
 template <int LEVEL, bool ROWS>
 __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D) {
@@ -966,10 +968,10 @@ __global__ __launch_bounds__(256) void k_hist(const float* __restrict__ r, Dev D
 }
 
 // ---------------------------------------------------------------------------
-// count: per chunk of the source, elements above and equal to T*, for rows
-// whose chunks the last histogram pass could not tally (ovf: a chunk with
-// more keys of T*'s upper 21 bits than its digit slots, as with many ties).
-// Other rows leave at once.
+// count: per chunk of the source, elements above and equal to T*, for the
+// chunks the last histogram pass could not tally (more keys of T*'s upper 21
+// bits than digit slots); the count goes out marked kEqCounted. Rows without
+// such a chunk (ovf clear) leave at once, and the other chunks are skipped.
 // ---------------------------------------------------------------------------
 template <bool ROWS>
 __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict__ r, Dev D) {
@@ -1004,6 +1006,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
   for (uint64_t c = bx; c < nchunks; c += nbx) {
     float nv[kChunkIt];
     load(c + nbx, nv);  // the block's next chunk, in flight during this one
+    if (D.ceq[R.chunk0 + c] <= (uint32_t)kDigCap) {  // tallied (block-uniform)
+#pragma unroll
+      for (int it = 0; it < kChunkIt; ++it) v[it] = nv[it];
+      continue;
+    }
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int it = 0; it < kChunkIt; ++it) {
@@ -1014,9 +1021,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_count(const float* __restrict
     }
     uint32_t tgt, teq;
     block_sum2<kChunkThreads>(gt, eq, s_sum, tgt, teq);
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0) {  // block_sum2's barriers follow every thread's read of the tally
       D.cgt[R.chunk0 + c] = tgt;
-      D.ceq[R.chunk0 + c] = teq;
+      D.ceq[R.chunk0 + c] = teq | kEqCounted;
     }
 #pragma unroll
     for (int it = 0; it < kChunkIt; ++it) v[it] = nv[it];
@@ -1045,7 +1052,6 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
     D.state[p].m = m;
   }
   const uint32_t d3 = T & 1023u;
-  const bool tallied = D.state[p].ovf == 0u;
   const bool rescan = D.state[p].mode != 0u;
   const uint64_t n = source_len(D, R, p, rescan);
   const uint64_t nchunks = (n + kChunk - 1) / kChunk;
@@ -1055,11 +1061,18 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
     const bool in = c < nchunks;
     uint32_t gt = in ? D.cgt[R.chunk0 + c] : 0u;
     uint32_t eq = in ? D.ceq[R.chunk0 + c] : 0u;
-    if (in && tallied) {  // keys of T*'s upper bits: above T* by their last digit, or equal
-      static_assert(kDigCap == 16, "two 16-byte loads of digits per chunk");
+    if (in && (eq & kEqCounted) == 0u) {  // keys of T*'s upper bits: above T* by their last digit, or equal
+      static_assert(kDigCap % 8 == 0, "16-byte loads of digits");
       const uint4* dg = reinterpret_cast<const uint4*>(D.cdig + (R.chunk0 + c) * kDigCap);
-      const uint4 a = dg[0], b = dg[1];
-      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t w[kDigCap / 2];
+#pragma unroll
+      for (int q = 0; q < kDigCap / 8; ++q) {
+        const uint4 a = dg[q];
+        w[4 * q] = a.x;
+        w[4 * q + 1] = a.y;
+        w[4 * q + 2] = a.z;
+        w[4 * q + 3] = a.w;
+      }
       uint32_t g2 = 0u, e2 = 0u;
 #pragma unroll
       for (int i = 0; i < kDigCap; ++i) {
@@ -1070,8 +1083,9 @@ __global__ __launch_bounds__(1024) void k_scan(Dev D) {
       }
       gt += g2;
       eq = e2;
-      D.ceq[R.chunk0 + c] = eq;  // the emit's tie test reads the final count
     }
+    eq &= ~kEqCounted;
+    if (in) D.ceq[R.chunk0 + c] = eq;  // the emit's tie test reads the final count
     uint32_t tot;
     const uint32_t eq_off = eq_carry + block_exclusive_scan<1024>(eq, scr, tot);
     eq_carry += tot;

@@ -292,12 +292,33 @@ def test_topk_wideresnet_full_size_two_ef_steps(dev):
 @pytest.mark.parametrize("scale", [64.0, 1 << 16])
 def test_topk_ties_around_the_threshold_on_the_candidate_path(dev, scale):
     """Values on a grid of 1/scale: at 1/64 every chunk of candidates holds
-    far more keys sharing T*'s upper 21 bits than the 16 last-digit slots
-    the last histogram pass keeps (the count pass then counts the row's
-    chunks), at 2^-16 only a few (the scan finishes the counts from the
-    slots). Both against the oracle, on the candidate path."""
+    far more keys sharing T*'s upper 21 bits than the 32 last-digit slots
+    the last histogram pass keeps (the count pass then counts those chunks),
+    at 2^-16 only a few (the scan finishes the counts from the slots). Both
+    against the oracle, on the candidate path."""
     rng = np.random.default_rng(int(scale))
     P, N, k = 3, 1 << 20, 10486
     g = (np.round(rng.standard_normal((P, N)) * scale) / scale).astype(np.float32)
     r = np.zeros_like(g)
+    _check(g, r, k, dev)
+
+
+def test_topk_some_chunks_past_their_digit_slots(dev):
+    """Ties at T* = 1.0 clustered in one stretch of a node (one chunk of
+    candidates holds thousands of them, the others none), spread thinly over
+    another node (every chunk within its digit slots), and both at once on a
+    third: the count pass counts only the crowded chunks and the scan
+    finishes the rest from their slots, against the oracle."""
+    rng = np.random.default_rng(29)
+    P, N, k = 3, 1 << 20, 10486
+    g = (rng.uniform(-0.9, 0.9, size=(P, N))).astype(np.float32)
+    for p in range(P):
+        g[p, rng.choice(N, 10000, replace=False)] = 2.0  # above T*
+    g[0, 500000:503000] = 1.0
+    g[1, np.arange(600) * 1747 + 11] = 1.0
+    g[2, 200000:201000] = -1.0
+    g[2, 700000:701000] = 1.0
+    g[2, np.arange(300) * 3001 + 5] = 1.0
+    r = np.zeros_like(g)
+    print("topk ties clustered and spread at T*", flush=True)
     _check(g, r, k, dev)
