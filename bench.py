@@ -137,7 +137,7 @@ class HipEvents:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the P node contributions live in one "
+        print(json.dumps({"error": "the library runs on one GPU only: the P node contributions live in one "
                                    "GPU's HBM and no collective between GPUs is part of it; run with --gpus 1"}))
         sys.exit(2)
 
