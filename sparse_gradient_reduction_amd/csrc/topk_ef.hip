@@ -1243,9 +1243,9 @@ __global__ __launch_bounds__(kChunk / IT) void k_emit(float* __restrict__ r, uin
           __builtin_nontemporal_store(e[it] + R.idx_off, &oi[pos]);
           __builtin_nontemporal_store(v[it], &ov[pos]);
         }
-        if (rescan || !high) r[pN + e[it]] = 0.0f;
+        if (rescan || !high) __builtin_nontemporal_store(0.0f, &r[pN + e[it]]);
       } else if (!rescan && high) {
-        r[pN + e[it]] = v[it];  // zeroed on the guess but not selected: restore
+        __builtin_nontemporal_store(v[it], &r[pN + e[it]]);  // zeroed on the guess but not selected: restore
       }
     }
     if constexpr (RUNS) {
